@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the output-centric MoE decode layer on one MI355X.
+
+One step = one MoE decode layer (gate/up kernel + down kernel) over one batch
+of synthetic input. Default workload: B=1 token, E=128 experts, top-8,
+H=2048, I=768, MXFP8 weights (the single-token wide-MoE decode layer).
+
+Weights must come from HBM, not from the 256 MB Infinity Cache: the timed run
+cycles through R identical copies of the layer's weights at distinct HBM
+addresses (like consecutive layers of a model), so any one copy's bytes are
+touched again only after R-1 other layers' worth of traffic (R * 39 MB >> the
+cache). The K steps are captured once in a HIP graph and replayed, so the
+time is the GPU's, not the Python launch loop's.
+
+Prints ONE JSON line. value = achieved GB/s over the unique routed-weight
+bytes (codes + scales of every distinct routed expert) per layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak, AMD specification
+METRIC = "µs/MoE layer + achieved HBM GB/s (routed weight bytes) vs peak, B=1..64"
+DEFAULT_WORKLOAD = "wide_B1_E128_k8_H2048_I768"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "output_centric_expert_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    p = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--copies", type=int, default=32, help="distinct HBM copies of the layer weights")
+    ap.add_argument("--tune", default=None, help="launch-shape override (moed_set_tuning spec)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and "
+              "there is no multi-GPU path in this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from output_centric_expert_amd import moedecode as md
+    from output_centric_expert_amd import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    md.load()
+    if args.tune:
+        md.moed_set_tuning(args.tune)
+
+    shape = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    L = synth.make_layer(shape, device="cuda")
+    x, ids, w = md.layer_device_inputs(L)
+    R = max(1, args.copies)
+    copies = [(L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
+    for _ in range(R - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s: {shape}, {R} weight copies")
+
+    B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
+    out = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((B, k, I), dtype=torch.float32, device="cuda")
+    ws = a.view(torch.uint8).view(-1)
+
+    def layer(r):
+        wg_q, wg_s, wu_q, wu_s, wd_q, wd_s = copies[r % R]
+        md.moe_decode(x, ids, w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=out, workspace=ws)
+
+    def gate_up(r):
+        wg_q, wg_s, wu_q, wu_s, _, _ = copies[r % R]
+        md.moe_decode_gate_up(x, ids, wg_q, wg_s, wu_q, wu_s, a=a)
+
+    def down(r):
+        _, _, _, _, wd_q, wd_s = copies[r % R]
+        md.moe_decode_down(a, ids, w, wd_q, wd_s, out=out)
+
+    K, W = args.steps, args.warmup
+    for r in range(W):                       # untimed warm-up steps
+        layer(r)
+    torch.cuda.synchronize()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(n):
+                fn(r)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, n, reps=1):
+        """ms per step of graph g (n steps), median over reps replays."""
+        res = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / n)
+        return float(np.median(res))
+
+    g_layer = capture(layer, K)
+    g_layer.replay()                         # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+
+    # ---- the timed region: exactly K steps ----
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    g_layer.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / K
+    # -------------------------------------------
+
+    # per-kernel average launch durations (same stream, same graph mechanism)
+    g_gu = capture(gate_up, K)
+    g_dn = capture(down, K)
+    g_gu.replay(); g_dn.replay()
+    torch.cuda.synchronize()
+    ms_gu = time_graph(g_gu, K, reps=3)
+    ms_dn = time_graph(g_dn, K, reps=3)
+    ms_layer_rep = time_graph(g_layer, K, reps=3)
+
+    # eager (one C-ABI call per step from Python) for reference
+    e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(); e0.record()
+    for r in range(K):
+        layer(r)
+    e1.record(); torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / K
+
+    U = L.unique_experts
+    uniq = L.unique_weight_bytes
+    gu_bytes = U * 2 * I * H * 33 // 32
+    dn_bytes = U * H * I * 33 // 32
+    gbs = uniq / (ms_per_step * 1e-3) / 1e9
+    gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
+    dn_gbs = dn_bytes / (ms_dn * 1e-3) / 1e9
+
+    traffic = load_traffic("gate_up", args.workload)
+    roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
+                "avg_launch_us": round(ms_gu * 1e3, 3)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(L, uniq, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights encoded to MXFP8, softmax top-k routing)",
+        "config": {"workload": args.workload, "B": B, "E": E, "k": k, "H": H, "I": I,
+                   "weights": "mxfp8 (e4m3 + ue8m0 per 32)", "activations": "bf16", "out": "bf16",
+                   "unique_experts": U, "unique_weight_bytes": uniq, "weight_copies": R,
+                   "timing": "HIP graph of K layers, HIP events on the launch stream"},
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
+        "us_gate_up": round(ms_gu * 1e3, 3),
+        "us_down": round(ms_dn * 1e3, 3),
+        "gbs_gate_up": round(gu_gbs, 1),
+        "gbs_down": round(dn_gbs, 1),
+        "us_per_layer_median3": round(ms_layer_rep * 1e3, 3),
+        "us_per_layer_eager": round(ms_eager * 1e3, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "tuning": args.tune or "built-in",
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(L, uniq, seconds):
+    """The float64 oracle, as it stands, on full layers of the same workload (host cores)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    oracle.build(force=False)
+    sel = sorted(set(int(e) for e in L.ids.ravel()))
+    remap = {e: n for n, e in enumerate(sel)}
+    ids_c = np.vectorize(remap.get)(L.ids).astype(np.int32)
+    idx = torch.tensor(sel, device=L.wg_q.device)
+    host = [t.index_select(0, idx).cpu() for t in (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
+    nthreads = min(os.cpu_count() or 1, 16)
+    used = oracle.threads(nthreads)
+    oracle.moe_decode(L.x, ids_c, L.w, *host, nthreads=nthreads)          # warm-up
+    n, t = 0, 0.0
+    while t < seconds or n < 3:
+        t0 = time.perf_counter()
+        oracle.moe_decode(L.x, ids_c, L.w, *host, nthreads=nthreads)
+        t += time.perf_counter() - t0
+        n += 1
+    per = t / n
+    return {"value": round(uniq / per / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"{n} full layers of the same workload (all B*H outputs; touched experts copied to host)",
+            "s_per_layer": round(per, 6)}
+
+
+if __name__ == "__main__":
+    main()

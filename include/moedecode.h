@@ -1,0 +1,156 @@
+/*
+ * libmoedecode -- output-centric MoE decode expert layer for MI355X (gfx950).
+ *
+ * The layer is the routed SwiGLU expert block of a mixture-of-experts model at
+ * decode time, computed the way the warp-decode post describes it
+ * (cursor.com/blog/warp-decode, sections "What changed" and "How the two
+ * kernels work"): parallelism is organised around OUTPUTS, not experts.
+ *
+ *   gate/up kernel: one 64-lane wavefront owns one intermediate neuron i of one
+ *     (token b, routed slot j) pair. It reads the routed expert id e, streams
+ *     the MXFP8 gate and up rows Wg[e][i][:] and Wu[e][i][:], decodes them in
+ *     registers, dots both against x[b][:] (read once for both projections),
+ *     reduces across lanes and writes one value  a[b][j][i] = SiLU(g) * u.
+ *   down kernel: one wavefront owns one output out[b][h]. It loops over the k
+ *     routed experts, streams Wd[e_j][h][:] against a[b][j][:], and folds each
+ *     routing weight w[b][j] into a single FP32 accumulator before one store.
+ *
+ * There are no gather, pad or scatter buffers and no per-expert output buffer
+ * ("Buffer removal" section); the only intermediate is a[B][k][I].
+ *
+ * Weight format (MXFP8): codes are OCP FP8 E4M3 (bias 7, NaN = 0x7F/0xFF, no
+ * infinities); every 32 consecutive codes along the reduction axis share one
+ * UE8M0 scale byte, value 2^(s-127) (0xFF = NaN) -- the "FP8 E4M3 with a UE8M0
+ * scale per 32 K values" block format of the GC-MoE summary (onedev.kr/papers/
+ * 1690, section "How to use"). Decoded weight = E4M3(code) * 2^(scale-127).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    memory) on the current device, C-contiguous, no strides. The caller owns
+ *    every buffer; the library allocates nothing on these paths.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise. They are stateless and thread-safe;
+ *    concurrent calls need distinct workspaces/outputs.
+ *  - Argument errors are reported before anything is launched. A launch
+ *    failure returns MOED_ERR_HIP; moed_last_hip_error() gives the raw code.
+ *  - Expert ids outside [0, E) are not an error: every output of the affected
+ *    token becomes NaN (no out-of-bounds read is made). NaN codes or scales
+ *    in the weights propagate as NaN.
+ *  - Duplicate ids within a token's row are legal and their terms add; the
+ *    routing weights need not sum to 1.
+ *  - Results are deterministic run to run (fixed reduction order).
+ */
+#ifndef MOEDECODE_H
+#define MOEDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOED_OK = 0,
+    MOED_ERR_NULL = 1,       /* a required pointer is NULL                       */
+    MOED_ERR_SHAPE = 2,      /* B<0, E<1, k<1, k>E, H or I not a positive multiple of 32,
+                                or a size beyond the limits below                */
+    MOED_ERR_DTYPE = 3,      /* unknown moed_dtype                                */
+    MOED_ERR_WORKSPACE = 4,  /* workspace smaller than moed_workspace_bytes()     */
+    MOED_ERR_ALIGN = 5,      /* x, a, workspace or a weight-code base not 16-byte aligned */
+    MOED_ERR_HIP = 6         /* a HIP launch failed; see moed_last_hip_error()    */
+} moed_status;
+
+typedef enum {
+    MOED_BF16 = 0,           /* bfloat16, round-to-nearest-even on store          */
+    MOED_F32 = 1             /* IEEE float32                                      */
+} moed_dtype;
+
+/* Size limits (checked): B*k*I and B*H below 2^31, k*I/16 below 2^22. */
+
+/*
+ * Bytes of workspace moe_decode() needs for the intermediate a[B][k][I]:
+ * B*k*I*4 for inter_dtype MOED_F32 (the accuracy-gated path), *2 for
+ * MOED_BF16. Returns 0 for invalid arguments.
+ */
+size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype);
+
+/*
+ * The whole layer (steps gate/up then down on `stream`).
+ *   x         [B][H]  bfloat16 activations
+ *   topk_ids  [B][k]  int32 routed expert ids
+ *   topk_w    [B][k]  float32 routing weights (folded in the down kernel)
+ *   wg_q/wu_q [E][I][H] uint8 E4M3 codes of the gate / up projections, K = H
+ *   wg_s/wu_s [E][I][H/32] uint8 UE8M0 scales
+ *   wd_q      [E][H][I] uint8 E4M3 codes of the down projection, K = I
+ *   wd_s      [E][H][I/32] uint8 UE8M0 scales
+ *   out       [B][H]  out_dtype
+ *   workspace >= moed_workspace_bytes(B, k, I, inter_dtype) bytes, 16-aligned
+ * B = 0 is valid and launches nothing.
+ */
+int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
+               const uint8_t *wg_q, const uint8_t *wg_s,
+               const uint8_t *wu_q, const uint8_t *wu_s,
+               const uint8_t *wd_q, const uint8_t *wd_s,
+               void *out, int out_dtype, int inter_dtype,
+               int B, int E, int k, int H, int I,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gate/up step alone: a[b][j][i] = SiLU(Wg^[e]·x[b])_i * (Wu^[e]·x[b])_i with
+ * e = topk_ids[b][j], stored as inter_dtype into `a` (B*k*I elements).
+ * SiLU(t) = t / (1 + exp(-t)).  (Warp-decode post, "How the two kernels work",
+ * first two paragraphs.)
+ *
+ * Layout of `a` (the same buffer moe_decode() keeps in its workspace): row
+ * bj = b*k + j is chunk-interleaved so the down kernel's loads are contiguous
+ * across a wavefront. With o = i/16 and cpr = I/16:
+ *   MOED_F32:  element index ((bj*4 + (i/4)%4) * cpr + o) * 4 + i%4
+ *   MOED_BF16: element index ((bj*2 + (i/8)%2) * cpr + o) * 8 + i%8
+ */
+int moe_decode_gate_up(const void *x, const int32_t *topk_ids,
+                       const uint8_t *wg_q, const uint8_t *wg_s,
+                       const uint8_t *wu_q, const uint8_t *wu_s,
+                       void *a, int inter_dtype,
+                       int B, int E, int k, int H, int I, void *stream);
+
+/*
+ * Down step alone: out[b][h] = sum_j topk_w[b][j] * (Wd^[e_j]·a[b][j])_h,
+ * one FP32 accumulator per output, one store. `a` is in the layout
+ * moe_decode_gate_up() writes. (Warp-decode post, "How the two kernels work",
+ * third and fourth paragraphs.)
+ */
+int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
+                    const float *topk_w, const uint8_t *wd_q, const uint8_t *wd_s,
+                    void *out, int out_dtype,
+                    int B, int E, int k, int H, int I, void *stream);
+
+/*
+ * Diagnostic: decode n MXFP8 values with the kernels' own in-register decoder.
+ * out[t] = E4M3(codes[t]) * 2^(scales[t]-127) as float32, through both decode
+ * routes the kernels use (path 0: FP8 -> FP32 conversion; path 1: FP8 -> BF16
+ * conversion), so a test can compare every code bit for bit with the format
+ * definition. Device pointers; n >= 0.
+ */
+int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out,
+                         int n, int path, void *stream);
+
+/* Human-readable name of a moed_status value. Never NULL. */
+const char *moed_status_string(int status);
+
+/* Raw hipError_t of the last MOED_ERR_HIP returned on this thread (0 if none). */
+int moed_last_hip_error(void);
+
+/*
+ * Benchmark-only tuning override (NOT thread-safe; meant for launch-shape
+ * sweeps). `spec` is a comma-separated list of key=value pairs, e.g.
+ * "gu_wpb=4,dn_wpb=2,gu_dot=1,nt=0"; NULL or "" restores the built-in table.
+ * Returns MOED_OK, or MOED_ERR_SHAPE for an unknown key or value.
+ */
+int moed_set_tuning(const char *spec);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDECODE_H */

@@ -1,0 +1,287 @@
+// Down kernel: one wavefront per output out[b][h] -- the second warp-decode
+// kernel (warp-decode post, "How the two kernels work", third and fourth
+// paragraphs), laid out for 64-lane CDNA4 wavefronts.
+//
+// Wave w owns (b, h) with w = b*H + h. It loops over the k routed slots of
+// token b; the slot, its expert id e_j and routing weight w[b][j] are uniform
+// across the wavefront (scalar loads into SGPRs), so each row's address is a
+// scalar base plus a per-lane offset and no load waits on another load.
+// The intermediate a is read in the chunk-interleaved order the gate/up
+// kernel writes (inter_index), so each 16-byte load is contiguous across
+// the wavefront.
+// Row Wd[e_j][h][:] (I codes) is split into 16-code chunks, chunk o going to
+// lane o % 64; JB slots x CPL chunks per lane are loaded (weights, the block
+// scale byte and the 16 matching values of a[b][j][:]) before the first
+// arithmetic. Each lane multiplies its chunk's partial dot by the block scale
+// and the routing weight and adds it into a single FP32 accumulator; after
+// all experts one DPP/ds_swizzle reduction and one scalar store (bf16
+// round-to-nearest-even, or f32) finish the output.
+#include "launch.h"
+#include "mx_device.h"
+
+namespace moed {
+
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT>
+__global__ void __launch_bounds__(256)
+moe_down_kernel(DownArgs p)
+{
+    constexpr int NA = A_BF16 ? 2 : 4;            // 16-byte pieces of a per chunk
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (int)(threadIdx.x / kWave));
+    const int n_out = p.B * p.H;
+    if (wave >= n_out)
+        return;
+    const int b = wave / p.H;
+    const int h = wave % p.H;
+    const int k = p.k;
+    const int I = p.I;
+    const int cpr = I / 16;                       // chunks per routed row
+    const int* ids = p.ids + (size_t)b * k;
+    const float* wts = p.w + (size_t)b * k;
+
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += JB) {
+        int e[JB];
+        float wt[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            const int jc = j < k ? j : k - 1;     // in-bounds even if the load is speculated
+            e[jj] = j < k ? ids[jc] : -1;
+            wt[jj] = j < k ? wts[jc] : 0.0f;
+        }
+        for (int o0 = 0; o0 < cpr; o0 += kWave * CPL) {
+            u32x4 wq[JB][CPL];
+            uint32_t ws[JB][CPL];
+            u32x4 av[JB][CPL][NA];
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                const int j = j0 + jj;
+                const bool live = j < k;
+                const bool ok = (unsigned)e[jj] < (unsigned)p.E;
+                const size_t row = (size_t)(ok ? e[jj] : 0) * (size_t)p.H + (size_t)h;
+                const uint8_t* wrow = p.wd_q + row * (size_t)I;
+                const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
+                // row bj of the chunk-interleaved intermediate: piece t of chunk o
+                // is at (bj * NA + t) * cpr + o, in 16-byte units
+                const size_t arow = ((size_t)b * k + (size_t)(live ? j : 0)) * (size_t)NA * (size_t)cpr;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int o = o0 + lane + kWave * cc;
+                    if (live && o < cpr) {
+                        if (ok) {
+                            wq[jj][cc] = ld<NT>(reinterpret_cast<const u32x4*>(wrow) + o);
+                            ws[jj][cc] = srow[o >> 1];
+                        } else {                  // invalid routing: NaN scale, no weight read
+                            wq[jj][cc] = u32x4{0, 0, 0, 0};
+                            ws[jj][cc] = 255u;
+                        }
+                        const u32x4* ap = static_cast<const u32x4*>(p.a) + arow + (size_t)o;
+#pragma unroll
+                        for (int t = 0; t < NA; ++t)
+                            av[jj][cc][t] = ap[(size_t)t * cpr];
+                    } else {
+                        wq[jj][cc] = u32x4{0, 0, 0, 0};
+                        ws[jj][cc] = 127u;
+#pragma unroll
+                        for (int t = 0; t < NA; ++t)
+                            av[jj][cc][t] = u32x4{0, 0, 0, 0};
+                    }
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    float part = 0.0f;
+                    if constexpr (A_BF16) {
+                        part = dot4_bf16(wq[jj][cc].x, av[jj][cc][0].x, av[jj][cc][0].y, part);
+                        part = dot4_bf16(wq[jj][cc].y, av[jj][cc][0].z, av[jj][cc][0].w, part);
+                        part = dot4_bf16(wq[jj][cc].z, av[jj][cc][1].x, av[jj][cc][1].y, part);
+                        part = dot4_bf16(wq[jj][cc].w, av[jj][cc][1].z, av[jj][cc][1].w, part);
+                    } else {
+                        part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[jj][cc][0]), part);
+                        part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[jj][cc][1]), part);
+                        part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[jj][cc][2]), part);
+                        part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[jj][cc][3]), part);
+                    }
+                    // fold the routing weight into the one accumulator
+                    acc = __builtin_fmaf(wt[jj], part * ue8m0_to_f32(ws[jj][cc]), acc);
+                }
+            }
+        }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(p.out)[wave] = f32_to_bf16_rne(acc);
+        else
+            static_cast<float*>(p.out)[wave] = acc;
+    }
+}
+
+// LDS-staged variant (used when a[b] fits in LDS): the waves of a workgroup
+// all serve the same token b, so a[b][:][:] is copied once per workgroup
+// into LDS and every wave reads its chunks from there instead of from L2.
+// Still one wavefront per output. The first slot group's weight loads are
+// issued before the copy, so the HBM latency of the weights overlaps the
+// L2 latency of the copy; the copy keeps the chunk-interleaved order, so the
+// per-chunk LDS reads are contiguous across lanes (no bank conflicts).
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT>
+__global__ void __launch_bounds__(1024)
+moe_down_staged_kernel(DownArgs p)
+{
+    extern __shared__ u32x4 a_lds[];
+    constexpr int NA = A_BF16 ? 2 : 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int nblk_h = (p.H + wpb - 1) / wpb;
+    const int b = blockIdx.x / nblk_h;
+    const int h = (blockIdx.x % nblk_h) * wpb + (int)(threadIdx.x / kWave);
+    const bool active = h < p.H;                  // idle waves still help copy a[b]
+    const int k = p.k;
+    const int I = p.I;
+    const int cpr = I / 16;
+    const int nunits = k * NA * cpr;              // 16-byte units of a[b]
+    const int* ids = p.ids + (size_t)b * k;
+    const float* wts = p.w + (size_t)b * k;
+
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += JB) {
+        int e[JB];
+        float wt[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            const int jc = j < k ? j : k - 1;
+            e[jj] = j < k ? ids[jc] : -1;
+            wt[jj] = j < k ? wts[jc] : 0.0f;
+        }
+        for (int o0 = 0; o0 < cpr; o0 += kWave * CPL) {
+            u32x4 wq[JB][CPL];
+            uint32_t ws[JB][CPL];
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                const bool live = active && (j0 + jj) < k;
+                const bool ok = (unsigned)e[jj] < (unsigned)p.E;
+                const size_t row = (size_t)(ok ? e[jj] : 0) * (size_t)p.H + (size_t)(active ? h : 0);
+                const uint8_t* wrow = p.wd_q + row * (size_t)I;
+                const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int o = o0 + lane + kWave * cc;
+                    if (live && ok && o < cpr) {
+                        wq[jj][cc] = ld<NT>(reinterpret_cast<const u32x4*>(wrow) + o);
+                        ws[jj][cc] = srow[o >> 1];
+                    } else {
+                        wq[jj][cc] = u32x4{0, 0, 0, 0};
+                        ws[jj][cc] = (live && !ok) ? 255u : 127u;   // invalid routing -> NaN
+                    }
+                }
+            }
+            if (j0 == 0 && o0 == 0) {             // copy a[b] into LDS once
+                const u32x4* src = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
+#pragma unroll 4
+                for (int u = threadIdx.x; u < nunits; u += blockDim.x)
+                    a_lds[u] = src[u];
+                __syncthreads();
+            }
+            if (!active)
+                return;                           // after the only barrier
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+                const int j = j0 + jj < k ? j0 + jj : 0;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int o = o0 + lane + kWave * cc;
+                    u32x4 av[NA];
+                    const int base = (j * NA) * cpr + (o < cpr ? o : 0);
+#pragma unroll
+                    for (int t = 0; t < NA; ++t)
+                        av[t] = a_lds[base + t * cpr];
+                    float part = 0.0f;
+                    if constexpr (A_BF16) {
+                        part = dot4_bf16(wq[jj][cc].x, av[0].x, av[0].y, part);
+                        part = dot4_bf16(wq[jj][cc].y, av[0].z, av[0].w, part);
+                        part = dot4_bf16(wq[jj][cc].z, av[1].x, av[1].y, part);
+                        part = dot4_bf16(wq[jj][cc].w, av[1].z, av[1].w, part);
+                    } else {
+                        part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[0]), part);
+                        part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[1]), part);
+                        part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[2]), part);
+                        part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[3]), part);
+                    }
+                    acc = __builtin_fmaf(wt[jj], part * ue8m0_to_f32(ws[jj][cc]), acc);
+                }
+            }
+        }
+    }
+    if (!active)
+        return;
+    acc = wave_sum(acc);
+    if (lane == 0) {
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h] = f32_to_bf16_rne(acc);
+        else
+            static_cast<float*>(p.out)[(size_t)b * p.H + h] = acc;
+    }
+}
+
+template <int CPL, int JB>
+static hipError_t dispatch_v(bool staged, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p, dim3 grid,
+                             dim3 block, size_t lds, hipStream_t s)
+{
+#define MOED_DN(A, O, N) \
+    if (a_bf16 == A && out_bf16 == O && nt == N) { \
+        if (staged) \
+            hipLaunchKernelGGL((moe_down_staged_kernel<CPL, JB, A, O, N>), grid, block, lds, s, p); \
+        else \
+            hipLaunchKernelGGL((moe_down_kernel<CPL, JB, A, O, N>), grid, block, 0, s, p); \
+    }
+    MOED_DN(false, false, false) MOED_DN(false, false, true) MOED_DN(false, true, false) MOED_DN(false, true, true)
+    MOED_DN(true, false, false) MOED_DN(true, false, true) MOED_DN(true, true, false) MOED_DN(true, true, true)
+#undef MOED_DN
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s)
+{
+    const long n_out = (long)p.B * p.H;
+    if (n_out == 0)
+        return hipSuccess;
+    // chunks per lane per row: the smallest of 1, 2, 4, 8 covering the row
+    // (longer rows take several passes); slots per group so that CPL * JB <= 8
+    const int cpr = p.I / 16;
+    int cpl = 1;
+    while (cpl < 8 && cpl * kWave < cpr)
+        cpl *= 2;
+    int cap = t.dn_umax < 1 ? 1 : t.dn_umax;
+    while (cpl > 1 && cpl > cap)
+        cpl /= 2;
+    // a[b] staged in LDS when it fits in 64 KiB
+    const size_t lds = (size_t)p.k * (size_t)p.I * (a_bf16 ? 2u : 4u);
+    const bool staged = t.dn_stage != 0 && lds <= 65536;
+    const int wpb = staged ? t.dn_wpb : (t.dn_wpb > 4 ? 4 : t.dn_wpb);
+    const dim3 block(wpb * kWave);
+    const dim3 grid(staged ? (unsigned)((long)p.B * ((p.H + wpb - 1) / wpb)) : (unsigned)((n_out + wpb - 1) / wpb));
+    const bool nt = t.nt != 0;
+    int jb = 8 / cpl;
+    while (jb > 1 && cpl * jb > cap)
+        jb /= 2;
+    switch (cpl * 16 + jb) {
+    case 1 * 16 + 8: return dispatch_v<1, 8>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 16 + 4: return dispatch_v<1, 4>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 16 + 2: return dispatch_v<1, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 16 + 1: return dispatch_v<1, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 2 * 16 + 4: return dispatch_v<2, 4>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 2 * 16 + 2: return dispatch_v<2, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 2 * 16 + 1: return dispatch_v<2, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 4 * 16 + 2: return dispatch_v<4, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 4 * 16 + 1: return dispatch_v<4, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 8 * 16 + 1: return dispatch_v<8, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moed

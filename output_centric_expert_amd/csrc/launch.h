@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moed {
+
+// Launch-shape knobs. The defaults are the built-in choice; moed_set_tuning()
+// can override them for sweeps.
+struct Tuning {
+    int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
+    int dn_wpb = 8;     // down: wavefronts per workgroup (1..16; at most 4 unstaged)
+    int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
+    int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
+    int nt = 1;         // 1 = non-temporal (streaming) weight loads
+    int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
+    int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
+};
+
+struct GateUpArgs {
+    const uint16_t* x;      // [B][H] bf16
+    const int32_t* ids;     // [B][k]
+    const uint8_t* wg_q;    // [E][I][H]
+    const uint8_t* wg_s;    // [E][I][H/32]
+    const uint8_t* wu_q;
+    const uint8_t* wu_s;
+    void* a;                // [B][k][I] f32 or bf16
+    int B, E, k, H, I;
+};
+
+struct DownArgs {
+    const void* a;          // [B][k][I] f32 or bf16
+    const int32_t* ids;     // [B][k]
+    const float* w;         // [B][k]
+    const uint8_t* wd_q;    // [E][H][I]
+    const uint8_t* wd_s;    // [E][H][I/32]
+    void* out;              // [B][H] f32 or bf16
+    int B, E, k, H, I;
+    float inv_cpr;          // 1 / (I/16), for the chunk -> (slot, offset) split
+};
+
+hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
+hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
+hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
+                                  int path, hipStream_t s);
+
+}  // namespace moed

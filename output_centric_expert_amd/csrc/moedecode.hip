@@ -1,0 +1,215 @@
+// C ABI of libmoedecode: argument checks, launch-shape choice, two launches.
+// Everything here runs on the host; all arithmetic of the layer runs in the
+// kernels of gate_up.hip and down.hip.
+#include <stdlib.h>
+#include <string.h>
+
+#include "moedecode.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+moed::Tuning g_tuning;          // built-in table unless moed_set_tuning() overrode it
+bool g_tuning_overridden = false;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline bool dtype_ok(int d) { return d == MOED_BF16 || d == MOED_F32; }
+
+int check_shape(int B, int E, int k, int H, int I)
+{
+    if (B < 0 || E < 1 || k < 1 || k > E)
+        return MOED_ERR_SHAPE;
+    if (H < 32 || I < 32 || (H % 32) != 0 || (I % 32) != 0)
+        return MOED_ERR_SHAPE;
+    const long long BK_I = (long long)B * k * I, B_H = (long long)B * H;
+    if (BK_I >= (1LL << 31) || B_H >= (1LL << 31) || (long long)k * (I / 16) >= (1LL << 22))
+        return MOED_ERR_SHAPE;
+    return MOED_OK;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return MOED_OK;
+    g_last_hip = (int)e;
+    return MOED_ERR_HIP;
+}
+
+// The built-in launch table. Waves per workgroup and the decode route were
+// picked by sweeps on MI355X (see the benchmark's tuning mode).
+moed::Tuning pick(int B, int H, int I)
+{
+    if (g_tuning_overridden)
+        return g_tuning;
+    moed::Tuning t;
+    (void)B; (void)H; (void)I;
+    return t;
+}
+
+moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
+                              const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                              void* a, int B, int E, int k, int H, int I)
+{
+    moed::GateUpArgs p;
+    p.x = static_cast<const uint16_t*>(x);
+    p.ids = ids;
+    p.wg_q = wg_q; p.wg_s = wg_s; p.wu_q = wu_q; p.wu_s = wu_s;
+    p.a = a;
+    p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
+    return p;
+}
+
+moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, const uint8_t* wd_q,
+                         const uint8_t* wd_s, void* out, int B, int E, int k, int H, int I)
+{
+    moed::DownArgs p;
+    p.a = a; p.ids = ids; p.w = w; p.wd_q = wd_q; p.wd_s = wd_s; p.out = out;
+    p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
+    p.inv_cpr = 1.0f / (float)(I / 16);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype)
+{
+    if (B < 0 || k < 1 || I < 1 || !dtype_ok(inter_dtype))
+        return 0;
+    return (size_t)B * (size_t)k * (size_t)I * (inter_dtype == MOED_F32 ? 4u : 2u);
+}
+
+int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg_q,
+                       const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                       void* a, int inter_dtype, int B, int E, int k, int H, int I, void* stream)
+{
+    if (int st = check_shape(B, E, k, H, I))
+        return st;
+    if (!dtype_ok(inter_dtype))
+        return MOED_ERR_DTYPE;
+    if (B == 0)
+        return MOED_OK;
+    if (!x || !topk_ids || !wg_q || !wg_s || !wu_q || !wu_s || !a)
+        return MOED_ERR_NULL;
+    if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(a))
+        return MOED_ERR_ALIGN;
+    const moed::Tuning t = pick(B, H, I);
+    return hip_status(moed::launch_gate_up(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a, B, E, k, H, I),
+                                           inter_dtype == MOED_BF16, t, static_cast<hipStream_t>(stream)));
+}
+
+int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
+                    const uint8_t* wd_q, const uint8_t* wd_s, void* out, int out_dtype,
+                    int B, int E, int k, int H, int I, void* stream)
+{
+    if (int st = check_shape(B, E, k, H, I))
+        return st;
+    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype))
+        return MOED_ERR_DTYPE;
+    if (B == 0)
+        return MOED_OK;
+    if (!a || !topk_ids || !topk_w || !wd_q || !wd_s || !out)
+        return MOED_ERR_NULL;
+    if (!aligned16(a) || !aligned16(wd_q))
+        return MOED_ERR_ALIGN;
+    const moed::Tuning t = pick(B, H, I);
+    return hip_status(moed::launch_down(down_args(a, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I),
+                                        inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
+               const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+               const uint8_t* wd_q, const uint8_t* wd_s, void* out, int out_dtype, int inter_dtype,
+               int B, int E, int k, int H, int I, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (int st = check_shape(B, E, k, H, I))
+        return st;
+    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype))
+        return MOED_ERR_DTYPE;
+    if (B == 0)
+        return MOED_OK;
+    if (!x || !topk_ids || !topk_w || !wg_q || !wg_s || !wu_q || !wu_s || !wd_q || !wd_s || !out || !workspace)
+        return MOED_ERR_NULL;
+    if (workspace_bytes < moed_workspace_bytes(B, k, I, inter_dtype))
+        return MOED_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(wd_q) || !aligned16(workspace))
+        return MOED_ERR_ALIGN;
+    const moed::Tuning t = pick(B, H, I);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool a_bf16 = inter_dtype == MOED_BF16;
+    int st = hip_status(moed::launch_gate_up(
+        gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, workspace, B, E, k, H, I), a_bf16, t, s));
+    if (st)
+        return st;
+    return hip_status(moed::launch_down(
+        down_args(workspace, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I), a_bf16,
+        out_dtype == MOED_BF16, t, s));
+}
+
+int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n, int path,
+                         void* stream)
+{
+    if (n < 0 || (path != 0 && path != 1))
+        return MOED_ERR_SHAPE;
+    if (n == 0)
+        return MOED_OK;
+    if (!codes || !scales || !out)
+        return MOED_ERR_NULL;
+    return hip_status(moed::launch_selftest_decode(codes, scales, out, n, path, static_cast<hipStream_t>(stream)));
+}
+
+const char* moed_status_string(int status)
+{
+    switch (status) {
+    case MOED_OK: return "MOED_OK";
+    case MOED_ERR_NULL: return "MOED_ERR_NULL: a required pointer is NULL";
+    case MOED_ERR_SHAPE: return "MOED_ERR_SHAPE: invalid or unsupported sizes";
+    case MOED_ERR_DTYPE: return "MOED_ERR_DTYPE: unknown dtype";
+    case MOED_ERR_WORKSPACE: return "MOED_ERR_WORKSPACE: workspace too small";
+    case MOED_ERR_ALIGN: return "MOED_ERR_ALIGN: pointer not 16-byte aligned";
+    case MOED_ERR_HIP: return "MOED_ERR_HIP: HIP launch failed";
+    default: return "unknown moed_status";
+    }
+}
+
+int moed_last_hip_error(void) { return g_last_hip; }
+
+int moed_set_tuning(const char* spec)
+{
+    moed::Tuning t;
+    if (!spec || !*spec) {
+        g_tuning = t;
+        g_tuning_overridden = false;
+        return MOED_OK;
+    }
+    char buf[512];
+    strncpy(buf, spec, sizeof buf - 1);
+    buf[sizeof buf - 1] = 0;
+    for (char* tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+        char* eq = strchr(tok, '=');
+        if (!eq)
+            return MOED_ERR_SHAPE;
+        *eq = 0;
+        char* end = nullptr;
+        const long v = strtol(eq + 1, &end, 10);
+        if (!end || *end)
+            return MOED_ERR_SHAPE;
+        if (!strcmp(tok, "gu_wpb") && v >= 1 && v <= 4) t.gu_wpb = (int)v;
+        else if (!strcmp(tok, "dn_wpb") && v >= 1 && v <= 16) t.dn_wpb = (int)v;
+        else if (!strcmp(tok, "dn_stage") && (v == 0 || v == 1)) t.dn_stage = (int)v;
+        else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
+        else if (!strcmp(tok, "nt") && (v == 0 || v == 1)) t.nt = (int)v;
+        else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
+        else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;
+        else return MOED_ERR_SHAPE;
+    }
+    g_tuning = t;
+    g_tuning_overridden = true;
+    return MOED_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+"""ctypes binding of libmoedecode (include/moedecode.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. Tensors are torch CUDA tensors (device memory on the current device);
+the stream is torch's current stream unless one is given. There is no CPU
+fallback -- if the shared library is missing or fails to load, importing the
+functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoedecode.so")
+
+MOED_OK, MOED_ERR_NULL, MOED_ERR_SHAPE, MOED_ERR_DTYPE, MOED_ERR_WORKSPACE, MOED_ERR_ALIGN, MOED_ERR_HIP = range(7)
+MOED_BF16, MOED_F32 = 0, 1
+
+EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down",
+           "moed_selftest_decode", "moed_status_string", "moed_last_hip_error", "moed_set_tuning")
+
+
+class MoedError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.moed_status_string(status).decode()
+        if status == MOED_ERR_HIP:
+            msg += f" (hipError {lib.moed_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoedecode.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built: run __graft_entry__.build() "
+                              "(or python -m output_centric_expert_amd.build)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.moed_workspace_bytes.argtypes = [I, I, I, I]
+        lib.moed_workspace_bytes.restype = Z
+        lib.moe_decode.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
+        lib.moe_decode.restype = I
+        lib.moe_decode_gate_up.argtypes = [P] * 7 + [I] * 6 + [P]
+        lib.moe_decode_gate_up.restype = I
+        lib.moe_decode_down.argtypes = [P, I, P, P, P, P, P, I] + [I] * 5 + [P]
+        lib.moe_decode_down.restype = I
+        lib.moed_selftest_decode.argtypes = [P, P, P, I, I, P]
+        lib.moed_selftest_decode.restype = I
+        lib.moed_status_string.argtypes = [I]
+        lib.moed_status_string.restype = ctypes.c_char_p
+        lib.moed_last_hip_error.argtypes = []
+        lib.moed_last_hip_error.restype = I
+        lib.moed_set_tuning.argtypes = [ctypes.c_char_p]
+        lib.moed_set_tuning.restype = I
+        _lib = lib
+    return _lib
+
+
+_DT = {torch.bfloat16: MOED_BF16, torch.float32: MOED_F32}
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None, shape=None, cuda=True):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else ctypes.c_void_p(0)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(st: int, where: str):
+    if st != MOED_OK:
+        raise MoedError(st, where)
+
+
+def moed_workspace_bytes(B: int, k: int, I: int, inter_dtype=torch.float32) -> int:
+    return int(load().moed_workspace_bytes(B, k, I, _DT[inter_dtype]))
+
+
+def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None,
+               out_dtype=torch.bfloat16, inter_dtype=torch.float32, workspace=None, stream=None):
+    """The whole layer: returns out [B, H] (out_dtype)."""
+    B, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg_q.shape[0], wg_q.shape[1]
+    if out is None:
+        out = torch.empty((B, H), dtype=out_dtype, device=x.device)
+    need = moed_workspace_bytes(B, k, I, inter_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    st = load().moe_decode(
+        _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (B, k)),
+        _ptr(wg_q, "wg_q", torch.uint8, (E, I, H)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wu_q, "wu_q", torch.uint8, (E, I, H)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wd_q, "wd_q", torch.uint8, (E, H, I)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
+        _ptr(out, "out", None, (B, H)), _DT[out.dtype], _DT[inter_dtype],
+        B, E, k, H, I, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, "moe_decode")
+    return out
+
+
+def moe_decode_gate_up(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a=None, inter_dtype=torch.float32,
+                       stream=None):
+    """Gate/up step alone: returns a = SiLU(gate) * up, shape [B, k, I] in the
+    library's chunk-interleaved element order (inter_to_bki() gives plain order)."""
+    B, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg_q.shape[0], wg_q.shape[1]
+    if a is None:
+        a = torch.empty((B, k, I), dtype=inter_dtype, device=x.device)
+    st = load().moe_decode_gate_up(
+        _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
+        _ptr(wg_q, "wg_q", torch.uint8, (E, I, H)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wu_q, "wu_q", torch.uint8, (E, I, H)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
+        _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], B, E, k, H, I, _stream(stream))
+    _check(st, "moe_decode_gate_up")
+    return a
+
+
+def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.bfloat16, stream=None):
+    """Down step alone: returns out [B, H] from a [B, k, I]."""
+    B, k, I = a.shape
+    E, H = wd_q.shape[0], wd_q.shape[1]
+    if out is None:
+        out = torch.empty((B, H), dtype=out_dtype, device=a.device)
+    st = load().moe_decode_down(
+        _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (B, k)),
+        _ptr(wd_q, "wd_q", torch.uint8, (E, H, I)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
+        _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, _stream(stream))
+    _check(st, "moe_decode_down")
+    return out
+
+
+def moed_selftest_decode(codes, scales, path: int, out=None, stream=None):
+    """Decode codes[t] * 2^(scales[t]-127) with the kernels' decoder; float32 result."""
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    st = load().moed_selftest_decode(_ptr(codes, "codes", torch.uint8), _ptr(scales, "scales", torch.uint8),
+                                     _ptr(out, "out", torch.float32), n, path, _stream(stream))
+    _check(st, "moed_selftest_decode")
+    return out
+
+
+def moed_set_tuning(spec: str | None):
+    _check(load().moed_set_tuning(spec.encode() if spec else None), "moed_set_tuning")
+
+
+def moed_status_string(status: int) -> str:
+    return load().moed_status_string(status).decode()
+
+
+def moed_last_hip_error() -> int:
+    return load().moed_last_hip_error()
+
+
+def inter_to_bki(a: torch.Tensor) -> torch.Tensor:
+    """Reorder the library's chunk-interleaved intermediate (see the header) to plain [B, k, I]."""
+    B, k, I = a.shape
+    q, per = (2, 8) if a.dtype == torch.bfloat16 else (4, 4)
+    return a.reshape(B * k, q, I // 16, per).permute(0, 2, 1, 3).reshape(B, k, I)
+
+
+def layer_device_inputs(L, device="cuda"):
+    """Host parts of a synth.LayerInputs -> device tensors (x bf16, ids int32, w f32)."""
+    x = torch.from_numpy(L.x.view("int16")).view(torch.bfloat16).to(device)
+    ids = torch.from_numpy(L.ids).to(device)
+    w = torch.from_numpy(L.w).to(device)
+    return x, ids, w

@@ -1,0 +1,128 @@
+"""Host-side checks of the C-ABI library: it loads, exports every function the
+header declares, and rejects bad arguments before launching anything (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from output_centric_expert_amd import moedecode as md
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moedecode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(md.LIB_PATH):
+        from output_centric_expert_amd import build
+        build.build_library()
+    return md.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_functions():
+    assert header_functions() == sorted(md.EXPORTS)
+
+
+def test_library_exports_every_header_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {md.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert md.moed_status_string(s).startswith("MOED_")
+    assert "unknown" in md.moed_status_string(99)
+    assert md.moed_last_hip_error() == 0
+
+
+def test_workspace_bytes(lib):
+    assert lib.moed_workspace_bytes(1, 8, 768, md.MOED_F32) == 8 * 768 * 4
+    assert lib.moed_workspace_bytes(64, 8, 2048, md.MOED_BF16) == 64 * 8 * 2048 * 2
+    assert lib.moed_workspace_bytes(0, 8, 768, md.MOED_F32) == 0
+    assert lib.moed_workspace_bytes(1, 8, 768, 7) == 0
+
+
+P = ctypes.c_void_p
+A = P(4096)          # a fake, 16-byte-aligned non-null address: never dereferenced
+MIS = P(4100)        # misaligned
+
+
+def call_decode(lib, x=A, ids=A, w=A, wq=A, ws=A, out=A, od=0, idt=1, B=1, E=8, k=2, H=256, I=128,
+                wsp=A, wsb=1 << 20):
+    return lib.moe_decode(x, ids, w, wq, ws, wq, ws, wq, ws, out, od, idt, B, E, k, H, I, wsp, wsb, None)
+
+
+def test_decode_rejects_before_launch(lib):
+    assert call_decode(lib, x=None) == md.MOED_ERR_NULL
+    assert call_decode(lib, ws=None) == md.MOED_ERR_NULL
+    assert call_decode(lib, wsp=None) == md.MOED_ERR_NULL
+    assert call_decode(lib, k=0) == md.MOED_ERR_SHAPE
+    assert call_decode(lib, k=9) == md.MOED_ERR_SHAPE          # k > E
+    assert call_decode(lib, H=250) == md.MOED_ERR_SHAPE        # not a multiple of 32
+    assert call_decode(lib, I=16) == md.MOED_ERR_SHAPE
+    assert call_decode(lib, B=-1) == md.MOED_ERR_SHAPE
+    assert call_decode(lib, E=0, k=0) == md.MOED_ERR_SHAPE
+    assert call_decode(lib, B=1 << 20, H=4096) == md.MOED_ERR_SHAPE   # B*H >= 2^31
+    assert call_decode(lib, od=2) == md.MOED_ERR_DTYPE
+    assert call_decode(lib, idt=-1) == md.MOED_ERR_DTYPE
+    assert call_decode(lib, wsb=1 * 2 * 128 * 4 - 1) == md.MOED_ERR_WORKSPACE
+    assert call_decode(lib, x=MIS) == md.MOED_ERR_ALIGN
+    assert call_decode(lib, wq=MIS) == md.MOED_ERR_ALIGN
+    assert call_decode(lib, wsp=MIS) == md.MOED_ERR_ALIGN
+    # B = 0 is a valid empty call: nothing launched, even with NULL pointers
+    assert call_decode(lib, B=0, x=None, out=None, wsp=None, wsb=0) == md.MOED_OK
+
+
+def test_step_entry_points_reject_before_launch(lib):
+    gu = lambda **kw: lib.moe_decode_gate_up(kw.get("x", A), A, A, A, A, A, kw.get("a", A), kw.get("idt", 1),
+                                             kw.get("B", 1), 8, kw.get("k", 2), 256, 128, None)
+    assert gu(x=None) == md.MOED_ERR_NULL
+    assert gu(a=MIS) == md.MOED_ERR_ALIGN
+    assert gu(idt=5) == md.MOED_ERR_DTYPE
+    assert gu(k=0) == md.MOED_ERR_SHAPE
+    assert gu(B=0, x=None) == md.MOED_OK
+    dn = lambda **kw: lib.moe_decode_down(kw.get("a", A), 1, A, A, kw.get("wq", A), A, kw.get("out", A),
+                                          kw.get("od", 0), 1, 8, 2, 256, 128, None)
+    assert dn(out=None) == md.MOED_ERR_NULL
+    assert dn(wq=MIS) == md.MOED_ERR_ALIGN
+    assert dn(od=3) == md.MOED_ERR_DTYPE
+    assert lib.moed_selftest_decode(A, A, A, 4, 2, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_selftest_decode(None, A, A, 4, 0, None) == md.MOED_ERR_NULL
+    assert lib.moed_selftest_decode(None, None, None, 0, 0, None) == md.MOED_OK
+
+
+def test_tuning_spec_parser(lib):
+    assert lib.moed_set_tuning(b"gu_wpb=2,dn_wpb=1,gu_dot=0,nt=1") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_wpb=9") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(None) == md.MOED_OK
+
+
+def test_inter_layout_roundtrip():
+    """inter_to_bki inverts the documented chunk-interleaved index formula."""
+    import torch
+    B, k, I = 2, 3, 96
+    for dt, q, per in ((torch.float32, 4, 4), (torch.bfloat16, 2, 8)):
+        flat = torch.empty(B * k * I, dtype=torch.float32)
+        for bj in range(B * k):
+            for i in range(I):
+                o, r = i // 16, i % per
+                qq = (i // per) % q
+                flat[((bj * q + qq) * (I // 16) + o) * per + r] = bj * 1000 + i
+        plain = md.inter_to_bki(flat.to(dt).reshape(B, k, I)).float()
+        want = torch.tensor([[[bj * 1000 + i for i in range(I)] for bj in range(b * k, b * k + k)] for b in range(B)],
+                            dtype=torch.float32).to(dt).float()
+        assert torch.equal(plain, want)

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 CPU oracle.
+
+Gate (the tolerance the layer is specified to): with float32 outputs,
+max |gpu - oracle| <= 2e-3 * rms(oracle) over the compared outputs. BF16
+outputs must be the round-to-nearest-even of the float32 result, bit for bit,
+and within that bound plus half a bf16 ulp of the oracle value.
+
+The five decode workloads run in the launch configuration the benchmark
+times. The three smaller ones are compared on every output; the two large
+ones on every output of four sampled tokens (the oracle is run on just those
+tokens, which is exact because tokens are independent) plus properties that
+hold at any size (determinism, finiteness, batch = concatenation of tokens).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from output_centric_expert_amd import moedecode as md
+from output_centric_expert_amd import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    md.load()                                   # raises if the HIP library is missing
+    oracle.build(force=False)
+    yield
+    md.moed_set_tuning(None)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def layer(shape, seed=None, **kw):
+    return synth.make_layer(shape, seed=seed, device="cuda", **kw)
+
+
+def small(B, E, k, H, I, seed=0, zipf=0.0):
+    return layer(synth.LayerShape(f"s{B}_{E}_{k}_{H}_{I}", B, E, k, H, I, zipf), seed=seed)
+
+
+def run(L, out_dtype=torch.float32, inter_dtype=torch.float32, ids=None, w=None, x=None):
+    xd, idd, wd = md.layer_device_inputs(L)
+    if ids is not None:
+        idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    if w is not None:
+        wd = torch.as_tensor(w, dtype=torch.float32).cuda().contiguous()
+    if x is not None:
+        xd = x
+    out = md.moe_decode(xd, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                        out_dtype=out_dtype, inter_dtype=inter_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_tokens(L, tokens, ids=None, w=None):
+    """Oracle output (and intermediate) for a subset of tokens, from the same weight bytes."""
+    ids = L.ids if ids is None else np.asarray(ids, np.int32)
+    w = L.w if w is None else np.asarray(w, np.float32)
+    ids_t = ids[tokens]
+    sel = sorted({int(e) for e in ids_t.ravel() if 0 <= e < L.shape.E})
+    remap = np.full(L.shape.E, -1, np.int64)
+    remap[sel] = np.arange(len(sel))
+    ids_c = np.where((ids_t >= 0) & (ids_t < L.shape.E), remap[np.clip(ids_t, 0, L.shape.E - 1)], -1)
+    idx = torch.tensor(sel if sel else [0], device=L.wg_q.device)
+    pick = lambda t: t.index_select(0, idx).cpu()
+    return oracle.moe_decode(np.ascontiguousarray(L.x[tokens]), np.ascontiguousarray(ids_c.astype(np.int32)),
+                             np.ascontiguousarray(w[tokens]), pick(L.wg_q), pick(L.wg_s), pick(L.wu_q),
+                             pick(L.wu_s), pick(L.wd_q), pick(L.wd_s), return_inter=True)
+
+
+def check_f32(gpu_out, ref, label, tol=TOL):
+    g = gpu_out.double().cpu().numpy() if torch.is_tensor(gpu_out) else gpu_out
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(g - ref)))
+    say(f"[{label}] max|err| = {err:.3e}  rms = {rms:.3e}  ratio = {err / rms:.3e}")
+    assert np.isfinite(g).all()
+    assert err <= tol * rms, f"{label}: max|err|/rms = {err / rms:.3e} > {tol}"
+    return err / rms
+
+
+def bf16_ulp(v):
+    v = np.abs(v)
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def check_bf16(gpu_bf16, gpu_f32, ref, label):
+    rne = gpu_f32.cpu().to(torch.bfloat16)                     # library RNE of our f32 result
+    assert torch.equal(gpu_bf16.cpu().view(torch.int16), rne.view(torch.int16)), f"{label}: bf16 != RNE(f32)"
+    g = gpu_bf16.double().cpu().numpy()
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    assert np.all(np.abs(g - ref) <= TOL * rms + 0.5 * bf16_ulp(ref)), label
+
+
+# --------------------------------------------------------------------------------------
+# decode self-test: every E4M3 code, both in-register routes, bit for bit
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_decode_all_codes_bit_exact(path):
+    scales = [127, 100, 120, 126, 128, 134, 147]
+    codes = np.tile(np.arange(256, dtype=np.uint8), len(scales))
+    sc = np.repeat(np.array(scales, np.uint8), 256)
+    got = md.moed_selftest_decode(torch.from_numpy(codes).cuda(), torch.from_numpy(sc).cuda(), path).cpu().numpy()
+    for t in range(codes.size):
+        ref = oracle.e4m3_value(int(codes[t])) * oracle.ue8m0_value(int(sc[t]))
+        if math.isnan(ref):
+            assert math.isnan(got[t]), (path, hex(codes[t]), sc[t])
+        else:
+            r32 = np.float32(ref)
+            assert float(r32) == ref                     # exactly representable
+            assert got[t] == r32 and np.signbit(got[t]) == np.signbit(r32), (path, hex(codes[t]), sc[t], got[t], ref)
+
+
+def test_decode_nan_scale():
+    codes = torch.tensor([0x38, 0x00, 0x81], dtype=torch.uint8).cuda()
+    sc = torch.full((3,), 255, dtype=torch.uint8).cuda()
+    for path in (0, 1):
+        assert torch.isnan(md.moed_selftest_decode(codes, sc, path)).all()
+
+
+# --------------------------------------------------------------------------------------
+# the five decode workloads
+# --------------------------------------------------------------------------------------
+
+FULL = ["tiny_B1_E8_k2_H256_I128", "wide_B1_E128_k8_H2048_I768", "batch_B8_E128_k8_H2048_I768"]
+SAMPLED = {"batch_B32_E128_k8_H4096_I1536": [0, 7, 19, 31],
+           "skewed_B64_E256_k8_H7168_I2048": [0, 21, 42, 63]}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_parity(name):
+    say(f"workload {name}: full parity")
+    L = layer(name)
+    ref, a_ref = oracle_tokens(L, list(range(L.shape.B)))
+    out32 = run(L, torch.float32)
+    check_f32(out32, ref, name)
+    out16 = run(L, torch.bfloat16)
+    check_bf16(out16, out32, ref, name)
+    # the gate/up step alone against the oracle's intermediate
+    x, ids, _ = md.layer_device_inputs(L)
+    a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+    torch.cuda.synchronize()
+    check_f32(a.reshape(L.shape.B, -1), a_ref.reshape(L.shape.B, -1), name + " a")
+
+
+@pytest.mark.parametrize("name", list(SAMPLED))
+def test_workload_sampled_parity(name):
+    say(f"workload {name}: sampled parity")
+    L = layer(name)
+    toks = SAMPLED[name]
+    out32 = run(L, torch.float32)
+    out32b = run(L, torch.float32)
+    assert torch.equal(out32, out32b), "not deterministic"
+    assert torch.isfinite(out32).all()
+    ref, _ = oracle_tokens(L, toks)
+    check_f32(out32[toks], ref, name)
+    out16 = run(L, torch.bfloat16)
+    check_bf16(out16[toks], out32[toks], ref, name)
+    # batch = concatenation of single-token calls, bit for bit
+    x, ids, w = md.layer_device_inputs(L)
+    for b in toks[:2]:
+        one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
+                            L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], out32[b])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_bf16_intermediate_variant_reported(name):
+    """The FP32-accumulate path that stores BF16 intermediates: error reported, not gated."""
+    L = layer(name)
+    ref, _ = oracle_tokens(L, list(range(L.shape.B)))
+    out = run(L, torch.float32, inter_dtype=torch.bfloat16)
+    g = out.double().cpu().numpy()
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    ratio = float(np.max(np.abs(g - ref))) / rms
+    say(f"[{name}] bf16-intermediate max|err|/rms = {ratio:.3e}")
+    assert np.isfinite(g).all() and ratio < 5e-2
+
+
+# --------------------------------------------------------------------------------------
+# ragged shapes, multi-pass rows, tuning variants
+# --------------------------------------------------------------------------------------
+
+SHAPES = [
+    (1, 4, 2, 32, 32),        # one MX block per row
+    (3, 6, 3, 96, 160),       # rows shorter than a wave; k*I/16 not a multiple of 64
+    (2, 5, 5, 2080, 96),      # k = E; 130 chunks per row: a ragged second chunk per lane
+    (2, 3, 2, 8224, 64),      # 514 chunks per row: more than 8 per lane -> two passes
+    (2, 8, 4, 128, 2080),     # down: k*I/16 = 520 -> two passes
+    (5, 16, 1, 64, 1056),     # k = 1
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_ragged_shapes(shape):
+    B, E, k, H, I = shape
+    L = small(B, E, k, H, I, seed=sum(shape))
+    ref, a_ref = oracle_tokens(L, list(range(B)))
+    check_f32(run(L), ref, f"ragged {shape}")
+    x, ids, _ = md.layer_device_inputs(L)
+    a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+    torch.cuda.synchronize()
+    check_f32(a.reshape(B, -1), a_ref.reshape(B, -1), f"ragged a {shape}")
+    # the down step alone on the gate/up step's buffer gives the layer
+    a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+    _, idd, wd = md.layer_device_inputs(L)
+    out = md.moe_decode_down(a_ws, idd, wd, L.wd_q, L.wd_s, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_f32(out, ref, f"ragged steps {shape}")
+
+
+@pytest.mark.parametrize("spec", ["gu_dot=0", "gu_dot=1", "nt=1", "gu_wpb=1,dn_wpb=1", "gu_wpb=2,dn_wpb=2",
+                                  "gu_umax=1,dn_umax=1", "gu_umax=3,dn_umax=5,gu_dot=0,nt=1"])
+def test_tuning_variants_keep_parity(spec):
+    for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
+        L = small(*shape, seed=3)
+        ref, _ = oracle_tokens(L, list(range(shape[0])))
+        md.moed_set_tuning(spec)
+        try:
+            check_f32(run(L), ref, f"{spec} {shape}")
+        finally:
+            md.moed_set_tuning(None)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_small_shapes(seed):
+    shape = synth.random_small_shape(np.random.default_rng(500 + seed), max_E=12, max_dim=320)
+    L = layer(shape, seed=seed)
+    ref, _ = oracle_tokens(L, list(range(shape.B)))
+    check_f32(run(L), ref, shape.name)
+
+
+# --------------------------------------------------------------------------------------
+# routing edge cases and invariants
+# --------------------------------------------------------------------------------------
+
+def test_duplicate_ids():
+    L = small(2, 6, 3, 256, 128, seed=11)
+    ids = L.ids.copy(); ids[:, 1] = ids[:, 0]
+    ref, _ = oracle_tokens(L, [0, 1], ids=ids)
+    check_f32(run(L, ids=ids), ref, "duplicate ids")
+
+
+def test_out_of_range_ids_give_nan_rows_only():
+    L = small(3, 6, 2, 256, 128, seed=12)
+    ids = L.ids.copy(); ids[1, 1] = 6; ids[2, 0] = -3
+    out = run(L, ids=ids).cpu()
+    assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+    ref, _ = oracle_tokens(L, [0])
+    check_f32(out[0:1], ref, "valid token next to invalid ones")
+
+
+def test_zero_routing_weights_give_zero():
+    L = small(2, 6, 3, 256, 128, seed=13)
+    out = run(L, w=np.zeros((2, 3), np.float32))
+    assert torch.all(out == 0)
+
+
+def test_power_of_two_weight_scaling_is_exact():
+    L = small(2, 6, 3, 256, 128, seed=14)
+    o1 = run(L)
+    o2 = run(L, w=L.w * np.float32(2.0))
+    assert torch.equal(o2, 2 * o1)
+
+
+def test_slot_permutation_invariance():
+    L = small(4, 16, 4, 512, 256, seed=15)
+    base = run(L)
+    perm = np.stack([np.random.default_rng(b).permutation(4) for b in range(4)])
+    ids = np.take_along_axis(L.ids, perm, 1); w = np.take_along_axis(L.w, perm, 1)
+    other = run(L, ids=ids, w=w)
+    ref, _ = oracle_tokens(L, [0, 1, 2, 3])
+    check_f32(other, ref, "permuted slots")
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    assert float((other - base).abs().max()) <= 1e-5 * rms
+
+
+def test_empty_batch_launches_nothing():
+    L = small(1, 4, 2, 64, 64, seed=16)
+    x, ids, w = md.layer_device_inputs(L)
+    out = md.moe_decode(x[:0], ids[:0], w[:0], L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                        out_dtype=torch.float32)
+    assert out.shape == (0, 64)
+
+
+def test_deterministic_repeats():
+    L = layer("batch_B8_E128_k8_H2048_I768")
+    first = run(L)
+    for _ in range(5):
+        assert torch.equal(run(L), first)
