@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--tune", default=None, help="launch-shape override (moed_set_tuning spec)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="eager launches for rocprofv3 --pmc passes (copy kernel of known size, "
+                         "then the two layer kernels); prints the launch plan, no timing")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -112,6 +115,10 @@ def main():
     def down(r):
         _, _, _, _, wd_q, wd_s = copies[r % R]
         md.moe_decode_down(a, ids, w, wd_q, wd_s, out=out)
+
+    if args.counters:
+        counters_run(md, x, ids, w, copies, out, a, ws, args.workload)
+        return
 
     K, W = args.steps, args.warmup
     for r in range(W):                       # untimed warm-up steps
@@ -174,6 +181,8 @@ def main():
     e1.record(); torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / K
 
+    peak = measured_read_peak(md)
+
     U = L.unique_experts
     uniq = L.unique_weight_bytes
     gu_bytes = U * 2 * I * H * 33 // 32
@@ -217,12 +226,61 @@ def main():
         "gbs_down": round(dn_gbs, 1),
         "us_per_layer_median3": round(ms_layer_rep * 1e3, 3),
         "us_per_layer_eager": round(ms_eager * 1e3, 3),
+        "measured_read_peak_gbs": round(peak, 1),
+        "frac_of_measured_read_peak": round(gbs / peak, 4),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "tuning": args.tune or "built-in",
     }
     print(json.dumps(res), flush=True)
+
+
+COPY_BYTES = 256 << 20      # known-size reference for counter calibration
+COUNTER_LAUNCHES = 8
+
+
+def counters_run(md, x, ids, w, copies, out, a, ws, workload):
+    """Launch plan for rocprofv3 --pmc: COUNTER_LAUNCHES copies of COPY_BYTES, then the
+    gate/up and down kernels COUNTER_LAUNCHES times each on rotating weight copies."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(COUNTER_LAUNCHES):
+        md.moed_bench_copy(src, dst)
+        torch.cuda.synchronize()
+    R = len(copies)
+    for r in range(COUNTER_LAUNCHES):
+        md.moe_decode_gate_up(x, ids, *copies[(r + 1) % R][:4], a=a)
+        torch.cuda.synchronize()
+    for r in range(COUNTER_LAUNCHES):
+        md.moe_decode_down(a, ids, w, *copies[(r + 1) % R][4:], out=out)
+        torch.cuda.synchronize()
+    print(json.dumps({"counters_plan": {"workload": workload, "copy_bytes": COPY_BYTES,
+                                        "launches_each": COUNTER_LAUNCHES,
+                                        "source_digest": source_digest()}}), flush=True)
+
+
+def measured_read_peak(md, nbytes=2 << 30, launches=20):
+    """Contiguous streaming-read bandwidth (GB/s) over two alternating 2 GiB buffers."""
+    import torch
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    md.moed_bench_read(bufs[0], sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(launches):
+        md.moed_bench_read(bufs[i % 2], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    del bufs
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(L, uniq, seconds):

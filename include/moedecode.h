@@ -135,6 +135,21 @@ int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
 int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out,
                          int n, int path, void *stream);
 
+/*
+ * Measurement kernels (not part of the layer).
+ * moed_bench_read: streams `bytes` from `src` with contiguous 16-byte loads --
+ *   the peak-read reference the warp-decode post compares against (section
+ *   "Hardware efficiency": peak measured with a copy kernel over contiguous
+ *   reads). `sink` (>= 4096 bytes, device) is scratch that is almost never
+ *   written. bytes % 16 == 0, src 16-byte aligned.
+ * moed_bench_copy: dst[0..bytes) = src[0..bytes); a kernel of known traffic
+ *   used to calibrate HBM byte counters. bytes % 16 == 0, both 16-aligned,
+ *   the ranges must not overlap.
+ * Both are asynchronous on `stream`; errors as for moe_decode().
+ */
+int moed_bench_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, void *stream);
+int moed_bench_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* Human-readable name of a moed_status value. Never NULL. */
 const char *moed_status_string(int status);
 

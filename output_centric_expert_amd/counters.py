@@ -1,0 +1,81 @@
+"""Turn rocprofv3 --pmc CSV output (FETCH_SIZE pass, WRITE_SIZE pass) of
+``bench.py --counters`` into the per-launch HBM-traffic summary the benchmark
+reports as roofline.traffic.
+
+The raw counters are scaled by what the same counters read for a copy kernel
+of known size (COPY_BYTES read + COPY_BYTES written), launched in the same run.
+
+    python -m output_centric_expert_amd.counters --fetch DIR --write DIR \\
+        --workload NAME --digest HEX --out profiles/counters_gate_up_NAME.json
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+
+
+def read_counter(d: str, name: str):
+    """{kernel-name-prefix: [value per dispatch]} for counter `name` (KiB)."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {d}")
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != name:
+                    continue
+                per[row["Kernel_Name"]][row.get("Dispatch_Id") or row.get("Correlation_Id")] += float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def pick(per: dict, needle: str):
+    vals = [v for k, vs in per.items() if needle in k for v in vs]
+    if not vals:
+        raise KeyError(f"no dispatch of a kernel matching {needle!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--digest", required=True)
+    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--gate-up-bytes", type=int, required=True, help="algorithmic bytes per gate/up launch")
+    ap.add_argument("--down-bytes", type=int, required=True, help="algorithmic bytes per down launch")
+    args = ap.parse_args()
+
+    fetch = read_counter(args.fetch, "FETCH_SIZE")
+    write = read_counter(args.write, "WRITE_SIZE")
+    cf, _ = pick(fetch, "moe_bench_copy_kernel")
+    cw, _ = pick(write, "moe_bench_copy_kernel")
+    f_fetch = args.copy_bytes / (cf * 1024.0)
+    f_write = args.copy_bytes / (cw * 1024.0)
+    res = {"workload": args.workload, "source_digest": args.digest,
+           "copy_kernel": {"bytes_read": args.copy_bytes, "bytes_written": args.copy_bytes,
+                           "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                           "fetch_scale": f_fetch, "write_scale": f_write}}
+    for key, needle, alg in (("gate_up", "moe_gate_up_kernel", args.gate_up_bytes),
+                             ("down", "moe_down", args.down_bytes)):
+        fv, n = pick(fetch, needle)
+        wv, _ = pick(write, needle)
+        hbm = fv * 1024.0 * f_fetch + wv * 1024.0 * f_write
+        res[key] = {"dispatches": n, "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv,
+                    "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
+                    "traffic_over_algorithmic": hbm / alg}
+    res["hbm_bytes_per_launch"] = res["gate_up"]["hbm_bytes_per_launch"]
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    with open(args.out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -42,6 +42,8 @@ struct DownArgs {
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
+hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
+hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
                                   int path, hipStream_t s);
 

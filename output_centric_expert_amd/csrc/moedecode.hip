@@ -162,6 +162,32 @@ int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out
     return hip_status(moed::launch_selftest_decode(codes, scales, out, n, path, static_cast<hipStream_t>(stream)));
 }
 
+int moed_bench_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream)
+{
+    if (bytes == 0)
+        return MOED_OK;
+    if (!src || !sink)
+        return MOED_ERR_NULL;
+    if (bytes % 16 != 0 || sink_bytes < 4096)
+        return MOED_ERR_SHAPE;
+    if (!aligned16(src))
+        return MOED_ERR_ALIGN;
+    return hip_status(moed::launch_bench_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+int moed_bench_copy(const void* src, void* dst, size_t bytes, void* stream)
+{
+    if (bytes == 0)
+        return MOED_OK;
+    if (!src || !dst)
+        return MOED_ERR_NULL;
+    if (bytes % 16 != 0)
+        return MOED_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(dst))
+        return MOED_ERR_ALIGN;
+    return hip_status(moed::launch_bench_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 const char* moed_status_string(int status)
 {
     switch (status) {

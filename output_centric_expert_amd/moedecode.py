@@ -20,7 +20,8 @@ MOED_OK, MOED_ERR_NULL, MOED_ERR_SHAPE, MOED_ERR_DTYPE, MOED_ERR_WORKSPACE, MOED
 MOED_BF16, MOED_F32 = 0, 1
 
 EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down",
-           "moed_selftest_decode", "moed_status_string", "moed_last_hip_error", "moed_set_tuning")
+           "moed_selftest_decode", "moed_bench_read", "moed_bench_copy", "moed_status_string",
+           "moed_last_hip_error", "moed_set_tuning")
 
 
 class MoedError(RuntimeError):
@@ -55,6 +56,10 @@ def load() -> ctypes.CDLL:
         lib.moe_decode_down.restype = I
         lib.moed_selftest_decode.argtypes = [P, P, P, I, I, P]
         lib.moed_selftest_decode.restype = I
+        lib.moed_bench_read.argtypes = [P, Z, P, Z, P]
+        lib.moed_bench_read.restype = I
+        lib.moed_bench_copy.argtypes = [P, P, Z, P]
+        lib.moed_bench_copy.restype = I
         lib.moed_status_string.argtypes = [I]
         lib.moed_status_string.restype = ctypes.c_char_p
         lib.moed_last_hip_error.argtypes = []
@@ -162,6 +167,20 @@ def moed_selftest_decode(codes, scales, path: int, out=None, stream=None):
                                      _ptr(out, "out", torch.float32), n, path, _stream(stream))
     _check(st, "moed_selftest_decode")
     return out
+
+
+def moed_bench_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None, stream=None):
+    """Stream-read `nbytes` (default: all) of `src` with the contiguous read kernel."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(load().moed_bench_read(_ptr(src, "src"), n, _ptr(sink, "sink"), sink.numel() * sink.element_size(),
+                                  _stream(stream)), "moed_bench_read")
+
+
+def moed_bench_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int | None = None, stream=None):
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if n > dst.numel() * dst.element_size():
+        raise ValueError("moed_bench_copy: dst too small")
+    _check(load().moed_bench_copy(_ptr(src, "src"), _ptr(dst, "dst"), n, _stream(stream)), "moed_bench_copy")
 
 
 def moed_set_tuning(spec: str | None):

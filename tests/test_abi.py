@@ -126,3 +126,14 @@ def test_inter_layout_roundtrip():
         want = torch.tensor([[[bj * 1000 + i for i in range(I)] for bj in range(b * k, b * k + k)] for b in range(B)],
                             dtype=torch.float32).to(dt).float()
         assert torch.equal(plain, want)
+
+
+def test_bench_kernels_reject_before_launch(lib):
+    assert lib.moed_bench_read(None, 64, A, 4096, None) == md.MOED_ERR_NULL
+    assert lib.moed_bench_read(A, 60, A, 4096, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_bench_read(A, 64, A, 1024, None) == md.MOED_ERR_SHAPE   # sink too small
+    assert lib.moed_bench_read(MIS, 64, A, 4096, None) == md.MOED_ERR_ALIGN
+    assert lib.moed_bench_read(None, 0, None, 0, None) == md.MOED_OK
+    assert lib.moed_bench_copy(A, None, 64, None) == md.MOED_ERR_NULL
+    assert lib.moed_bench_copy(A, A, 65, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_bench_copy(A, MIS, 64, None) == md.MOED_ERR_ALIGN

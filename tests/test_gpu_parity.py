@@ -300,3 +300,13 @@ def test_deterministic_repeats():
     first = run(L)
     for _ in range(5):
         assert torch.equal(run(L), first)
+
+
+def test_bench_kernels():
+    src = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    md.moed_bench_copy(src, dst)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    md.moed_bench_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
