@@ -66,6 +66,8 @@ def main():
     ap.add_argument("--tune", default=None, help="launch-shape override (moed_set_tuning spec)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--all", action="store_true",
+                    help="time every decode workload (one JSON line each); not the driver's line")
     ap.add_argument("--counters", action="store_true",
                     help="eager launches for rocprofv3 --pmc passes (copy kernel of known size, "
                          "then the two layer kernels); prints the launch plan, no timing")
@@ -88,39 +90,104 @@ def main():
     if args.tune:
         md.moed_set_tuning(args.tune)
 
+    if args.all:
+        all_workloads(md, synth, args)
+        return
+
     shape = synth.WORKLOADS[args.workload]
     t0 = time.time()
     L = synth.make_layer(shape, device="cuda")
-    x, ids, w = md.layer_device_inputs(L)
     R = max(1, args.copies)
-    copies = [(L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
-    for _ in range(R - 1):
-        copies.append(tuple(t.clone() for t in copies[0]))
-    torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s: {shape}, {R} weight copies")
-
-    B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
-    out = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
-    a = torch.empty((B, k, I), dtype=torch.float32, device="cuda")
-    ws = a.view(torch.uint8).view(-1)
-
-    def layer(r):
-        wg_q, wg_s, wu_q, wu_s, wd_q, wd_s = copies[r % R]
-        md.moe_decode(x, ids, w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=out, workspace=ws)
-
-    def gate_up(r):
-        wg_q, wg_s, wu_q, wu_s, _, _ = copies[r % R]
-        md.moe_decode_gate_up(x, ids, wg_q, wg_s, wu_q, wu_s, a=a)
-
-    def down(r):
-        _, _, _, _, wd_q, wd_s = copies[r % R]
-        md.moe_decode_down(a, ids, w, wd_q, wd_s, out=out)
-
     if args.counters:
-        counters_run(md, x, ids, w, copies, out, a, ws, args.workload)
+        x, ids, w = md.layer_device_inputs(L)
+        copies = weight_copies(L, R)
+        out = torch.empty((shape.B, shape.H), dtype=torch.bfloat16, device="cuda")
+        a = torch.empty((shape.B, shape.k, shape.I), dtype=torch.float32, device="cuda")
+        counters_run(md, x, ids, w, copies, out, a, args.workload)
         return
 
     K, W = args.steps, args.warmup
+    t = measure_layer(md, L, R, K, W)
+    peak = measured_read_peak(md)
+    B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
+    U = L.unique_experts
+    uniq = L.unique_weight_bytes
+    gu_bytes = U * 2 * I * H * 33 // 32
+    ms_per_step, ms_gu = t["ms_per_step"], t["ms_gate_up"]
+    gbs = uniq / (ms_per_step * 1e-3) / 1e9
+    gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
+
+    traffic = load_traffic("gate_up", args.workload)
+    roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
+                "avg_launch_us": round(ms_gu * 1e3, 3)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(L, uniq, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights encoded to MXFP8, softmax top-k routing)",
+        "config": {"workload": args.workload, "B": B, "E": E, "k": k, "H": H, "I": I,
+                   "weights": "mxfp8 (e4m3 + ue8m0 per 32)", "activations": "bf16", "out": "bf16",
+                   "unique_experts": U, "unique_weight_bytes": uniq, "weight_copies": R,
+                   "timing": "HIP graph of K layers, HIP events on the launch stream"},
+        **timing_fields(L, t),
+        "measured_read_peak_gbs": round(peak, 1),
+        "frac_of_measured_read_peak": round(gbs / peak, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "tuning": args.tune or "built-in",
+    }
+    print(json.dumps(res), flush=True)
+
+
+COPY_BYTES = 256 << 20      # known-size reference for counter calibration
+COUNTER_LAUNCHES = 8
+
+
+def weight_copies(L, R):
+    """R copies of the layer's weight tensors at distinct HBM addresses (copy 0 = L's own)."""
+    first = (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)
+    return [first] + [tuple(t.clone() for t in first) for _ in range(R - 1)]
+
+
+def measure_layer(md, L, R, K, W):
+    """Time K layers (HIP graph, R rotating weight copies); also the two kernels alone and
+    an eager loop. Returns milliseconds."""
+    import numpy as np
+    import torch
+
+    sh = L.shape
+    x, ids, w = md.layer_device_inputs(L)
+    copies = weight_copies(L, R)
+    torch.cuda.synchronize()
+    out = torch.empty((sh.B, sh.H), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((sh.B, sh.k, sh.I), dtype=torch.float32, device="cuda")
+    ws = a.view(torch.uint8).view(-1)
+
+    def layer(r):
+        md.moe_decode(x, ids, w, *copies[r % R], out=out, workspace=ws)
+
+    def gate_up(r):
+        md.moe_decode_gate_up(x, ids, *copies[r % R][:4], a=a)
+
+    def down(r):
+        md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out)
+
     for r in range(W):                       # untimed warm-up steps
         layer(r)
     torch.cuda.synchronize()
@@ -134,7 +201,6 @@ def main():
         return g
 
     def time_graph(g, n, reps=1):
-        """ms per step of graph g (n steps), median over reps replays."""
         res = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -164,83 +230,65 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / K
     # -------------------------------------------
 
-    # per-kernel average launch durations (same stream, same graph mechanism)
     g_gu = capture(gate_up, K)
     g_dn = capture(down, K)
     g_gu.replay(); g_dn.replay()
     torch.cuda.synchronize()
-    ms_gu = time_graph(g_gu, K, reps=3)
-    ms_dn = time_graph(g_dn, K, reps=3)
-    ms_layer_rep = time_graph(g_layer, K, reps=3)
-
-    # eager (one C-ABI call per step from Python) for reference
+    res = {"ms_per_step": ms_per_step, "wall_s": wall,
+           "ms_gate_up": time_graph(g_gu, K, reps=3), "ms_down": time_graph(g_dn, K, reps=3),
+           "ms_layer_median3": time_graph(g_layer, K, reps=3)}
+    del g_layer, g_gu, g_dn
     e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+    n_eager = min(K, 200)
     torch.cuda.synchronize(); e0.record()
-    for r in range(K):
+    for r in range(n_eager):
         layer(r)
     e1.record(); torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / K
+    res["ms_eager"] = e0.elapsed_time(e1) / n_eager
+    return res
 
-    peak = measured_read_peak(md)
 
+def timing_fields(L, t):
+    sh = L.shape
     U = L.unique_experts
-    uniq = L.unique_weight_bytes
-    gu_bytes = U * 2 * I * H * 33 // 32
-    dn_bytes = U * H * I * 33 // 32
-    gbs = uniq / (ms_per_step * 1e-3) / 1e9
-    gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
-    dn_gbs = dn_bytes / (ms_dn * 1e-3) / 1e9
-
-    traffic = load_traffic("gate_up", args.workload)
-    roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
-                "avg_launch_us": round(ms_gu * 1e3, 3)}
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(L, uniq, args.cpu_seconds)
-
-    res = {
-        "metric": METRIC,
-        "value": round(gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights encoded to MXFP8, softmax top-k routing)",
-        "config": {"workload": args.workload, "B": B, "E": E, "k": k, "H": H, "I": I,
-                   "weights": "mxfp8 (e4m3 + ue8m0 per 32)", "activations": "bf16", "out": "bf16",
-                   "unique_experts": U, "unique_weight_bytes": uniq, "weight_copies": R,
-                   "timing": "HIP graph of K layers, HIP events on the launch stream"},
-        "us_per_layer": round(ms_per_step * 1e3, 3),
-        "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
-        "us_gate_up": round(ms_gu * 1e3, 3),
-        "us_down": round(ms_dn * 1e3, 3),
-        "gbs_gate_up": round(gu_gbs, 1),
-        "gbs_down": round(dn_gbs, 1),
-        "us_per_layer_median3": round(ms_layer_rep * 1e3, 3),
-        "us_per_layer_eager": round(ms_eager * 1e3, 3),
-        "measured_read_peak_gbs": round(peak, 1),
-        "frac_of_measured_read_peak": round(gbs / peak, 4),
-        "wall_s_timed": round(wall, 4),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "tuning": args.tune or "built-in",
-    }
-    print(json.dumps(res), flush=True)
+    gu_bytes = U * 2 * sh.I * sh.H * 33 // 32
+    dn_bytes = U * sh.H * sh.I * 33 // 32
+    return {"us_per_layer": round(t["ms_per_step"] * 1e3, 3),
+            "frac_of_peak_hbm": round(L.unique_weight_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "us_gate_up": round(t["ms_gate_up"] * 1e3, 3), "us_down": round(t["ms_down"] * 1e3, 3),
+            "gbs_gate_up": round(gu_bytes / (t["ms_gate_up"] * 1e-3) / 1e9, 1),
+            "gbs_down": round(dn_bytes / (t["ms_down"] * 1e-3) / 1e9, 1),
+            "us_per_layer_median3": round(t["ms_layer_median3"] * 1e3, 3),
+            "us_per_layer_eager": round(t["ms_eager"] * 1e3, 3),
+            "wall_s_timed": round(t["wall_s"], 4)}
 
 
-COPY_BYTES = 256 << 20      # known-size reference for counter calibration
-COUNTER_LAUNCHES = 8
+# weight copies and steps per workload for --all: copies * touched bytes >> 256 MB cache
+ALL_PLAN = {"tiny_B1_E8_k2_H256_I128": (32, 2000), "wide_B1_E128_k8_H2048_I768": (32, 2000),
+            "batch_B8_E128_k8_H2048_I768": (8, 1000), "batch_B32_E128_k8_H4096_I1536": (2, 100),
+            "skewed_B64_E256_k8_H7168_I2048": (2, 40)}
 
 
-def counters_run(md, x, ids, w, copies, out, a, ws, workload):
+def all_workloads(md, synth, args):
+    import torch
+    peak = measured_read_peak(md)
+    for name in synth.WORKLOAD_ORDER:
+        R, K = ALL_PLAN[name]
+        L = synth.make_layer(name, device="cuda")
+        t = measure_layer(md, L, R, K, min(args.warmup, 10))
+        gbs = L.unique_weight_bytes / (t["ms_per_step"] * 1e-3) / 1e9
+        line = {"workload": name, "steps": K, "weight_copies": R, "unique_experts": L.unique_experts,
+                "unique_weight_bytes": L.unique_weight_bytes, "gbs": round(gbs, 1),
+                **timing_fields(L, t), "frac_of_measured_read_peak": round(gbs / peak, 4),
+                "measured_read_peak_gbs": round(peak, 1)}
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline(L, L.unique_weight_bytes, min(args.cpu_seconds, 10.0))
+        print(json.dumps(line), flush=True)
+        del L
+        torch.cuda.empty_cache()
+
+
+def counters_run(md, x, ids, w, copies, out, a, workload):
     """Launch plan for rocprofv3 --pmc: COUNTER_LAUNCHES copies of COPY_BYTES, then the
     gate/up and down kernels COUNTER_LAUNCHES times each on rotating weight copies."""
     import torch
@@ -291,23 +339,30 @@ def cpu_baseline(L, uniq, seconds):
     import oracle
 
     oracle.build(force=False)
-    sel = sorted(set(int(e) for e in L.ids.ravel()))
+    B = L.shape.B
+    toks = list(range(B)) if B <= 8 else list(range(0, B, B // 4))[:4]   # bounded sample
+    ids_t = L.ids[toks]
+    sel = sorted(set(int(e) for e in ids_t.ravel()))
     remap = {e: n for n, e in enumerate(sel)}
-    ids_c = np.vectorize(remap.get)(L.ids).astype(np.int32)
+    ids_c = np.ascontiguousarray(np.vectorize(remap.get)(ids_t).astype(np.int32))
+    x_t = np.ascontiguousarray(L.x[toks])
+    w_t = np.ascontiguousarray(L.w[toks])
     idx = torch.tensor(sel, device=L.wg_q.device)
     host = [t.index_select(0, idx).cpu() for t in (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
     nthreads = min(os.cpu_count() or 1, 16)
     used = oracle.threads(nthreads)
-    oracle.moe_decode(L.x, ids_c, L.w, *host, nthreads=nthreads)          # warm-up
+    oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads)          # warm-up
     n, t = 0, 0.0
     while t < seconds or n < 3:
         t0 = time.perf_counter()
-        oracle.moe_decode(L.x, ids_c, L.w, *host, nthreads=nthreads)
+        oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads)
         t += time.perf_counter() - t0
         n += 1
-    per = t / n
+    per_tok = t / n / len(toks)
+    per = per_tok * B                       # the oracle's cost is linear in tokens
+    what = "full layers" if len(toks) == B else f"runs of {len(toks)} of the {B} tokens (cost per layer scaled by B/{len(toks)})"
     return {"value": round(uniq / per / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
-            "sample": f"{n} full layers of the same workload (all B*H outputs; touched experts copied to host)",
+            "sample": f"{n} {what} of the same workload (touched experts copied to host)",
             "s_per_layer": round(per, 6)}
 
 

@@ -1,0 +1,89 @@
+"""Accuracy study on the GPU path (reported; gated only on its direction).
+
+The warp-decode post ("Improved accuracy") says outputs land 1.4x closer to a
+full 32-bit reference than the classical path's. Here, per workload:
+  reading A = float64 layer with the unquantized weight draws (oracle/accuracy.py),
+  reading B = the float64 MXFP8-weight oracle,
+  ours      = the HIP path (bf16 output; also f32 output and the BF16-intermediate variant),
+  classical = the classical path's numerics emulated on the CPU (MXFP8 activations,
+              FP32 accumulation, BF16 per-expert outputs).
+ratio = rms error of classical / rms error of ours, both against reading A.
+"""
+import json
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import accuracy as acc
+from output_centric_expert_amd import moedecode as md
+from output_centric_expert_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+PLAN = {"tiny_B1_E8_k2_H256_I128": (6, None), "wide_B1_E128_k8_H2048_I768": (3, None),
+        "batch_B8_E128_k8_H2048_I768": (2, None), "batch_B32_E128_k8_H4096_I1536": (1, [0, 31]),
+        "skewed_B64_E256_k8_H7168_I2048": (1, [0, 63])}
+
+
+def _deq(q, s):
+    return (q.view(torch.float8_e4m3fn).double() *
+            s.view(torch.float8_e8m0fnu).double().repeat_interleave(32, -1)).numpy()
+
+
+@pytest.mark.parametrize("name", list(PLAN))
+def test_accuracy_vs_full_precision_reference(name):
+    assert torch.cuda.is_available()
+    md.load()
+    nseeds, toks = PLAN[name]
+    rows = []
+    for s in range(nseeds):
+        L = synth.make_layer(name, seed=synth.workload_seed(name) + 100 * s, device="cuda", keep_dense=True)
+        t = list(range(L.shape.B)) if toks is None else toks
+        x, ids, w = md.layer_device_inputs(L)
+        outs = {}
+        for key, od, idt in (("ours_bf16", torch.bfloat16, torch.float32), ("ours_f32", torch.float32, torch.float32),
+                             ("bf16_inter", torch.float32, torch.bfloat16)):
+            o = md.moe_decode(x, ids, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                              out_dtype=od, inter_dtype=idt)
+            torch.cuda.synchronize()
+            outs[key] = o.double().cpu().numpy()[t]
+        sel = sorted({int(e) for e in L.ids[t].ravel()})
+        remap = np.full(L.shape.E, -1)
+        remap[sel] = np.arange(len(sel))
+        ids_c = remap[L.ids[t]].astype(np.int32)
+        idx = torch.tensor(sel, device="cuda")
+        pick = lambda z: z.index_select(0, idx).cpu()
+        xd = synth.bf16_bits_to_float64(L.x[t])
+        A = acc.reference_dense(xd, ids_c, L.w[t], pick(L.dense["gate"]).numpy(), pick(L.dense["up"]).numpy(),
+                                pick(L.dense["down"]).numpy())
+        Bref = oracle.moe_decode(np.ascontiguousarray(L.x[t]), ids_c, np.ascontiguousarray(L.w[t]),
+                                 pick(L.wg_q), pick(L.wg_s), pick(L.wu_q), pick(L.wu_s), pick(L.wd_q), pick(L.wd_s))
+        cls = acc.classical_emulation(xd, ids_c, L.w[t], _deq(pick(L.wg_q), pick(L.wg_s)),
+                                      _deq(pick(L.wu_q), pick(L.wu_s)), _deq(pick(L.wd_q), pick(L.wd_s)))
+        r = {k: acc.error_stats(v, A) for k, v in outs.items()}
+        r["classical"] = acc.error_stats(cls, A)
+        r["ours_f32_vs_oracle"] = acc.error_stats(outs["ours_f32"], Bref)
+        r["bf16_inter_vs_oracle"] = acc.error_stats(outs["bf16_inter"], Bref)
+        r["classical_vs_oracle"] = acc.error_stats(cls, Bref)
+        r["ratio_A"] = r["classical"]["rms_err"] / r["ours_bf16"]["rms_err"]
+        r["ratio_B"] = r["classical_vs_oracle"]["rms_err"] / max(
+            acc.error_stats(outs["ours_bf16"], Bref)["rms_err"], 1e-300)
+        rows.append(r)
+        del L
+        torch.cuda.empty_cache()
+    summary = {"workload": name, "seeds": nseeds, "tokens": "all" if toks is None else toks,
+               "ratio_A_mean": float(np.mean([r["ratio_A"] for r in rows])),
+               "ratio_B_mean": float(np.mean([r["ratio_B"] for r in rows])),
+               "ours_bf16_vs_A_rms_over_rms": float(np.mean([r["ours_bf16"]["rms_err_over_rms"] for r in rows])),
+               "classical_vs_A_rms_over_rms": float(np.mean([r["classical"]["rms_err_over_rms"] for r in rows])),
+               "ours_f32_vs_oracle_max_over_rms": float(max(r["ours_f32_vs_oracle"]["max_err_over_rms"] for r in rows)),
+               "ours_f32_vs_oracle_min_cosine": float(min(r["ours_f32_vs_oracle"]["min_cosine"] for r in rows)),
+               "bf16_inter_vs_oracle_max_over_rms": float(max(r["bf16_inter_vs_oracle"]["max_err_over_rms"] for r in rows)),
+               "classical_vs_oracle_max_over_rms": float(max(r["classical_vs_oracle"]["max_err_over_rms"] for r in rows))}
+    print("ACCURACY " + json.dumps(summary), flush=True)
+    sys.stdout.flush()
+    assert summary["ours_f32_vs_oracle_max_over_rms"] <= 2e-3
+    assert summary["ratio_A_mean"] > 1.0          # closer to full precision than the classical path
