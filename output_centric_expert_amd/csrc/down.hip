@@ -124,12 +124,94 @@ moe_down_kernel(DownArgs p)
 // LDS-staged variant (used when a[b] fits in LDS): the waves of a workgroup
 // all serve the same token b, so a[b][:][:] is copied once per workgroup
 // into LDS and every wave reads its chunks from there instead of from L2.
-// Still one wavefront per output. The first slot group's weight loads are
-// issued before the copy, so the HBM latency of the weights overlaps the
-// L2 latency of the copy; the copy keeps the chunk-interleaved order, so the
-// per-chunk LDS reads are contiguous across lanes (no bank conflicts).
+// Still one wavefront per output. The first kCopyRegs units per thread of the
+// copy are loaded, then the first slot group's weights; since loads retire in
+// issue order, the LDS writes wait only for the copy, and each slot's FMAs
+// start as soon as that slot's weights have arrived. The copy keeps the
+// chunk-interleaved order, so the per-chunk LDS reads are contiguous across
+// lanes (no bank conflicts).
+constexpr int kCopyRegs = 4;                  // a[b] units per thread loaded ahead of the weights
+
+// One slot group (JB routed slots x CPL chunks per lane) of the staged down
+// kernel: issue its weight and scale loads ... Every load is unconditional
+// from a clamped, in-bounds address (a lane past the end of the row re-reads
+// the row's last chunk, an invalid expert id reads expert 0's row); lanes that
+// must not contribute get the scale factor 0 (or NaN for an invalid id, which
+// makes the token's output NaN). Without branches around the loads all of them
+// issue back to back.
+template <int CPL, int JB, bool NT>
+__device__ __forceinline__ void down_group_load(const DownArgs& p, const int* ids, const float* wts, int j0,
+                                                int o0, int h, bool active, int lane, int cpr,
+                                                u32x4 (&wq)[JB][CPL], uint32_t (&ws)[JB][CPL], float (&wt)[JB],
+                                                float (&mask)[JB][CPL])
+{
+    const int k = p.k;
+    const int I = p.I;
+    int eid[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int jc = j0 + jj < k ? j0 + jj : k - 1;
+        eid[jj] = ids[jc];
+        wt[jj] = wts[jc];
+    }
+    const int hc = active ? h : 0;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const bool live = active && (j0 + jj) < k;
+        const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
+        const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
+        const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wd_q + row * (size_t)I);
+        const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int o = o0 + lane + kWave * cc;
+            const int oc = o < cpr ? o : cpr - 1;
+            wq[jj][cc] = ld<NT>(wrow + oc);
+            ws[jj][cc] = srow[oc >> 1];
+            mask[jj][cc] = (live && o < cpr) ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+        }
+    }
+}
+
+// ... and fold it into the accumulator, reading a from LDS.
+template <int CPL, int JB, bool A_BF16>
+__device__ __forceinline__ float down_group_dot(const u32x4* a_lds, int k, int j0, int o0, int lane, int cpr,
+                                                const u32x4 (&wq)[JB][CPL], const uint32_t (&ws)[JB][CPL],
+                                                const float (&wt)[JB], const float (&mask)[JB][CPL], float acc)
+{
+    constexpr int NA = A_BF16 ? 2 : 4;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj < k ? j0 + jj : k - 1;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int o = o0 + lane + kWave * cc;
+            u32x4 av[NA];
+            const int base = (j * NA) * cpr + (o < cpr ? o : cpr - 1);
+#pragma unroll
+            for (int t = 0; t < NA; ++t)
+                av[t] = a_lds[base + t * cpr];
+            float part = 0.0f;
+            if constexpr (A_BF16) {
+                part = dot4_bf16(wq[jj][cc].x, av[0].x, av[0].y, part);
+                part = dot4_bf16(wq[jj][cc].y, av[0].z, av[0].w, part);
+                part = dot4_bf16(wq[jj][cc].z, av[1].x, av[1].y, part);
+                part = dot4_bf16(wq[jj][cc].w, av[1].z, av[1].w, part);
+            } else {
+                part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[0]), part);
+                part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[1]), part);
+                part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[2]), part);
+                part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[3]), part);
+            }
+            // fold the routing weight into the one accumulator
+            acc = __builtin_fmaf(wt[jj] * mask[jj][cc], part * ue8m0_to_f32(ws[jj][cc]), acc);
+        }
+    }
+    return acc;
+}
+
 template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(512)
 moe_down_staged_kernel(DownArgs p)
 {
     extern __shared__ u32x4 a_lds[];
@@ -141,84 +223,47 @@ moe_down_staged_kernel(DownArgs p)
     const int h = (blockIdx.x % nblk_h) * wpb + (int)(threadIdx.x / kWave);
     const bool active = h < p.H;                  // idle waves still help copy a[b]
     const int k = p.k;
-    const int I = p.I;
-    const int cpr = I / 16;
+    const int cpr = p.I / 16;
     const int nunits = k * NA * cpr;              // 16-byte units of a[b]
     const int* ids = p.ids + (size_t)b * k;
     const float* wts = p.w + (size_t)b * k;
+    const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
 
-    float acc = 0.0f;
+    // 1) the first kCopyRegs units per thread of a[b], 2) the first group's
+    // weights, 3) the LDS writes (which wait only for the copy), one barrier
+    u32x4 cp[kCopyRegs];
+#pragma unroll
+    for (int q = 0; q < kCopyRegs; ++q) {
+        const int u = (int)threadIdx.x + q * (int)blockDim.x;
+        cp[q] = u < nunits ? asrc[u] : u32x4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 wq[JB][CPL];
+    uint32_t ws[JB][CPL];
+    float wt[JB];
+    float mask[JB][CPL];
+    down_group_load<CPL, JB, NT>(p, ids, wts, 0, 0, h, active, lane, cpr, wq, ws, wt, mask);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kCopyRegs; ++q) {
+        const int u = (int)threadIdx.x + q * (int)blockDim.x;
+        if (u < nunits)
+            a_lds[u] = cp[q];
+    }
+    for (int u = (int)threadIdx.x + kCopyRegs * (int)blockDim.x; u < nunits; u += blockDim.x)
+        a_lds[u] = asrc[u];
+    __syncthreads();
+    if (!active)
+        return;                                   // after the only barrier
+
+    float acc = down_group_dot<CPL, JB, A_BF16>(a_lds, k, 0, 0, lane, cpr, wq, ws, wt, mask, 0.0f);
+    // remaining row passes and slot groups (none when one group covers the layer)
     for (int j0 = 0; j0 < k; j0 += JB) {
-        int e[JB];
-        float wt[JB];
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-            const int j = j0 + jj;
-            const int jc = j < k ? j : k - 1;
-            e[jj] = j < k ? ids[jc] : -1;
-            wt[jj] = j < k ? wts[jc] : 0.0f;
-        }
-        for (int o0 = 0; o0 < cpr; o0 += kWave * CPL) {
-            u32x4 wq[JB][CPL];
-            uint32_t ws[JB][CPL];
-#pragma unroll
-            for (int jj = 0; jj < JB; ++jj) {
-                const bool live = active && (j0 + jj) < k;
-                const bool ok = (unsigned)e[jj] < (unsigned)p.E;
-                const size_t row = (size_t)(ok ? e[jj] : 0) * (size_t)p.H + (size_t)(active ? h : 0);
-                const uint8_t* wrow = p.wd_q + row * (size_t)I;
-                const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int o = o0 + lane + kWave * cc;
-                    if (live && ok && o < cpr) {
-                        wq[jj][cc] = ld<NT>(reinterpret_cast<const u32x4*>(wrow) + o);
-                        ws[jj][cc] = srow[o >> 1];
-                    } else {
-                        wq[jj][cc] = u32x4{0, 0, 0, 0};
-                        ws[jj][cc] = (live && !ok) ? 255u : 127u;   // invalid routing -> NaN
-                    }
-                }
-            }
-            if (j0 == 0 && o0 == 0) {             // copy a[b] into LDS once
-                const u32x4* src = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
-#pragma unroll 4
-                for (int u = threadIdx.x; u < nunits; u += blockDim.x)
-                    a_lds[u] = src[u];
-                __syncthreads();
-            }
-            if (!active)
-                return;                           // after the only barrier
-#pragma unroll
-            for (int jj = 0; jj < JB; ++jj) {
-                const int j = j0 + jj < k ? j0 + jj : 0;
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int o = o0 + lane + kWave * cc;
-                    u32x4 av[NA];
-                    const int base = (j * NA) * cpr + (o < cpr ? o : 0);
-#pragma unroll
-                    for (int t = 0; t < NA; ++t)
-                        av[t] = a_lds[base + t * cpr];
-                    float part = 0.0f;
-                    if constexpr (A_BF16) {
-                        part = dot4_bf16(wq[jj][cc].x, av[0].x, av[0].y, part);
-                        part = dot4_bf16(wq[jj][cc].y, av[0].z, av[0].w, part);
-                        part = dot4_bf16(wq[jj][cc].z, av[1].x, av[1].y, part);
-                        part = dot4_bf16(wq[jj][cc].w, av[1].z, av[1].w, part);
-                    } else {
-                        part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[0]), part);
-                        part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[1]), part);
-                        part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[2]), part);
-                        part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[3]), part);
-                    }
-                    acc = __builtin_fmaf(wt[jj], part * ue8m0_to_f32(ws[jj][cc]), acc);
-                }
-            }
+        for (int o0 = (j0 == 0 ? kWave * CPL : 0); o0 < cpr; o0 += kWave * CPL) {
+            down_group_load<CPL, JB, NT>(p, ids, wts, j0, o0, h, true, lane, cpr, wq, ws, wt, mask);
+            acc = down_group_dot<CPL, JB, A_BF16>(a_lds, k, j0, o0, lane, cpr, wq, ws, wt, mask, acc);
         }
     }
-    if (!active)
-        return;
     acc = wave_sum(acc);
     if (lane == 0) {
         if constexpr (OUT_BF16)
@@ -262,12 +307,12 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     // a[b] staged in LDS when it fits in 64 KiB
     const size_t lds = (size_t)p.k * (size_t)p.I * (a_bf16 ? 2u : 4u);
     const bool staged = t.dn_stage != 0 && lds <= 65536;
-    const int wpb = staged ? t.dn_wpb : (t.dn_wpb > 4 ? 4 : t.dn_wpb);
+    const int wpb = t.dn_wpb > (staged ? 8 : 4) ? (staged ? 8 : 4) : t.dn_wpb;
     const dim3 block(wpb * kWave);
     const dim3 grid(staged ? (unsigned)((long)p.B * ((p.H + wpb - 1) / wpb)) : (unsigned)((n_out + wpb - 1) / wpb));
     const bool nt = t.nt != 0;
     int jb = 8 / cpl;
-    while (jb > 1 && cpl * jb > cap)
+    while (jb > 1 && (cpl * jb > cap || jb / 2 >= p.k))
         jb /= 2;
     switch (cpl * 16 + jb) {
     case 1 * 16 + 8: return dispatch_v<1, 8>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);

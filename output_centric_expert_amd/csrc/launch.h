@@ -10,7 +10,7 @@ namespace moed {
 // can override them for sweeps.
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
-    int dn_wpb = 8;     // down: wavefronts per workgroup (1..16; at most 4 unstaged)
+    int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 1;         // 1 = non-temporal (streaming) weight loads

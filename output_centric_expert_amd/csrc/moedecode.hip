@@ -225,7 +225,7 @@ int moed_set_tuning(const char* spec)
         if (!end || *end)
             return MOED_ERR_SHAPE;
         if (!strcmp(tok, "gu_wpb") && v >= 1 && v <= 4) t.gu_wpb = (int)v;
-        else if (!strcmp(tok, "dn_wpb") && v >= 1 && v <= 16) t.dn_wpb = (int)v;
+        else if (!strcmp(tok, "dn_wpb") && v >= 1 && v <= 8) t.dn_wpb = (int)v;
         else if (!strcmp(tok, "dn_stage") && (v == 0 || v == 1)) t.dn_stage = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && (v == 0 || v == 1)) t.nt = (int)v;

@@ -135,10 +135,14 @@ __device__ __forceinline__ size_t inter_index(int bj, int i, int I)
         return (((size_t)bj * 4 + (size_t)((i >> 2) & 3)) * cpr + o) * 4 + (size_t)(i & 3);
 }
 
-// SiLU(g) * u with SiLU(t) = t / (1 + exp(-t)); exp overflow gives -0, not NaN.
+// SiLU(g) * u with SiLU(t) = t / (1 + exp(-t)), from the hardware base-2
+// exponential and reciprocal (v_exp_f32, v_rcp_f32; about 1e-6 relative for
+// |t| < 100). Overflow of exp(-t) gives rcp(inf) = 0, so the result is -0,
+// never NaN.
 __device__ __forceinline__ float swiglu(float g, float u)
 {
-    return g / (1.0f + expf(-g)) * u;
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 }  // namespace moed
