@@ -3,12 +3,13 @@
 // "How the two kernels work", first two paragraphs), laid out for 64-lane
 // CDNA4 wavefronts.
 //
-// Wave w owns (b, j, i) with w = (b*k + j)*I + i. It reads e = ids[b][j] with
-// a scalar load, then streams the gate row Wg[e][i][:] and the up row
-// Wu[e][i][:] in 16-byte chunks: chunk c (16 codes) goes to lane c % 64, so
-// each wave-wide load instruction covers 1 KiB of one row contiguously. Every
-// load of a pass is issued before the first FMA. The matching 16 bf16
-// activations x[b][16c..16c+15] are loaded once and used by both projections.
+// Wave w owns (b, j, i) with w = (b*k + j)*I + i. It first issues the loads
+// of its 16 bf16 activations per chunk, x[b][16c..16c+15] (used by both
+// projections), then reads e = ids[b][j] with a scalar load and streams the
+// gate row Wg[e][i][:] and the up row Wu[e][i][:] in 16-byte chunks: chunk c
+// (16 codes) goes to lane c % 64, so each wave-wide load instruction covers
+// 1 KiB of one row contiguously. Every load of a pass is issued before the
+// first FMA, without branches around them.
 // Each lane keeps two FP32 accumulators (gate, up); after the row the 64
 // partials are reduced with DPP/ds_swizzle and one value SiLU(g)*u is stored,
 // at its place in the chunk-interleaved intermediate layout (inter_index).
@@ -30,50 +31,45 @@ moe_gate_up_kernel(GateUpArgs p)
     const int i = wave % p.I;
     const int bj = wave / p.I;
     const int b = bj / p.k;
-    const int e = p.ids[bj];
-
-    const size_t a_idx = inter_index<A_BF16>(bj, i, p.I);
-    if ((unsigned)e >= (unsigned)p.E) {           // invalid routing: NaN, no weight read
-        if (lane == 0) {
-            if constexpr (A_BF16)
-                static_cast<uint16_t*>(p.a)[a_idx] = 0x7FC0u;
-            else
-                static_cast<float*>(p.a)[a_idx] = __builtin_nanf("");
-        }
-        return;
-    }
-
     const int H = p.H;
     const int nch = H / 16;                       // 16-code chunks per row
-    const size_t row = (size_t)e * (size_t)p.I + (size_t)i;
-    const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * (size_t)H);
-    const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * (size_t)H);
-    const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
-    const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
     const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
 
     float g = 0.0f, u = 0.0f;
+    bool bad_id = false;
     for (int base = 0; base < nch; base += kWave * U) {
-        u32x4 wg[U], wu[U], xa[U], xb[U];
-        uint32_t sg[U], su[U];
+        // x first: its address does not depend on the routed id, so these loads
+        // overlap the id's scalar load. Every load is unconditional from a
+        // clamped, in-bounds address; chunks past the row end get scale 0.
+        u32x4 xa[U], xb[U];
 #pragma unroll
         for (int m = 0; m < U; ++m) {
             const int c = base + lane + kWave * m;
-            if (c < nch) {
-                wg[m] = ld<NT>(gq + c);
-                wu[m] = ld<NT>(uq + c);
-                sg[m] = gs[c >> 1];
-                su[m] = us[c >> 1];
-                xa[m] = xq[2 * c];
-                xb[m] = xq[2 * c + 1];
-            } else {
-                wg[m] = u32x4{0, 0, 0, 0};
-                wu[m] = u32x4{0, 0, 0, 0};
-                xa[m] = u32x4{0, 0, 0, 0};
-                xb[m] = u32x4{0, 0, 0, 0};
-                sg[m] = 127u;
-                su[m] = 127u;
-            }
+            const int cc = c < nch ? c : nch - 1;
+            xa[m] = xq[2 * cc];
+            xb[m] = xq[2 * cc + 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int e_raw = p.ids[bj];
+        bad_id = (unsigned)e_raw >= (unsigned)p.E;   // invalid routing: expert 0's rows are read, result NaN
+        const int e = bad_id ? 0 : e_raw;
+        const size_t row = (size_t)e * (size_t)p.I + (size_t)i;
+        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * (size_t)H);
+        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * (size_t)H);
+        const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+        const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+        u32x4 wg[U], wu[U];
+        uint32_t sg[U], su[U];
+        float live[U];
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            const int c = base + lane + kWave * m;
+            const int cc = c < nch ? c : nch - 1;
+            wg[m] = ld<NT>(gq + cc);
+            wu[m] = ld<NT>(uq + cc);
+            sg[m] = gs[cc >> 1];
+            su[m] = us[cc >> 1];
+            live[m] = c < nch ? 1.0f : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < U; ++m) {
@@ -97,14 +93,15 @@ moe_gate_up_kernel(GateUpArgs p)
                 pg = dot4_f32(wg[m].w, xb[m].z, xb[m].w, pg);
                 pu = dot4_f32(wu[m].w, xb[m].z, xb[m].w, pu);
             }
-            g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]), g);
-            u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]), u);
+            g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g);
+            u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u);
         }
     }
     g = wave_sum(g);
     u = wave_sum(u);
     if (lane == 0) {
-        const float v = swiglu(g, u);
+        const float v = bad_id ? __builtin_nanf("") : swiglu(g, u);
+        const size_t a_idx = inter_index<A_BF16>(bj, i, p.I);
         if constexpr (A_BF16)
             static_cast<uint16_t*>(p.a)[a_idx] = f32_to_bf16_rne(v);
         else
