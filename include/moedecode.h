@@ -129,8 +129,10 @@ int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
  * Diagnostic: decode n MXFP8 values with the kernels' own in-register decoder.
  * out[t] = E4M3(codes[t]) * 2^(scales[t]-127) as float32, through both decode
  * routes the kernels use (path 0: FP8 -> FP32 conversion; path 1: FP8 -> BF16
- * conversion), so a test can compare every code bit for bit with the format
- * definition. Device pointers; n >= 0.
+ * conversion, scale applied afterwards), so a test can compare every code bit for bit with the format
+ * definition; path 2 is the large-batch route, FP8 -> BF16 with the block
+ * scale folded into the conversion (exact for scale codes 10..245).
+ * Device pointers; n >= 0; path in {0, 1, 2}.
  */
 int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out,
                          int n, int path, void *stream);
@@ -159,7 +161,8 @@ int moed_last_hip_error(void);
 /*
  * Benchmark-only tuning override (NOT thread-safe; meant for launch-shape
  * sweeps). `spec` is a comma-separated list of key=value pairs, e.g.
- * "gu_wpb=4,dn_wpb=2,gu_dot=1,nt=0"; NULL or "" restores the built-in table.
+ * "gu_wpb=4,dn_wpb=2,gu_dot=1,nt=0,gu_group=2"; NULL or "" restores the
+ * built-in table.
  * Returns MOED_OK, or MOED_ERR_SHAPE for an unknown key or value.
  */
 int moed_set_tuning(const char *spec);

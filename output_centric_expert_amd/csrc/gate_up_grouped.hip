@@ -1,0 +1,209 @@
+// Gate/up for large decode batches: the same outputs a[b][j][i] as the
+// per-slot kernel, computed so that each expert's rows are decoded once per
+// 16 slots instead of once per slot.
+//
+// When many tokens share an expert (batch 32-64 with top-8 of 128-256
+// experts), the per-slot kernel re-reads and re-decodes every routed row once
+// per (token, slot): 2-10x the unique weight bytes. Here a workgroup owns
+// (expert e, 64 neurons); it compacts the list of slots routed to e (in slot
+// order, from topk_ids), and each wavefront computes a tile of 16 neurons x
+// 16 of those slots with MFMA:
+//   A = the gate (or up) rows, decoded exactly from MXFP8 to BF16 with the
+//       block scale folded into the conversion (v_cvt_scalef32_pk_bf16_fp8;
+//       exact for scale codes 10..245, where the scaled E4M3 values stay
+//       normal, finite BF16 numbers),
+//   B = the BF16 activations of the 16 slots' tokens,
+//   D = FP32 accumulators (v_mfma_f32_16x16x32_bf16, products exact in FP32).
+// Each output is still written once, by the one lane that holds it, as
+// SiLU(g) * u into the chunk-interleaved intermediate. There is no gather of
+// activations and no per-expert buffer: the slot list is an index list in LDS.
+//
+// MFMA lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies A row l%16 and
+// B column l%16, both for k = 8*(l/16) .. +7, and receives D rows
+// 4*(l/16) .. +3 of column l%16.
+#include "launch.h"
+#include "mx_device.h"
+
+namespace moed {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroupWaves = 4;                  // wavefronts per workgroup, 16 neurons each
+constexpr int kGroupNeurons = 16 * kGroupWaves;
+constexpr int kUK = 4;                          // K steps (of 32) whose loads are issued together
+
+// 8 E4M3 codes (two dwords) times 2^(s-127) -> 8 BF16 values, exactly.
+__device__ __forceinline__ bf16x8 decode8_scaled(u32x2 codes, float scale)
+{
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Deterministic compaction: slots[0..count) = the indices t < n (in increasing
+// order) with pred(t). All threads of the workgroup must call it.
+template <typename Pred>
+__device__ __forceinline__ int compact_slots(int n, int* slots, int* wave_cnt, Pred pred)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    int total = 0;
+    for (int base = 0; base < n; base += kGroupWaves * kWave) {
+        const int t = base + tid;
+        const bool f = t < n && pred(t);
+        const unsigned long long m = __ballot(f);
+        const int before = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wave_cnt[w] = __popcll(m);
+        __syncthreads();
+        int off = total;
+        for (int q = 0; q < w; ++q)
+            off += wave_cnt[q];
+        if (f)
+            slots[off + before] = t;
+        int sum = 0;
+        for (int q = 0; q < kGroupWaves; ++q)
+            sum += wave_cnt[q];
+        __syncthreads();
+        total += sum;
+    }
+    return total;
+}
+
+template <bool A_BF16, bool NT>
+__global__ void __launch_bounds__(kGroupWaves * kWave)
+moe_gate_up_grouped_kernel(GateUpArgs p)
+{
+    extern __shared__ int slots[];               // B*k entries
+    __shared__ int wave_cnt[kGroupWaves];
+    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
+    const int e = blockIdx.x / nblk;
+    const int n_block = (blockIdx.x % nblk) * kGroupNeurons;
+    const int nslots = p.B * p.k;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int* ids = p.ids;
+    const int E = p.E;
+    const int I = p.I;
+    const int H = p.H;
+
+    // slots routed to an id outside [0, E) get NaN, written by expert 0's workgroups
+    if (e == 0) {
+        const int nbad = compact_slots(nslots, slots, wave_cnt,
+                                       [&](int t) { return (unsigned)ids[t] >= (unsigned)E; });
+        for (int q = threadIdx.x; q < nbad * kGroupNeurons; q += blockDim.x) {
+            const int bj = slots[q / kGroupNeurons];
+            const int i = n_block + q % kGroupNeurons;
+            if (i < I) {
+                const size_t idx = inter_index<A_BF16>(bj, i, I);
+                if constexpr (A_BF16)
+                    static_cast<uint16_t*>(p.a)[idx] = 0x7FC0u;
+                else
+                    static_cast<float*>(p.a)[idx] = __builtin_nanf("");
+            }
+        }
+        __syncthreads();                          // the list is reused below
+    }
+    const int count = compact_slots(nslots, slots, wave_cnt, [&](int t) { return ids[t] == e; });
+    if (count == 0)
+        return;                                   // whole workgroup: no barrier follows
+    const int n0 = n_block + 16 * w;              // this wavefront's 16 neurons
+    if (n0 >= I)
+        return;
+
+    const int kb = lane / 16;                     // which 8-wide k block of a 32-step
+    const int col = lane % 16;                    // A row (neuron) / B column (slot)
+    const size_t row = (size_t)e * (size_t)I + (size_t)(n0 + col);
+    const uint8_t* gq = p.wg_q + row * (size_t)H + 8 * kb;
+    const uint8_t* uq = p.wu_q + row * (size_t)H + 8 * kb;
+    const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+    const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+    const int nsteps = H / 32;
+
+    for (int s0 = 0; s0 < count; s0 += 16) {
+        const int sidx = s0 + col < count ? s0 + col : count - 1;   // extra columns repeat a slot
+        const int bj = slots[sidx];
+        const int b = bj / p.k;
+        const uint16_t* xr = p.x + (size_t)b * (size_t)H + 8 * kb;
+        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 du = {0.0f, 0.0f, 0.0f, 0.0f};
+        int st = 0;
+        for (; st + kUK <= nsteps; st += kUK) {
+            u32x2 cg[kUK], cu[kUK];
+            uint32_t sg[kUK], su[kUK];
+            u32x4 xv[kUK];
+#pragma unroll
+            for (int q = 0; q < kUK; ++q) {
+                const int k0 = (st + q) * 32;
+                cg[q] = ld<NT>(reinterpret_cast<const u32x2*>(gq + k0));
+                cu[q] = ld<NT>(reinterpret_cast<const u32x2*>(uq + k0));
+                sg[q] = gs[st + q];
+                su[q] = us[st + q];
+                xv[q] = *reinterpret_cast<const u32x4*>(xr + k0);
+            }
+#pragma unroll
+            for (int q = 0; q < kUK; ++q) {
+                const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[q]);
+                dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cg[q], ue8m0_to_f32(sg[q])), bx, dg, 0, 0, 0);
+                du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cu[q], ue8m0_to_f32(su[q])), bx, du, 0, 0, 0);
+            }
+        }
+        for (; st < nsteps; ++st) {
+            const int k0 = st * 32;
+            const u32x2 cg = ld<NT>(reinterpret_cast<const u32x2*>(gq + k0));
+            const u32x2 cu = ld<NT>(reinterpret_cast<const u32x2*>(uq + k0));
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k0);
+            const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
+            dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cg, ue8m0_to_f32(gs[st])), bx, dg, 0, 0, 0);
+            du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cu, ue8m0_to_f32(us[st])), bx, du, 0, 0, 0);
+        }
+        // lane holds D rows 4*kb .. +3 (neurons) of column col (slot s0 + col)
+        if (s0 + col < count) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = n0 + 4 * kb + r;
+                const float v = swiglu(dg[r], du[r]);
+                const size_t idx = inter_index<A_BF16>(bj, i, I);
+                if constexpr (A_BF16)
+                    static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
+                else
+                    static_cast<float*>(p.a)[idx] = v;
+            }
+        }
+    }
+}
+
+size_t gate_up_grouped_lds(int B, int k)
+{
+    return (size_t)B * (size_t)k * sizeof(int);
+}
+
+hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s)
+{
+    if ((long)p.B * p.k == 0)
+        return hipSuccess;
+    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
+    const dim3 grid((unsigned)((long)p.E * nblk));
+    const dim3 block(kGroupWaves * kWave);
+    const size_t lds = gate_up_grouped_lds(p.B, p.k);
+    // rows are re-read for every further 16-slot tile: keep them cacheable
+    const bool nt = false;
+    (void)t;
+    if (a_bf16) {
+        if (nt) hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p);
+        else hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p);
+    } else {
+        if (nt) hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p);
+        else hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moed

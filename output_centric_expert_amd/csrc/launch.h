@@ -15,6 +15,8 @@ struct Tuning {
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 1;         // 1 = non-temporal (streaming) weight loads
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
+    int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
+                        // MFMA tiles (rows decoded once per 16 slots); 2 = choose by batch size
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
 };
 
@@ -41,6 +43,8 @@ struct DownArgs {
 };
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
+hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
+size_t gate_up_grouped_lds(int B, int k);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

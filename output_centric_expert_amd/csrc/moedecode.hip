@@ -48,6 +48,25 @@ moed::Tuning pick(int B, int H, int I)
     return t;
 }
 
+// Expert-grouped gate/up pays off once there are about two or more slots per
+// expert on average (each routed row then serves several tokens); its slot
+// list must fit in 64 KiB of LDS.
+bool use_grouped(const moed::Tuning& t, int B, int E, int k)
+{
+    if (moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
+        return false;
+    if (t.gu_group == 1)
+        return true;
+    return (long)B * k >= 2L * E;
+}
+
+hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tuning& t, hipStream_t s)
+{
+    if (use_grouped(t, p.B, p.E, p.k))
+        return moed::launch_gate_up_grouped(p, a_bf16, t, s);
+    return moed::launch_gate_up(p, a_bf16, t, s);
+}
+
 moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
                               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
                               void* a, int B, int E, int k, int H, int I)
@@ -97,8 +116,8 @@ int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(a))
         return MOED_ERR_ALIGN;
     const moed::Tuning t = pick(B, H, I);
-    return hip_status(moed::launch_gate_up(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a, B, E, k, H, I),
-                                           inter_dtype == MOED_BF16, t, static_cast<hipStream_t>(stream)));
+    return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a, B, E, k, H, I),
+                                     inter_dtype == MOED_BF16, t, static_cast<hipStream_t>(stream)));
 }
 
 int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
@@ -141,7 +160,7 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
     const moed::Tuning t = pick(B, H, I);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool a_bf16 = inter_dtype == MOED_BF16;
-    int st = hip_status(moed::launch_gate_up(
+    int st = hip_status(gate_up_launch(
         gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, workspace, B, E, k, H, I), a_bf16, t, s));
     if (st)
         return st;
@@ -153,7 +172,7 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
 int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n, int path,
                          void* stream)
 {
-    if (n < 0 || (path != 0 && path != 1))
+    if (n < 0 || path < 0 || path > 2)
         return MOED_ERR_SHAPE;
     if (n == 0)
         return MOED_OK;
@@ -230,6 +249,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && (v == 0 || v == 1)) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
+        else if (!strcmp(tok, "gu_group") && v >= 0 && v <= 2) t.gu_group = (int)v;
         else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;
         else return MOED_ERR_SHAPE;
     }

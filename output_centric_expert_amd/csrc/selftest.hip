@@ -19,6 +19,13 @@ moe_selftest_decode_kernel(const uint8_t* codes, const uint8_t* scales, float* o
     const int pos = t & 3;
     const uint32_t word = (0x5A5A5A5Au & ~(0xFFu << (8 * pos))) | (c << (8 * pos));
     float v;
+    if (path == 2) {
+        // the grouped kernel's route: FP8 -> BF16 with the block scale folded in
+        const bf16x2 w = pos >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, s, true)
+                                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, s, false);
+        out[t] = (float)((pos & 1) ? w.y : w.x);
+        return;
+    }
     if (path == 0) {
         const f32x2 w = pos >= 2 ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
                                  : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);

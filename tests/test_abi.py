@@ -98,7 +98,8 @@ def test_step_entry_points_reject_before_launch(lib):
     assert dn(out=None) == md.MOED_ERR_NULL
     assert dn(wq=MIS) == md.MOED_ERR_ALIGN
     assert dn(od=3) == md.MOED_ERR_DTYPE
-    assert lib.moed_selftest_decode(A, A, A, 4, 2, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_selftest_decode(A, A, A, 4, 3, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_selftest_decode(A, A, A, 4, -1, None) == md.MOED_ERR_SHAPE
     assert lib.moed_selftest_decode(None, A, A, 4, 0, None) == md.MOED_ERR_NULL
     assert lib.moed_selftest_decode(None, None, None, 0, 0, None) == md.MOED_OK
 
@@ -106,6 +107,8 @@ def test_step_entry_points_reject_before_launch(lib):
 def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"gu_wpb=2,dn_wpb=1,gu_dot=0,nt=1") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_wpb=9") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_group=1,dn_stage=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_group=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(None) == md.MOED_OK

@@ -106,7 +106,7 @@ def check_bf16(gpu_bf16, gpu_f32, ref, label):
 # decode self-test: every E4M3 code, both in-register routes, bit for bit
 # --------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_decode_all_codes_bit_exact(path):
     scales = [127, 100, 120, 126, 128, 134, 147]
     codes = np.tile(np.arange(256, dtype=np.uint8), len(scales))
@@ -125,7 +125,7 @@ def test_decode_all_codes_bit_exact(path):
 def test_decode_nan_scale():
     codes = torch.tensor([0x38, 0x00, 0x81], dtype=torch.uint8).cuda()
     sc = torch.full((3,), 255, dtype=torch.uint8).cuda()
-    for path in (0, 1):
+    for path in (0, 1, 2):
         assert torch.isnan(md.moed_selftest_decode(codes, sc, path)).all()
 
 
@@ -167,13 +167,20 @@ def test_workload_sampled_parity(name):
     check_f32(out32[toks], ref, name)
     out16 = run(L, torch.bfloat16)
     check_bf16(out16[toks], out32[toks], ref, name)
-    # batch = concatenation of single-token calls, bit for bit
+    # batch = concatenation of single-token calls, bit for bit, on each gate/up path
+    # (the per-slot and the expert-grouped paths accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for b in toks[:2]:
-        one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
-                            L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32)
-        torch.cuda.synchronize()
-        assert torch.equal(one[0], out32[b])
+    for spec in ("gu_group=0", "gu_group=1"):
+        md.moed_set_tuning(spec)
+        try:
+            full = run(L, torch.float32)
+            for b in toks[:2]:
+                one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
+                                    L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32)
+                torch.cuda.synchronize()
+                assert torch.equal(one[0], full[b]), spec
+        finally:
+            md.moed_set_tuning(None)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -222,7 +229,8 @@ def test_ragged_shapes(shape):
 
 
 @pytest.mark.parametrize("spec", ["gu_dot=0", "gu_dot=1", "nt=1", "gu_wpb=1,dn_wpb=1", "gu_wpb=2,dn_wpb=2",
-                                  "gu_umax=1,dn_umax=1", "gu_umax=3,dn_umax=5,gu_dot=0,nt=1"])
+                                  "gu_umax=1,dn_umax=1", "gu_umax=3,dn_umax=5,gu_dot=0,nt=1",
+                                  "gu_group=1", "gu_group=0", "dn_stage=0", "gu_group=1,nt=0"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
@@ -310,3 +318,54 @@ def test_bench_kernels():
     md.moed_bench_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# --------------------------------------------------------------------------------------
+# expert-grouped gate/up (MFMA tiles of 16 neurons x 16 slots)
+# --------------------------------------------------------------------------------------
+
+GROUPED = [
+    (40, 3, 2, 96, 160),      # ~27 slots per expert: two slot tiles, ragged rows
+    (24, 6, 4, 2080, 64),     # K steps not a multiple of the 4-step batch (65 steps)
+    (3, 40, 5, 256, 96),      # mostly single-slot experts, many empty workgroups
+    (64, 8, 8, 512, 288),     # every expert touched by many tokens
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_grouped_gate_up(shape):
+    B = shape[0]
+    L = small(*shape, seed=sum(shape) + 1)
+    ref, a_ref = oracle_tokens(L, list(range(B)))
+    md.moed_set_tuning("gu_group=1")
+    try:
+        check_f32(run(L), ref, f"grouped {shape}")
+        x, ids, _ = md.layer_device_inputs(L)
+        a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+        torch.cuda.synchronize()
+        check_f32(a.reshape(B, -1), a_ref.reshape(B, -1), f"grouped a {shape}")
+        a16 = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
+                                                    inter_dtype=torch.bfloat16))
+        torch.cuda.synchronize()
+        assert torch.isfinite(a16.float()).all()
+        # bit-exact agreement between repeated runs
+        assert torch.equal(run(L), run(L))
+    finally:
+        md.moed_set_tuning(None)
+
+
+def test_grouped_duplicates_and_invalid_ids():
+    L = small(20, 5, 3, 128, 96, seed=77)
+    ids = L.ids.copy()
+    ids[:, 1] = ids[:, 0]                 # duplicate slot in every token
+    ids[3, 2] = 5                         # out of range
+    ids[7, 0] = -1
+    md.moed_set_tuning("gu_group=1")
+    try:
+        out = run(L, ids=ids).cpu()
+    finally:
+        md.moed_set_tuning(None)
+    assert torch.isnan(out[3]).all() and torch.isnan(out[7]).all()
+    good = [b for b in range(20) if b not in (3, 7)]
+    ref, _ = oracle_tokens(L, good, ids=ids)
+    check_f32(out[good], ref, "grouped duplicates")
