@@ -28,12 +28,14 @@ moe_down_kernel(DownArgs p)
     constexpr int NA = A_BF16 ? 2 : 4;            // 16-byte pieces of a per chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (int)(threadIdx.x / kWave));
+    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(blk * wpb + (int)(threadIdx.x / kWave));
     const int n_out = p.B * p.H;
     if (wave >= n_out)
         return;
-    const int b = wave / p.H;
-    const int h = wave % p.H;
+    // token-major (w = b*H + h) or hidden-major (w = h*B + b)
+    const int b = p.order == 0 ? wave / p.H : wave % p.B;
+    const int h = p.order == 0 ? wave % p.H : wave / p.B;
     const int k = p.k;
     const int I = p.I;
     const int cpr = I / 16;                       // chunks per routed row
@@ -115,9 +117,9 @@ moe_down_kernel(DownArgs p)
     acc = wave_sum(acc);
     if (lane == 0) {
         if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(p.out)[wave] = f32_to_bf16_rne(acc);
+            static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h] = f32_to_bf16_rne(acc);
         else
-            static_cast<float*>(p.out)[wave] = acc;
+            static_cast<float*>(p.out)[(size_t)b * p.H + h] = acc;
     }
 }
 
@@ -219,8 +221,10 @@ moe_down_staged_kernel(DownArgs p)
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
     const int nblk_h = (p.H + wpb - 1) / wpb;
-    const int b = blockIdx.x / nblk_h;
-    const int h = (blockIdx.x % nblk_h) * wpb + (int)(threadIdx.x / kWave);
+    // workgroup (b, hb): token-major (b*nblk_h + hb) or hidden-major (hb*B + b)
+    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int b = p.order == 0 ? blk / nblk_h : blk % p.B;
+    const int h = (p.order == 0 ? blk % nblk_h : blk / p.B) * wpb + (int)(threadIdx.x / kWave);
     const bool active = h < p.H;                  // idle waves still help copy a[b]
     const int k = p.k;
     const int cpr = p.I / 16;
@@ -310,21 +314,23 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     const int wpb = t.dn_wpb > (staged ? 8 : 4) ? (staged ? 8 : 4) : t.dn_wpb;
     const dim3 block(wpb * kWave);
     const dim3 grid(staged ? (unsigned)((long)p.B * ((p.H + wpb - 1) / wpb)) : (unsigned)((n_out + wpb - 1) / wpb));
-    const bool nt = t.nt != 0;
+    const bool nt = t.nt == 2 ? (long)p.B * p.k < (long)p.E : t.nt != 0;
+    DownArgs q = p;
+    q.order = t.dn_order;
     int jb = 8 / cpl;
     while (jb > 1 && (cpl * jb > cap || jb / 2 >= p.k))
         jb /= 2;
     switch (cpl * 16 + jb) {
-    case 1 * 16 + 8: return dispatch_v<1, 8>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 1 * 16 + 4: return dispatch_v<1, 4>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 1 * 16 + 2: return dispatch_v<1, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 1 * 16 + 1: return dispatch_v<1, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 2 * 16 + 4: return dispatch_v<2, 4>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 2 * 16 + 2: return dispatch_v<2, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 2 * 16 + 1: return dispatch_v<2, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 4 * 16 + 2: return dispatch_v<4, 2>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 4 * 16 + 1: return dispatch_v<4, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
-    case 8 * 16 + 1: return dispatch_v<8, 1>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 16 + 8: return dispatch_v<1, 8>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 4: return dispatch_v<1, 4>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 2: return dispatch_v<1, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 1: return dispatch_v<1, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 4: return dispatch_v<2, 4>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 2: return dispatch_v<2, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 1: return dispatch_v<2, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 4 * 16 + 2: return dispatch_v<4, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 4 * 16 + 1: return dispatch_v<4, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 8 * 16 + 1: return dispatch_v<8, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -6,8 +6,8 @@
 // experts), the per-slot kernel re-reads and re-decodes every routed row once
 // per (token, slot): 2-10x the unique weight bytes. Here a workgroup owns
 // (expert e, 64 neurons); it compacts the list of slots routed to e (in slot
-// order, from topk_ids), and each wavefront computes a tile of 16 neurons x
-// 16 of those slots with MFMA:
+// order, from topk_ids), and each wavefront computes tiles of 16 neurons x 16
+// of those slots (up to four tiles per pass over the rows) with MFMA:
 //   A = the gate (or up) rows, decoded exactly from MXFP8 to BF16 with the
 //       block scale folded into the conversion (v_cvt_scalef32_pk_bf16_fp8;
 //       exact for scale codes 10..245, where the scaled E4M3 values stay
@@ -31,7 +31,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroupWaves = 4;                  // wavefronts per workgroup, 16 neurons each
 constexpr int kGroupNeurons = 16 * kGroupWaves;
-constexpr int kUK = 4;                          // K steps (of 32) whose loads are issued together
+constexpr int kTiles = 4;                       // 16-slot tiles per pass over a row
 
 // 8 E4M3 codes (two dwords) times 2^(s-127) -> 8 BF16 values, exactly.
 __device__ __forceinline__ bf16x8 decode8_scaled(u32x2 codes, float scale)
@@ -77,7 +77,106 @@ __device__ __forceinline__ int compact_slots(int n, int* slots, int* wave_cnt, P
     return total;
 }
 
-template <bool A_BF16, bool NT>
+struct GroupedRow {
+    const uint8_t* gq;      // this lane's gate row (codes)
+    const uint8_t* uq;      // up row
+    const uint8_t* gs;      // gate row scales
+    const uint8_t* us;      // up row scales
+    int nsteps;             // MX blocks per row = MFMA K steps
+    int n0;                 // first neuron of the wavefront's tile
+    int kb;                 // lane / 16
+    int col;                // lane % 16
+};
+
+// One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1).
+// K is walked in groups of 4 MX blocks (128 codes); inside a group, lane
+// (row, kb) supplies block kb's 32 contiguous codes over the 4 MFMA steps
+// (8 per step) and x uses the same k order, so the products summed are the
+// row-times-x products, only in another order. One 32-byte load per row and
+// one scale byte per row per group.
+template <int NTL, bool A_BF16>
+__device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedRow& r, const int* slots,
+                                             int count, int t0)
+{
+    const int H = p.H;
+    int bj[NTL];
+    const uint16_t* xr[NTL];
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        const int si = (t0 + tt) * 16 + r.col;
+        const int sidx = si < count ? si : count - 1;   // extra columns repeat a slot
+        bj[tt] = slots[sidx];
+        xr[tt] = p.x + (size_t)(bj[tt] / p.k) * (size_t)H;
+    }
+    f32x4 dg[NTL], du[NTL];
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        dg[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        du[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    int st = 0;
+    for (; st + 4 <= r.nsteps; st += 4) {
+        const int kbase = st * 32 + 32 * r.kb;    // this lane's MX block
+        const u32x4 g0 = *reinterpret_cast<const u32x4*>(r.gq + kbase);
+        const u32x4 g1 = *reinterpret_cast<const u32x4*>(r.gq + kbase + 16);
+        const u32x4 u0 = *reinterpret_cast<const u32x4*>(r.uq + kbase);
+        const u32x4 u1 = *reinterpret_cast<const u32x4*>(r.uq + kbase + 16);
+        const float sgf = ue8m0_to_f32(r.gs[st + r.kb]);
+        const float suf = ue8m0_to_f32(r.us[st + r.kb]);
+        u32x4 xv[NTL][4];
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xv[tt][q] = *reinterpret_cast<const u32x4*>(xr[tt] + kbase + 8 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 gsrc = q < 2 ? g0 : g1;
+            const u32x4 usrc = q < 2 ? u0 : u1;
+            const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
+            const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
+            const bf16x8 ag = decode8_scaled(cgq, sgf);
+            const bf16x8 au = decode8_scaled(cuq, suf);
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt) {
+                const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[tt][q]);
+                dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
+                du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
+            }
+        }
+    }
+    for (; st < r.nsteps; ++st) {                 // leftover blocks: plain k order
+        const int k0 = st * 32 + 8 * r.kb;
+        const u32x2 cg = *reinterpret_cast<const u32x2*>(r.gq + k0);
+        const u32x2 cu = *reinterpret_cast<const u32x2*>(r.uq + k0);
+        const bf16x8 ag = decode8_scaled(cg, ue8m0_to_f32(r.gs[st]));
+        const bf16x8 au = decode8_scaled(cu, ue8m0_to_f32(r.us[st]));
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr[tt] + k0));
+            dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
+            du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
+        }
+    }
+    // lane holds D rows 4*kb .. +3 (neurons) of column col of each tile
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        if ((t0 + tt) * 16 + r.col < count) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = r.n0 + 4 * r.kb + q;
+                const float v = swiglu(dg[tt][q], du[tt][q]);
+                const size_t idx = inter_index<A_BF16>(bj[tt], i, p.I);
+                if constexpr (A_BF16)
+                    static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
+                else
+                    static_cast<float*>(p.a)[idx] = v;
+            }
+        }
+    }
+}
+
+template <bool A_BF16>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
 moe_gate_up_grouped_kernel(GateUpArgs p)
 {
@@ -118,64 +217,27 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
     if (n0 >= I)
         return;
 
-    const int kb = lane / 16;                     // which 8-wide k block of a 32-step
+    const int kb = lane / 16;                     // which quarter of a k group
     const int col = lane % 16;                    // A row (neuron) / B column (slot)
     const size_t row = (size_t)e * (size_t)I + (size_t)(n0 + col);
-    const uint8_t* gq = p.wg_q + row * (size_t)H + 8 * kb;
-    const uint8_t* uq = p.wu_q + row * (size_t)H + 8 * kb;
+    const uint8_t* gq = p.wg_q + row * (size_t)H;
+    const uint8_t* uq = p.wu_q + row * (size_t)H;
     const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
     const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
-    const int nsteps = H / 32;
+    const int nsteps = H / 32;                    // MX blocks per row = MFMA K steps
+    const int ntiles = (count + 15) / 16;
 
-    for (int s0 = 0; s0 < count; s0 += 16) {
-        const int sidx = s0 + col < count ? s0 + col : count - 1;   // extra columns repeat a slot
-        const int bj = slots[sidx];
-        const int b = bj / p.k;
-        const uint16_t* xr = p.x + (size_t)b * (size_t)H + 8 * kb;
-        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4 du = {0.0f, 0.0f, 0.0f, 0.0f};
-        int st = 0;
-        for (; st + kUK <= nsteps; st += kUK) {
-            u32x2 cg[kUK], cu[kUK];
-            uint32_t sg[kUK], su[kUK];
-            u32x4 xv[kUK];
-#pragma unroll
-            for (int q = 0; q < kUK; ++q) {
-                const int k0 = (st + q) * 32;
-                cg[q] = ld<NT>(reinterpret_cast<const u32x2*>(gq + k0));
-                cu[q] = ld<NT>(reinterpret_cast<const u32x2*>(uq + k0));
-                sg[q] = gs[st + q];
-                su[q] = us[st + q];
-                xv[q] = *reinterpret_cast<const u32x4*>(xr + k0);
-            }
-#pragma unroll
-            for (int q = 0; q < kUK; ++q) {
-                const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[q]);
-                dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cg[q], ue8m0_to_f32(sg[q])), bx, dg, 0, 0, 0);
-                du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cu[q], ue8m0_to_f32(su[q])), bx, du, 0, 0, 0);
-            }
-        }
-        for (; st < nsteps; ++st) {
-            const int k0 = st * 32;
-            const u32x2 cg = ld<NT>(reinterpret_cast<const u32x2*>(gq + k0));
-            const u32x2 cu = ld<NT>(reinterpret_cast<const u32x2*>(uq + k0));
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + k0);
-            const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
-            dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cg, ue8m0_to_f32(gs[st])), bx, dg, 0, 0, 0);
-            du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_scaled(cu, ue8m0_to_f32(us[st])), bx, du, 0, 0, 0);
-        }
-        // lane holds D rows 4*kb .. +3 (neurons) of column col (slot s0 + col)
-        if (s0 + col < count) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = n0 + 4 * kb + r;
-                const float v = swiglu(dg[r], du[r]);
-                const size_t idx = inter_index<A_BF16>(bj, i, I);
-                if constexpr (A_BF16)
-                    static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
-                else
-                    static_cast<float*>(p.a)[idx] = v;
-            }
+    // Each pass covers up to kTiles tiles of 16 slots, so a row is decoded once
+    // per 16*kTiles slots; the tile count of a pass is a template argument, so
+    // the hot loop has no per-tile branches.
+    for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
+        const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
+        const GroupedRow r{gq, uq, gs, us, nsteps, n0, kb, col};
+        switch (nt) {
+        case 1: grouped_pass<1, A_BF16>(p, r, slots, count, t0); break;
+        case 2: grouped_pass<2, A_BF16>(p, r, slots, count, t0); break;
+        case 3: grouped_pass<3, A_BF16>(p, r, slots, count, t0); break;
+        default: grouped_pass<4, A_BF16>(p, r, slots, count, t0); break;
         }
     }
 }
@@ -193,16 +255,11 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const dim3 grid((unsigned)((long)p.E * nblk));
     const dim3 block(kGroupWaves * kWave);
     const size_t lds = gate_up_grouped_lds(p.B, p.k);
-    // rows are re-read for every further 16-slot tile: keep them cacheable
-    const bool nt = false;
-    (void)t;
-    if (a_bf16) {
-        if (nt) hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p);
-        else hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p);
-    } else {
-        if (nt) hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p);
-        else hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p);
-    }
+    (void)t;                                      // rows are re-read per pass: cached loads
+    if (a_bf16)
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true>), grid, block, lds, s, p);
+    else
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false>), grid, block, lds, s, p);
     return hipGetLastError();
 }
 

@@ -12,12 +12,19 @@ struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
     int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
+    int dn_group = 0;   // down: 0 = one wavefront per output; 1 = MFMA tiles of 16 outputs x
+                        // 16 tokens (rows decoded once per 16 tokens); 2 = choose by batch size.
+                        // 0 by default: the tiled kernel has not beaten the per-output one
+                        // (hidden-major order, cached loads) on any measured batch
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
-    int nt = 1;         // 1 = non-temporal (streaming) weight loads
+    int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
+                        // except in the down kernel once B*k >= E (tokens then share rows)
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
                         // MFMA tiles (rows decoded once per 16 slots); 2 = choose by batch size
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
+    int dn_order = 1;   // down workgroup order: 0 = token-major; 1 = hidden-major, each XCD
+                        // taking a contiguous range; 2 = hidden-major, plain round robin
 };
 
 struct GateUpArgs {
@@ -40,6 +47,7 @@ struct DownArgs {
     void* out;              // [B][H] f32 or bf16
     int B, E, k, H, I;
     float inv_cpr;          // 1 / (I/16), for the chunk -> (slot, offset) split
+    int order;              // workgroup order (Tuning::dn_order)
 };
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
@@ -48,6 +56,8 @@ size_t gate_up_grouped_lds(int B, int k);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
+bool down_grouped_fits(int E, int k);
 hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
                                   int path, hipStream_t s);
 

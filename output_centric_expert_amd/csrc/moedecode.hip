@@ -67,6 +67,22 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
     return moed::launch_gate_up(p, a_bf16, t, s);
 }
 
+bool use_down_grouped(const moed::Tuning& t, int B, int E, int k)
+{
+    if (!moed::down_grouped_fits(E, k) || t.dn_group == 0)
+        return false;
+    if (t.dn_group == 1)
+        return true;
+    return (long)B * k >= 2L * E;
+}
+
+hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, hipStream_t s)
+{
+    if (use_down_grouped(t, p.B, p.E, p.k))
+        return moed::launch_down_grouped(p, a_bf16, out_bf16, t, s);
+    return moed::launch_down(p, a_bf16, out_bf16, t, s);
+}
+
 moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
                               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
                               void* a, int B, int E, int k, int H, int I)
@@ -87,6 +103,7 @@ moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, cons
     p.a = a; p.ids = ids; p.w = w; p.wd_q = wd_q; p.wd_s = wd_s; p.out = out;
     p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
     p.inv_cpr = 1.0f / (float)(I / 16);
+    p.order = 0;
     return p;
 }
 
@@ -135,7 +152,7 @@ int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, con
     if (!aligned16(a) || !aligned16(wd_q))
         return MOED_ERR_ALIGN;
     const moed::Tuning t = pick(B, H, I);
-    return hip_status(moed::launch_down(down_args(a, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I),
+    return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I),
                                         inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -164,7 +181,7 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, workspace, B, E, k, H, I), a_bf16, t, s));
     if (st)
         return st;
-    return hip_status(moed::launch_down(
+    return hip_status(down_launch(
         down_args(workspace, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I), a_bf16,
         out_dtype == MOED_BF16, t, s));
 }
@@ -246,11 +263,13 @@ int moed_set_tuning(const char* spec)
         if (!strcmp(tok, "gu_wpb") && v >= 1 && v <= 4) t.gu_wpb = (int)v;
         else if (!strcmp(tok, "dn_wpb") && v >= 1 && v <= 8) t.dn_wpb = (int)v;
         else if (!strcmp(tok, "dn_stage") && (v == 0 || v == 1)) t.dn_stage = (int)v;
+        else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
-        else if (!strcmp(tok, "nt") && (v == 0 || v == 1)) t.nt = (int)v;
+        else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
         else if (!strcmp(tok, "gu_group") && v >= 0 && v <= 2) t.gu_group = (int)v;
         else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;
+        else if (!strcmp(tok, "dn_order") && v >= 0 && v <= 2) t.dn_order = (int)v;
         else return MOED_ERR_SHAPE;
     }
     g_tuning = t;

@@ -107,6 +107,18 @@ __device__ __forceinline__ float wave_sum(float v)
     return lo + hi;
 }
 
+// Workgroups go to the 8 XCDs of the chip in turn (workgroup i to XCD i % 8),
+// and each XCD has its own L2. xcd_contiguous(i, n) renumbers the n
+// workgroups of a launch so that every XCD runs one contiguous range of
+// logical indices: work that reads the same bytes and sits at neighbouring
+// logical indices then meets in one L2. It is a bijection of [0, n).
+__device__ __forceinline__ int xcd_contiguous(int i, int n)
+{
+    const int x = i % 8, slot = i / 8;
+    const int q = n / 8, r = n % 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+}
+
 // float32 -> bfloat16 bits, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {

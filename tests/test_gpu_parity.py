@@ -167,10 +167,10 @@ def test_workload_sampled_parity(name):
     check_f32(out32[toks], ref, name)
     out16 = run(L, torch.bfloat16)
     check_bf16(out16[toks], out32[toks], ref, name)
-    # batch = concatenation of single-token calls, bit for bit, on each gate/up path
-    # (the per-slot and the expert-grouped paths accumulate in different orders)
+    # batch = concatenation of single-token calls, bit for bit, on each kernel pair
+    # (the per-slot/per-output and the grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for spec in ("gu_group=0", "gu_group=1"):
+    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1"):
         md.moed_set_tuning(spec)
         try:
             full = run(L, torch.float32)
@@ -230,7 +230,10 @@ def test_ragged_shapes(shape):
 
 @pytest.mark.parametrize("spec", ["gu_dot=0", "gu_dot=1", "nt=1", "gu_wpb=1,dn_wpb=1", "gu_wpb=2,dn_wpb=2",
                                   "gu_umax=1,dn_umax=1", "gu_umax=3,dn_umax=5,gu_dot=0,nt=1",
-                                  "gu_group=1", "gu_group=0", "dn_stage=0", "gu_group=1,nt=0"])
+                                  "gu_group=1", "gu_group=0", "dn_stage=0", "gu_group=1,nt=0",
+                                  "dn_group=1", "gu_group=1,dn_group=1", "dn_group=0",
+                                  "dn_order=1", "dn_order=2", "dn_order=1,dn_stage=0,dn_wpb=3",
+                                  "dn_order=2,dn_wpb=5,nt=0"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
@@ -321,7 +324,8 @@ def test_bench_kernels():
 
 
 # --------------------------------------------------------------------------------------
-# expert-grouped gate/up (MFMA tiles of 16 neurons x 16 slots)
+# expert-grouped gate/up (MFMA tiles of 16 neurons x 16 slots) and the
+# tile-of-16-outputs x 16-tokens down kernel
 # --------------------------------------------------------------------------------------
 
 GROUPED = [
@@ -337,9 +341,10 @@ def test_grouped_gate_up(shape):
     B = shape[0]
     L = small(*shape, seed=sum(shape) + 1)
     ref, a_ref = oracle_tokens(L, list(range(B)))
-    md.moed_set_tuning("gu_group=1")
+    md.moed_set_tuning("gu_group=1,dn_group=1")
     try:
         check_f32(run(L), ref, f"grouped {shape}")
+        check_bf16(run(L, torch.bfloat16), run(L), ref, f"grouped bf16 {shape}")
         x, ids, _ = md.layer_device_inputs(L)
         a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
         torch.cuda.synchronize()
@@ -360,7 +365,7 @@ def test_grouped_duplicates_and_invalid_ids():
     ids[:, 1] = ids[:, 0]                 # duplicate slot in every token
     ids[3, 2] = 5                         # out of range
     ids[7, 0] = -1
-    md.moed_set_tuning("gu_group=1")
+    md.moed_set_tuning("gu_group=1,dn_group=1")
     try:
         out = run(L, ids=ids).cpu()
     finally:
