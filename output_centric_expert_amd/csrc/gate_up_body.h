@@ -1,0 +1,101 @@
+// Per-wave body of the gate/up step (one wavefront per intermediate neuron of
+// one (token, routed slot) pair; warp-decode post, "How the two kernels work",
+// first two paragraphs), shared by the two-launch gate/up kernel and the
+// single-launch layer kernel.
+//
+// Wave w owns (b, j, i) with w = (b*k + j)*I + i. It first issues the loads
+// of its 16 bf16 activations per chunk, x[b][16c..16c+15] (used by both
+// projections), then reads e = ids[b][j] with a scalar load and streams the
+// gate row Wg[e][i][:] and the up row Wu[e][i][:] in 16-byte chunks: chunk c
+// (16 codes) goes to lane c % 64, so each wave-wide load instruction covers
+// 1 KiB of one row contiguously. Every load of a pass is issued before the
+// first FMA, without branches around them. Each lane keeps two FP32
+// accumulators (gate, up); the caller reduces them across the wavefront.
+#pragma once
+
+#include "launch.h"
+#include "mx_device.h"
+
+namespace moed {
+
+// Lane partials of g = Wg[e][i]·x[b] and u = Wu[e][i]·x[b] for wave `wave`;
+// bad_id is set when ids[b][j] is outside [0, E) (the caller then stores NaN).
+template <int U, bool DOT_BF16, bool NT>
+__device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int lane, float& g_out, float& u_out,
+                                             bool& bad_out)
+{
+    const int i = wave % p.I;
+    const int bj = wave / p.I;
+    const int b = bj / p.k;
+    const int H = p.H;
+    const int nch = H / 16;                       // 16-code chunks per row
+    const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
+
+    float g = 0.0f, u = 0.0f;
+    bool bad_id = false;
+    for (int base = 0; base < nch; base += kWave * U) {
+        // x first: its address does not depend on the routed id, so these loads
+        // overlap the id's scalar load. Every load is unconditional from a
+        // clamped, in-bounds address; chunks past the row end get scale 0.
+        u32x4 xa[U], xb[U];
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            const int c = base + lane + kWave * m;
+            const int cc = c < nch ? c : nch - 1;
+            xa[m] = xq[2 * cc];
+            xb[m] = xq[2 * cc + 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int e_raw = p.ids[bj];
+        bad_id = (unsigned)e_raw >= (unsigned)p.E;   // invalid routing: expert 0's rows are read, result NaN
+        const int e = bad_id ? 0 : e_raw;
+        const size_t row = (size_t)e * (size_t)p.I + (size_t)i;
+        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * (size_t)H);
+        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * (size_t)H);
+        const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+        const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+        u32x4 wg[U], wu[U];
+        uint32_t sg[U], su[U];
+        float live[U];
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            const int c = base + lane + kWave * m;
+            const int cc = c < nch ? c : nch - 1;
+            wg[m] = ld<NT>(gq + cc);
+            wu[m] = ld<NT>(uq + cc);
+            sg[m] = gs[cc >> 1];
+            su[m] = us[cc >> 1];
+            live[m] = c < nch ? 1.0f : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            float pg = 0.0f, pu = 0.0f;
+            if constexpr (DOT_BF16) {
+                pg = dot4_bf16(wg[m].x, xa[m].x, xa[m].y, pg);
+                pu = dot4_bf16(wu[m].x, xa[m].x, xa[m].y, pu);
+                pg = dot4_bf16(wg[m].y, xa[m].z, xa[m].w, pg);
+                pu = dot4_bf16(wu[m].y, xa[m].z, xa[m].w, pu);
+                pg = dot4_bf16(wg[m].z, xb[m].x, xb[m].y, pg);
+                pu = dot4_bf16(wu[m].z, xb[m].x, xb[m].y, pu);
+                pg = dot4_bf16(wg[m].w, xb[m].z, xb[m].w, pg);
+                pu = dot4_bf16(wu[m].w, xb[m].z, xb[m].w, pu);
+            } else {
+                pg = dot4_f32(wg[m].x, xa[m].x, xa[m].y, pg);
+                pu = dot4_f32(wu[m].x, xa[m].x, xa[m].y, pu);
+                pg = dot4_f32(wg[m].y, xa[m].z, xa[m].w, pg);
+                pu = dot4_f32(wu[m].y, xa[m].z, xa[m].w, pu);
+                pg = dot4_f32(wg[m].z, xb[m].x, xb[m].y, pg);
+                pu = dot4_f32(wu[m].z, xb[m].x, xb[m].y, pu);
+                pg = dot4_f32(wg[m].w, xb[m].z, xb[m].w, pg);
+                pu = dot4_f32(wu[m].w, xb[m].z, xb[m].w, pu);
+            }
+            g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g);
+            u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u);
+        }
+    }
+    g_out = g;
+    u_out = u;
+    bad_out = bad_id;
+}
+
+}  // namespace moed
