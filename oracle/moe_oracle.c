@@ -17,11 +17,18 @@
  *     a[b][j][i] = SiLU(g[i]) * u[i],  SiLU(t) = t / (1 + exp(-t))
  *   out[b][h] = sum_j w[b][j] * sum_i Wd^[e_j][h][i] * a[b][j][i]
  *
- * where W^ is the MXFP8 weight decoded exactly:
- *   W^[e][n][c] = E4M3(q[e][n][c]) * UE8M0(s[e][n][c / 32])
- * (FP8 E4M3 codes with one UE8M0 scale per 32 values along the reduction
- * axis, as the GC-MoE summary's section "How to use" names the block format;
- * element formats per the OCP Microscaling v1.0 definition).
+ * where W^ is the block-scaled weight decoded exactly, in one of two formats
+ * (fmt argument of the *_fmt functions; the plain functions are MXFP8):
+ *   MXFP8 (fmt 0): W^[e][n][c] = E4M3(q[e][n][c]) * UE8M0(s[e][n][c / 32])
+ *     (FP8 E4M3 codes with one UE8M0 scale per 32 values along the
+ *     reduction axis, as the GC-MoE summary's section "How to use" names the
+ *     block format);
+ *   MXFP4 (fmt 1): W^[e][n][c] = E2M1(nibble c of row n) * UE8M0(s[e][n][c / 32])
+ *     (the FP4 E2M1 routed weights with the same K32 UE8M0 granularity that
+ *     the same section describes), two codes per byte: element c is the low
+ *     nibble of byte c/2 when c is even and the high nibble when c is odd, so
+ *     a row of K codes is K/2 bytes.
+ * Element formats per the OCP Microscaling v1.0 definition.
  *
  * Conventions the definition leaves open, and the reading taken here:
  *  - duplicate expert ids in a token's row are legal and their terms add;
@@ -58,6 +65,23 @@ double oracle_e4m3_value(unsigned code)
     return sign ? -mag : mag;
 }
 
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit. Exponent field
+ * 0 is subnormal (m/2); there are no NaN and no infinities, so the values are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives. */
+double oracle_e2m1_value(unsigned code)
+{
+    code &= 0xFu;
+    const int sign = (code >> 3) & 1;
+    const int ex = (code >> 1) & 0x3;
+    const int man = code & 0x1;
+    double mag;
+    if (ex == 0)
+        mag = (double)man * 0.5;
+    else
+        mag = ldexp(1.0 + (double)man / 2.0, ex - 1);
+    return sign ? -mag : mag;
+}
+
 /* UE8M0: an unsigned 8-bit exponent, value 2^(code - 127); code 0xFF is NaN. */
 double oracle_ue8m0_value(unsigned code)
 {
@@ -87,6 +111,14 @@ static int bad_shape(int B, int E, int k, int H, int I)
     return B < 0 || E < 1 || k < 1 || k > E || H < 32 || I < 32 || (H % 32) || (I % 32);
 }
 
+enum { FMT_MXFP8 = 0, FMT_MXFP4 = 1 };
+
+/* Bytes of codes in a row of n values. */
+static long row_bytes(long n, int fmt)
+{
+    return fmt == FMT_MXFP4 ? n / 2 : n;
+}
+
 static int set_threads(int nthreads)
 {
 #ifdef _OPENMP
@@ -106,28 +138,37 @@ static double swiglu(double g, double u)
     return g / (1.0 + exp(-g)) * u;
 }
 
-/* One row dot: sum_c W^[c] * v[c] over a row of n codes with n/32 scales. */
+/* One row dot: sum_c W^[c] * v[c] over a row of n values with n/32 scales.
+ * MXFP8: code c is byte c. MXFP4: code c is nibble c (low nibble first). */
 static double mx_row_dot(const double tab[256], const uint8_t *q, const uint8_t *s,
-                         const double *v, long n)
+                         const double *v, long n, int fmt)
 {
     double acc = 0.0;
-    for (long c = 0; c < n; ++c)
-        acc += tab[q[c]] * oracle_ue8m0_value(s[c / 32]) * v[c];
+    for (long c = 0; c < n; ++c) {
+        double wv;
+        if (fmt == FMT_MXFP4)
+            wv = oracle_e2m1_value((c % 2) ? (unsigned)(q[c / 2] >> 4) : (unsigned)(q[c / 2] & 0xFu));
+        else
+            wv = tab[q[c]];
+        acc += wv * oracle_ue8m0_value(s[c / 32]) * v[c];
+    }
     return acc;
 }
 
 /*
  * Gate/up half of the layer: a[b][j][i] = SiLU(g) * u, float64 [B][k][I].
- * x: bf16 bits [B][H]; ids: int32 [B][k]; w*_q: uint8 [E][I][H];
- * w*_s: uint8 [E][I][H/32]. Returns 0, or -2 on a bad shape.
+ * x: bf16 bits [B][H]; ids: int32 [B][k]; w*_q: uint8 [E][I][H] (MXFP8) or
+ * [E][I][H/2] (MXFP4); w*_s: uint8 [E][I][H/32]. Returns 0, or -2 on a bad
+ * shape or format.
  */
-int oracle_gate_up(const uint16_t *x, const int32_t *ids,
-                   const uint8_t *wg_q, const uint8_t *wg_s,
-                   const uint8_t *wu_q, const uint8_t *wu_s,
-                   int B, int E, int k, int H, int I, double *a, int nthreads)
+int oracle_gate_up_fmt(const uint16_t *x, const int32_t *ids,
+                       const uint8_t *wg_q, const uint8_t *wg_s,
+                       const uint8_t *wu_q, const uint8_t *wu_s,
+                       int B, int E, int k, int H, int I, double *a, int nthreads, int fmt)
 {
-    if (bad_shape(B, E, k, H, I))
+    if (bad_shape(B, E, k, H, I) || (fmt != FMT_MXFP8 && fmt != FMT_MXFP4))
         return -2;
+    const long rb = row_bytes(H, fmt);
     double tab[256];
     fill_e4m3_table(tab);
     set_threads(nthreads);
@@ -149,27 +190,36 @@ int oracle_gate_up(const uint16_t *x, const int32_t *ids,
             continue;
         }
         const size_t row = (size_t)e * (size_t)I + (size_t)i;
-        const double g = mx_row_dot(tab, wg_q + row * (size_t)H, wg_s + row * (size_t)(H / 32),
-                                    xd + b * H, H);
-        const double u = mx_row_dot(tab, wu_q + row * (size_t)H, wu_s + row * (size_t)(H / 32),
-                                    xd + b * H, H);
+        const double g = mx_row_dot(tab, wg_q + row * (size_t)rb, wg_s + row * (size_t)(H / 32),
+                                    xd + b * H, H, fmt);
+        const double u = mx_row_dot(tab, wu_q + row * (size_t)rb, wu_s + row * (size_t)(H / 32),
+                                    xd + b * H, H, fmt);
         a[r] = swiglu(g, u);
     }
     free(xd);
     return 0;
 }
 
+int oracle_gate_up(const uint16_t *x, const int32_t *ids,
+                   const uint8_t *wg_q, const uint8_t *wg_s,
+                   const uint8_t *wu_q, const uint8_t *wu_s,
+                   int B, int E, int k, int H, int I, double *a, int nthreads)
+{
+    return oracle_gate_up_fmt(x, ids, wg_q, wg_s, wu_q, wu_s, B, E, k, H, I, a, nthreads, FMT_MXFP8);
+}
+
 /*
  * Down half: out[b][h] = sum_j w[b][j] * sum_i Wd^[e_j][h][i] * a[b][j][i].
- * a: float64 [B][k][I]; w: float32 [B][k]; wd_q: uint8 [E][H][I];
- * wd_s: uint8 [E][H][I/32]; out: float64 [B][H].
+ * a: float64 [B][k][I]; w: float32 [B][k]; wd_q: uint8 [E][H][I] (MXFP8) or
+ * [E][H][I/2] (MXFP4); wd_s: uint8 [E][H][I/32]; out: float64 [B][H].
  */
-int oracle_down(const double *a, const int32_t *ids, const float *w,
-                const uint8_t *wd_q, const uint8_t *wd_s,
-                int B, int E, int k, int H, int I, double *out, int nthreads)
+int oracle_down_fmt(const double *a, const int32_t *ids, const float *w,
+                    const uint8_t *wd_q, const uint8_t *wd_s,
+                    int B, int E, int k, int H, int I, double *out, int nthreads, int fmt)
 {
-    if (bad_shape(B, E, k, H, I))
+    if (bad_shape(B, E, k, H, I) || (fmt != FMT_MXFP8 && fmt != FMT_MXFP4))
         return -2;
+    const long rb = row_bytes(I, fmt);
     double tab[256];
     fill_e4m3_table(tab);
     set_threads(nthreads);
@@ -186,8 +236,8 @@ int oracle_down(const double *a, const int32_t *ids, const float *w,
                 break;
             }
             const size_t row = (size_t)e * (size_t)H + (size_t)h;
-            const double d = mx_row_dot(tab, wd_q + row * (size_t)I, wd_s + row * (size_t)(I / 32),
-                                        a + (b * k + j) * I, I);
+            const double d = mx_row_dot(tab, wd_q + row * (size_t)rb, wd_s + row * (size_t)(I / 32),
+                                        a + (b * k + j) * I, I, fmt);
             acc += (double)w[b * k + j] * d;
         }
         out[o] = acc;
@@ -195,16 +245,23 @@ int oracle_down(const double *a, const int32_t *ids, const float *w,
     return 0;
 }
 
+int oracle_down(const double *a, const int32_t *ids, const float *w,
+                const uint8_t *wd_q, const uint8_t *wd_s,
+                int B, int E, int k, int H, int I, double *out, int nthreads)
+{
+    return oracle_down_fmt(a, ids, w, wd_q, wd_s, B, E, k, H, I, out, nthreads, FMT_MXFP8);
+}
+
 /* The whole layer. `a` may be NULL (scratch is then allocated here); when
  * given it receives the float64 intermediate [B][k][I]. */
-int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
-                      const uint8_t *wg_q, const uint8_t *wg_s,
-                      const uint8_t *wu_q, const uint8_t *wu_s,
-                      const uint8_t *wd_q, const uint8_t *wd_s,
-                      int B, int E, int k, int H, int I,
-                      double *out, double *a, int nthreads)
+int oracle_moe_decode_fmt(const uint16_t *x, const int32_t *ids, const float *w,
+                          const uint8_t *wg_q, const uint8_t *wg_s,
+                          const uint8_t *wu_q, const uint8_t *wu_s,
+                          const uint8_t *wd_q, const uint8_t *wd_s,
+                          int B, int E, int k, int H, int I,
+                          double *out, double *a, int nthreads, int fmt)
 {
-    if (bad_shape(B, E, k, H, I))
+    if (bad_shape(B, E, k, H, I) || (fmt != FMT_MXFP8 && fmt != FMT_MXFP4))
         return -2;
     double *scratch = NULL;
     if (!a) {
@@ -213,11 +270,22 @@ int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
             return -1;
         a = scratch;
     }
-    int rc = oracle_gate_up(x, ids, wg_q, wg_s, wu_q, wu_s, B, E, k, H, I, a, nthreads);
+    int rc = oracle_gate_up_fmt(x, ids, wg_q, wg_s, wu_q, wu_s, B, E, k, H, I, a, nthreads, fmt);
     if (rc == 0)
-        rc = oracle_down(a, ids, w, wd_q, wd_s, B, E, k, H, I, out, nthreads);
+        rc = oracle_down_fmt(a, ids, w, wd_q, wd_s, B, E, k, H, I, out, nthreads, fmt);
     free(scratch);
     return rc;
+}
+
+int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
+                      const uint8_t *wg_q, const uint8_t *wg_s,
+                      const uint8_t *wu_q, const uint8_t *wu_s,
+                      const uint8_t *wd_q, const uint8_t *wd_s,
+                      int B, int E, int k, int H, int I,
+                      double *out, double *a, int nthreads)
+{
+    return oracle_moe_decode_fmt(x, ids, w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, out, a,
+                                 nthreads, FMT_MXFP8);
 }
 
 /* Threads an OpenMP region in this library will use for a given request. */

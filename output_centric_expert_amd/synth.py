@@ -23,6 +23,12 @@ sections "Traditional MoE path", "Buffer removal", "Hardware efficiency"):
   (8 = the largest E4M3 exponent), clamped to [-127, 127]; an all-zero block
   gets exponent -127; elements = v * 2^-exponent clamped to +-448 and rounded
   to nearest-even E4M3. Scale code = exponent + 127.
+* MXFP4 weights (wformat="mxfp4"; the FP4 E2M1 routed weights with K32 UE8M0
+  scales of the same GC-MoE section): shared exponent = floor(log2 amax) - 2
+  (2 = the largest E2M1 exponent, 6 = 1.5 * 2^2), elements clamped to +-6 and
+  rounded to the nearest E2M1 value, ties to the even code; two codes per
+  byte, element 2t in the low nibble of byte t and element 2t+1 in the high
+  nibble.
 
 Weights are drawn with torch on the requested device (so multi-GB inputs are
 made in HBM in well under a second); x and routing are drawn with numpy on the
@@ -40,6 +46,9 @@ import torch
 BLOCK = 32            # elements per MX block (one UE8M0 scale each)
 E4M3_MAX = 448.0      # largest finite OCP E4M3 magnitude
 E4M3_EMAX = 8         # exponent of E4M3_MAX (448 = 1.75 * 2^8)
+E2M1_MAX = 6.0        # largest OCP E2M1 magnitude
+E2M1_EMAX = 2         # exponent of E2M1_MAX (6 = 1.5 * 2^2)
+WFORMATS = ("mxfp8", "mxfp4")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -61,8 +70,14 @@ class LayerShape:
 
     @property
     def bytes_per_expert(self) -> int:
-        """Codes + scales of one expert's gate, up and down matrices."""
+        """Codes + scales of one expert's gate, up and down matrices (MXFP8)."""
         return 3 * self.I * self.H * (BLOCK + 1) // BLOCK
+
+    def weight_bytes_per_expert(self, wformat: str = "mxfp8") -> int:
+        """Codes + scales of one expert's three matrices in the given format."""
+        if wformat == "mxfp4":
+            return 3 * self.I * self.H * (BLOCK // 2 + 1) // BLOCK
+        return self.bytes_per_expert
 
 
 # The five decode workloads, smallest first.
@@ -150,6 +165,33 @@ def encode_mxfp8(w: torch.Tensor):
     return codes.contiguous(), scales.contiguous()
 
 
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)   # between the 8 magnitudes
+
+
+def encode_mxfp4(w: torch.Tensor):
+    """Encode float32 [..., K] (K % 32 == 0) to (packed codes uint8 [..., K/2], scales uint8 [..., K/32])."""
+    if w.dtype != torch.float32 or w.shape[-1] % BLOCK:
+        raise ValueError("encode_mxfp4 wants float32 with a last dim that is a multiple of 32")
+    K = w.shape[-1]
+    blk = w.reshape(*w.shape[:-1], K // BLOCK, BLOCK)
+    amax = blk.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)
+    se = (ex.to(torch.int32) - 1) - E2M1_EMAX       # floor(log2 amax) - emax
+    se = torch.where(amax > 0, se, torch.full_like(se, -127)).clamp_(-127, 127)
+    mul = torch.exp2((-se).to(torch.float32))
+    scaled = blk * mul.unsqueeze(-1)
+    mag = scaled.abs().clamp_(max=E2M1_MAX)
+    mids = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=w.device)
+    idx = torch.searchsorted(mids, mag.contiguous())   # number of midpoints below the value
+    # a value exactly on a midpoint goes to the even code (mantissa bit 0)
+    on_mid = (idx < len(_E2M1_MIDPOINTS)) & (mag == mids[idx.clamp(max=len(_E2M1_MIDPOINTS) - 1)])
+    idx = torch.where(on_mid & (idx % 2 == 1), idx + 1, idx)
+    codes = (idx | torch.where(scaled < 0, 8, 0)).to(torch.uint8).reshape(*w.shape[:-1], K)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    scales = (se + 127).to(torch.uint8)
+    return packed.contiguous(), scales.contiguous()
+
+
 @dataclasses.dataclass
 class LayerInputs:
     shape: LayerShape
@@ -165,6 +207,7 @@ class LayerInputs:
     wd_q: torch.Tensor       # uint8 [E, H, I]
     wd_s: torch.Tensor       # uint8 [E, H, I/32]
     dense: dict | None = None  # unquantized float32 draws, when asked for
+    wformat: str = "mxfp8"     # "mxfp4": codes packed two per byte ([E, I, H/2], [E, H, I/2])
 
     @property
     def unique_experts(self) -> int:
@@ -172,14 +215,17 @@ class LayerInputs:
 
     @property
     def unique_weight_bytes(self) -> int:
-        return self.unique_experts * self.shape.bytes_per_expert
+        return self.unique_experts * self.shape.weight_bytes_per_expert(self.wformat)
 
 
 def make_weights(E: int, N: int, K: int, seed: int, tensor_id: int, device,
-                 keep_dense: bool = False, experts_per_draw: int = 8):
-    """N(0, 0.02) weights [E, N, K] encoded to MXFP8, drawn on `device` in expert groups."""
+                 keep_dense: bool = False, experts_per_draw: int = 8, wformat: str = "mxfp8"):
+    """N(0, 0.02) weights [E, N, K] encoded to MXFP8 (or MXFP4), drawn on `device` in expert groups."""
+    if wformat not in WFORMATS:
+        raise ValueError(f"unknown weight format {wformat!r}")
     device = torch.device(device)
-    q = torch.empty((E, N, K), dtype=torch.uint8, device=device)
+    encode = encode_mxfp4 if wformat == "mxfp4" else encode_mxfp8
+    q = torch.empty((E, N, K // 2 if wformat == "mxfp4" else K), dtype=torch.uint8, device=device)
     s = torch.empty((E, N, K // BLOCK), dtype=torch.uint8, device=device)
     dense = torch.empty((E, N, K), dtype=torch.float32, device=device) if keep_dense else None
     gen = torch.Generator(device=device)
@@ -188,7 +234,7 @@ def make_weights(E: int, N: int, K: int, seed: int, tensor_id: int, device,
         gen.manual_seed(int(seed) * 1_000_003 + tensor_id * 10_007 + e0)
         d = torch.randn((e1 - e0, N, K), generator=gen, dtype=torch.float32, device=device)
         d.mul_(0.02)
-        q[e0:e1], s[e0:e1] = encode_mxfp8(d)
+        q[e0:e1], s[e0:e1] = encode(d)
         if keep_dense:
             dense[e0:e1] = d
         del d
@@ -196,7 +242,8 @@ def make_weights(E: int, N: int, K: int, seed: int, tensor_id: int, device,
 
 
 def make_layer(shape: LayerShape | str, seed: int | None = None, device="cpu",
-               keep_dense: bool = False, contiguous_hot: bool = False) -> LayerInputs:
+               keep_dense: bool = False, contiguous_hot: bool = False,
+               wformat: str = "mxfp8") -> LayerInputs:
     """All inputs of one decode layer. Weights live on `device`, the rest on the host."""
     if isinstance(shape, str):
         shape = WORKLOADS[shape]
@@ -205,11 +252,11 @@ def make_layer(shape: LayerShape | str, seed: int | None = None, device="cpu",
     B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
     x = make_activations(B, H, seed)
     ids, w, probs = make_routing(B, E, k, seed, shape.zipf_s, contiguous_hot)
-    wg_q, wg_s, dg = make_weights(E, I, H, seed, 0, device, keep_dense)
-    wu_q, wu_s, du = make_weights(E, I, H, seed, 1, device, keep_dense)
-    wd_q, wd_s, dd = make_weights(E, H, I, seed, 2, device, keep_dense)
+    wg_q, wg_s, dg = make_weights(E, I, H, seed, 0, device, keep_dense, wformat=wformat)
+    wu_q, wu_s, du = make_weights(E, I, H, seed, 1, device, keep_dense, wformat=wformat)
+    wd_q, wd_s, dd = make_weights(E, H, I, seed, 2, device, keep_dense, wformat=wformat)
     dense = dict(gate=dg, up=du, down=dd) if keep_dense else None
-    return LayerInputs(shape, seed, x, ids, w, probs, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, dense)
+    return LayerInputs(shape, seed, x, ids, w, probs, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, dense, wformat)
 
 
 def random_small_shape(rng: np.random.Generator, max_E=8, max_dim=128) -> LayerShape:
