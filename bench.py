@@ -62,6 +62,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--wformat", default="mxfp8", choices=["mxfp8", "mxfp4"],
+                    help="routed-weight format (the headline metric is quoted on mxfp8)")
     ap.add_argument("--copies", type=int, default=32, help="distinct HBM copies of the layer weights")
     ap.add_argument("--tune", default=None, help="launch-shape override (moed_set_tuning spec)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -96,7 +98,7 @@ def main():
 
     shape = synth.WORKLOADS[args.workload]
     t0 = time.time()
-    L = synth.make_layer(shape, device="cuda")
+    L = synth.make_layer(shape, device="cuda", wformat=args.wformat)
     R = max(1, args.copies)
     log(f"inputs ready in {time.time() - t0:.1f} s: {shape}, {R} weight copies")
     if args.counters:
@@ -104,7 +106,7 @@ def main():
         copies = weight_copies(L, R)
         out = torch.empty((shape.B, shape.H), dtype=torch.bfloat16, device="cuda")
         a = torch.empty((shape.B, shape.k, shape.I), dtype=torch.float32, device="cuda")
-        counters_run(md, x, ids, w, copies, out, a, args.workload)
+        counters_run(md, x, ids, w, copies, out, a, args.workload, L.wformat)
         return
 
     K, W = args.steps, args.warmup
@@ -113,12 +115,12 @@ def main():
     B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
     U = L.unique_experts
     uniq = L.unique_weight_bytes
-    gu_bytes = U * 2 * I * H * 33 // 32
+    gu_bytes, _ = kernel_bytes(L)
     ms_per_step, ms_gu = t["ms_per_step"], t["ms_gate_up"]
     gbs = uniq / (ms_per_step * 1e-3) / 1e9
     gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
 
-    traffic = load_traffic("gate_up", args.workload)
+    traffic = load_traffic("gate_up", args.workload) if L.wformat == "mxfp8" else None
     roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
@@ -140,9 +142,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights encoded to MXFP8, softmax top-k routing)",
+        "data": f"synthetic (seeded N(0,1) activations, N(0,0.02) weights encoded to {L.wformat.upper()}, "
+                "softmax top-k routing)",
         "config": {"workload": args.workload, "B": B, "E": E, "k": k, "H": H, "I": I,
-                   "weights": "mxfp8 (e4m3 + ue8m0 per 32)", "activations": "bf16", "out": "bf16",
+                   "weights": WEIGHT_DESC[L.wformat], "activations": "bf16", "out": "bf16",
                    "unique_experts": U, "unique_weight_bytes": uniq, "weight_copies": R,
                    "timing": "HIP graph of K layers, HIP events on the launch stream"},
         **timing_fields(L, t),
@@ -179,14 +182,16 @@ def measure_layer(md, L, R, K, W):
     a = torch.empty((sh.B, sh.k, sh.I), dtype=torch.float32, device="cuda")
     ws = a.view(torch.uint8).view(-1)
 
+    wf = L.wformat
+
     def layer(r):
-        md.moe_decode(x, ids, w, *copies[r % R], out=out, workspace=ws)
+        md.moe_decode(x, ids, w, *copies[r % R], out=out, workspace=ws, wformat=wf)
 
     def gate_up(r):
-        md.moe_decode_gate_up(x, ids, *copies[r % R][:4], a=a)
+        md.moe_decode_gate_up(x, ids, *copies[r % R][:4], a=a, wformat=wf)
 
     def down(r):
-        md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out)
+        md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out, wformat=wf)
 
     for r in range(W):                       # untimed warm-up steps
         layer(r)
@@ -248,11 +253,19 @@ def measure_layer(md, L, R, K, W):
     return res
 
 
-def timing_fields(L, t):
+WEIGHT_DESC = {"mxfp8": "mxfp8 (e4m3 + ue8m0 per 32)", "mxfp4": "mxfp4 (e2m1 two per byte + ue8m0 per 32)"}
+
+
+def kernel_bytes(L):
+    """Algorithmic weight bytes per launch (unique routed experts' codes + scales): gate/up, down."""
     sh = L.shape
     U = L.unique_experts
-    gu_bytes = U * 2 * sh.I * sh.H * 33 // 32
-    dn_bytes = U * sh.H * sh.I * 33 // 32
+    per_matrix = sh.I * sh.H * (17 if L.wformat == "mxfp4" else 33) // 32
+    return U * 2 * per_matrix, U * per_matrix
+
+
+def timing_fields(L, t):
+    gu_bytes, dn_bytes = kernel_bytes(L)
     return {"us_per_layer": round(t["ms_per_step"] * 1e3, 3),
             "frac_of_peak_hbm": round(L.unique_weight_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "us_gate_up": round(t["ms_gate_up"] * 1e3, 3), "us_down": round(t["ms_down"] * 1e3, 3),
@@ -274,10 +287,11 @@ def all_workloads(md, synth, args):
     peak = measured_read_peak(md)
     for name in synth.WORKLOAD_ORDER:
         R, K = ALL_PLAN[name]
-        L = synth.make_layer(name, device="cuda")
+        L = synth.make_layer(name, device="cuda", wformat=args.wformat)
         t = measure_layer(md, L, R, K, min(args.warmup, 10))
         gbs = L.unique_weight_bytes / (t["ms_per_step"] * 1e-3) / 1e9
-        line = {"workload": name, "steps": K, "weight_copies": R, "unique_experts": L.unique_experts,
+        line = {"workload": name, "wformat": L.wformat, "steps": K, "weight_copies": R,
+                "unique_experts": L.unique_experts,
                 "unique_weight_bytes": L.unique_weight_bytes, "gbs": round(gbs, 1),
                 **timing_fields(L, t), "frac_of_measured_read_peak": round(gbs / peak, 4),
                 "measured_read_peak_gbs": round(peak, 1)}
@@ -288,7 +302,7 @@ def all_workloads(md, synth, args):
         torch.cuda.empty_cache()
 
 
-def counters_run(md, x, ids, w, copies, out, a, workload):
+def counters_run(md, x, ids, w, copies, out, a, workload, wformat="mxfp8"):
     """Launch plan for rocprofv3 --pmc: COUNTER_LAUNCHES copies of COPY_BYTES, then the
     gate/up and down kernels COUNTER_LAUNCHES times each on rotating weight copies."""
     import torch
@@ -301,10 +315,10 @@ def counters_run(md, x, ids, w, copies, out, a, workload):
         torch.cuda.synchronize()
     R = len(copies)
     for r in range(COUNTER_LAUNCHES):
-        md.moe_decode_gate_up(x, ids, *copies[(r + 1) % R][:4], a=a)
+        md.moe_decode_gate_up(x, ids, *copies[(r + 1) % R][:4], a=a, wformat=wformat)
         torch.cuda.synchronize()
     for r in range(COUNTER_LAUNCHES):
-        md.moe_decode_down(a, ids, w, *copies[(r + 1) % R][4:], out=out)
+        md.moe_decode_down(a, ids, w, *copies[(r + 1) % R][4:], out=out, wformat=wformat)
         torch.cuda.synchronize()
     print(json.dumps({"counters_plan": {"workload": workload, "copy_bytes": COPY_BYTES,
                                         "launches_each": COUNTER_LAUNCHES,
@@ -351,11 +365,11 @@ def cpu_baseline(L, uniq, seconds):
     host = [t.index_select(0, idx).cpu() for t in (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
     nthreads = min(os.cpu_count() or 1, 16)
     used = oracle.threads(nthreads)
-    oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads)          # warm-up
+    oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)     # warm-up
     n, t = 0, 0.0
     while t < seconds or n < 3:
         t0 = time.perf_counter()
-        oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads)
+        oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)
         t += time.perf_counter() - t0
         n += 1
     per_tok = t / n / len(toks)

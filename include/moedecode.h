@@ -18,11 +18,18 @@
  * There are no gather, pad or scatter buffers and no per-expert output buffer
  * ("Buffer removal" section); the only intermediate is a[B][k][I].
  *
- * Weight format (MXFP8): codes are OCP FP8 E4M3 (bias 7, NaN = 0x7F/0xFF, no
- * infinities); every 32 consecutive codes along the reduction axis share one
- * UE8M0 scale byte, value 2^(s-127) (0xFF = NaN) -- the "FP8 E4M3 with a UE8M0
- * scale per 32 K values" block format of the GC-MoE summary (onedev.kr/papers/
- * 1690, section "How to use"). Decoded weight = E4M3(code) * 2^(scale-127).
+ * Weight formats (argument weight_format; both from the GC-MoE summary,
+ * onedev.kr/papers/1690, section "How to use", which names FP8 E4M3 and FP4
+ * E2M1 block formats with one UE8M0 scale per 32 values along K):
+ *  - MOED_MXFP8: codes are OCP FP8 E4M3 (bias 7, NaN = 0x7F/0xFF, no
+ *    infinities), one byte each; a row of K values is K bytes.
+ *  - MOED_MXFP4: codes are OCP FP4 E2M1 (bias 1; values 0, 0.5, 1, 1.5, 2,
+ *    3, 4, 6 and negatives; no NaN, no infinities), two per byte: element 2t
+ *    in the low nibble (bits 3..0) of byte t, element 2t+1 in the high nibble;
+ *    a row of K values is K/2 bytes.
+ * In both, every 32 consecutive values along the reduction axis share one
+ * UE8M0 scale byte, value 2^(s-127) (0xFF = NaN), in a separate [..][K/32]
+ * tensor. Decoded weight = element(code) * 2^(scale-127).
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -55,7 +62,7 @@ typedef enum {
     MOED_ERR_NULL = 1,       /* a required pointer is NULL                       */
     MOED_ERR_SHAPE = 2,      /* B<0, E<1, k<1, k>E, H or I not a positive multiple of 32,
                                 or a size beyond the limits below                */
-    MOED_ERR_DTYPE = 3,      /* unknown moed_dtype                                */
+    MOED_ERR_DTYPE = 3,      /* unknown moed_dtype or moed_wformat                */
     MOED_ERR_WORKSPACE = 4,  /* workspace smaller than moed_workspace_bytes()     */
     MOED_ERR_ALIGN = 5,      /* x, a, workspace or a weight-code base not 16-byte aligned */
     MOED_ERR_HIP = 6         /* a HIP launch failed; see moed_last_hip_error()    */
@@ -65,6 +72,11 @@ typedef enum {
     MOED_BF16 = 0,           /* bfloat16, round-to-nearest-even on store          */
     MOED_F32 = 1             /* IEEE float32                                      */
 } moed_dtype;
+
+typedef enum {
+    MOED_MXFP8 = 0,          /* E4M3 codes, one per byte                          */
+    MOED_MXFP4 = 1           /* E2M1 codes, two per byte (low nibble first)       */
+} moed_wformat;
 
 /* Size limits (checked): B*k*I and B*H below 2^31, k*I/16 below 2^22. */
 
@@ -80,10 +92,13 @@ size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype);
  *   x         [B][H]  bfloat16 activations
  *   topk_ids  [B][k]  int32 routed expert ids
  *   topk_w    [B][k]  float32 routing weights (folded in the down kernel)
- *   wg_q/wu_q [E][I][H] uint8 E4M3 codes of the gate / up projections, K = H
+ *   wg_q/wu_q [E][I][H] uint8 codes of the gate / up projections, K = H
+ *             ([E][I][H/2] for MOED_MXFP4)
  *   wg_s/wu_s [E][I][H/32] uint8 UE8M0 scales
- *   wd_q      [E][H][I] uint8 E4M3 codes of the down projection, K = I
+ *   wd_q      [E][H][I] uint8 codes of the down projection, K = I
+ *             ([E][H][I/2] for MOED_MXFP4)
  *   wd_s      [E][H][I/32] uint8 UE8M0 scales
+ *   weight_format  MOED_MXFP8 or MOED_MXFP4 (all three projections)
  *   out       [B][H]  out_dtype
  *   workspace >= moed_workspace_bytes(B, k, I, inter_dtype) bytes, 16-aligned
  * B = 0 is valid and launches nothing.
@@ -91,7 +106,7 @@ size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype);
 int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
                const uint8_t *wg_q, const uint8_t *wg_s,
                const uint8_t *wu_q, const uint8_t *wu_s,
-               const uint8_t *wd_q, const uint8_t *wd_s,
+               const uint8_t *wd_q, const uint8_t *wd_s, int weight_format,
                void *out, int out_dtype, int inter_dtype,
                int B, int E, int k, int H, int I,
                void *workspace, size_t workspace_bytes, void *stream);
@@ -110,7 +125,7 @@ int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
  */
 int moe_decode_gate_up(const void *x, const int32_t *topk_ids,
                        const uint8_t *wg_q, const uint8_t *wg_s,
-                       const uint8_t *wu_q, const uint8_t *wu_s,
+                       const uint8_t *wu_q, const uint8_t *wu_s, int weight_format,
                        void *a, int inter_dtype,
                        int B, int E, int k, int H, int I, void *stream);
 
@@ -122,17 +137,22 @@ int moe_decode_gate_up(const void *x, const int32_t *topk_ids,
  */
 int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
                     const float *topk_w, const uint8_t *wd_q, const uint8_t *wd_s,
-                    void *out, int out_dtype,
+                    int weight_format, void *out, int out_dtype,
                     int B, int E, int k, int H, int I, void *stream);
 
 /*
- * Diagnostic: decode n MXFP8 values with the kernels' own in-register decoder.
- * out[t] = E4M3(codes[t]) * 2^(scales[t]-127) as float32, through both decode
- * routes the kernels use (path 0: FP8 -> FP32 conversion; path 1: FP8 -> BF16
- * conversion, scale applied afterwards), so a test can compare every code bit for bit with the format
- * definition; path 2 is the large-batch route, FP8 -> BF16 with the block
- * scale folded into the conversion (exact for scale codes 10..245).
- * Device pointers; n >= 0; path in {0, 1, 2}.
+ * Diagnostic: decode n block-scaled values with the kernels' own in-register
+ * decoders, so a test can compare every code bit for bit with the format
+ * definitions. out[t] = element(codes[t]) * 2^(scales[t]-127) as float32:
+ *   path 0: E4M3, FP8 -> FP32 conversion, scale applied afterwards;
+ *   path 1: E4M3, FP8 -> BF16 conversion, scale applied afterwards;
+ *   path 2: E4M3, FP8 -> BF16 with the block scale folded into the conversion
+ *           (the large-batch route; exact for scale codes 10..245);
+ *   path 3: E2M1 (low nibble of codes[t]), FP4 -> BF16, scale afterwards;
+ *   path 4: E2M1 (low nibble of codes[t]), FP4 -> FP32, scale afterwards.
+ * The E2M1 paths place code t at nibble t % 8 of a packed dword, so every
+ * byte select and both nibble positions are exercised.
+ * Device pointers; n >= 0; path in {0, ..., 4}.
  */
 int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out,
                          int n, int path, void *stream);

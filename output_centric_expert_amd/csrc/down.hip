@@ -20,11 +20,11 @@
 
 namespace moed {
 
-template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT>
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT, bool FP4>
 __global__ void __launch_bounds__(256)
 moe_down_kernel(DownArgs p)
 {
-    constexpr int NA = A_BF16 ? 2 : 4;            // 16-byte pieces of a per chunk
+    constexpr int NP = APieces<FP4, A_BF16>::N;   // 16-byte pieces of a per weight chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
     const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
@@ -37,9 +37,12 @@ moe_down_kernel(DownArgs p)
     const int h = p.order == 0 ? wave % p.H : wave / p.B;
     const int k = p.k;
     const int I = p.I;
-    const int cpr = I / 16;                       // chunks per routed row
+    const int cpr16 = I / 16;                     // 16-value groups per row of a
+    const int cpr = FP4 ? I / 32 : cpr16;         // weight chunks per routed row
+    const size_t row_bytes = FP4 ? (size_t)(I / 2) : (size_t)I;
     const int* ids = p.ids + (size_t)b * k;
     const float* wts = p.w + (size_t)b * k;
+    const u32x4* a16 = static_cast<const u32x4*>(p.a);
 
     float acc = 0.0f;
     for (int j0 = 0; j0 < k; j0 += JB) {
@@ -55,39 +58,36 @@ moe_down_kernel(DownArgs p)
         for (int o0 = 0; o0 < cpr; o0 += kWave * CPL) {
             u32x4 wq[JB][CPL];
             uint32_t ws[JB][CPL];
-            u32x4 av[JB][CPL][NA];
+            u32x4 av[JB][CPL][NP];
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
                 const int j = j0 + jj;
                 const bool live = j < k;
                 const bool ok = (unsigned)e[jj] < (unsigned)p.E;
                 const size_t row = (size_t)(ok ? e[jj] : 0) * (size_t)p.H + (size_t)h;
-                const uint8_t* wrow = p.wd_q + row * (size_t)I;
+                const uint8_t* wrow = p.wd_q + row * row_bytes;
                 const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
-                // row bj of the chunk-interleaved intermediate: piece t of chunk o
-                // is at (bj * NA + t) * cpr + o, in 16-byte units
-                const size_t arow = ((size_t)b * k + (size_t)(live ? j : 0)) * (size_t)NA * (size_t)cpr;
+                const int bj = b * k + (live ? j : 0);
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
                     const int o = o0 + lane + kWave * cc;
                     if (live && o < cpr) {
                         if (ok) {
                             wq[jj][cc] = ld<NT>(reinterpret_cast<const u32x4*>(wrow) + o);
-                            ws[jj][cc] = srow[o >> 1];
+                            ws[jj][cc] = srow[FP4 ? o : o >> 1];
                         } else {                  // invalid routing: NaN scale, no weight read
                             wq[jj][cc] = u32x4{0, 0, 0, 0};
                             ws[jj][cc] = 255u;
                         }
-                        const u32x4* ap = static_cast<const u32x4*>(p.a) + arow + (size_t)o;
 #pragma unroll
-                        for (int t = 0; t < NA; ++t)
-                            av[jj][cc][t] = ap[(size_t)t * cpr];
+                        for (int q = 0; q < NP; ++q)
+                            av[jj][cc][q] = a16[a_unit<FP4, A_BF16>(bj, o, q, cpr16)];
                     } else {
                         wq[jj][cc] = u32x4{0, 0, 0, 0};
                         ws[jj][cc] = 127u;
 #pragma unroll
-                        for (int t = 0; t < NA; ++t)
-                            av[jj][cc][t] = u32x4{0, 0, 0, 0};
+                        for (int q = 0; q < NP; ++q)
+                            av[jj][cc][q] = u32x4{0, 0, 0, 0};
                     }
                 }
             }
@@ -95,18 +95,7 @@ moe_down_kernel(DownArgs p)
             for (int jj = 0; jj < JB; ++jj) {
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
-                    float part = 0.0f;
-                    if constexpr (A_BF16) {
-                        part = dot4_bf16(wq[jj][cc].x, av[jj][cc][0].x, av[jj][cc][0].y, part);
-                        part = dot4_bf16(wq[jj][cc].y, av[jj][cc][0].z, av[jj][cc][0].w, part);
-                        part = dot4_bf16(wq[jj][cc].z, av[jj][cc][1].x, av[jj][cc][1].y, part);
-                        part = dot4_bf16(wq[jj][cc].w, av[jj][cc][1].z, av[jj][cc][1].w, part);
-                    } else {
-                        part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[jj][cc][0]), part);
-                        part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[jj][cc][1]), part);
-                        part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[jj][cc][2]), part);
-                        part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[jj][cc][3]), part);
-                    }
+                    const float part = chunk_dot<FP4, A_BF16>(wq[jj][cc], av[jj][cc]);
                     // fold the routing weight into the one accumulator
                     acc = __builtin_fmaf(wt[jj], part * ue8m0_to_f32(ws[jj][cc]), acc);
                 }
@@ -131,7 +120,7 @@ moe_down_kernel(DownArgs p)
 // start as soon as that slot's weights have arrived. The copy keeps the
 // chunk-interleaved order, so the per-chunk LDS reads are contiguous across
 // lanes (no bank conflicts).
-template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT>
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT, bool FP4>
 __global__ void __launch_bounds__(512)
 moe_down_staged_kernel(DownArgs p)
 {
@@ -146,8 +135,9 @@ moe_down_staged_kernel(DownArgs p)
     const int h = (p.order == 0 ? blk % nblk_h : blk / p.B) * wpb + (int)(threadIdx.x / kWave);
     const bool active = h < p.H;                  // idle waves still help copy a[b]
     const int k = p.k;
-    const int cpr = p.I / 16;
-    const int nunits = k * NA * cpr;              // 16-byte units of a[b]
+    const int cpr16 = p.I / 16;                   // 16-value groups per row of a
+    const int cpr = FP4 ? p.I / 32 : cpr16;       // weight chunks per routed row
+    const int nunits = k * NA * cpr16;            // 16-byte units of a[b]
     const int* ids = p.ids + (size_t)b * k;
     const float* wts = p.w + (size_t)b * k;
     const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
@@ -165,7 +155,7 @@ moe_down_staged_kernel(DownArgs p)
     uint32_t ws[JB][CPL];
     float wt[JB];
     float mask[JB][CPL];
-    down_group_load<CPL, JB, NT>(p, ids, wts, 0, 0, h, active, lane, cpr, wq, ws, wt, mask);
+    down_group_load<CPL, JB, NT, FP4>(p, ids, wts, 0, 0, h, active, lane, cpr, wq, ws, wt, mask);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < kCopyRegs; ++q) {
@@ -179,12 +169,12 @@ moe_down_staged_kernel(DownArgs p)
     if (!active)
         return;                                   // after the only barrier
 
-    float acc = down_group_dot<CPL, JB, A_BF16>(a_lds, k, 0, 0, lane, cpr, wq, ws, wt, mask, 0.0f);
+    float acc = down_group_dot<CPL, JB, A_BF16, FP4>(a_lds, k, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
     // remaining row passes and slot groups (none when one group covers the layer)
     for (int j0 = 0; j0 < k; j0 += JB) {
         for (int o0 = (j0 == 0 ? kWave * CPL : 0); o0 < cpr; o0 += kWave * CPL) {
-            down_group_load<CPL, JB, NT>(p, ids, wts, j0, o0, h, true, lane, cpr, wq, ws, wt, mask);
-            acc = down_group_dot<CPL, JB, A_BF16>(a_lds, k, j0, o0, lane, cpr, wq, ws, wt, mask, acc);
+            down_group_load<CPL, JB, NT, FP4>(p, ids, wts, j0, o0, h, true, lane, cpr, wq, ws, wt, mask);
+            acc = down_group_dot<CPL, JB, A_BF16, FP4>(a_lds, k, j0, o0, lane, cpr, cpr16, wq, ws, wt, mask, acc);
         }
     }
     acc = wave_sum(acc);
@@ -196,21 +186,29 @@ moe_down_staged_kernel(DownArgs p)
     }
 }
 
-template <int CPL, int JB>
+template <int CPL, int JB, bool FP4>
 static hipError_t dispatch_v(bool staged, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p, dim3 grid,
                              dim3 block, size_t lds, hipStream_t s)
 {
 #define MOED_DN(A, O, N) \
     if (a_bf16 == A && out_bf16 == O && nt == N) { \
         if (staged) \
-            hipLaunchKernelGGL((moe_down_staged_kernel<CPL, JB, A, O, N>), grid, block, lds, s, p); \
+            hipLaunchKernelGGL((moe_down_staged_kernel<CPL, JB, A, O, N, FP4>), grid, block, lds, s, p); \
         else \
-            hipLaunchKernelGGL((moe_down_kernel<CPL, JB, A, O, N>), grid, block, 0, s, p); \
+            hipLaunchKernelGGL((moe_down_kernel<CPL, JB, A, O, N, FP4>), grid, block, 0, s, p); \
     }
     MOED_DN(false, false, false) MOED_DN(false, false, true) MOED_DN(false, true, false) MOED_DN(false, true, true)
     MOED_DN(true, false, false) MOED_DN(true, false, true) MOED_DN(true, true, false) MOED_DN(true, true, true)
 #undef MOED_DN
     return hipGetLastError();
+}
+
+template <int CPL, int JB>
+static hipError_t dispatch_f(bool fp4, bool staged, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p,
+                             dim3 grid, dim3 block, size_t lds, hipStream_t s)
+{
+    return fp4 ? dispatch_v<CPL, JB, true>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s)
+               : dispatch_v<CPL, JB, false>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
 }
 
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s)
@@ -220,16 +218,21 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
         return hipSuccess;
     // chunks per lane per row: the smallest of 1, 2, 4, 8 covering the row
     // (longer rows take several passes); slots per group so that CPL * JB <= 8
-    const int cpr = p.I / 16;
-    int cpl = 1;
-    while (cpl < 8 && cpl * kWave < cpr)
-        cpl *= 2;
-    int cap = t.dn_umax < 1 ? 1 : t.dn_umax;
-    while (cpl > 1 && cpl > cap)
-        cpl /= 2;
+    const bool fp4 = p.wfmt == kMXFP4;
+    const int cpr = fp4 ? p.I / 32 : p.I / 16;
     // a[b] staged in LDS when it fits in 64 KiB
     const size_t lds = (size_t)p.k * (size_t)p.I * (a_bf16 ? 2u : 4u);
     const bool staged = t.dn_stage != 0 && lds <= 65536;
+    int cap = t.dn_umax < 1 ? 1 : t.dn_umax;
+    // the unstaged kernel holds every piece of a for its chunks in registers:
+    // 8 pieces per MXFP4 chunk (float32 a), so at most 2 chunks in flight
+    if (fp4 && !staged && cap > 2)
+        cap = 2;
+    int cpl = 1;
+    while (cpl < 8 && cpl * kWave < cpr)
+        cpl *= 2;
+    while (cpl > 1 && cpl > cap)
+        cpl /= 2;
     const int wpb = t.dn_wpb > (staged ? 8 : 4) ? (staged ? 8 : 4) : t.dn_wpb;
     const dim3 block(wpb * kWave);
     const dim3 grid(staged ? (unsigned)((long)p.B * ((p.H + wpb - 1) / wpb)) : (unsigned)((n_out + wpb - 1) / wpb));
@@ -240,16 +243,16 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     while (jb > 1 && (cpl * jb > cap || jb / 2 >= p.k))
         jb /= 2;
     switch (cpl * 16 + jb) {
-    case 1 * 16 + 8: return dispatch_v<1, 8>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 1 * 16 + 4: return dispatch_v<1, 4>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 1 * 16 + 2: return dispatch_v<1, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 1 * 16 + 1: return dispatch_v<1, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 2 * 16 + 4: return dispatch_v<2, 4>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 2 * 16 + 2: return dispatch_v<2, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 2 * 16 + 1: return dispatch_v<2, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 4 * 16 + 2: return dispatch_v<4, 2>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 4 * 16 + 1: return dispatch_v<4, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
-    case 8 * 16 + 1: return dispatch_v<8, 1>(staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 8: return dispatch_f<1, 8>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 4: return dispatch_f<1, 4>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 2: return dispatch_f<1, 2>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 1 * 16 + 1: return dispatch_f<1, 1>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 4: return dispatch_f<2, 4>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 2: return dispatch_f<2, 2>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 2 * 16 + 1: return dispatch_f<2, 1>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 4 * 16 + 2: return dispatch_f<4, 2>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 4 * 16 + 1: return dispatch_f<4, 1>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    case 8 * 16 + 1: return dispatch_f<8, 1>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,8 +1,13 @@
 // Slot-group helpers of the down step (one wavefront per output out[b][h];
 // warp-decode post, "How the two kernels work", third and fourth
-// paragraphs), shared by the LDS-staged down kernel and the single-launch
-// layer kernel. a[b] sits in LDS in the chunk-interleaved order the gate/up
-// step writes (inter_index), in 16-byte units.
+// paragraphs), shared by the down kernels. a sits in the chunk-interleaved
+// order the gate/up step writes (inter_index), in 16-byte units: piece t of
+// the 16-value group g of row bj is unit (bj*NA + t)*(I/16) + g, NA = 4 for
+// float32 a, 2 for bfloat16 a.
+//
+// A weight chunk is 16 bytes of a row: 16 MXFP8 codes (half an MX block, the
+// 16-value group g = o) or 32 MXFP4 codes (one MX block, the groups 2o and
+// 2o+1).
 #pragma once
 
 #include "launch.h"
@@ -12,14 +17,65 @@ namespace moed {
 
 constexpr int kCopyRegs = 4;                  // a[b] units per thread loaded ahead of the weights
 
+// 16-byte pieces of a one weight chunk is dotted with.
+template <bool FP4, bool A_BF16>
+struct APieces {
+    static constexpr int NA = A_BF16 ? 2 : 4;             // per 16-value group
+    static constexpr int N = FP4 ? 2 * NA : NA;
+};
+
+// Unit index of piece q of weight chunk o of row bj (cpr16 = I/16). MXFP4:
+// q = g*NA + t covers group 2o + g.
+template <bool FP4, bool A_BF16>
+__device__ __forceinline__ int a_unit(int bj, int o, int q, int cpr16)
+{
+    constexpr int NA = APieces<FP4, A_BF16>::NA;
+    if constexpr (FP4)
+        return (bj * NA + q % NA) * cpr16 + 2 * o + q / NA;
+    else
+        return (bj * NA + q) * cpr16 + o;
+}
+
+// Partial dot of one weight chunk (scale 1) with its pieces of a.
+template <bool FP4, bool A_BF16>
+__device__ __forceinline__ float chunk_dot(const u32x4& w, const u32x4 (&av)[APieces<FP4, A_BF16>::N])
+{
+    float part = 0.0f;
+    if constexpr (FP4) {
+        // dword d = codes 8d..8d+7 = values 8(d%2).. of group d/2
+        if constexpr (A_BF16) {                 // piece t of a group = values 8t..8t+7: piece d
+            part = dot8_fp4_bf16(w.x, av[0], part);
+            part = dot8_fp4_bf16(w.y, av[1], part);
+            part = dot8_fp4_bf16(w.z, av[2], part);
+            part = dot8_fp4_bf16(w.w, av[3], part);
+        } else {                                // piece t = values 4t..4t+3: pieces 2d, 2d+1
+            part = dot8_fp4_f32a(w.x, __builtin_bit_cast(f32x4, av[0]), __builtin_bit_cast(f32x4, av[1]), part);
+            part = dot8_fp4_f32a(w.y, __builtin_bit_cast(f32x4, av[2]), __builtin_bit_cast(f32x4, av[3]), part);
+            part = dot8_fp4_f32a(w.z, __builtin_bit_cast(f32x4, av[4]), __builtin_bit_cast(f32x4, av[5]), part);
+            part = dot8_fp4_f32a(w.w, __builtin_bit_cast(f32x4, av[6]), __builtin_bit_cast(f32x4, av[7]), part);
+        }
+    } else if constexpr (A_BF16) {
+        part = dot4_bf16(w.x, av[0].x, av[0].y, part);
+        part = dot4_bf16(w.y, av[0].z, av[0].w, part);
+        part = dot4_bf16(w.z, av[1].x, av[1].y, part);
+        part = dot4_bf16(w.w, av[1].z, av[1].w, part);
+    } else {
+        part = dot4_f32a(w.x, __builtin_bit_cast(f32x4, av[0]), part);
+        part = dot4_f32a(w.y, __builtin_bit_cast(f32x4, av[1]), part);
+        part = dot4_f32a(w.z, __builtin_bit_cast(f32x4, av[2]), part);
+        part = dot4_f32a(w.w, __builtin_bit_cast(f32x4, av[3]), part);
+    }
+    return part;
+}
+
 // One slot group (JB routed slots x CPL chunks per lane) of the staged down
-// kernel: issue its weight and scale loads ... Every load is unconditional
-// from a clamped, in-bounds address (a lane past the end of the row re-reads
-// the row's last chunk, an invalid expert id reads expert 0's row); lanes that
-// must not contribute get the scale factor 0 (or NaN for an invalid id, which
-// makes the token's output NaN). Without branches around the loads all of them
-// issue back to back.
-template <int CPL, int JB, bool NT>
+// kernel: issue its weight and scale loads (cpr = weight chunks per row).
+// Every load is unconditional from a clamped, in-bounds address (a lane past
+// the end of the row re-reads the row's last chunk, an invalid expert id reads
+// expert 0's row); lanes that must not contribute get the scale factor 0 (or
+// NaN for an invalid id, which makes the token's output NaN). Without branches
+// around the loads all of them issue back to back.
+template <int CPL, int JB, bool NT, bool FP4>
 __device__ __forceinline__ void down_group_load(const DownArgs& p, const int* ids, const float* wts, int j0,
                                                 int o0, int h, bool active, int lane, int cpr,
                                                 u32x4 (&wq)[JB][CPL], uint32_t (&ws)[JB][CPL], float (&wt)[JB],
@@ -27,6 +83,7 @@ __device__ __forceinline__ void down_group_load(const DownArgs& p, const int* id
 {
     const int k = p.k;
     const int I = p.I;
+    const size_t row_bytes = FP4 ? (size_t)(I / 2) : (size_t)I;
     int eid[JB];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
@@ -40,49 +97,40 @@ __device__ __forceinline__ void down_group_load(const DownArgs& p, const int* id
         const bool live = active && (j0 + jj) < k;
         const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
         const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
-        const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wd_q + row * (size_t)I);
+        const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes);
         const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const int o = o0 + lane + kWave * cc;
             const int oc = o < cpr ? o : cpr - 1;
             wq[jj][cc] = ld<NT>(wrow + oc);
-            ws[jj][cc] = srow[oc >> 1];
+            ws[jj][cc] = srow[FP4 ? oc : oc >> 1];
             mask[jj][cc] = (live && o < cpr) ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
         }
     }
 }
 
-// ... and fold it into the accumulator, reading a from LDS.
-template <int CPL, int JB, bool A_BF16>
+// ... and fold it into the accumulator, reading a[b] from LDS (row j of the
+// staged copy is bj = j).
+template <int CPL, int JB, bool A_BF16, bool FP4>
 __device__ __forceinline__ float down_group_dot(const u32x4* a_lds, int k, int j0, int o0, int lane, int cpr,
-                                                const u32x4 (&wq)[JB][CPL], const uint32_t (&ws)[JB][CPL],
-                                                const float (&wt)[JB], const float (&mask)[JB][CPL], float acc)
+                                                int cpr16, const u32x4 (&wq)[JB][CPL],
+                                                const uint32_t (&ws)[JB][CPL], const float (&wt)[JB],
+                                                const float (&mask)[JB][CPL], float acc)
 {
-    constexpr int NA = A_BF16 ? 2 : 4;
+    constexpr int NP = APieces<FP4, A_BF16>::N;
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
         const int j = j0 + jj < k ? j0 + jj : k - 1;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             const int o = o0 + lane + kWave * cc;
-            u32x4 av[NA];
-            const int base = (j * NA) * cpr + (o < cpr ? o : cpr - 1);
+            const int oc = o < cpr ? o : cpr - 1;
+            u32x4 av[NP];
 #pragma unroll
-            for (int t = 0; t < NA; ++t)
-                av[t] = a_lds[base + t * cpr];
-            float part = 0.0f;
-            if constexpr (A_BF16) {
-                part = dot4_bf16(wq[jj][cc].x, av[0].x, av[0].y, part);
-                part = dot4_bf16(wq[jj][cc].y, av[0].z, av[0].w, part);
-                part = dot4_bf16(wq[jj][cc].z, av[1].x, av[1].y, part);
-                part = dot4_bf16(wq[jj][cc].w, av[1].z, av[1].w, part);
-            } else {
-                part = dot4_f32a(wq[jj][cc].x, __builtin_bit_cast(f32x4, av[0]), part);
-                part = dot4_f32a(wq[jj][cc].y, __builtin_bit_cast(f32x4, av[1]), part);
-                part = dot4_f32a(wq[jj][cc].z, __builtin_bit_cast(f32x4, av[2]), part);
-                part = dot4_f32a(wq[jj][cc].w, __builtin_bit_cast(f32x4, av[3]), part);
-            }
+            for (int q = 0; q < NP; ++q)
+                av[q] = a_lds[a_unit<FP4, A_BF16>(j, oc, q, cpr16)];
+            const float part = chunk_dot<FP4, A_BF16>(wq[jj][cc], av);
             // fold the routing weight into the one accumulator
             acc = __builtin_fmaf(wt[jj] * mask[jj][cc], part * ue8m0_to_f32(ws[jj][cc]), acc);
         }

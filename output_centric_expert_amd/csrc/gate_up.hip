@@ -9,7 +9,7 @@
 
 namespace moed {
 
-template <int U, bool DOT_BF16, bool A_BF16, bool NT>
+template <int U, bool DOT_BF16, bool A_BF16, bool NT, bool FP4>
 __global__ void __launch_bounds__(256)
 moe_gate_up_kernel(GateUpArgs p)
 {
@@ -21,7 +21,7 @@ moe_gate_up_kernel(GateUpArgs p)
         return;                                   // whole wavefront leaves together
     float g, u;
     bool bad_id;
-    gate_up_wave<U, DOT_BF16, NT>(p, wave, lane, g, u, bad_id);
+    gate_up_wave<U, DOT_BF16, NT, FP4>(p, wave, lane, g, u, bad_id);
     g = wave_sum(g);
     u = wave_sum(u);
     if (lane == 0) {
@@ -34,12 +34,12 @@ moe_gate_up_kernel(GateUpArgs p)
     }
 }
 
-template <bool DOT_BF16, bool A_BF16, bool NT>
+template <bool DOT_BF16, bool A_BF16, bool NT, bool FP4>
 static hipError_t dispatch_u(int U, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
 {
     switch (U) {
 #define MOED_GU_CASE(N) \
-    case N: hipLaunchKernelGGL((moe_gate_up_kernel<N, DOT_BF16, A_BF16, NT>), grid, block, 0, s, p); break;
+    case N: hipLaunchKernelGGL((moe_gate_up_kernel<N, DOT_BF16, A_BF16, NT, FP4>), grid, block, 0, s, p); break;
         MOED_GU_CASE(1) MOED_GU_CASE(2) MOED_GU_CASE(3) MOED_GU_CASE(4)
         MOED_GU_CASE(5) MOED_GU_CASE(6) MOED_GU_CASE(7) MOED_GU_CASE(8)
 #undef MOED_GU_CASE
@@ -53,7 +53,8 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
     const long n_out = (long)p.B * p.k * p.I;
     if (n_out == 0)
         return hipSuccess;
-    const int nch = p.H / 16;
+    const bool fp4 = p.wfmt == kMXFP4;
+    const int nch = fp4 ? p.H / 32 : p.H / 16;    // 16-byte chunks per row
     int U = (nch + kWave - 1) / kWave;
     if (U > t.gu_umax)
         U = t.gu_umax;
@@ -63,16 +64,22 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
     const dim3 block(wpb * kWave);
     const dim3 grid((unsigned)((n_out + wpb - 1) / wpb));
     const bool dot = t.gu_dot != 0, nt = t.nt != 0;
-    if (dot) {
-        if (a_bf16) return nt ? dispatch_u<true, true, true>(U, p, grid, block, s)
-                              : dispatch_u<true, true, false>(U, p, grid, block, s);
-        return nt ? dispatch_u<true, false, true>(U, p, grid, block, s)
-                  : dispatch_u<true, false, false>(U, p, grid, block, s);
+    if (fp4) {                                    // one decode route (BF16 dot2)
+        if (a_bf16) return nt ? dispatch_u<true, true, true, true>(U, p, grid, block, s)
+                              : dispatch_u<true, true, false, true>(U, p, grid, block, s);
+        return nt ? dispatch_u<true, false, true, true>(U, p, grid, block, s)
+                  : dispatch_u<true, false, false, true>(U, p, grid, block, s);
     }
-    if (a_bf16) return nt ? dispatch_u<false, true, true>(U, p, grid, block, s)
-                          : dispatch_u<false, true, false>(U, p, grid, block, s);
-    return nt ? dispatch_u<false, false, true>(U, p, grid, block, s)
-              : dispatch_u<false, false, false>(U, p, grid, block, s);
+    if (dot) {
+        if (a_bf16) return nt ? dispatch_u<true, true, true, false>(U, p, grid, block, s)
+                              : dispatch_u<true, true, false, false>(U, p, grid, block, s);
+        return nt ? dispatch_u<true, false, true, false>(U, p, grid, block, s)
+                  : dispatch_u<true, false, false, false>(U, p, grid, block, s);
+    }
+    if (a_bf16) return nt ? dispatch_u<false, true, true, false>(U, p, grid, block, s)
+                          : dispatch_u<false, true, false, false>(U, p, grid, block, s);
+    return nt ? dispatch_u<false, false, true, false>(U, p, grid, block, s)
+              : dispatch_u<false, false, false, false>(U, p, grid, block, s);
 }
 
 }  // namespace moed

@@ -8,7 +8,8 @@
 // projections), then reads e = ids[b][j] with a scalar load and streams the
 // gate row Wg[e][i][:] and the up row Wu[e][i][:] in 16-byte chunks: chunk c
 // (16 codes) goes to lane c % 64, so each wave-wide load instruction covers
-// 1 KiB of one row contiguously. Every load of a pass is issued before the
+// 1 KiB of one row contiguously (MXFP4: a chunk is 32 codes, one MX block).
+// Every load of a pass is issued before the
 // first FMA, without branches around them. Each lane keeps two FP32
 // accumulators (gate, up); the caller reduces them across the wavefront.
 #pragma once
@@ -20,15 +21,20 @@ namespace moed {
 
 // Lane partials of g = Wg[e][i]·x[b] and u = Wu[e][i]·x[b] for wave `wave`;
 // bad_id is set when ids[b][j] is outside [0, E) (the caller then stores NaN).
-template <int U, bool DOT_BF16, bool NT>
+// FP4: MXFP4 weights -- a 16-byte chunk is 32 codes (one MX block, one scale
+// byte) against 32 activations; MXFP8: 16 codes (half a block) against 16.
+// MXFP4 always takes the BF16 dot2 route.
+template <int U, bool DOT_BF16, bool NT, bool FP4 = false>
 __device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int lane, float& g_out, float& u_out,
                                              bool& bad_out)
 {
+    constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
     const int i = wave % p.I;
     const int bj = wave / p.I;
     const int b = bj / p.k;
     const int H = p.H;
-    const int nch = H / 16;                       // 16-code chunks per row
+    const int nch = FP4 ? H / 32 : H / 16;        // 16-byte chunks per row
+    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
     const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
 
     float g = 0.0f, u = 0.0f;
@@ -37,21 +43,22 @@ __device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int 
         // x first: its address does not depend on the routed id, so these loads
         // overlap the id's scalar load. Every load is unconditional from a
         // clamped, in-bounds address; chunks past the row end get scale 0.
-        u32x4 xa[U], xb[U];
+        u32x4 xv[U][NX];
 #pragma unroll
         for (int m = 0; m < U; ++m) {
             const int c = base + lane + kWave * m;
             const int cc = c < nch ? c : nch - 1;
-            xa[m] = xq[2 * cc];
-            xb[m] = xq[2 * cc + 1];
+#pragma unroll
+            for (int t = 0; t < NX; ++t)
+                xv[m][t] = xq[NX * cc + t];
         }
         __builtin_amdgcn_sched_barrier(0);
         const int e_raw = p.ids[bj];
         bad_id = (unsigned)e_raw >= (unsigned)p.E;   // invalid routing: expert 0's rows are read, result NaN
         const int e = bad_id ? 0 : e_raw;
         const size_t row = (size_t)e * (size_t)p.I + (size_t)i;
-        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * (size_t)H);
-        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * (size_t)H);
+        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
+        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
         const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
         const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
         u32x4 wg[U], wu[U];
@@ -63,31 +70,45 @@ __device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int 
             const int cc = c < nch ? c : nch - 1;
             wg[m] = ld<NT>(gq + cc);
             wu[m] = ld<NT>(uq + cc);
-            sg[m] = gs[cc >> 1];
-            su[m] = us[cc >> 1];
+            sg[m] = gs[FP4 ? cc : cc >> 1];
+            su[m] = us[FP4 ? cc : cc >> 1];
             live[m] = c < nch ? 1.0f : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < U; ++m) {
             float pg = 0.0f, pu = 0.0f;
-            if constexpr (DOT_BF16) {
-                pg = dot4_bf16(wg[m].x, xa[m].x, xa[m].y, pg);
-                pu = dot4_bf16(wu[m].x, xa[m].x, xa[m].y, pu);
-                pg = dot4_bf16(wg[m].y, xa[m].z, xa[m].w, pg);
-                pu = dot4_bf16(wu[m].y, xa[m].z, xa[m].w, pu);
-                pg = dot4_bf16(wg[m].z, xb[m].x, xb[m].y, pg);
-                pu = dot4_bf16(wu[m].z, xb[m].x, xb[m].y, pu);
-                pg = dot4_bf16(wg[m].w, xb[m].z, xb[m].w, pg);
-                pu = dot4_bf16(wu[m].w, xb[m].z, xb[m].w, pu);
+            if constexpr (FP4) {
+                // dword d of the chunk = codes 8d..8d+7, against x piece d
+                pg = dot8_fp4_bf16(wg[m].x, xv[m][0], pg);
+                pu = dot8_fp4_bf16(wu[m].x, xv[m][0], pu);
+                pg = dot8_fp4_bf16(wg[m].y, xv[m][1], pg);
+                pu = dot8_fp4_bf16(wu[m].y, xv[m][1], pu);
+                pg = dot8_fp4_bf16(wg[m].z, xv[m][2], pg);
+                pu = dot8_fp4_bf16(wu[m].z, xv[m][2], pu);
+                pg = dot8_fp4_bf16(wg[m].w, xv[m][3], pg);
+                pu = dot8_fp4_bf16(wu[m].w, xv[m][3], pu);
+            } else if constexpr (DOT_BF16) {
+                const u32x4& xa = xv[m][0];
+                const u32x4& xb = xv[m][NX - 1];
+                pg = dot4_bf16(wg[m].x, xa.x, xa.y, pg);
+                pu = dot4_bf16(wu[m].x, xa.x, xa.y, pu);
+                pg = dot4_bf16(wg[m].y, xa.z, xa.w, pg);
+                pu = dot4_bf16(wu[m].y, xa.z, xa.w, pu);
+                pg = dot4_bf16(wg[m].z, xb.x, xb.y, pg);
+                pu = dot4_bf16(wu[m].z, xb.x, xb.y, pu);
+                pg = dot4_bf16(wg[m].w, xb.z, xb.w, pg);
+                pu = dot4_bf16(wu[m].w, xb.z, xb.w, pu);
             } else {
-                pg = dot4_f32(wg[m].x, xa[m].x, xa[m].y, pg);
-                pu = dot4_f32(wu[m].x, xa[m].x, xa[m].y, pu);
-                pg = dot4_f32(wg[m].y, xa[m].z, xa[m].w, pg);
-                pu = dot4_f32(wu[m].y, xa[m].z, xa[m].w, pu);
-                pg = dot4_f32(wg[m].z, xb[m].x, xb[m].y, pg);
-                pu = dot4_f32(wu[m].z, xb[m].x, xb[m].y, pu);
-                pg = dot4_f32(wg[m].w, xb[m].z, xb[m].w, pg);
-                pu = dot4_f32(wu[m].w, xb[m].z, xb[m].w, pu);
+                const u32x4& xa = xv[m][0];
+                const u32x4& xb = xv[m][NX - 1];
+                pg = dot4_f32(wg[m].x, xa.x, xa.y, pg);
+                pu = dot4_f32(wu[m].x, xa.x, xa.y, pu);
+                pg = dot4_f32(wg[m].y, xa.z, xa.w, pg);
+                pu = dot4_f32(wu[m].y, xa.z, xa.w, pu);
+                pg = dot4_f32(wg[m].z, xb.x, xb.y, pg);
+                pu = dot4_f32(wu[m].z, xb.x, xb.y, pu);
+                pg = dot4_f32(wg[m].w, xb.z, xb.w, pg);
+                pu = dot4_f32(wu[m].w, xb.z, xb.w, pu);
             }
             g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g);
             u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u);

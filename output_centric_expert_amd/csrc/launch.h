@@ -27,6 +27,10 @@ struct Tuning {
                         // taking a contiguous range; 2 = hidden-major, plain round robin
 };
 
+// Weight formats (moed_wformat in the C ABI).
+constexpr int kMXFP8 = 0;   // E4M3 codes, one per byte
+constexpr int kMXFP4 = 1;   // E2M1 codes, two per byte (element 2t in the low nibble of byte t)
+
 struct GateUpArgs {
     const uint16_t* x;      // [B][H] bf16
     const int32_t* ids;     // [B][k]
@@ -36,6 +40,7 @@ struct GateUpArgs {
     const uint8_t* wu_s;
     void* a;                // [B][k][I] f32 or bf16
     int B, E, k, H, I;
+    int wfmt;               // kMXFP8 or kMXFP4 (codes [E][I][H/2])
 };
 
 struct DownArgs {
@@ -48,6 +53,7 @@ struct DownArgs {
     int B, E, k, H, I;
     float inv_cpr;          // 1 / (I/16), for the chunk -> (slot, offset) split
     int order;              // workgroup order (Tuning::dn_order)
+    int wfmt;               // kMXFP8 or kMXFP4 (codes [E][H][I/2])
 };
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);

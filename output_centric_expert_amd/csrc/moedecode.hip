@@ -17,6 +17,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline bool dtype_ok(int d) { return d == MOED_BF16 || d == MOED_F32; }
 
+inline bool wformat_ok(int f) { return f == MOED_MXFP8 || f == MOED_MXFP4; }
+
 int check_shape(int B, int E, int k, int H, int I)
 {
     if (B < 0 || E < 1 || k < 1 || k > E)
@@ -51,9 +53,9 @@ moed::Tuning pick(int B, int H, int I)
 // Expert-grouped gate/up pays off once there are about two or more slots per
 // expert on average (each routed row then serves several tokens); its slot
 // list must fit in 64 KiB of LDS.
-bool use_grouped(const moed::Tuning& t, int B, int E, int k)
+bool use_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
 {
-    if (moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
+    if (wfmt != moed::kMXFP8 || moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
@@ -62,14 +64,14 @@ bool use_grouped(const moed::Tuning& t, int B, int E, int k)
 
 hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tuning& t, hipStream_t s)
 {
-    if (use_grouped(t, p.B, p.E, p.k))
+    if (use_grouped(t, p.B, p.E, p.k, p.wfmt))
         return moed::launch_gate_up_grouped(p, a_bf16, t, s);
     return moed::launch_gate_up(p, a_bf16, t, s);
 }
 
-bool use_down_grouped(const moed::Tuning& t, int B, int E, int k)
+bool use_down_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
 {
-    if (!moed::down_grouped_fits(E, k) || t.dn_group == 0)
+    if (wfmt != moed::kMXFP8 || !moed::down_grouped_fits(E, k) || t.dn_group == 0)
         return false;
     if (t.dn_group == 1)
         return true;
@@ -78,14 +80,14 @@ bool use_down_grouped(const moed::Tuning& t, int B, int E, int k)
 
 hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, hipStream_t s)
 {
-    if (use_down_grouped(t, p.B, p.E, p.k))
+    if (use_down_grouped(t, p.B, p.E, p.k, p.wfmt))
         return moed::launch_down_grouped(p, a_bf16, out_bf16, t, s);
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
 
 moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
                               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
-                              void* a, int B, int E, int k, int H, int I)
+                              int wfmt, void* a, int B, int E, int k, int H, int I)
 {
     moed::GateUpArgs p;
     p.x = static_cast<const uint16_t*>(x);
@@ -93,17 +95,19 @@ moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* 
     p.wg_q = wg_q; p.wg_s = wg_s; p.wu_q = wu_q; p.wu_s = wu_s;
     p.a = a;
     p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
+    p.wfmt = wfmt;
     return p;
 }
 
 moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, const uint8_t* wd_q,
-                         const uint8_t* wd_s, void* out, int B, int E, int k, int H, int I)
+                         const uint8_t* wd_s, int wfmt, void* out, int B, int E, int k, int H, int I)
 {
     moed::DownArgs p;
     p.a = a; p.ids = ids; p.w = w; p.wd_q = wd_q; p.wd_s = wd_s; p.out = out;
     p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
     p.inv_cpr = 1.0f / (float)(I / 16);
     p.order = 0;
+    p.wfmt = wfmt;
     return p;
 }
 
@@ -119,12 +123,12 @@ size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype)
 }
 
 int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg_q,
-                       const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                       const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, int weight_format,
                        void* a, int inter_dtype, int B, int E, int k, int H, int I, void* stream)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
-    if (!dtype_ok(inter_dtype))
+    if (!dtype_ok(inter_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
     if (B == 0)
         return MOED_OK;
@@ -133,17 +137,18 @@ int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(a))
         return MOED_ERR_ALIGN;
     const moed::Tuning t = pick(B, H, I);
-    return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a, B, E, k, H, I),
+    return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, a,
+                                                  B, E, k, H, I),
                                      inter_dtype == MOED_BF16, t, static_cast<hipStream_t>(stream)));
 }
 
 int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
-                    const uint8_t* wd_q, const uint8_t* wd_s, void* out, int out_dtype,
+                    const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
                     int B, int E, int k, int H, int I, void* stream)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
-    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype))
+    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
     if (B == 0)
         return MOED_OK;
@@ -152,19 +157,20 @@ int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, con
     if (!aligned16(a) || !aligned16(wd_q))
         return MOED_ERR_ALIGN;
     const moed::Tuning t = pick(B, H, I);
-    return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I),
+    return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I),
                                         inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t,
                                         static_cast<hipStream_t>(stream)));
 }
 
 int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
                const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
-               const uint8_t* wd_q, const uint8_t* wd_s, void* out, int out_dtype, int inter_dtype,
-               int B, int E, int k, int H, int I, void* workspace, size_t workspace_bytes, void* stream)
+               const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
+               int inter_dtype, int B, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
+               void* stream)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
-    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype))
+    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
     if (B == 0)
         return MOED_OK;
@@ -178,18 +184,18 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool a_bf16 = inter_dtype == MOED_BF16;
     int st = hip_status(gate_up_launch(
-        gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, workspace, B, E, k, H, I), a_bf16, t, s));
+        gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, workspace, B, E, k, H, I), a_bf16, t, s));
     if (st)
         return st;
     return hip_status(down_launch(
-        down_args(workspace, topk_ids, topk_w, wd_q, wd_s, out, B, E, k, H, I), a_bf16,
+        down_args(workspace, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I), a_bf16,
         out_dtype == MOED_BF16, t, s));
 }
 
 int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n, int path,
                          void* stream)
 {
-    if (n < 0 || path < 0 || path > 2)
+    if (n < 0 || path < 0 || path > 4)
         return MOED_ERR_SHAPE;
     if (n == 0)
         return MOED_OK;

@@ -10,6 +10,12 @@
 // bfloat16 (3 mantissa bits, exponents 2^-9 .. 2^8) and in float32, and the
 // product of an E4M3 value with a bfloat16 activation (4 x 8 significant bits)
 // is exact in float32. Only the float32 accumulation rounds.
+//
+// MXFP4 decode: a weight is E2M1(code) * 2^(scale - 127), codes two per byte
+// (element 2t in the low nibble of byte t). A 16-byte chunk holds 32 codes,
+// exactly one MX block, so the block scale is again applied once per lane
+// partial. E2M1 values (2 significant bits, 0.5 .. 6) are exact in bfloat16 and
+// float32, and so are their products with bfloat16 activations.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,6 +79,41 @@ __device__ __forceinline__ float dot4_f32(uint32_t codes, uint32_t x01, uint32_t
     acc = __builtin_fmaf(w01.y, bf16_hi(x01), acc);
     acc = __builtin_fmaf(w23.x, bf16_lo(x23), acc);
     acc = __builtin_fmaf(w23.y, bf16_hi(x23), acc);
+    return acc;
+}
+
+// acc + sum_{t<8} E2M1(nibble t of codes) * x[t], x[0..7] as 8 bf16 in a u32x4
+// (dword d = the pair 2d, 2d+1): byte d of the codes converts to the same pair
+// (v_cvt_scalef32_pk_bf16_fp4, scale 1), then one BF16 dot2 per pair.
+__device__ __forceinline__ float dot8_fp4_bf16(uint32_t codes, u32x4 x, float acc)
+{
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0),
+                                          as_bf16x2(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1),
+                                          as_bf16x2(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2),
+                                          as_bf16x2(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3),
+                                          as_bf16x2(x.w), acc, false);
+    return acc;
+}
+
+// acc + sum_{t<8} E2M1(nibble t of codes) * a[t] with float32 activations
+// a[0..3] = lo, a[4..7] = hi (v_cvt_scalef32_pk_f32_fp4, scale 1, then FMAs).
+__device__ __forceinline__ float dot8_fp4_f32a(uint32_t codes, f32x4 lo, f32x4 hi, float acc)
+{
+    const f32x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const f32x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const f32x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const f32x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    acc = __builtin_fmaf(w0.x, lo.x, acc);
+    acc = __builtin_fmaf(w0.y, lo.y, acc);
+    acc = __builtin_fmaf(w1.x, lo.z, acc);
+    acc = __builtin_fmaf(w1.y, lo.w, acc);
+    acc = __builtin_fmaf(w2.x, hi.x, acc);
+    acc = __builtin_fmaf(w2.y, hi.y, acc);
+    acc = __builtin_fmaf(w3.x, hi.z, acc);
+    acc = __builtin_fmaf(w3.y, hi.w, acc);
     return acc;
 }
 

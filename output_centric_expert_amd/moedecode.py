@@ -48,11 +48,11 @@ def load() -> ctypes.CDLL:
         P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         lib.moed_workspace_bytes.argtypes = [I, I, I, I]
         lib.moed_workspace_bytes.restype = Z
-        lib.moe_decode.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
+        lib.moe_decode.argtypes = [P] * 9 + [I, P] + [I] * 7 + [P, Z, P]
         lib.moe_decode.restype = I
-        lib.moe_decode_gate_up.argtypes = [P] * 7 + [I] * 6 + [P]
+        lib.moe_decode_gate_up.argtypes = [P] * 6 + [I, P] + [I] * 6 + [P]
         lib.moe_decode_gate_up.restype = I
-        lib.moe_decode_down.argtypes = [P, I, P, P, P, P, P, I] + [I] * 5 + [P]
+        lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P]
         lib.moe_decode_down.restype = I
         lib.moed_selftest_decode.argtypes = [P, P, P, I, I, P]
         lib.moed_selftest_decode.restype = I
@@ -102,12 +102,25 @@ def moed_workspace_bytes(B: int, k: int, I: int, inter_dtype=torch.float32) -> i
     return int(load().moed_workspace_bytes(B, k, I, _DT[inter_dtype]))
 
 
+_WF = {"mxfp8": 0, "mxfp4": 1}          # moed_wformat
+
+
+def _kb(K: int, wformat: str) -> int:
+    """Code bytes per row of K values."""
+    if wformat not in _WF:
+        raise ValueError(f"unknown weight format {wformat!r}")
+    return K // 2 if wformat == "mxfp4" else K
+
+
 def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None,
-               out_dtype=torch.bfloat16, inter_dtype=torch.float32, workspace=None, stream=None):
-    """The whole layer: returns out [B, H] (out_dtype)."""
+               out_dtype=torch.bfloat16, inter_dtype=torch.float32, workspace=None, stream=None,
+               wformat="mxfp8"):
+    """The whole layer: returns out [B, H] (out_dtype). wformat: "mxfp8" or "mxfp4"
+    (codes [E, I, H/2] and [E, H, I/2], two per byte, low nibble first)."""
     B, H = x.shape
     k = topk_ids.shape[1]
     E, I = wg_q.shape[0], wg_q.shape[1]
+    HB, IB = _kb(H, wformat), _kb(I, wformat)
     if out is None:
         out = torch.empty((B, H), dtype=out_dtype, device=x.device)
     need = moed_workspace_bytes(B, k, I, inter_dtype)
@@ -116,44 +129,47 @@ def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None
     st = load().moe_decode(
         _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(topk_w, "topk_w", torch.float32, (B, k)),
-        _ptr(wg_q, "wg_q", torch.uint8, (E, I, H)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
-        _ptr(wu_q, "wu_q", torch.uint8, (E, I, H)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
-        _ptr(wd_q, "wd_q", torch.uint8, (E, H, I)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
-        _ptr(out, "out", None, (B, H)), _DT[out.dtype], _DT[inter_dtype],
+        _ptr(wg_q, "wg_q", torch.uint8, (E, I, HB)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wu_q, "wu_q", torch.uint8, (E, I, HB)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
+        _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], _DT[inter_dtype],
         B, E, k, H, I, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(st, "moe_decode")
     return out
 
 
 def moe_decode_gate_up(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a=None, inter_dtype=torch.float32,
-                       stream=None):
+                       stream=None, wformat="mxfp8"):
     """Gate/up step alone: returns a = SiLU(gate) * up, shape [B, k, I] in the
     library's chunk-interleaved element order (inter_to_bki() gives plain order)."""
     B, H = x.shape
     k = topk_ids.shape[1]
     E, I = wg_q.shape[0], wg_q.shape[1]
+    HB = _kb(H, wformat)
     if a is None:
         a = torch.empty((B, k, I), dtype=inter_dtype, device=x.device)
     st = load().moe_decode_gate_up(
         _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
-        _ptr(wg_q, "wg_q", torch.uint8, (E, I, H)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
-        _ptr(wu_q, "wu_q", torch.uint8, (E, I, H)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
-        _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], B, E, k, H, I, _stream(stream))
+        _ptr(wg_q, "wg_q", torch.uint8, (E, I, HB)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wu_q, "wu_q", torch.uint8, (E, I, HB)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
+        _WF[wformat], _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], B, E, k, H, I, _stream(stream))
     _check(st, "moe_decode_gate_up")
     return a
 
 
-def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.bfloat16, stream=None):
+def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.bfloat16, stream=None,
+                    wformat="mxfp8"):
     """Down step alone: returns out [B, H] from a [B, k, I]."""
     B, k, I = a.shape
     E, H = wd_q.shape[0], wd_q.shape[1]
+    IB = _kb(I, wformat)
     if out is None:
         out = torch.empty((B, H), dtype=out_dtype, device=a.device)
     st = load().moe_decode_down(
         _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(topk_w, "topk_w", torch.float32, (B, k)),
-        _ptr(wd_q, "wd_q", torch.uint8, (E, H, I)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
-        _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, _stream(stream))
+        _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
+        _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, _stream(stream))
     _check(st, "moe_decode_down")
     return out
 

@@ -60,8 +60,8 @@ MIS = P(4100)        # misaligned
 
 
 def call_decode(lib, x=A, ids=A, w=A, wq=A, ws=A, out=A, od=0, idt=1, B=1, E=8, k=2, H=256, I=128,
-                wsp=A, wsb=1 << 20):
-    return lib.moe_decode(x, ids, w, wq, ws, wq, ws, wq, ws, out, od, idt, B, E, k, H, I, wsp, wsb, None)
+                wsp=A, wsb=1 << 20, wf=0):
+    return lib.moe_decode(x, ids, w, wq, ws, wq, ws, wq, ws, wf, out, od, idt, B, E, k, H, I, wsp, wsb, None)
 
 
 def test_decode_rejects_before_launch(lib):
@@ -77,6 +77,9 @@ def test_decode_rejects_before_launch(lib):
     assert call_decode(lib, B=1 << 20, H=4096) == md.MOED_ERR_SHAPE   # B*H >= 2^31
     assert call_decode(lib, od=2) == md.MOED_ERR_DTYPE
     assert call_decode(lib, idt=-1) == md.MOED_ERR_DTYPE
+    assert call_decode(lib, wf=2) == md.MOED_ERR_DTYPE          # unknown weight format
+    assert call_decode(lib, wf=-1) == md.MOED_ERR_DTYPE
+    assert call_decode(lib, wf=1, x=None) == md.MOED_ERR_NULL   # MXFP4 goes through the same checks
     assert call_decode(lib, wsb=1 * 2 * 128 * 4 - 1) == md.MOED_ERR_WORKSPACE
     assert call_decode(lib, x=MIS) == md.MOED_ERR_ALIGN
     assert call_decode(lib, wq=MIS) == md.MOED_ERR_ALIGN
@@ -86,19 +89,21 @@ def test_decode_rejects_before_launch(lib):
 
 
 def test_step_entry_points_reject_before_launch(lib):
-    gu = lambda **kw: lib.moe_decode_gate_up(kw.get("x", A), A, A, A, A, A, kw.get("a", A), kw.get("idt", 1),
-                                             kw.get("B", 1), 8, kw.get("k", 2), 256, 128, None)
+    gu = lambda **kw: lib.moe_decode_gate_up(kw.get("x", A), A, A, A, A, A, kw.get("wf", 0), kw.get("a", A),
+                                             kw.get("idt", 1), kw.get("B", 1), 8, kw.get("k", 2), 256, 128, None)
     assert gu(x=None) == md.MOED_ERR_NULL
     assert gu(a=MIS) == md.MOED_ERR_ALIGN
     assert gu(idt=5) == md.MOED_ERR_DTYPE
+    assert gu(wf=3) == md.MOED_ERR_DTYPE
     assert gu(k=0) == md.MOED_ERR_SHAPE
     assert gu(B=0, x=None) == md.MOED_OK
-    dn = lambda **kw: lib.moe_decode_down(kw.get("a", A), 1, A, A, kw.get("wq", A), A, kw.get("out", A),
-                                          kw.get("od", 0), 1, 8, 2, 256, 128, None)
+    dn = lambda **kw: lib.moe_decode_down(kw.get("a", A), 1, A, A, kw.get("wq", A), A, kw.get("wf", 0),
+                                          kw.get("out", A), kw.get("od", 0), 1, 8, 2, 256, 128, None)
     assert dn(out=None) == md.MOED_ERR_NULL
     assert dn(wq=MIS) == md.MOED_ERR_ALIGN
     assert dn(od=3) == md.MOED_ERR_DTYPE
-    assert lib.moed_selftest_decode(A, A, A, 4, 3, None) == md.MOED_ERR_SHAPE
+    assert dn(wf=7) == md.MOED_ERR_DTYPE
+    assert lib.moed_selftest_decode(A, A, A, 4, 5, None) == md.MOED_ERR_SHAPE
     assert lib.moed_selftest_decode(A, A, A, 4, -1, None) == md.MOED_ERR_SHAPE
     assert lib.moed_selftest_decode(None, A, A, 4, 0, None) == md.MOED_ERR_NULL
     assert lib.moed_selftest_decode(None, None, None, 0, 0, None) == md.MOED_OK
