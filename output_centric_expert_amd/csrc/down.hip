@@ -120,7 +120,7 @@ moe_down_kernel(DownArgs p)
 // start as soon as that slot's weights have arrived. The copy keeps the
 // chunk-interleaved order, so the per-chunk LDS reads are contiguous across
 // lanes (no bank conflicts).
-template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT, bool FP4>
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool NT, bool FP4, int G>
 __global__ void __launch_bounds__(512)
 moe_down_staged_kernel(DownArgs p)
 {
@@ -155,7 +155,7 @@ moe_down_staged_kernel(DownArgs p)
     uint32_t ws[JB][CPL];
     float wt[JB];
     float mask[JB][CPL];
-    down_group_load<CPL, JB, NT, FP4>(p, ids, wts, 0, 0, h, active, lane, cpr, wq, ws, wt, mask);
+    down_group_load<CPL, JB, NT, FP4, G>(p, ids, wts, 0, 0, h, active, lane, cpr, wq, ws, wt, mask);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < kCopyRegs; ++q) {
@@ -169,12 +169,14 @@ moe_down_staged_kernel(DownArgs p)
     if (!active)
         return;                                   // after the only barrier
 
-    float acc = down_group_dot<CPL, JB, A_BF16, FP4>(a_lds, k, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
+    float acc = down_group_dot<CPL, JB, A_BF16, FP4, G>(a_lds, k, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
     // remaining row passes and slot groups (none when one group covers the layer)
-    for (int j0 = 0; j0 < k; j0 += JB) {
-        for (int o0 = (j0 == 0 ? kWave * CPL : 0); o0 < cpr; o0 += kWave * CPL) {
-            down_group_load<CPL, JB, NT, FP4>(p, ids, wts, j0, o0, h, true, lane, cpr, wq, ws, wt, mask);
-            acc = down_group_dot<CPL, JB, A_BF16, FP4>(a_lds, k, j0, o0, lane, cpr, cpr16, wq, ws, wt, mask, acc);
+    constexpr int LW = LaneGroups<G>::LW;
+    for (int j0 = 0; j0 < k; j0 += G * JB) {
+        for (int o0 = (j0 == 0 ? LW * CPL : 0); o0 < cpr; o0 += LW * CPL) {
+            down_group_load<CPL, JB, NT, FP4, G>(p, ids, wts, j0, o0, h, true, lane, cpr, wq, ws, wt, mask);
+            acc = down_group_dot<CPL, JB, A_BF16, FP4, G>(a_lds, k, j0, o0, lane, cpr, cpr16, wq, ws, wt, mask,
+                                                          acc);
         }
     }
     acc = wave_sum(acc);
@@ -186,15 +188,15 @@ moe_down_staged_kernel(DownArgs p)
     }
 }
 
-template <int CPL, int JB, bool FP4>
+template <int CPL, int JB, bool FP4, int G = 1>
 static hipError_t dispatch_v(bool staged, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p, dim3 grid,
                              dim3 block, size_t lds, hipStream_t s)
 {
 #define MOED_DN(A, O, N) \
     if (a_bf16 == A && out_bf16 == O && nt == N) { \
         if (staged) \
-            hipLaunchKernelGGL((moe_down_staged_kernel<CPL, JB, A, O, N, FP4>), grid, block, lds, s, p); \
-        else \
+            hipLaunchKernelGGL((moe_down_staged_kernel<CPL, JB, A, O, N, FP4, G>), grid, block, lds, s, p); \
+        else if constexpr (G == 1) \
             hipLaunchKernelGGL((moe_down_kernel<CPL, JB, A, O, N, FP4>), grid, block, 0, s, p); \
     }
     MOED_DN(false, false, false) MOED_DN(false, false, true) MOED_DN(false, true, false) MOED_DN(false, true, true)
@@ -209,6 +211,24 @@ static hipError_t dispatch_f(bool fp4, bool staged, bool a_bf16, bool out_bf16, 
 {
     return fp4 ? dispatch_v<CPL, JB, true>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s)
                : dispatch_v<CPL, JB, false>(staged, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+}
+
+// staged kernel with G lane groups (one chunk per lane, JB slots per group)
+template <int G>
+static hipError_t dispatch_g(int jb, bool fp4, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p, dim3 grid,
+                             dim3 block, size_t lds, hipStream_t s)
+{
+    switch (jb * 2 + (fp4 ? 1 : 0)) {
+    case 8 * 2 + 0: return dispatch_v<1, 8, false, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 8 * 2 + 1: return dispatch_v<1, 8, true, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 4 * 2 + 0: return dispatch_v<1, 4, false, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 4 * 2 + 1: return dispatch_v<1, 4, true, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 2 * 2 + 0: return dispatch_v<1, 2, false, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 2 * 2 + 1: return dispatch_v<1, 2, true, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 2 + 0: return dispatch_v<1, 1, false, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    case 1 * 2 + 1: return dispatch_v<1, 1, true, G>(true, a_bf16, out_bf16, nt, p, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s)
@@ -239,6 +259,22 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     const bool nt = t.nt == 2 ? (long)p.B * p.k < (long)p.E : t.nt != 0;
     DownArgs q = p;
     q.order = t.dn_order;
+    // lane groups (staged kernel): rows of at most 16 or 32 chunks share the
+    // wavefront among 4 or 2 slots at a time (at most k groups)
+    int groups = 1;
+    if (staged && t.dn_lanegroups != 0) {
+        while (groups < 4 && cpr <= kWave / (2 * groups) && 2 * groups <= p.k)
+            groups *= 2;
+    }
+    if (groups > 1) {
+        const int per = (p.k + groups - 1) / groups;   // slots per group
+        int jbg = 8;
+        while (jbg > 1 && (jbg > cap || jbg / 2 >= per))
+            jbg /= 2;
+        if (groups == 2)
+            return dispatch_g<2>(jbg, fp4, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+        return dispatch_g<4>(jbg, fp4, a_bf16, out_bf16, nt, q, grid, block, lds, s);
+    }
     int jb = 8 / cpl;
     while (jb > 1 && (cpl * jb > cap || jb / 2 >= p.k))
         jb /= 2;

@@ -68,6 +68,18 @@ __device__ __forceinline__ float chunk_dot(const u32x4& w, const u32x4 (&av)[APi
     return part;
 }
 
+// Lane groups: with G > 1 (rows of at most 64/G chunks) the wavefront is cut
+// into G groups of LW = 64/G lanes; group g takes the slots j = j0 + g + G*jj
+// and lane c of a group the chunks o = o0 + c + LW*cc. With G = 1 every lane
+// takes every slot and the slot (expert id, routing weight) is uniform across
+// the wavefront.
+template <int G>
+struct LaneGroups {
+    static constexpr int LW = kWave / G;
+    __device__ static int group(int lane) { return G == 1 ? 0 : lane / LW; }
+    __device__ static int chunk(int lane) { return G == 1 ? lane : lane % LW; }
+};
+
 // One slot group (JB routed slots x CPL chunks per lane) of the staged down
 // kernel: issue its weight and scale loads (cpr = weight chunks per row).
 // Every load is unconditional from a clamped, in-bounds address (a lane past
@@ -75,33 +87,37 @@ __device__ __forceinline__ float chunk_dot(const u32x4& w, const u32x4 (&av)[APi
 // expert 0's row); lanes that must not contribute get the scale factor 0 (or
 // NaN for an invalid id, which makes the token's output NaN). Without branches
 // around the loads all of them issue back to back.
-template <int CPL, int JB, bool NT, bool FP4>
+template <int CPL, int JB, bool NT, bool FP4, int G = 1>
 __device__ __forceinline__ void down_group_load(const DownArgs& p, const int* ids, const float* wts, int j0,
                                                 int o0, int h, bool active, int lane, int cpr,
                                                 u32x4 (&wq)[JB][CPL], uint32_t (&ws)[JB][CPL], float (&wt)[JB],
                                                 float (&mask)[JB][CPL])
 {
+    using LG = LaneGroups<G>;
     const int k = p.k;
     const int I = p.I;
     const size_t row_bytes = FP4 ? (size_t)(I / 2) : (size_t)I;
+    const int js = j0 + LG::group(lane);
+    const int lc = LG::chunk(lane);
     int eid[JB];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
-        const int jc = j0 + jj < k ? j0 + jj : k - 1;
+        const int j = js + G * jj;
+        const int jc = j < k ? j : k - 1;
         eid[jj] = ids[jc];
         wt[jj] = wts[jc];
     }
     const int hc = active ? h : 0;
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
-        const bool live = active && (j0 + jj) < k;
+        const bool live = active && (js + G * jj) < k;
         const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
         const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
         const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes);
         const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-            const int o = o0 + lane + kWave * cc;
+            const int o = o0 + lc + LG::LW * cc;
             const int oc = o < cpr ? o : cpr - 1;
             wq[jj][cc] = ld<NT>(wrow + oc);
             ws[jj][cc] = srow[FP4 ? oc : oc >> 1];
@@ -112,19 +128,22 @@ __device__ __forceinline__ void down_group_load(const DownArgs& p, const int* id
 
 // ... and fold it into the accumulator, reading a[b] from LDS (row j of the
 // staged copy is bj = j).
-template <int CPL, int JB, bool A_BF16, bool FP4>
+template <int CPL, int JB, bool A_BF16, bool FP4, int G = 1>
 __device__ __forceinline__ float down_group_dot(const u32x4* a_lds, int k, int j0, int o0, int lane, int cpr,
                                                 int cpr16, const u32x4 (&wq)[JB][CPL],
                                                 const uint32_t (&ws)[JB][CPL], const float (&wt)[JB],
                                                 const float (&mask)[JB][CPL], float acc)
 {
+    using LG = LaneGroups<G>;
     constexpr int NP = APieces<FP4, A_BF16>::N;
+    const int js = j0 + LG::group(lane);
+    const int lc = LG::chunk(lane);
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
-        const int j = j0 + jj < k ? j0 + jj : k - 1;
+        const int j = js + G * jj < k ? js + G * jj : k - 1;
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
-            const int o = o0 + lane + kWave * cc;
+            const int o = o0 + lc + LG::LW * cc;
             const int oc = o < cpr ? o : cpr - 1;
             u32x4 av[NP];
 #pragma unroll

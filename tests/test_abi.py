@@ -120,6 +120,8 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"dn_order=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"nt=2") == md.MOED_OK
     assert lib.moed_set_tuning(b"nt=3") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"dn_lanegroups=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_lanegroups=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(None) == md.MOED_OK
