@@ -149,10 +149,12 @@ int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
  *   path 2: E4M3, FP8 -> BF16 with the block scale folded into the conversion
  *           (the large-batch route; exact for scale codes 10..245);
  *   path 3: E2M1 (low nibble of codes[t]), FP4 -> BF16, scale afterwards;
- *   path 4: E2M1 (low nibble of codes[t]), FP4 -> FP32, scale afterwards.
+ *   path 4: E2M1 (low nibble of codes[t]), FP4 -> FP32, scale afterwards;
+ *   path 5: E2M1, FP4 -> BF16 with the block scale folded into the conversion
+ *           (the large-batch route; exact for scale codes 2..252).
  * The E2M1 paths place code t at nibble t % 8 of a packed dword, so every
  * byte select and both nibble positions are exercised.
- * Device pointers; n >= 0; path in {0, ..., 4}.
+ * Device pointers; n >= 0; path in {0, ..., 5}.
  */
 int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out,
                          int n, int path, void *stream);

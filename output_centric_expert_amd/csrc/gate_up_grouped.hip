@@ -8,10 +8,11 @@
 // (expert e, 64 neurons); it compacts the list of slots routed to e (in slot
 // order, from topk_ids), and each wavefront computes tiles of 16 neurons x 16
 // of those slots (up to four tiles per pass over the rows) with MFMA:
-//   A = the gate (or up) rows, decoded exactly from MXFP8 to BF16 with the
-//       block scale folded into the conversion (v_cvt_scalef32_pk_bf16_fp8;
-//       exact for scale codes 10..245, where the scaled E4M3 values stay
-//       normal, finite BF16 numbers),
+//   A = the gate (or up) rows, decoded exactly from MXFP8 (or MXFP4) to BF16
+//       with the block scale folded into the conversion
+//       (v_cvt_scalef32_pk_bf16_fp8 / _fp4; exact for scale codes 10..245
+//       (E4M3) or 2..252 (E2M1), where the scaled values stay normal, finite
+//       BF16 numbers),
 //   B = the BF16 activations of the 16 slots' tokens,
 //   D = FP32 accumulators (v_mfma_f32_16x16x32_bf16, products exact in FP32).
 // Each output is still written once, by the one lane that holds it, as
@@ -40,6 +41,21 @@ __device__ __forceinline__ bf16x8 decode8_scaled(u32x2 codes, float scale)
     const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
     const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// 8 E2M1 codes (one dword, element 2t in the low nibble of byte t) times
+// 2^(s-127) -> 8 BF16 values, exactly while the scaled values stay normal,
+// finite BF16 numbers (scale codes 2..252).
+__device__ __forceinline__ bf16x8 decode8_scaled_fp4(uint32_t codes, float scale)
+{
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
     bf16x8 r;
     r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
     r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
@@ -92,9 +108,9 @@ struct GroupedRow {
 // K is walked in groups of 4 MX blocks (128 codes); inside a group, lane
 // (row, kb) supplies block kb's 32 contiguous codes over the 4 MFMA steps
 // (8 per step) and x uses the same k order, so the products summed are the
-// row-times-x products, only in another order. One 32-byte load per row and
-// one scale byte per row per group.
-template <int NTL, bool A_BF16>
+// row-times-x products, only in another order. One 32-byte (MXFP8) or
+// 16-byte (MXFP4) load per row and one scale byte per row per group.
+template <int NTL, bool A_BF16, bool FP4>
 __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedRow& r, const int* slots,
                                              int count, int t0)
 {
@@ -116,11 +132,12 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
     }
     int st = 0;
     for (; st + 4 <= r.nsteps; st += 4) {
-        const int kbase = st * 32 + 32 * r.kb;    // this lane's MX block
-        const u32x4 g0 = *reinterpret_cast<const u32x4*>(r.gq + kbase);
-        const u32x4 g1 = *reinterpret_cast<const u32x4*>(r.gq + kbase + 16);
-        const u32x4 u0 = *reinterpret_cast<const u32x4*>(r.uq + kbase);
-        const u32x4 u1 = *reinterpret_cast<const u32x4*>(r.uq + kbase + 16);
+        const int kbase = st * 32 + 32 * r.kb;    // this lane's MX block (value index)
+        const int bbase = FP4 ? kbase / 2 : kbase;   // its first code byte
+        const u32x4 g0 = *reinterpret_cast<const u32x4*>(r.gq + bbase);
+        const u32x4 u0 = *reinterpret_cast<const u32x4*>(r.uq + bbase);
+        const u32x4 g1 = FP4 ? g0 : *reinterpret_cast<const u32x4*>(r.gq + bbase + 16);
+        const u32x4 u1 = FP4 ? u0 : *reinterpret_cast<const u32x4*>(r.uq + bbase + 16);
         const float sgf = ue8m0_to_f32(r.gs[st + r.kb]);
         const float suf = ue8m0_to_f32(r.us[st + r.kb]);
         u32x4 xv[NTL][4];
@@ -131,12 +148,18 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
                 xv[tt][q] = *reinterpret_cast<const u32x4*>(xr[tt] + kbase + 8 * q);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const u32x4 gsrc = q < 2 ? g0 : g1;
-            const u32x4 usrc = q < 2 ? u0 : u1;
-            const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
-            const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
-            const bf16x8 ag = decode8_scaled(cgq, sgf);
-            const bf16x8 au = decode8_scaled(cuq, suf);
+            bf16x8 ag, au;
+            if constexpr (FP4) {                  // dword q = codes 8q .. 8q+7
+                ag = decode8_scaled_fp4(g0[q], sgf);
+                au = decode8_scaled_fp4(u0[q], suf);
+            } else {
+                const u32x4 gsrc = q < 2 ? g0 : g1;
+                const u32x4 usrc = q < 2 ? u0 : u1;
+                const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
+                const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
+                ag = decode8_scaled(cgq, sgf);
+                au = decode8_scaled(cuq, suf);
+            }
 #pragma unroll
             for (int tt = 0; tt < NTL; ++tt) {
                 const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[tt][q]);
@@ -147,10 +170,18 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
     }
     for (; st < r.nsteps; ++st) {                 // leftover blocks: plain k order
         const int k0 = st * 32 + 8 * r.kb;
-        const u32x2 cg = *reinterpret_cast<const u32x2*>(r.gq + k0);
-        const u32x2 cu = *reinterpret_cast<const u32x2*>(r.uq + k0);
-        const bf16x8 ag = decode8_scaled(cg, ue8m0_to_f32(r.gs[st]));
-        const bf16x8 au = decode8_scaled(cu, ue8m0_to_f32(r.us[st]));
+        bf16x8 ag, au;
+        if constexpr (FP4) {
+            const uint32_t cg = *reinterpret_cast<const uint32_t*>(r.gq + k0 / 2);
+            const uint32_t cu = *reinterpret_cast<const uint32_t*>(r.uq + k0 / 2);
+            ag = decode8_scaled_fp4(cg, ue8m0_to_f32(r.gs[st]));
+            au = decode8_scaled_fp4(cu, ue8m0_to_f32(r.us[st]));
+        } else {
+            const u32x2 cg = *reinterpret_cast<const u32x2*>(r.gq + k0);
+            const u32x2 cu = *reinterpret_cast<const u32x2*>(r.uq + k0);
+            ag = decode8_scaled(cg, ue8m0_to_f32(r.gs[st]));
+            au = decode8_scaled(cu, ue8m0_to_f32(r.us[st]));
+        }
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt) {
             const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr[tt] + k0));
@@ -176,7 +207,7 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
     }
 }
 
-template <bool A_BF16>
+template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
 moe_gate_up_grouped_kernel(GateUpArgs p)
 {
@@ -220,8 +251,9 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
     const int kb = lane / 16;                     // which quarter of a k group
     const int col = lane % 16;                    // A row (neuron) / B column (slot)
     const size_t row = (size_t)e * (size_t)I + (size_t)(n0 + col);
-    const uint8_t* gq = p.wg_q + row * (size_t)H;
-    const uint8_t* uq = p.wu_q + row * (size_t)H;
+    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
+    const uint8_t* gq = p.wg_q + row * row_bytes;
+    const uint8_t* uq = p.wu_q + row * row_bytes;
     const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
     const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
     const int nsteps = H / 32;                    // MX blocks per row = MFMA K steps
@@ -234,10 +266,10 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
         const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
         const GroupedRow r{gq, uq, gs, us, nsteps, n0, kb, col};
         switch (nt) {
-        case 1: grouped_pass<1, A_BF16>(p, r, slots, count, t0); break;
-        case 2: grouped_pass<2, A_BF16>(p, r, slots, count, t0); break;
-        case 3: grouped_pass<3, A_BF16>(p, r, slots, count, t0); break;
-        default: grouped_pass<4, A_BF16>(p, r, slots, count, t0); break;
+        case 1: grouped_pass<1, A_BF16, FP4>(p, r, slots, count, t0); break;
+        case 2: grouped_pass<2, A_BF16, FP4>(p, r, slots, count, t0); break;
+        case 3: grouped_pass<3, A_BF16, FP4>(p, r, slots, count, t0); break;
+        default: grouped_pass<4, A_BF16, FP4>(p, r, slots, count, t0); break;
         }
     }
 }
@@ -256,10 +288,18 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const dim3 block(kGroupWaves * kWave);
     const size_t lds = gate_up_grouped_lds(p.B, p.k);
     (void)t;                                      // rows are re-read per pass: cached loads
-    if (a_bf16)
-        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true>), grid, block, lds, s, p);
-    else
-        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false>), grid, block, lds, s, p);
+    const bool fp4 = p.wfmt == kMXFP4;
+    if (fp4) {
+        if (a_bf16)
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p);
+        else
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p);
+    } else {
+        if (a_bf16)
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p);
+        else
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p);
+    }
     return hipGetLastError();
 }
 

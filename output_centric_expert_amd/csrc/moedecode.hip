@@ -55,7 +55,8 @@ moed::Tuning pick(int B, int H, int I)
 // list must fit in 64 KiB of LDS.
 bool use_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
 {
-    if (wfmt != moed::kMXFP8 || moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
+    (void)wfmt;                                   // both weight formats have a grouped kernel
+    if (moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
@@ -195,7 +196,7 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
 int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n, int path,
                          void* stream)
 {
-    if (n < 0 || path < 0 || path > 4)
+    if (n < 0 || path < 0 || path > 5)
         return MOED_ERR_SHAPE;
     if (n == 0)
         return MOED_OK;

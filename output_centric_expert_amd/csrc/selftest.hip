@@ -25,6 +25,17 @@ moe_selftest_decode_kernel(const uint8_t* codes, const uint8_t* scales, float* o
         const int nib = t & 7;
         const uint32_t word = (0x3C3C3C3Cu & ~(0xFu << (4 * nib))) | ((c & 0xFu) << (4 * nib));
         float v;
+        if (path == 5) {                          // E2M1 -> BF16, scale folded (the grouped route)
+            bf16x2 w;
+            switch (nib >> 1) {
+            case 0: w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 0); break;
+            case 1: w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 1); break;
+            case 2: w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 2); break;
+            default: w = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 3); break;
+            }
+            out[t] = (float)((nib & 1) ? w.y : w.x);
+            return;
+        }
         if (path == 3) {                          // E2M1 -> BF16 (the gate/up dot2 route)
             bf16x2 w;
             switch (nib >> 1) {

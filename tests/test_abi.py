@@ -103,7 +103,7 @@ def test_step_entry_points_reject_before_launch(lib):
     assert dn(wq=MIS) == md.MOED_ERR_ALIGN
     assert dn(od=3) == md.MOED_ERR_DTYPE
     assert dn(wf=7) == md.MOED_ERR_DTYPE
-    assert lib.moed_selftest_decode(A, A, A, 4, 5, None) == md.MOED_ERR_SHAPE
+    assert lib.moed_selftest_decode(A, A, A, 4, 6, None) == md.MOED_ERR_SHAPE
     assert lib.moed_selftest_decode(A, A, A, 4, -1, None) == md.MOED_ERR_SHAPE
     assert lib.moed_selftest_decode(None, A, A, 4, 0, None) == md.MOED_ERR_NULL
     assert lib.moed_selftest_decode(None, None, None, 0, 0, None) == md.MOED_OK

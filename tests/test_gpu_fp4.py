@@ -68,7 +68,7 @@ def oracle_tokens(L, tokens, ids=None):
 # decode self-test
 # --------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", [3, 4])
+@pytest.mark.parametrize("path", [3, 4, 5])
 def test_e2m1_decode_all_codes_bit_exact(path):
     scales = [127, 100, 120, 126, 128, 134, 147, 2]   # every product a normal float32
     # 16 codes x 8 nibble positions per scale (t % 8 picks the nibble inside the packed dword)
@@ -85,7 +85,7 @@ def test_e2m1_decode_all_codes_bit_exact(path):
 def test_e2m1_decode_nan_scale():
     codes = torch.tensor([0x2, 0x0, 0xF, 0x9], dtype=torch.uint8).cuda()
     sc = torch.full((4,), 255, dtype=torch.uint8).cuda()
-    for path in (3, 4):
+    for path in (3, 4, 5):
         assert torch.isnan(md.moed_selftest_decode(codes, sc, path)).all()
 
 
@@ -128,12 +128,21 @@ def test_fp4_workload_sampled_parity(name):
     assert torch.equal(run(L), out), "not deterministic"
     ref, _ = oracle_tokens(L, toks)
     check_f32(out[toks], ref, "mxfp4 " + name)
+    # batch = concatenation of single-token calls, bit for bit, on each gate/up kernel
+    # (the per-slot and the grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for b in toks[:2]:                      # batch = concatenation of single-token calls
-        one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
-                            L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32, wformat=WF)
-        torch.cuda.synchronize()
-        assert torch.equal(one[0], out[b])
+    for spec in ("gu_group=0", "gu_group=1"):
+        md.moed_set_tuning(spec)
+        try:
+            full = run(L)
+            for b in toks[:2]:
+                one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
+                                    L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32,
+                                    wformat=WF)
+                torch.cuda.synchronize()
+                assert torch.equal(one[0], full[b]), spec
+        finally:
+            md.moed_set_tuning(None)
 
 
 SHAPES = [
@@ -193,3 +202,30 @@ def test_fp4_random_small_shapes(seed):
     L = layer(sh, seed=seed)
     ref, _ = oracle_tokens(L, list(range(sh.B)))
     check_f32(run(L), ref, f"mxfp4 random {sh.name}")
+
+
+GROUPED = [
+    (40, 3, 2, 96, 160),      # ~27 slots per expert: two slot tiles, ragged rows
+    (24, 6, 4, 2080, 64),     # K steps not a multiple of the 4-step group (65 steps)
+    (3, 40, 5, 256, 96),      # mostly single-slot experts
+    (64, 8, 8, 512, 288),     # every expert touched by many tokens
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_fp4_grouped_gate_up(shape):
+    B = shape[0]
+    L = small(*shape, seed=sum(shape) + 21)
+    ref, a_ref = oracle_tokens(L, list(range(B)))
+    md.moed_set_tuning("gu_group=1")
+    try:
+        out = run(L)
+        check_f32(out, ref, f"mxfp4 grouped {shape}")
+        check_bf16(run(L, torch.bfloat16), out, ref, f"mxfp4 grouped bf16 {shape}")
+        x, ids, _ = md.layer_device_inputs(L)
+        a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF))
+        torch.cuda.synchronize()
+        check_f32(a.reshape(B, -1), a_ref.reshape(B, -1), f"mxfp4 grouped a {shape}")
+        assert torch.equal(run(L), out)
+    finally:
+        md.moed_set_tuning(None)
