@@ -69,6 +69,8 @@ def _load():
         lib.oracle_down_fmt.restype = I
         lib.oracle_moe_decode_fmt.argtypes = [P] * 9 + [I] * 5 + [P, P, I, I]
         lib.oracle_moe_decode_fmt.restype = I
+        lib.oracle_route.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
+        lib.oracle_route.restype = I
         lib.oracle_threads.argtypes = [I]
         lib.oracle_threads.restype = I
         _lib = lib
@@ -172,6 +174,20 @@ def moe_decode(x, ids, w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, return_inter=False
     if rc:
         raise ValueError(f"oracle_moe_decode failed ({rc})")
     return (out, a) if return_inter else out
+
+
+def route(logits, k, n_shared=0, routed_scale=1.0):
+    """Router front-end in float64 from float32 logits [B, E]: (ids int32 [B, k+n_shared],
+    w float32 [B, k+n_shared]); see oracle_route in moe_oracle.c."""
+    logits = _host(logits, np.float32)
+    B, E = logits.shape
+    kt = k + n_shared
+    ids = np.empty((B, kt), np.int32)
+    w = np.empty((B, kt), np.float32)
+    rc = _load().oracle_route(_p(logits), B, E, k, n_shared, float(routed_scale), _p(ids), _p(w))
+    if rc:
+        raise ValueError(f"oracle_route failed ({rc})")
+    return ids, w
 
 
 def moe_decode_layer(L, return_inter=False, nthreads=0):

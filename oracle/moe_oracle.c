@@ -288,6 +288,66 @@ int oracle_moe_decode(const uint16_t *x, const int32_t *ids, const float *w,
                                  nthreads, FMT_MXFP8);
 }
 
+/*
+ * Router front-end: per token b, from float32 logits l[b][0..E):
+ *   ids[b][0..k) = the k experts with the largest logits, in descending
+ *     order, ties to the lower expert id (softmax is strictly increasing, so
+ *     this is the top-k of the routing probabilities p = softmax(l));
+ *   w[b][j] = p[ids[b][j]] / sum_{j'<k} p[ids[b][j']] * routed_scale
+ *     = exp(l_j - m) / sum_{j'} exp(l_j' - m) * routed_scale, m = the largest
+ *     logit (the renormalised top-k probabilities);
+ *   then n_shared shared-expert slots: ids[b][k + s] = E + s, w = 1.
+ * Output rows have k + n_shared entries. A NaN logit is never selected; when
+ * fewer than k logits can be selected the remaining ids are -1 with weight
+ * NaN. Weights computed in float64, stored as float32 (round to nearest).
+ * Returns 0, or -2 on bad sizes (k < 1, k > E, n_shared < 0).
+ */
+int oracle_route(const float *logits, int B, int E, int k, int n_shared, double routed_scale,
+                 int32_t *ids, float *w)
+{
+    if (B < 0 || E < 1 || k < 1 || k > E || n_shared < 0)
+        return -2;
+    const int kt = k + n_shared;
+    char *taken = (char *)malloc((size_t)E);
+    double *sel = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!taken || !sel) {
+        free(taken);
+        free(sel);
+        return -1;
+    }
+    for (int b = 0; b < B; ++b) {
+        const float *l = logits + (size_t)b * E;
+        memset(taken, 0, (size_t)E);
+        int nsel = 0;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e] || isnan(l[e]))
+                    continue;
+                if (best < 0 || l[e] > l[best])      /* strict: ties keep the lower id */
+                    best = e;
+            }
+            ids[(size_t)b * kt + j] = best;
+            if (best >= 0) {
+                taken[best] = 1;
+                sel[nsel++] = (double)l[best];
+            }
+        }
+        double sum = 0.0;
+        for (int j = 0; j < nsel; ++j)
+            sum += exp(sel[j] - sel[0]);
+        for (int j = 0; j < k; ++j)
+            w[(size_t)b * kt + j] = j < nsel ? (float)(exp(sel[j] - sel[0]) / sum * routed_scale) : NAN;
+        for (int s = 0; s < n_shared; ++s) {
+            ids[(size_t)b * kt + k + s] = E + s;
+            w[(size_t)b * kt + k + s] = 1.0f;
+        }
+    }
+    free(taken);
+    free(sel);
+    return 0;
+}
+
 /* Threads an OpenMP region in this library will use for a given request. */
 int oracle_threads(int nthreads)
 {
