@@ -141,6 +141,32 @@ int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
                     int B, int E, int k, int H, int I, void *stream);
 
 /*
+ * Router front-end: the layer's topk_ids / topk_w from float32 router logits
+ * [B][E] (device), on `stream`. Per token: the k experts with the largest
+ * logits, in descending order, ties to the lower expert id (the top-k of the
+ * routing probabilities softmax(logits), which is strictly increasing); their
+ * weights exp(l_j - m) / sum_j' exp(l_j' - m) * routed_scale with m the largest
+ * logit (the renormalised top-k probabilities, computed in float32); then
+ * n_shared shared-expert slots with ids E, E+1, ... and weight 1. Rows of
+ * topk_ids (int32) and topk_w (float32) hold k + n_shared entries.
+ *
+ * Shared experts: store each shared expert as an extra expert after the E
+ * routed ones in the weight tensors (a shared expert of intermediate size
+ * n*I as n such experts) and call moe_decode with E + n_shared experts and
+ * k + n_shared slots: its term is then folded into the same accumulator as
+ * the routed ones, and every output is still stored once (the GC-MoE
+ * summary, onedev.kr/papers/1690, "How to use", fuses shared experts into the
+ * routed-expert pass in the same way).
+ *
+ * A NaN logit is never selected; if fewer than k experts can be selected the
+ * missing slots get id -1 (the layer then writes NaN for that token) and a NaN
+ * weight. Limits (MOED_ERR_SHAPE): 1 <= k <= min(E, 64), E <= 2048,
+ * n_shared >= 0. B = 0 launches nothing.
+ */
+int moe_route(const float *logits, int B, int E, int k, int n_shared, float routed_scale,
+              int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
  * Diagnostic: decode n block-scaled values with the kernels' own in-register
  * decoders, so a test can compare every code bit for bit with the format
  * definitions. out[t] = element(codes[t]) * 2^(scales[t]-127) as float32:

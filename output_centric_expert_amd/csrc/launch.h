@@ -65,6 +65,12 @@ hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStrea
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 bool down_grouped_fits(int E, int k);
+// Router front-end (router.hip): top-k of float32 logits with renormalised
+// softmax weights, plus shared-expert slots.
+constexpr int kRouteMaxE = 2048;
+constexpr int kRouteMaxK = 64;
+hipError_t launch_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* ids,
+                        float* w, hipStream_t s);
 hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
                                   int path, hipStream_t s);
 

@@ -193,6 +193,21 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         out_dtype == MOED_BF16, t, s));
 }
 
+int moe_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* topk_ids,
+              float* topk_w, void* stream)
+{
+    if (B < 0 || E < 1 || E > moed::kRouteMaxE || k < 1 || k > E || k > moed::kRouteMaxK || n_shared < 0)
+        return MOED_ERR_SHAPE;
+    if ((long long)B * (k + n_shared) >= (1LL << 31) || (long long)B * E >= (1LL << 31))
+        return MOED_ERR_SHAPE;
+    if (B == 0)
+        return MOED_OK;
+    if (!logits || !topk_ids || !topk_w)
+        return MOED_ERR_NULL;
+    return hip_status(moed::launch_route(logits, B, E, k, n_shared, routed_scale, topk_ids, topk_w,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moed_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n, int path,
                          void* stream)
 {

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoedecode.so")
 MOED_OK, MOED_ERR_NULL, MOED_ERR_SHAPE, MOED_ERR_DTYPE, MOED_ERR_WORKSPACE, MOED_ERR_ALIGN, MOED_ERR_HIP = range(7)
 MOED_BF16, MOED_F32 = 0, 1
 
-EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down",
+EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down", "moe_route",
            "moed_selftest_decode", "moed_bench_read", "moed_bench_copy", "moed_status_string",
            "moed_last_hip_error", "moed_set_tuning")
 
@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
         lib.moe_decode_gate_up.restype = I
         lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P]
         lib.moe_decode_down.restype = I
+        lib.moe_route.argtypes = [P, I, I, I, I, ctypes.c_float, P, P, P]
+        lib.moe_route.restype = I
         lib.moed_selftest_decode.argtypes = [P, P, P, I, I, P]
         lib.moed_selftest_decode.restype = I
         lib.moed_bench_read.argtypes = [P, Z, P, Z, P]
@@ -172,6 +174,22 @@ def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.b
         _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, _stream(stream))
     _check(st, "moe_decode_down")
     return out
+
+
+def moe_route(logits, k: int, n_shared: int = 0, routed_scale: float = 1.0, ids=None, w=None, stream=None):
+    """Router front-end on the GPU: (topk_ids int32 [B, k+n_shared], topk_w float32 [B, k+n_shared])
+    from float32 logits [B, E]; shared slots get ids E, E+1, ... and weight 1."""
+    B, E = logits.shape
+    kt = k + n_shared
+    if ids is None:
+        ids = torch.empty((B, kt), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((B, kt), dtype=torch.float32, device=logits.device)
+    st = load().moe_route(_ptr(logits, "logits", torch.float32, (B, E)), B, E, k, n_shared, float(routed_scale),
+                          _ptr(ids, "topk_ids", torch.int32, (B, kt)), _ptr(w, "topk_w", torch.float32, (B, kt)),
+                          _stream(stream))
+    _check(st, "moe_route")
+    return ids, w
 
 
 def moed_selftest_decode(codes, scales, path: int, out=None, stream=None):

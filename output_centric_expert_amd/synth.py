@@ -128,13 +128,20 @@ def make_activations(B: int, H: int, seed: int) -> np.ndarray:
     return float64_to_bf16_bits(_rng(seed, 0).standard_normal((B, H)))
 
 
-def make_routing(B: int, E: int, k: int, seed: int, zipf_s: float = 0.0,
-                 contiguous_hot: bool = False):
-    """Router output for B tokens: (ids int32 [B,k], w float32 [B,k], probs float64 [B,E])."""
+def make_router_logits(B: int, E: int, seed: int, zipf_s: float = 0.0,
+                       contiguous_hot: bool = False) -> np.ndarray:
+    """Router logits [B, E] in float64: N(0, 1), plus the log-Zipf prior when zipf_s > 0."""
     logits = _rng(seed, 1).standard_normal((B, E))
     if zipf_s > 0.0:
         rank = np.arange(1, E + 1) if contiguous_hot else _rng(seed, 2).permutation(E) + 1
         logits = logits - zipf_s * np.log(rank.astype(np.float64))[None, :]
+    return logits
+
+
+def make_routing(B: int, E: int, k: int, seed: int, zipf_s: float = 0.0,
+                 contiguous_hot: bool = False):
+    """Router output for B tokens: (ids int32 [B,k], w float32 [B,k], probs float64 [B,E])."""
+    logits = make_router_logits(B, E, seed, zipf_s, contiguous_hot)
     z = logits - logits.max(axis=1, keepdims=True)
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)

@@ -109,6 +109,20 @@ def test_step_entry_points_reject_before_launch(lib):
     assert lib.moed_selftest_decode(None, None, None, 0, 0, None) == md.MOED_OK
 
 
+def test_route_rejects_before_launch(lib):
+    rt = lambda **kw: lib.moe_route(kw.get("lg", A), kw.get("B", 2), kw.get("E", 128), kw.get("k", 8),
+                                    kw.get("ns", 0), 1.0, kw.get("ids", A), kw.get("w", A), None)
+    assert rt(lg=None) == md.MOED_ERR_NULL
+    assert rt(ids=None) == md.MOED_ERR_NULL
+    assert rt(k=0) == md.MOED_ERR_SHAPE
+    assert rt(k=129) == md.MOED_ERR_SHAPE            # k > E
+    assert rt(E=4096, k=8) == md.MOED_ERR_SHAPE      # E above the router's 2048
+    assert rt(E=256, k=65) == md.MOED_ERR_SHAPE      # k above 64
+    assert rt(ns=-1) == md.MOED_ERR_SHAPE
+    assert rt(B=-1) == md.MOED_ERR_SHAPE
+    assert rt(B=0, lg=None, ids=None, w=None) == md.MOED_OK
+
+
 def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"gu_wpb=2,dn_wpb=1,gu_dot=0,nt=1") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_wpb=9") == md.MOED_ERR_SHAPE
