@@ -4,15 +4,15 @@
 // in the GC-MoE summary's fused epilogue, onedev.kr/papers/1690, "How to
 // use").
 //
-// One wavefront per token. Lane l keeps the logits of experts l, l+64, ...
-// as 64-bit keys: an order-preserving map of the float32 value in the high
-// word and (2^32 - 1 - id) in the low word, so a larger key is a larger logit
-// and, among equal logits, a lower expert id. +0 and -0 map to the same key;
-// a NaN logit maps to key 0 and is never selected. Round j takes the wave-wide
-// maximum key over the experts not yet taken (a xor butterfly of 64-bit
-// shuffles); its owner lane marks it taken and lane j keeps it. Softmax is
-// strictly increasing, so these are the top-k routing probabilities in
-// descending order. The routed weights are exp(l_j - m) / sum_j' exp(l_j' - m)
+// One wavefront per token. Experts are ordered by 64-bit keys: an
+// order-preserving map of the float32 logit in the high word and
+// (2^32 - 1 - id) in the low word, so a larger key is a larger logit and,
+// among equal logits, a lower expert id. +0 and -0 map to the same key; a NaN
+// logit maps to key 0 and is never selected. Softmax is strictly increasing,
+// so the k largest keys are the top-k routing probabilities, in descending
+// order. Round j takes the wave-wide maximum key over the experts not yet
+// taken (DPP / ds_swizzle exchanges, no LDS memory); its owner lane marks it
+// taken and lane j keeps it. The routed weights are exp(l_j - m) / sum_j' exp(l_j' - m)
 // (m = the largest selected logit) times routed_scale; shared slot s gets id
 // E + s and weight 1. If fewer than k experts can be selected (NaN logits),
 // the missing slots get id -1 (an id the layer turns into NaN outputs) and a
@@ -45,24 +45,38 @@ __device__ __forceinline__ int key_id(uint64_t key)
     return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
 }
 
+// One exchange step of the 64-bit maximum: both halves moved by the same DPP
+// pattern, then the larger key kept.
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+
+// Maximum of a 64-bit key over the 64 lanes (every lane gets it), with the
+// exchange pattern of wave_sum: DPP quad_perm xor 1 and xor 2, row_half_mirror
+// and row_mirror inside each 16-lane row, a ds_swizzle (lane ^ 16) between row
+// pairs, and the two 32-lane halves through readlane. All lanes must be active.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off /= 2) {
-        const uint32_t lo = __shfl_xor((uint32_t)(v & 0xFFFFFFFFull), off);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
+    v = max_dpp<0xB1>(v);                         // quad_perm [1,0,3,2]
+    v = max_dpp<0x4E>(v);                         // quad_perm [2,3,0,1]
+    v = max_dpp<0x141>(v);                        // row_half_mirror
+    v = max_dpp<0x140>(v);                        // row_mirror
+    {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)v, (0x10 << 10) | 0x1F);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), (0x10 << 10) | 0x1F);
         const uint64_t o = ((uint64_t)hi << 32) | lo;
         v = o > v ? o : v;
     }
-    return v;
-}
-
-__device__ __forceinline__ float wave_add(float v)
-{
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off /= 2)
-        v += __shfl_xor(v, off);
-    return v;
+    const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+    const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
+    return a > c ? a : c;
 }
 
 }  // namespace
@@ -107,7 +121,7 @@ moe_route_kernel(const float* logits, int B, int E, int k, int n_shared, float r
     const float m = key_value(first);
     const bool ok = lane < k && mine != 0ull;
     const float ex = ok ? expf(key_value(mine) - m) : 0.0f;
-    const float sum = wave_add(ex);
+    const float sum = wave_sum(ex);
     if (lane < k) {
         ids[(size_t)b * kt + lane] = ok ? key_id(mine) : -1;
         w[(size_t)b * kt + lane] = ok ? ex / sum * routed_scale : __builtin_nanf("");
@@ -123,9 +137,9 @@ hipError_t launch_route(const float* logits, int B, int E, int k, int n_shared, 
 {
     if (B == 0)
         return hipSuccess;
+    const int per_lane = (E + kWave - 1) / kWave;
     constexpr int wpb = 4;
     const dim3 grid((unsigned)((B + wpb - 1) / wpb)), block(wpb * kWave);
-    const int per_lane = (E + kWave - 1) / kWave;
 #define MOED_RT(N) \
     hipLaunchKernelGGL((moe_route_kernel<N>), grid, block, 0, s, logits, B, E, k, n_shared, routed_scale, ids, w)
     if (per_lane <= 1) MOED_RT(1);
