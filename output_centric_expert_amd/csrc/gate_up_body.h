@@ -19,25 +19,58 @@
 
 namespace moed {
 
-// Lane partials of g = Wg[e][i]·x[b] and u = Wu[e][i]·x[b] for wave `wave`;
-// bad_id is set when ids[b][j] is outside [0, E) (the caller then stores NaN).
-// FP4: MXFP4 weights -- a 16-byte chunk is 32 codes (one MX block, one scale
-// byte) against 32 activations; MXFP8: 16 codes (half a block) against 16.
-// MXFP4 always takes the BF16 dot2 route.
-template <int U, bool DOT_BF16, bool NT, bool FP4 = false>
-__device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int lane, float& g_out, float& u_out,
-                                             bool& bad_out)
+// Partial dot (scale 1) of one 16-byte chunk of a gate or up row with its x
+// pieces: 16 MXFP8 codes against 16 activations (x pieces 0, 1) or 32 MXFP4
+// codes against 32 (pieces 0..3; dword d of the chunk = codes 8d..8d+7).
+template <bool FP4, bool DOT_BF16, int NX>
+__device__ __forceinline__ float gu_chunk_dot(const u32x4& w, const u32x4 (&x)[NX])
+{
+    float p = 0.0f;
+    if constexpr (FP4) {
+        p = dot8_fp4_bf16(w.x, x[0], p);
+        p = dot8_fp4_bf16(w.y, x[1], p);
+        p = dot8_fp4_bf16(w.z, x[2], p);
+        p = dot8_fp4_bf16(w.w, x[3], p);
+    } else if constexpr (DOT_BF16) {
+        p = dot4_bf16(w.x, x[0].x, x[0].y, p);
+        p = dot4_bf16(w.y, x[0].z, x[0].w, p);
+        p = dot4_bf16(w.z, x[NX - 1].x, x[NX - 1].y, p);
+        p = dot4_bf16(w.w, x[NX - 1].z, x[NX - 1].w, p);
+    } else {
+        p = dot4_f32(w.x, x[0].x, x[0].y, p);
+        p = dot4_f32(w.y, x[0].z, x[0].w, p);
+        p = dot4_f32(w.z, x[NX - 1].x, x[NX - 1].y, p);
+        p = dot4_f32(w.w, x[NX - 1].z, x[NX - 1].w, p);
+    }
+    return p;
+}
+
+// Lane partials of g = Wg[e][i]·x[b] and u = Wu[e][i]·x[b] for the NPW
+// neurons i = i0 .. i0+NPW-1 of slot bj, where n0 = bj*I + i0 (I is a multiple
+// of NPW, so they share the slot and its x[b], which is loaded once for all
+// of them); bad_id is set when ids[b][j] is outside [0, E) (the caller then
+// stores NaN). FP4: MXFP4 weights -- a 16-byte chunk is 32 codes (one MX
+// block, one scale byte) against 32 activations; MXFP8: 16 codes (half a
+// block) against 16. MXFP4 always takes the BF16 dot2 route.
+template <int U, bool DOT_BF16, bool NT, bool FP4 = false, int NPW = 1>
+__device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int n0, int lane, float (&g_out)[NPW],
+                                             float (&u_out)[NPW], bool& bad_out)
 {
     constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
-    const int i = wave % p.I;
-    const int bj = wave / p.I;
+    const int i0 = n0 % p.I;
+    const int bj = n0 / p.I;
     const int b = bj / p.k;
     const int H = p.H;
     const int nch = FP4 ? H / 32 : H / 16;        // 16-byte chunks per row
     const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
     const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
 
-    float g = 0.0f, u = 0.0f;
+    float g[NPW], u[NPW];
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+        g[n] = 0.0f;
+        u[n] = 0.0f;
+    }
     bool bad_id = false;
     for (int base = 0; base < nch; base += kWave * U) {
         // x first: its address does not depend on the routed id, so these loads
@@ -56,66 +89,43 @@ __device__ __forceinline__ void gate_up_wave(const GateUpArgs& p, int wave, int 
         const int e_raw = p.ids[bj];
         bad_id = (unsigned)e_raw >= (unsigned)p.E;   // invalid routing: expert 0's rows are read, result NaN
         const int e = bad_id ? 0 : e_raw;
-        const size_t row = (size_t)e * (size_t)p.I + (size_t)i;
-        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
-        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
-        const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
-        const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
-        u32x4 wg[U], wu[U];
-        uint32_t sg[U], su[U];
+        u32x4 wg[NPW][U], wu[NPW][U];
+        uint32_t sg[NPW][U], su[NPW][U];
         float live[U];
 #pragma unroll
-        for (int m = 0; m < U; ++m) {
-            const int c = base + lane + kWave * m;
-            const int cc = c < nch ? c : nch - 1;
-            wg[m] = ld<NT>(gq + cc);
-            wu[m] = ld<NT>(uq + cc);
-            sg[m] = gs[FP4 ? cc : cc >> 1];
-            su[m] = us[FP4 ? cc : cc >> 1];
-            live[m] = c < nch ? 1.0f : 0.0f;
+        for (int n = 0; n < NPW; ++n) {
+            const size_t row = (size_t)e * (size_t)p.I + (size_t)(i0 + n);
+            const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
+            const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
+            const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+            const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+#pragma unroll
+            for (int m = 0; m < U; ++m) {
+                const int c = base + lane + kWave * m;
+                const int cc = c < nch ? c : nch - 1;
+                wg[n][m] = ld<NT>(gq + cc);
+                wu[n][m] = ld<NT>(uq + cc);
+                sg[n][m] = gs[FP4 ? cc : cc >> 1];
+                su[n][m] = us[FP4 ? cc : cc >> 1];
+                live[m] = c < nch ? 1.0f : 0.0f;
+            }
         }
 #pragma unroll
-        for (int m = 0; m < U; ++m) {
-            float pg = 0.0f, pu = 0.0f;
-            if constexpr (FP4) {
-                // dword d of the chunk = codes 8d..8d+7, against x piece d
-                pg = dot8_fp4_bf16(wg[m].x, xv[m][0], pg);
-                pu = dot8_fp4_bf16(wu[m].x, xv[m][0], pu);
-                pg = dot8_fp4_bf16(wg[m].y, xv[m][1], pg);
-                pu = dot8_fp4_bf16(wu[m].y, xv[m][1], pu);
-                pg = dot8_fp4_bf16(wg[m].z, xv[m][2], pg);
-                pu = dot8_fp4_bf16(wu[m].z, xv[m][2], pu);
-                pg = dot8_fp4_bf16(wg[m].w, xv[m][3], pg);
-                pu = dot8_fp4_bf16(wu[m].w, xv[m][3], pu);
-            } else if constexpr (DOT_BF16) {
-                const u32x4& xa = xv[m][0];
-                const u32x4& xb = xv[m][NX - 1];
-                pg = dot4_bf16(wg[m].x, xa.x, xa.y, pg);
-                pu = dot4_bf16(wu[m].x, xa.x, xa.y, pu);
-                pg = dot4_bf16(wg[m].y, xa.z, xa.w, pg);
-                pu = dot4_bf16(wu[m].y, xa.z, xa.w, pu);
-                pg = dot4_bf16(wg[m].z, xb.x, xb.y, pg);
-                pu = dot4_bf16(wu[m].z, xb.x, xb.y, pu);
-                pg = dot4_bf16(wg[m].w, xb.z, xb.w, pg);
-                pu = dot4_bf16(wu[m].w, xb.z, xb.w, pu);
-            } else {
-                const u32x4& xa = xv[m][0];
-                const u32x4& xb = xv[m][NX - 1];
-                pg = dot4_f32(wg[m].x, xa.x, xa.y, pg);
-                pu = dot4_f32(wu[m].x, xa.x, xa.y, pu);
-                pg = dot4_f32(wg[m].y, xa.z, xa.w, pg);
-                pu = dot4_f32(wu[m].y, xa.z, xa.w, pu);
-                pg = dot4_f32(wg[m].z, xb.x, xb.y, pg);
-                pu = dot4_f32(wu[m].z, xb.x, xb.y, pu);
-                pg = dot4_f32(wg[m].w, xb.z, xb.w, pg);
-                pu = dot4_f32(wu[m].w, xb.z, xb.w, pu);
+        for (int n = 0; n < NPW; ++n) {
+#pragma unroll
+            for (int m = 0; m < U; ++m) {
+                const float pg = gu_chunk_dot<FP4, DOT_BF16, NX>(wg[n][m], xv[m]);
+                const float pu = gu_chunk_dot<FP4, DOT_BF16, NX>(wu[n][m], xv[m]);
+                g[n] = __builtin_fmaf(pg, ue8m0_to_f32(sg[n][m]) * live[m], g[n]);
+                u[n] = __builtin_fmaf(pu, ue8m0_to_f32(su[n][m]) * live[m], u[n]);
             }
-            g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g);
-            u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u);
         }
     }
-    g_out = g;
-    u_out = u;
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+        g_out[n] = g[n];
+        u_out[n] = u[n];
+    }
     bad_out = bad_id;
 }
 

@@ -10,6 +10,7 @@ namespace moed {
 // can override them for sweeps.
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
+    int gu_npw = 1;     // gate/up (per-slot kernel): neurons per wavefront (1 or 2; 2 shares x)
     int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
     int dn_group = 0;   // down: 0 = one wavefront per output; 1 = MFMA tiles of 16 outputs x

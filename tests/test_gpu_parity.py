@@ -233,7 +233,8 @@ def test_ragged_shapes(shape):
                                   "gu_group=1", "gu_group=0", "dn_stage=0", "gu_group=1,nt=0",
                                   "dn_group=1", "gu_group=1,dn_group=1", "dn_group=0",
                                   "dn_order=1", "dn_order=2", "dn_order=1,dn_stage=0,dn_wpb=3",
-                                  "dn_order=2,dn_wpb=5,nt=0", "dn_lanegroups=0", "dn_lanegroups=1,dn_umax=1"])
+                                  "dn_order=2,dn_wpb=5,nt=0", "dn_lanegroups=0", "dn_lanegroups=1,dn_umax=1",
+                                  "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
