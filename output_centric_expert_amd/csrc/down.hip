@@ -188,6 +188,119 @@ moe_down_staged_kernel(DownArgs p)
     }
 }
 
+// LDS-staged variant with R consecutive outputs per wavefront (used once
+// tokens share experts, B*k >= E, where the copy of a[b] and the LDS reads of
+// it, not the weight stream, bound the kernel): each piece of a read from LDS
+// serves R rows, and a workgroup of 8 wavefronts covers 8R outputs per copy of
+// a[b]. The per-output arithmetic is that of the one-row kernel, bit for bit.
+// Weights are loaded through the caches (rows are shared between tokens).
+template <int CPL, int JB, bool A_BF16, bool OUT_BF16, bool FP4, int R>
+__global__ void __launch_bounds__(512)
+moe_down_rows_kernel(DownArgs p)
+{
+    extern __shared__ u32x4 a_lds[];
+    constexpr int NA = A_BF16 ? 2 : 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int nblk_h = (p.H + wpb * R - 1) / (wpb * R);
+    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int b = p.order == 0 ? blk / nblk_h : blk % p.B;
+    const int h0 = ((p.order == 0 ? blk % nblk_h : blk / p.B) * wpb + (int)(threadIdx.x / kWave)) * R;
+    const bool active = h0 < p.H;
+    const int k = p.k;
+    const int cpr16 = p.I / 16;
+    const int cpr = FP4 ? p.I / 32 : cpr16;
+    const int nunits = k * NA * cpr16;
+    const int* ids = p.ids + (size_t)b * k;
+    const float* wts = p.w + (size_t)b * k;
+    const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
+
+    u32x4 cp[kCopyRegs];
+#pragma unroll
+    for (int q = 0; q < kCopyRegs; ++q) {
+        const int u = (int)threadIdx.x + q * (int)blockDim.x;
+        cp[q] = u < nunits ? asrc[u] : u32x4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 wq[R][JB][CPL];
+    uint32_t ws[R][JB][CPL];
+    float wt[JB];
+    float mask[R][JB][CPL];
+    down_group_load_rows<CPL, JB, FP4, R>(p, ids, wts, 0, 0, active ? h0 : 0, lane, cpr, wq, ws, wt, mask);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kCopyRegs; ++q) {
+        const int u = (int)threadIdx.x + q * (int)blockDim.x;
+        if (u < nunits)
+            a_lds[u] = cp[q];
+    }
+    for (int u = (int)threadIdx.x + kCopyRegs * (int)blockDim.x; u < nunits; u += blockDim.x)
+        a_lds[u] = asrc[u];
+    __syncthreads();
+    if (!active)
+        return;                                   // after the only barrier
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+    down_group_dot_rows<CPL, JB, A_BF16, FP4, R>(a_lds, k, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, acc);
+    for (int j0 = 0; j0 < k; j0 += JB) {
+        for (int o0 = (j0 == 0 ? kWave * CPL : 0); o0 < cpr; o0 += kWave * CPL) {
+            down_group_load_rows<CPL, JB, FP4, R>(p, ids, wts, j0, o0, h0, lane, cpr, wq, ws, wt, mask);
+            down_group_dot_rows<CPL, JB, A_BF16, FP4, R>(a_lds, k, j0, o0, lane, cpr, cpr16, wq, ws, wt, mask, acc);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = wave_sum(acc[r]);
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (h0 + r < p.H) {
+                if constexpr (OUT_BF16)
+                    static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h0 + r] = f32_to_bf16_rne(acc[r]);
+                else
+                    static_cast<float*>(p.out)[(size_t)b * p.H + h0 + r] = acc[r];
+            }
+        }
+    }
+}
+
+template <int CPL, int JB, int R>
+static hipError_t dispatch_rows(bool fp4, bool a_bf16, bool out_bf16, const DownArgs& p, dim3 grid, dim3 block,
+                                size_t lds, hipStream_t s)
+{
+#define MOED_DR(F, A, O) \
+    if (fp4 == F && a_bf16 == A && out_bf16 == O) \
+        hipLaunchKernelGGL((moe_down_rows_kernel<CPL, JB, A, O, F, R>), grid, block, lds, s, p);
+    MOED_DR(false, false, false) MOED_DR(false, false, true) MOED_DR(false, true, false) MOED_DR(false, true, true)
+    MOED_DR(true, false, false) MOED_DR(true, false, true) MOED_DR(true, true, false) MOED_DR(true, true, true)
+#undef MOED_DR
+    return hipGetLastError();
+}
+
+// R outputs per wavefront, rows covered in one pass (CPL * 64 >= chunks per
+// row): CPL as for one row, JB cut so that R * CPL * JB <= 4 where it can be
+// (in one pass the FMA order per lane does not depend on JB).
+template <int R>
+static hipError_t launch_rows(int cpl, bool fp4, bool a_bf16, bool out_bf16, const DownArgs& p, int wpb,
+                              size_t lds, hipStream_t s)
+{
+    const dim3 grid((unsigned)((long)p.B * ((p.H + R * wpb - 1) / (R * wpb)))), block(wpb * kWave);
+    int jb = 8 / cpl;
+    while (jb > 1 && (R * cpl * jb > 4 || jb / 2 >= p.k))
+        jb /= 2;
+    switch (cpl * 16 + jb) {
+    case 1 * 16 + 2: return dispatch_rows<1, 2, R>(fp4, a_bf16, out_bf16, p, grid, block, lds, s);
+    case 1 * 16 + 1: return dispatch_rows<1, 1, R>(fp4, a_bf16, out_bf16, p, grid, block, lds, s);
+    case 2 * 16 + 1: return dispatch_rows<2, 1, R>(fp4, a_bf16, out_bf16, p, grid, block, lds, s);
+    case 4 * 16 + 1: return dispatch_rows<4, 1, R>(fp4, a_bf16, out_bf16, p, grid, block, lds, s);
+    case 8 * 16 + 1: return dispatch_rows<8, 1, R>(fp4, a_bf16, out_bf16, p, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int CPL, int JB, bool FP4, int G = 1>
 static hipError_t dispatch_v(bool staged, bool a_bf16, bool out_bf16, bool nt, const DownArgs& p, dim3 grid,
                              dim3 block, size_t lds, hipStream_t s)
@@ -278,6 +391,16 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     int jb = 8 / cpl;
     while (jb > 1 && (cpl * jb > cap || jb / 2 >= p.k))
         jb /= 2;
+    // several outputs per wavefront once tokens share experts (the same CPL, so
+    // the same arithmetic per output as one output per wavefront)
+    // (measured: 4 once B*k >= E, 2 for smaller batches, 1 for a single token,
+    // where halving the workgroup count would leave CUs idle)
+    const int rows = t.dn_rows != 0 ? t.dn_rows : ((long)p.B * p.k >= (long)p.E ? 4 : (p.B >= 2 ? 2 : 1));
+    if (staged && rows > 1 && cpl * kWave >= cpr) {
+        if (rows == 4)
+            return launch_rows<4>(cpl, fp4, a_bf16, out_bf16, q, wpb, lds, s);
+        return launch_rows<2>(cpl, fp4, a_bf16, out_bf16, q, wpb, lds, s);
+    }
     switch (cpl * 16 + jb) {
     case 1 * 16 + 8: return dispatch_f<1, 8>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);
     case 1 * 16 + 4: return dispatch_f<1, 4>(fp4, staged, a_bf16, out_bf16, nt, q, grid, block, lds, s);

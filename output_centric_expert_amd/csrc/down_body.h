@@ -157,4 +157,75 @@ __device__ __forceinline__ float down_group_dot(const u32x4* a_lds, int k, int j
     return acc;
 }
 
+// Variants for a wavefront that owns R consecutive outputs h0 .. h0+R-1 of one
+// token (rows Wd[e][h0+r] of the same experts): each piece of a read from LDS
+// serves all R rows. Per row the loads, the order of the FMAs and their
+// operands are those of down_group_load / down_group_dot, so every output is
+// the same float as with one row per wavefront.
+template <int CPL, int JB, bool FP4, int R>
+__device__ __forceinline__ void down_group_load_rows(const DownArgs& p, const int* ids, const float* wts, int j0,
+                                                     int o0, int h0, int lane, int cpr,
+                                                     u32x4 (&wq)[R][JB][CPL], uint32_t (&ws)[R][JB][CPL],
+                                                     float (&wt)[JB], float (&mask)[R][JB][CPL])
+{
+    const int k = p.k;
+    const int I = p.I;
+    const size_t row_bytes = FP4 ? (size_t)(I / 2) : (size_t)I;
+    int eid[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int jc = j0 + jj < k ? j0 + jj : k - 1;
+        eid[jj] = ids[jc];
+        wt[jj] = wts[jc];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool row_live = h0 + r < p.H;
+        const int hc = row_live ? h0 + r : 0;
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const bool live = row_live && (j0 + jj) < k;
+            const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
+            const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
+            const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes);
+            const uint8_t* srow = p.wd_s + row * (size_t)(I / 32);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int o = o0 + lane + kWave * cc;
+                const int oc = o < cpr ? o : cpr - 1;
+                wq[r][jj][cc] = *(wrow + oc);
+                ws[r][jj][cc] = srow[FP4 ? oc : oc >> 1];
+                mask[r][jj][cc] = (live && o < cpr) ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+            }
+        }
+    }
+}
+
+template <int CPL, int JB, bool A_BF16, bool FP4, int R>
+__device__ __forceinline__ void down_group_dot_rows(const u32x4* a_lds, int k, int j0, int o0, int lane, int cpr,
+                                                    int cpr16, const u32x4 (&wq)[R][JB][CPL],
+                                                    const uint32_t (&ws)[R][JB][CPL], const float (&wt)[JB],
+                                                    const float (&mask)[R][JB][CPL], float (&acc)[R])
+{
+    constexpr int NP = APieces<FP4, A_BF16>::N;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj < k ? j0 + jj : k - 1;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int o = o0 + lane + kWave * cc;
+            const int oc = o < cpr ? o : cpr - 1;
+            u32x4 av[NP];
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+                av[q] = a_lds[a_unit<FP4, A_BF16>(j, oc, q, cpr16)];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float part = chunk_dot<FP4, A_BF16>(wq[r][jj][cc], av);
+                acc[r] = __builtin_fmaf(wt[jj] * mask[r][jj][cc], part * ue8m0_to_f32(ws[r][jj][cc]), acc[r]);
+            }
+        }
+    }
+}
+
 }  // namespace moed

@@ -24,6 +24,8 @@ struct Tuning {
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
                         // MFMA tiles (rows decoded once per 16 slots); 2 = choose by batch size
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
+    int dn_rows = 0;    // down (staged): outputs per wavefront, 1, 2 or 4; 0 = by batch (4 once
+                        // B*k >= E, 2 for B >= 2, 1 for B = 1)
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
     int dn_order = 1;   // down workgroup order: 0 = token-major; 1 = hidden-major, each XCD
                         // taking a contiguous range; 2 = hidden-major, plain round robin

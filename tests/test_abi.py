@@ -138,6 +138,9 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"dn_lanegroups=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_npw=2") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_npw=3") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"dn_rows=2") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_rows=3") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"dn_rows=4") == md.MOED_OK
     assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(None) == md.MOED_OK

@@ -234,7 +234,8 @@ def test_ragged_shapes(shape):
                                   "dn_group=1", "gu_group=1,dn_group=1", "dn_group=0",
                                   "dn_order=1", "dn_order=2", "dn_order=1,dn_stage=0,dn_wpb=3",
                                   "dn_order=2,dn_wpb=5,nt=0", "dn_lanegroups=0", "dn_lanegroups=1,dn_umax=1",
-                                  "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0"])
+                                  "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0",
+                                  "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
