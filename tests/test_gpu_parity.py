@@ -376,3 +376,48 @@ def test_grouped_duplicates_and_invalid_ids():
     good = [b for b in range(20) if b not in (3, 7)]
     ref, _ = oracle_tokens(L, good, ids=ids)
     check_f32(out[good], ref, "grouped duplicates")
+
+
+# --------------------------------------------------------------------------------------
+# HIP graph capture: replays equal the eager result, with eager work between replays
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,wformat", [("wide_B1_E128_k8_H2048_I768", "mxfp8"),
+                                          ("batch_B8_E128_k8_H2048_I768", "mxfp4"),
+                                          ("batch_B32_E128_k8_H4096_I1536", "mxfp8")])
+def test_graph_replays_match_eager(name, wformat):
+    L = synth.make_layer(name, device="cuda", wformat=wformat)
+    x, ids, w = md.layer_device_inputs(L)
+    sh = L.shape
+    logits = torch.from_numpy(synth.make_router_logits(sh.B, sh.E, L.seed, sh.zipf_s).astype(np.float32)).cuda()
+    ws = torch.empty(md.moed_workspace_bytes(sh.B, sh.k, sh.I), dtype=torch.uint8, device="cuda")
+    rid = torch.empty_like(ids)
+    rw = torch.empty_like(w)
+    outs = [torch.empty((sh.B, sh.H), dtype=torch.float32, device="cuda") for _ in range(2)]
+
+    def step(o_given, o_routed):
+        md.moe_decode(x, ids, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out=o_given, workspace=ws,
+                      wformat=wformat)
+        md.moe_route(logits, sh.k, ids=rid, w=rw)
+        md.moe_decode(x, rid, rw, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out=o_routed, workspace=ws,
+                      wformat=wformat)
+
+    eager = [torch.empty_like(o) for o in outs]
+    step(*eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(*outs)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        rid.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep}"
+        other = md.moe_decode(x, ids, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                              out_dtype=torch.bfloat16, wformat=wformat)      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(other.float()).all()
