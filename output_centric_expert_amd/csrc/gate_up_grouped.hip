@@ -104,24 +104,67 @@ struct GroupedRow {
     int col;                // lane % 16
 };
 
-// One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1).
-// K is walked in groups of 4 MX blocks (128 codes); inside a group, lane
-// (row, kb) supplies block kb's 32 contiguous codes over the 4 MFMA steps
-// (8 per step) and x uses the same k order, so the products summed are the
-// row-times-x products, only in another order. One 32-byte (MXFP8) or
-// 16-byte (MXFP4) load per row and one scale byte per row per group.
+// x pieces of one 128-value K group for up to kTiles tiles of 16 slots, shared
+// by the workgroup's wavefronts through LDS (two buffers): unit
+// (tt*16 + col)*16 + (c ^ col) holds x[slot(tt, col)][128g + 8c .. 8c+7] for
+// c = 4*kb + q, the piece MFMA step q of lane (col, kb) reads. The XOR by col
+// keeps the cooperative writes (16 threads per slot, one 256-byte run of x
+// each) and the MFMA reads (16 lanes, one per slot) free of LDS bank
+// conflicts.
+constexpr int kXUnitsPerTile = 16 * 16;          // 16-byte units per tile and group
+
+struct GroupW {
+    u32x4 g0, g1, u0, u1;                        // this lane's codes of the group (g1/u1: MXFP8 only)
+    float gsc, usc;                              // block scales
+};
+
+template <bool FP4>
+__device__ __forceinline__ GroupW load_group_w(const GroupedRow& r, int g)
+{
+    GroupW w;
+    const int kbase = g * 128 + 32 * r.kb;       // this lane's MX block (value index)
+    const int bbase = FP4 ? kbase / 2 : kbase;   // its first code byte
+    w.g0 = *reinterpret_cast<const u32x4*>(r.gq + bbase);
+    w.u0 = *reinterpret_cast<const u32x4*>(r.uq + bbase);
+    if constexpr (FP4) {
+        w.g1 = w.g0;
+        w.u1 = w.u0;
+    } else {
+        w.g1 = *reinterpret_cast<const u32x4*>(r.gq + bbase + 16);
+        w.u1 = *reinterpret_cast<const u32x4*>(r.uq + bbase + 16);
+    }
+    w.gsc = ue8m0_to_f32(r.gs[4 * g + r.kb]);
+    w.usc = ue8m0_to_f32(r.us[4 * g + r.kb]);
+    return w;
+}
+
+// One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1),
+// with the slots' x shared through LDS and the next group's x and weight rows
+// loaded while the current group's MFMAs run. Every thread of the workgroup
+// calls it (it has barriers); `store` is false for wavefronts whose neurons
+// lie past I (they compute on a clamped row and write nothing). K is walked
+// in groups of 4 MX blocks (128 codes): inside a group, lane (row, kb)
+// supplies block kb's 32 contiguous codes over the 4 MFMA steps and x uses the
+// same k order, so the products summed are the row-times-x products, only in
+// another order. Leftover blocks (H/32 not a multiple of 4) take x from
+// global memory in plain k order.
 template <int NTL, bool A_BF16, bool FP4>
 __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedRow& r, const int* slots,
-                                             int count, int t0)
+                                             int count, int t0, u32x4* xs, bool store)
 {
     const int H = p.H;
-    int bj[NTL];
+    const int tid = threadIdx.x;
+    const int lcol = tid / 16;                    // cooperative x load: slot column ...
+    const int lc = tid % 16;                      // ... and 16-byte piece of the group
+    const uint16_t* xl[NTL];                      // x row of this thread's load column, per tile
+    int bj[NTL];                                  // slot of this lane's MFMA column, per tile
     const uint16_t* xr[NTL];
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
+        const int sl = (t0 + tt) * 16 + lcol;
+        xl[tt] = p.x + (size_t)(slots[sl < count ? sl : count - 1] / p.k) * (size_t)H;
         const int si = (t0 + tt) * 16 + r.col;
-        const int sidx = si < count ? si : count - 1;   // extra columns repeat a slot
-        bj[tt] = slots[sidx];
+        bj[tt] = slots[si < count ? si : count - 1];  // extra columns repeat a slot
         xr[tt] = p.x + (size_t)(bj[tt] / p.k) * (size_t)H;
     }
     f32x4 dg[NTL], du[NTL];
@@ -130,45 +173,62 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
         dg[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         du[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    int st = 0;
-    for (; st + 4 <= r.nsteps; st += 4) {
-        const int kbase = st * 32 + 32 * r.kb;    // this lane's MX block (value index)
-        const int bbase = FP4 ? kbase / 2 : kbase;   // its first code byte
-        const u32x4 g0 = *reinterpret_cast<const u32x4*>(r.gq + bbase);
-        const u32x4 u0 = *reinterpret_cast<const u32x4*>(r.uq + bbase);
-        const u32x4 g1 = FP4 ? g0 : *reinterpret_cast<const u32x4*>(r.gq + bbase + 16);
-        const u32x4 u1 = FP4 ? u0 : *reinterpret_cast<const u32x4*>(r.uq + bbase + 16);
-        const float sgf = ue8m0_to_f32(r.gs[st + r.kb]);
-        const float suf = ue8m0_to_f32(r.us[st + r.kb]);
-        u32x4 xv[NTL][4];
+    const int ngroups = r.nsteps / 4;
+    constexpr int kBuf = NTL * kXUnitsPerTile;
+    u32x4 xreg[NTL];
+    GroupW wc{};
+    if (ngroups > 0) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt)
+            xreg[tt] = *reinterpret_cast<const u32x4*>(xl[tt] + 8 * lc);
+        wc = load_group_w<FP4>(r, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xv[tt][q] = *reinterpret_cast<const u32x4*>(xr[tt] + kbase + 8 * q);
+        for (int tt = 0; tt < NTL; ++tt)
+            xs[(tt * 16 + lcol) * 16 + (lc ^ lcol)] = xreg[tt];
+    }
+    __syncthreads();
+    for (int g = 0; g < ngroups; ++g) {
+        const u32x4* xb = xs + (g & 1) * kBuf;
+        const bool more = g + 1 < ngroups;
+        GroupW wn = wc;
+        if (more) {                               // next group's loads, ahead of this group's MFMAs
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt)
+                xreg[tt] = *reinterpret_cast<const u32x4*>(xl[tt] + (g + 1) * 128 + 8 * lc);
+            wn = load_group_w<FP4>(r, g + 1);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             bf16x8 ag, au;
             if constexpr (FP4) {                  // dword q = codes 8q .. 8q+7
-                ag = decode8_scaled_fp4(g0[q], sgf);
-                au = decode8_scaled_fp4(u0[q], suf);
+                ag = decode8_scaled_fp4(wc.g0[q], wc.gsc);
+                au = decode8_scaled_fp4(wc.u0[q], wc.usc);
             } else {
-                const u32x4 gsrc = q < 2 ? g0 : g1;
-                const u32x4 usrc = q < 2 ? u0 : u1;
+                const u32x4 gsrc = q < 2 ? wc.g0 : wc.g1;
+                const u32x4 usrc = q < 2 ? wc.u0 : wc.u1;
                 const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
                 const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
-                ag = decode8_scaled(cgq, sgf);
-                au = decode8_scaled(cuq, suf);
+                ag = decode8_scaled(cgq, wc.gsc);
+                au = decode8_scaled(cuq, wc.usc);
             }
+            const int c = 4 * r.kb + q;
 #pragma unroll
             for (int tt = 0; tt < NTL; ++tt) {
-                const bf16x8 bx = __builtin_bit_cast(bf16x8, xv[tt][q]);
+                const bf16x8 bx = __builtin_bit_cast(bf16x8, xb[(tt * 16 + r.col) * 16 + (c ^ r.col)]);
                 dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
                 du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
             }
         }
+        if (more) {
+            u32x4* xn = xs + ((g + 1) & 1) * kBuf;
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt)
+                xn[(tt * 16 + lcol) * 16 + (lc ^ lcol)] = xreg[tt];
+        }
+        __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
+        wc = wn;
     }
-    for (; st < r.nsteps; ++st) {                 // leftover blocks: plain k order
+    for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
         const int k0 = st * 32 + 8 * r.kb;
         bf16x8 ag, au;
         if constexpr (FP4) {
@@ -189,6 +249,8 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
             du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
         }
     }
+    if (!store)
+        return;
     // lane holds D rows 4*kb .. +3 (neurons) of column col of each tile
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
@@ -244,13 +306,14 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
     const int count = compact_slots(nslots, slots, wave_cnt, [&](int t) { return ids[t] == e; });
     if (count == 0)
         return;                                   // whole workgroup: no barrier follows
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list
     const int n0 = n_block + 16 * w;              // this wavefront's 16 neurons
-    if (n0 >= I)
-        return;
+    const bool store = n0 < I;                    // wavefronts past I still take part in the barriers
 
     const int kb = lane / 16;                     // which quarter of a k group
     const int col = lane % 16;                    // A row (neuron) / B column (slot)
-    const size_t row = (size_t)e * (size_t)I + (size_t)(n0 + col);
+    const int nr = store ? n0 + col : I - 1;      // a valid row for the wavefronts past I
+    const size_t row = (size_t)e * (size_t)I + (size_t)(nr < I ? nr : I - 1);
     const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
     const uint8_t* gq = p.wg_q + row * row_bytes;
     const uint8_t* uq = p.wu_q + row * row_bytes;
@@ -266,17 +329,19 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
         const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
         const GroupedRow r{gq, uq, gs, us, nsteps, n0, kb, col};
         switch (nt) {
-        case 1: grouped_pass<1, A_BF16, FP4>(p, r, slots, count, t0); break;
-        case 2: grouped_pass<2, A_BF16, FP4>(p, r, slots, count, t0); break;
-        case 3: grouped_pass<3, A_BF16, FP4>(p, r, slots, count, t0); break;
-        default: grouped_pass<4, A_BF16, FP4>(p, r, slots, count, t0); break;
+        case 1: grouped_pass<1, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+        case 2: grouped_pass<2, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+        case 3: grouped_pass<3, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+        default: grouped_pass<4, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
         }
     }
 }
 
 size_t gate_up_grouped_lds(int B, int k)
 {
-    return (size_t)B * (size_t)k * sizeof(int);
+    // slot list (rounded up to 16 bytes), then two buffers of x tiles
+    const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
+    return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4);
 }
 
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s)
