@@ -180,7 +180,8 @@ def measure_layer(md, L, R, K, W):
     torch.cuda.synchronize()
     out = torch.empty((sh.B, sh.H), dtype=torch.bfloat16, device="cuda")
     a = torch.empty((sh.B, sh.k, sh.I), dtype=torch.float32, device="cuda")
-    ws = a.view(torch.uint8).view(-1)
+    ws = torch.empty(md.moed_workspace_bytes(sh.B, sh.k, sh.H, sh.I), dtype=torch.uint8, device="cuda")
+    y = torch.empty(sh.B * sh.k * sh.H, dtype=torch.float32, device="cuda")   # down's per-slot partials
 
     wf = L.wformat
 
@@ -191,7 +192,7 @@ def measure_layer(md, L, R, K, W):
         md.moe_decode_gate_up(x, ids, *copies[r % R][:4], a=a, wformat=wf)
 
     def down(r):
-        md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out, wformat=wf)
+        md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out, wformat=wf, partials=y)
 
     for r in range(W):                       # untimed warm-up steps
         layer(r)
@@ -250,7 +251,35 @@ def measure_layer(md, L, R, K, W):
         layer(r)
     e1.record(); torch.cuda.synchronize()
     res["ms_eager"] = e0.elapsed_time(e1) / n_eager
+
+    # router front-end: route alone, and route + layer (ids and weights made on the GPU
+    # from float32 logits every step), graph-timed like the layer
+    logits = torch.from_numpy(synth_router_logits(L)).cuda()
+    rid = torch.empty_like(ids)
+    rw = torch.empty_like(w)
+
+    def route(r):
+        md.moe_route(logits, sh.k, ids=rid, w=rw)
+
+    def routed_layer(r):
+        md.moe_route(logits, sh.k, ids=rid, w=rw)
+        md.moe_decode(x, rid, rw, *copies[r % R], out=out, workspace=ws, wformat=wf)
+
+    g_rt = capture(route, K)
+    g_rl = capture(routed_layer, K)
+    g_rt.replay(); g_rl.replay()
+    torch.cuda.synchronize()
+    res["ms_route"] = time_graph(g_rt, K, reps=3)
+    res["ms_routed_layer"] = time_graph(g_rl, K, reps=3)
+    del g_rt, g_rl
     return res
+
+
+def synth_router_logits(L):
+    """float32 router logits [B, E] of the layer's workload (same recipe as its routing)."""
+    from output_centric_expert_amd import synth
+    sh = L.shape
+    return synth.make_router_logits(sh.B, sh.E, L.seed, sh.zipf_s).astype("float32")
 
 
 WEIGHT_DESC = {"mxfp8": "mxfp8 (e4m3 + ue8m0 per 32)", "mxfp4": "mxfp4 (e2m1 two per byte + ue8m0 per 32)"}
@@ -273,6 +302,8 @@ def timing_fields(L, t):
             "gbs_down": round(dn_bytes / (t["ms_down"] * 1e-3) / 1e9, 1),
             "us_per_layer_median3": round(t["ms_layer_median3"] * 1e3, 3),
             "us_per_layer_eager": round(t["ms_eager"] * 1e3, 3),
+            "us_route": round(t["ms_route"] * 1e3, 3),
+            "us_per_layer_with_router": round(t["ms_routed_layer"] * 1e3, 3),
             "wall_s_timed": round(t["wall_s"], 4)}
 
 
@@ -314,11 +345,12 @@ def counters_run(md, x, ids, w, copies, out, a, workload, wformat="mxfp8"):
         md.moed_bench_copy(src, dst)
         torch.cuda.synchronize()
     R = len(copies)
+    y = torch.empty(a.shape[0] * a.shape[1] * out.shape[1], dtype=torch.float32, device="cuda")
     for r in range(COUNTER_LAUNCHES):
         md.moe_decode_gate_up(x, ids, *copies[(r + 1) % R][:4], a=a, wformat=wformat)
         torch.cuda.synchronize()
     for r in range(COUNTER_LAUNCHES):
-        md.moe_decode_down(a, ids, w, *copies[(r + 1) % R][4:], out=out, wformat=wformat)
+        md.moe_decode_down(a, ids, w, *copies[(r + 1) % R][4:], out=out, wformat=wformat, partials=y)
         torch.cuda.synchronize()
     print(json.dumps({"counters_plan": {"workload": workload, "copy_bytes": COPY_BYTES,
                                         "launches_each": COUNTER_LAUNCHES,

@@ -81,11 +81,14 @@ typedef enum {
 /* Size limits (checked): B*k*I and B*H below 2^31, k*I/16 below 2^22. */
 
 /*
- * Bytes of workspace moe_decode() needs for the intermediate a[B][k][I]:
- * B*k*I*4 for inter_dtype MOED_F32 (the accuracy-gated path), *2 for
- * MOED_BF16. Returns 0 for invalid arguments.
+ * Bytes of workspace moe_decode() needs: the intermediate a[B][k][I]
+ * (B*k*I*4 bytes for inter_dtype MOED_F32, the accuracy-gated path; *2 for
+ * MOED_BF16), rounded up to 256 bytes, then B*k*H float32 per-slot partials
+ * y[b][j][h] = topk_w[b][j] * (Wd^[e]·a[b][j])_h, which the expert-major down
+ * step writes when tokens share experts (batches with B*k >= 2E) and adds up
+ * per token in slot order. Returns 0 for B = 0 and for invalid arguments.
  */
-size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype);
+size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype);
 
 /*
  * The whole layer (steps gate/up then down on `stream`).
@@ -100,8 +103,14 @@ size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype);
  *   wd_s      [E][H][I/32] uint8 UE8M0 scales
  *   weight_format  MOED_MXFP8 or MOED_MXFP4 (all three projections)
  *   out       [B][H]  out_dtype
- *   workspace >= moed_workspace_bytes(B, k, I, inter_dtype) bytes, 16-aligned
+ *   workspace >= moed_workspace_bytes(B, k, H, I, inter_dtype) bytes, 16-aligned
  * B = 0 is valid and launches nothing.
+ *
+ * Once tokens share experts (B*k >= 2E) the down step runs expert-major: the
+ * decoded rows of each routed expert serve every slot routed to it, each slot's
+ * weighted partial goes to the workspace, and a second launch adds each
+ * token's k partials in slot order and stores the output once. Smaller batches
+ * use the one-wavefront-per-output down of moe_decode_down().
  */
 int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
                const uint8_t *wg_q, const uint8_t *wg_s,
@@ -130,15 +139,24 @@ int moe_decode_gate_up(const void *x, const int32_t *topk_ids,
                        int B, int E, int k, int H, int I, void *stream);
 
 /*
- * Down step alone: out[b][h] = sum_j topk_w[b][j] * (Wd^[e_j]·a[b][j])_h,
- * one FP32 accumulator per output, one store. `a` is in the layout
- * moe_decode_gate_up() writes. (Warp-decode post, "How the two kernels work",
- * third and fourth paragraphs.)
+ * Down step alone: out[b][h] = sum_j topk_w[b][j] * (Wd^[e_j]·a[b][j])_h.
+ * `a` is in the layout moe_decode_gate_up() writes. (Warp-decode post, "How
+ * the two kernels work", third and fourth paragraphs.)
+ *   partials  NULL: one wavefront per output, one FP32 accumulator over the k
+ *             routed experts, one store.
+ *             Else float32 scratch of partials_bytes >= B*k*H*4 bytes,
+ *             16-aligned, owned by the caller: once tokens share experts
+ *             (B*k >= 2E) the expert-major form runs (the form moe_decode()
+ *             uses), writing topk_w[b][j] * (Wd^[e_j]·a[b][j]) there and then
+ *             adding each token's k partials in slot order; smaller batches
+ *             still take the per-output form and leave it untouched.
+ *             Too small: MOED_ERR_WORKSPACE; misaligned: MOED_ERR_ALIGN.
  */
 int moe_decode_down(const void *a, int inter_dtype, const int32_t *topk_ids,
                     const float *topk_w, const uint8_t *wd_q, const uint8_t *wd_s,
                     int weight_format, void *out, int out_dtype,
-                    int B, int E, int k, int H, int I, void *stream);
+                    int B, int E, int k, int H, int I,
+                    float *partials, size_t partials_bytes, void *stream);
 
 /*
  * Router front-end: the layer's topk_ids / topk_w from float32 router logits

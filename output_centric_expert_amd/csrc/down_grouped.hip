@@ -1,277 +1,338 @@
-// Down for large decode batches: still output-centric -- every out[b][h] is
-// accumulated in one FP32 accumulator over all of token b's routed experts
-// and stored once -- but a workgroup owns a tile of 16 outputs h x 16 tokens
-// b, so each routed down row is decoded once per 16 tokens instead of once
-// per token.
+// Down for large decode batches (tokens sharing experts): expert-major, so
+// each routed down row is read and decoded once per workgroup pass (up to 64
+// slots) instead of once per (token, slot).
 //
-// The workgroup lists (in increasing expert order) the experts its tokens are
-// routed to and loops over them. For expert e the contribution to the tile is
-// the MFMA product
-//   A = Wd[e][h0 .. h0+15][:], decoded exactly from MXFP8 to BF16 with the
+// Step 1, moe_down_expert_kernel: a workgroup owns (expert e, 64 output rows
+// hb .. hb+63), four wavefronts of 16 rows each. It compacts the list of slots
+// s = (b, j) routed to e (in slot order, from topk_ids) and computes, for
+// tiles of 16 of those slots, the MFMA product
+//   A = Wd[e][h][:], decoded exactly from MXFP8 / MXFP4 to BF16 with the
 //       block scale folded into the conversion,
-//   B[:, c] = sum over token c's slots j routed to e of w[c][j] * a[c][j][:]
-//       (zero for tokens not routed to e), an FP32 value carried as two BF16
-//       numbers hi + lo (hi = RNE(v), lo = RNE(v - hi); about 16 significant
-//       bits), so that both products are exact in FP32,
-//   D += A * B_hi + A * B_lo   (v_mfma_f32_16x16x32_bf16, FP32 accumulation).
-// The routing weight is folded into B before the product. The four
-// wavefronts of the workgroup split I between them; their FP32 partial tiles
-// are added in a fixed order through LDS, and lane (h, b) stores out[b][h].
-// Tokens with an expert id outside [0, E) get NaN outputs.
-#include "launch.h"
-#include "mx_device.h"
+//   B[:, s] = a[s][:], a float32 value carried as two BF16 numbers hi + lo
+//       (hi = RNE(v), lo = RNE(v - hi); about 16 significant bits), so that
+//       both products are exact in FP32 (a BF16 intermediate needs only hi),
+//   D += A * B_hi + A * B_lo   (v_mfma_f32_16x16x32_bf16, FP32 accumulation),
+// and writes the slot's weighted partial y[s][h] = w[s] * D[h][s]. The slots'
+// a is split once per workgroup and shared by its wavefronts through
+// double-buffered LDS tiles (the unit layout of the grouped gate/up kernel);
+// K is walked in groups of 4 MX blocks, the next group's loads issued before
+// the current group's MFMAs.
+//
+// Step 2, moe_down_combine_kernel: out[b][h] = sum over j of y[(b, j)][h], the
+// token's k slots added in slot order and stored once; a token with an
+// expert id outside [0, E) gets NaN.
+//
+// The per-slot partials are the price of reading each routed row once: they
+// take B*k*H*4 bytes of workspace and a second, small HBM-bound launch.
+#include "grouped_common.h"
 
 namespace moed {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
+namespace {
 
-constexpr int kDnWaves = 4;                      // wavefronts per workgroup, splitting I
-constexpr int kDnMaxExperts = 2048;              // expert bitmap capacity (E <= this)
-constexpr int kDnMaxK = 64;                      // routed slots per token (k <= this)
+constexpr int kDnUnits = 16 * 16;                // 16-byte units per tile and K group (one of hi / lo)
 
-__device__ __forceinline__ bf16x8 decode8_scaled_dn(u32x2 codes, float scale)
+// 8 float32 values -> 8 bf16 hi and 8 bf16 lo (hi + lo = v to about 2^-17 relative).
+__device__ __forceinline__ void split8(const f32x4& v0, const f32x4& v1, u32x4& hi, u32x4& lo)
 {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
-    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
-    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
-    bf16x8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-// v (8 float32) -> hi, lo (8 bf16 each) with hi + lo = v to ~2^-17 relative.
-__device__ __forceinline__ void split_hi_lo(const f32x8& v, bf16x8& hi, bf16x8& lo)
-{
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t h[8], l[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const uint16_t hb = f32_to_bf16_rne(v[t]);
-        const float hf = __uint_as_float((uint32_t)hb << 16);
-        const uint16_t lb = f32_to_bf16_rne(v[t] - hf);
-        hi[t] = __builtin_bit_cast(__bf16, hb);
-        lo[t] = __builtin_bit_cast(__bf16, lb);
+        h[t] = f32_to_bf16_rne(v[t]);
+        l[t] = f32_to_bf16_rne(v[t] - __uint_as_float(h[t] << 16));
     }
+    hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
 }
 
+// a[s][i0 .. i0+7] (i0 a multiple of 8) from the chunk-interleaved
+// intermediate, as hi / lo bf16 (a bf16 intermediate: hi only).
 template <bool A_BF16>
-__device__ __forceinline__ f32x8 load_a8(const void* a, int bj, int i0, int I)
+__device__ __forceinline__ void load_a8_split(const void* a, int s, int i0, int I, u32x4& hi, u32x4& lo)
 {
-    // 8 consecutive values a[bj][i0 .. i0+7] (i0 % 8 == 0) from the
-    // chunk-interleaved intermediate
-    f32x8 v;
-    const size_t cpr = (size_t)(I / 16);
-    const size_t o = (size_t)(i0 >> 4);
+    const size_t cpr16 = (size_t)(I / 16);
+    const size_t o = (size_t)(i0 / 16);
     if constexpr (A_BF16) {
-        const size_t idx = (((size_t)bj * 2 + (size_t)((i0 >> 3) & 1)) * cpr + o) * 8;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a) + idx);
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+        const u32x4* a16 = static_cast<const u32x4*>(a);
+        hi = a16[((size_t)s * 2 + (size_t)((i0 / 8) % 2)) * cpr16 + o];
+        lo = u32x4{0u, 0u, 0u, 0u};
     } else {
-        const size_t q0 = (size_t)((i0 >> 2) & 3);
-        const float* af = static_cast<const float*>(a);
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(af + (((size_t)bj * 4 + q0) * cpr + o) * 4);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(af + (((size_t)bj * 4 + q0 + 1) * cpr + o) * 4);
-        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        const f32x4* a32 = static_cast<const f32x4*>(a);
+        const size_t t = (size_t)((i0 / 4) % 4);  // 0 or 2
+        const f32x4 v0 = a32[((size_t)s * 4 + t) * cpr16 + o];
+        const f32x4 v1 = a32[((size_t)s * 4 + t + 1) * cpr16 + o];
+        split8(v0, v1, hi, lo);
     }
-    return v;
 }
 
-template <bool A_BF16, bool OUT_BF16>
-__global__ void __launch_bounds__(kDnWaves * kWave)
-moe_down_grouped_kernel(DownArgs p)
-{
-    __shared__ unsigned bitmap[kDnMaxExperts / 32];
-    __shared__ int experts[kDnMaxExperts];
-    __shared__ int wave_cnt[kDnWaves];
-    __shared__ f32x4 partial[kDnWaves - 1][kWave];
-    __shared__ int tile_ids[16 * kDnMaxK];
-    __shared__ float tile_w[16 * kDnMaxK];
+struct DnRow {
+    const uint8_t* q;       // this lane's down row (codes)
+    const uint8_t* s;       // its scales
+    int nsteps;             // MX blocks per row (I/32) = MFMA K steps
+    int kb;                 // lane / 16
+    int col;                // lane % 16
+};
 
-    const int H = p.H, I = p.I, k = p.k, E = p.E, B = p.B;
-    const int nht = H / 16;                       // H is a multiple of 32
-    const int h0 = (blockIdx.x % nht) * 16;
-    const int b0 = (blockIdx.x / nht) * 16;
+struct DnGroupW {
+    u32x4 c0, c1;           // codes of the lane's MX block in the group (c1: MXFP8 only)
+    float sc;
+};
+
+template <bool FP4>
+__device__ __forceinline__ DnGroupW load_dn_w(const DnRow& r, int g)
+{
+    DnGroupW w;
+    const int kbase = g * 128 + 32 * r.kb;
+    const int bbase = FP4 ? kbase / 2 : kbase;
+    w.c0 = *reinterpret_cast<const u32x4*>(r.q + bbase);
+    w.c1 = FP4 ? w.c0 : *reinterpret_cast<const u32x4*>(r.q + bbase + 16);
+    w.sc = ue8m0_to_f32(r.s[4 * g + r.kb]);
+    return w;
+}
+
+// MFMA step q of the group: codes 8q .. 8q+7 of the lane's block.
+template <bool FP4>
+__device__ __forceinline__ bf16x8 dn_decode(const DnGroupW& w, int q)
+{
+    if constexpr (FP4)
+        return decode8_scaled_fp4(w.c0[q], w.sc);
+    const u32x4 src = q < 2 ? w.c0 : w.c1;
+    return decode8_scaled((q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y}, w.sc);
+}
+
+}  // namespace
+
+// One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1).
+// Every thread of the workgroup calls it (it has barriers); `store` is false
+// for wavefronts whose rows lie past H (they compute on a clamped row and
+// write nothing). Inside a K group lane (row, kb) supplies block kb's 32
+// codes over the 4 MFMA steps and the B operand uses the same k order;
+// leftover blocks (I/32 not a multiple of 4) take a from global memory in
+// plain k order.
+template <int NTL, bool A_BF16, bool FP4>
+__device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow& r, const int* slots, int count,
+                                                 int t0, u32x4* xs, bool store, int h0, float* y)
+{
+    const int I = p.I;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int w = tid / kWave;
-    const int kb = lane / 16;
-    const int col = lane % 16;
-
-    // 1) the tile's expert set as a bitmap, then an ordered list
-    const int nwords = (E + 31) / 32;
-    for (int q = tid; q < nwords; q += blockDim.x)
-        bitmap[q] = 0u;
-    __syncthreads();
-    const int ntok = B - b0 < 16 ? B - b0 : 16;
-    for (int q = tid; q < ntok * k; q += blockDim.x) {
-        const int e = p.ids[(size_t)b0 * k + q];
-        tile_ids[q] = e;
-        tile_w[q] = p.w[(size_t)b0 * k + q];
-        if ((unsigned)e < (unsigned)E)
-            atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    const int lcol = tid / 16;                    // cooperative load: slot column ...
+    const int lc = tid % 16;                      // ... and 8-value piece of the group
+    constexpr int kHalf = NTL * kDnUnits;         // lo tiles follow the hi tiles
+    constexpr int kBuf = (A_BF16 ? 1 : 2) * kHalf;
+    int ls[NTL];                                  // slot of this thread's load column, per tile
+    int bj[NTL];                                  // slot of this lane's MFMA column, per tile
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        const int sl = (t0 + tt) * 16 + lcol;
+        ls[tt] = slots[sl < count ? sl : count - 1];
+        const int si = (t0 + tt) * 16 + r.col;
+        bj[tt] = slots[si < count ? si : count - 1];  // extra columns repeat a slot
+    }
+    f32x4 d[NTL];
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt)
+        d[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ngroups = r.nsteps / 4;
+    u32x4 hreg[NTL], lreg[NTL];
+    DnGroupW wc{};
+    if (ngroups > 0) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            load_a8_split<A_BF16>(p.a, ls[tt], 8 * lc, I, hreg[tt], lreg[tt]);
+        wc = load_dn_w<FP4>(r, 0);
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
+            xs[u] = hreg[tt];
+            if constexpr (!A_BF16)
+                xs[kHalf + u] = lreg[tt];
+        }
     }
     __syncthreads();
-    int nexp = 0;
-    for (int base = 0; base < nwords; base += kDnWaves * kWave) {
-        const int q = base + tid;
-        const unsigned word = q < nwords ? bitmap[q] : 0u;
-        const int cnt = __popc(word);
-        // exclusive prefix of cnt over the workgroup (wave scan + wave totals)
-        int incl = cnt;
+    for (int g = 0; g < ngroups; ++g) {
+        const u32x4* xb = xs + (g & 1) * kBuf;
+        const bool more = g + 1 < ngroups;
+        DnGroupW wn = wc;
+        if (more) {                               // next group's loads, ahead of this group's MFMAs
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(incl, d);
-            if (lane >= d)
-                incl += y;
+            for (int tt = 0; tt < NTL; ++tt)
+                load_a8_split<A_BF16>(p.a, ls[tt], (g + 1) * 128 + 8 * lc, I, hreg[tt], lreg[tt]);
+            wn = load_dn_w<FP4>(r, g + 1);
         }
-        if (lane == kWave - 1)
-            wave_cnt[w] = incl;
-        __syncthreads();
-        int off = nexp;
-        for (int r = 0; r < w; ++r)
-            off += wave_cnt[r];
-        int pos = off + incl - cnt;
-        unsigned m = word;
-        while (m) {
-            const int bit = __ffs(m) - 1;
-            experts[pos++] = q * 32 + bit;
-            m &= m - 1u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bf16x8 aw = dn_decode<FP4>(wc, q);
+            const int c = 4 * r.kb + q;
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt) {
+                const int u = (tt * 16 + r.col) * 16 + (c ^ r.col);
+                d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, xb[u]), d[tt], 0, 0,
+                                                                0);
+                if constexpr (!A_BF16)
+                    d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        aw, __builtin_bit_cast(bf16x8, xb[kHalf + u]), d[tt], 0, 0, 0);
+            }
         }
-        int sum = 0;
-        for (int r = 0; r < kDnWaves; ++r)
-            sum += wave_cnt[r];
-        __syncthreads();
-        nexp += sum;
+        if (more) {
+            u32x4* xn = xs + ((g + 1) & 1) * kBuf;
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt) {
+                const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
+                xn[u] = hreg[tt];
+                if constexpr (!A_BF16)
+                    xn[kHalf + u] = lreg[tt];
+            }
+        }
+        __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
+        wc = wn;
     }
-
-    // 2) this lane's token (column col) and whether it has an invalid id
-    const int ccol = col < ntok ? col : 0;
-    const int bcol = b0 + ccol;
-    bool bad = false;
-    for (int j = 0; j < k; ++j)
-        bad |= (unsigned)tile_ids[ccol * k + j] >= (unsigned)E;
-
-    // 3) the wavefront's share of I: 128-code groups w, w+4, ...; leftover
-    //    32-code blocks (I/32 % 4) go to wavefront 0 in plain k order
-    const size_t row_base = (size_t)(h0 + col);
-    const int ngroups = I / 128;
-    const int nleft = (I / 32) % 4;
-    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int x = 0; x < nexp; ++x) {
-        const int e = experts[x];
-        // this column's coefficient and slot for expert e
-        float coef = 0.0f;
-        int jsel = -1;
-        for (int j = 0; j < k; ++j) {
-            if (tile_ids[ccol * k + j] == e) {
-                coef += tile_w[ccol * k + j];
-                jsel = jsel < 0 ? j : jsel;
-            }
-        }
-        const bool has = jsel >= 0 && col < ntok;
-        const int bj = bcol * k + (jsel < 0 ? 0 : jsel);
-        const size_t row = (size_t)e * (size_t)H + row_base;
-        const uint8_t* wq = p.wd_q + row * (size_t)I;
-        const uint8_t* ws = p.wd_s + row * (size_t)(I / 32);
-        for (int g = w; g < ngroups; g += kDnWaves) {
-            const int kbase = g * 128 + 32 * kb;  // this lane's MX block (permuted k order)
-            const u32x4 c0 = *reinterpret_cast<const u32x4*>(wq + kbase);
-            const u32x4 c1 = *reinterpret_cast<const u32x4*>(wq + kbase + 16);
-            const float sc = ue8m0_to_f32(ws[g * 4 + kb]);
-            f32x8 av[4];
+    for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
+        const int k0 = st * 32 + 8 * r.kb;
+        bf16x8 aw;
+        if constexpr (FP4)
+            aw = decode8_scaled_fp4(*reinterpret_cast<const uint32_t*>(r.q + k0 / 2), ue8m0_to_f32(r.s[st]));
+        else
+            aw = decode8_scaled(*reinterpret_cast<const u32x2*>(r.q + k0), ue8m0_to_f32(r.s[st]));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (has) {
-                    av[q] = load_a8<A_BF16>(p.a, bj, kbase + 8 * q, I);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        av[q][t] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 src = q < 2 ? c0 : c1;
-                const u32x2 cq = (q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y};
-                const bf16x8 aw = decode8_scaled_dn(cq, sc);
-                f32x8 v;
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    v[t] = coef * av[q][t];
-                bf16x8 bhi, blo;
-                split_hi_lo(v, bhi, blo);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bhi, d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, blo, d, 0, 0, 0);
-            }
-        }
-        if (w == 0) {
-            for (int st = ngroups * 4; st < ngroups * 4 + nleft; ++st) {
-                const int k0 = st * 32 + 8 * kb;
-                const u32x2 cq = *reinterpret_cast<const u32x2*>(wq + k0);
-                const bf16x8 aw = decode8_scaled_dn(cq, ue8m0_to_f32(ws[st]));
-                f32x8 v;
-                if (has) {
-                    const f32x8 av = load_a8<A_BF16>(p.a, bj, k0, I);
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        v[t] = coef * av[t];
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        v[t] = 0.0f;
-                }
-                bf16x8 bhi, blo;
-                split_hi_lo(v, bhi, blo);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bhi, d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, blo, d, 0, 0, 0);
-            }
+        for (int tt = 0; tt < NTL; ++tt) {
+            u32x4 hi, lo;
+            load_a8_split<A_BF16>(p.a, bj[tt], k0, I, hi, lo);
+            d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, hi), d[tt], 0, 0, 0);
+            if constexpr (!A_BF16)
+                d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, lo), d[tt], 0, 0, 0);
         }
     }
-
-    // 4) add the four partial tiles in a fixed order; one store per output
-    if (w > 0)
-        partial[w - 1][lane] = d;
-    __syncthreads();
-    if (w != 0)
+    if (!store)
         return;
+    // lane holds D rows 4*kb .. +3 (outputs h, H a multiple of 16) of column col (slot)
 #pragma unroll
-    for (int r = 0; r < kDnWaves - 1; ++r)
-        d += partial[r][lane];
-    if (col < ntok) {
-        const int b = b0 + col;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = h0 + 4 * kb + r;
-            const float v = bad ? __builtin_nanf("") : d[r];
-            if constexpr (OUT_BF16)
-                static_cast<uint16_t*>(p.out)[(size_t)b * H + h] = f32_to_bf16_rne(v);
-            else
-                static_cast<float*>(p.out)[(size_t)b * H + h] = v;
+    for (int tt = 0; tt < NTL; ++tt) {
+        if ((t0 + tt) * 16 + r.col < count) {
+            const int s = bj[tt];
+            const float wgt = p.w[s];
+            *reinterpret_cast<f32x4*>(y + (size_t)s * (size_t)p.H + (size_t)(h0 + 4 * r.kb)) = wgt * d[tt];
         }
     }
 }
 
-hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s)
+template <bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(kGroupWaves * kWave)
+moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
 {
-    (void)t;
-    if ((long)p.B * p.H == 0)
-        return hipSuccess;
-    const dim3 grid((unsigned)((long)(p.H / 16) * ((p.B + 15) / 16)));
-    const dim3 block(kDnWaves * kWave);
-    if (a_bf16) {
-        if (out_bf16) hipLaunchKernelGGL((moe_down_grouped_kernel<true, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((moe_down_grouped_kernel<true, false>), grid, block, 0, s, p);
-    } else {
-        if (out_bf16) hipLaunchKernelGGL((moe_down_grouped_kernel<false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((moe_down_grouped_kernel<false, false>), grid, block, 0, s, p);
+    extern __shared__ int slots[];                // B*k entries, then the a tiles
+    __shared__ int wave_cnt[kGroupWaves];
+    const int nblk = (p.H + kGroupNeurons - 1) / kGroupNeurons;
+    const int e = blockIdx.x / nblk;
+    const int hb = (blockIdx.x % nblk) * kGroupNeurons;
+    const int nslots = p.B * p.k;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int* ids = p.ids;
+    const int count = compact_slots(nslots, slots, wave_cnt, [&](int t) { return ids[t] == e; });
+    if (count == 0)
+        return;                                   // whole workgroup: no barrier follows
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));
+    const int h0 = hb + 16 * w;                   // this wavefront's 16 rows
+    const bool store = h0 < p.H;                  // wavefronts past H still take part in the barriers
+    const int col = lane % 16;
+    const int hr = h0 + col < p.H ? h0 + col : p.H - 1;
+    const size_t row = (size_t)e * (size_t)p.H + (size_t)hr;
+    const size_t row_bytes = FP4 ? (size_t)(p.I / 2) : (size_t)p.I;
+    const DnRow r{p.wd_q + row * row_bytes, p.wd_s + row * (size_t)(p.I / 32), p.I / 32, lane / 16, col};
+    const int ntiles = (count + 15) / 16;
+    for (int t0 = 0; t0 < ntiles; t0 += max_tiles) {
+        const int nt = ntiles - t0 < max_tiles ? ntiles - t0 : max_tiles;
+        switch (nt) {
+        case 1: expert_down_pass<1, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        case 2: expert_down_pass<2, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        case 3: expert_down_pass<3, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        default: expert_down_pass<4, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        }
     }
+}
+
+// Four consecutive outputs per thread (H is a multiple of 4).
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256)
+moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k, int H, void* out)
+{
+    const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int hq = H / 4;
+    if (q >= (long)B * hq)
+        return;
+    const int b = (int)(q / hq);
+    const int h = (int)(q % hq) * 4;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const size_t s = (size_t)b * (size_t)k + (size_t)j;
+        if ((unsigned)ids[s] >= (unsigned)E)
+            bad = true;
+        else
+            acc += *reinterpret_cast<const f32x4*>(y + s * (size_t)H + (size_t)h);
+    }
+    if (bad)
+        acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    const size_t o = (size_t)b * (size_t)H + (size_t)h;
+    if constexpr (OUT_BF16) {
+        const uint32_t lo = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = u32x2{lo, hi};
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc;
+    }
+}
+
+size_t down_grouped_lds(int B, int k, bool a_bf16, int max_tiles)
+{
+    // slot list (rounded up to 16 bytes), then two buffers of hi (and lo) tiles
+    const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
+    return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4);
+}
+
+int down_grouped_tiles(int B, int k, bool a_bf16, int requested)
+{
+    if (requested > 0)
+        return down_grouped_lds(B, k, a_bf16, requested) <= 65536 ? requested : 0;
+    for (int mt = kTiles; mt >= 1; --mt)
+        if (down_grouped_lds(B, k, a_bf16, mt) <= 65536)
+            return mt;
+    return 0;
+}
+
+hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
+                               hipStream_t s)
+{
+    if ((long)p.B * p.k == 0)
+        return hipSuccess;
+    if (max_tiles < 1 || max_tiles > kTiles || (p.H % 16) != 0)
+        return hipErrorInvalidValue;
+    const int nblk = (p.H + kGroupNeurons - 1) / kGroupNeurons;
+    const dim3 grid((unsigned)((long)p.E * nblk)), block(kGroupWaves * kWave);
+    const size_t lds = down_grouped_lds(p.B, p.k, a_bf16, max_tiles);
+    const bool fp4 = p.wfmt == kMXFP4;
+    if (fp4) {
+        if (a_bf16)
+            hipLaunchKernelGGL((moe_down_expert_kernel<true, true>), grid, block, lds, s, p, y, max_tiles);
+        else
+            hipLaunchKernelGGL((moe_down_expert_kernel<false, true>), grid, block, lds, s, p, y, max_tiles);
+    } else {
+        if (a_bf16)
+            hipLaunchKernelGGL((moe_down_expert_kernel<true, false>), grid, block, lds, s, p, y, max_tiles);
+        else
+            hipLaunchKernelGGL((moe_down_expert_kernel<false, false>), grid, block, lds, s, p, y, max_tiles);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const long n = (long)p.B * (p.H / 4);
+    const dim3 g2((unsigned)((n + 255) / 256)), b2(256);
+    if (out_bf16)
+        hipLaunchKernelGGL((moe_down_combine_kernel<true>), g2, b2, 0, s, y, p.ids, p.B, p.E, p.k, p.H, p.out);
+    else
+        hipLaunchKernelGGL((moe_down_combine_kernel<false>), g2, b2, 0, s, y, p.ids, p.B, p.E, p.k, p.H, p.out);
     return hipGetLastError();
 }
-
-bool down_grouped_fits(int E, int k) { return E <= kDnMaxExperts && k <= kDnMaxK; }
 
 }  // namespace moed

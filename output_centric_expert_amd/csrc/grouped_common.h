@@ -1,0 +1,79 @@
+// Helpers shared by the expert-grouped kernels (large decode batches): exact
+// MXFP8 / MXFP4 -> BF16 decode with the block scale folded in (the MFMA A
+// operand), the deterministic slot-list compaction, and the launch shape
+// (workgroups of 4 wavefronts, 16 rows each; up to 4 tiles of 16 slots per
+// pass over a row).
+#pragma once
+
+#include "launch.h"
+#include "mx_device.h"
+
+namespace moed {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroupWaves = 4;                  // wavefronts per workgroup, 16 neurons each
+constexpr int kGroupNeurons = 16 * kGroupWaves;
+constexpr int kTiles = 4;                       // 16-slot tiles per pass over a row
+
+// 8 E4M3 codes (two dwords) times 2^(s-127) -> 8 BF16 values, exactly.
+__device__ __forceinline__ bf16x8 decode8_scaled(u32x2 codes, float scale)
+{
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// 8 E2M1 codes (one dword, element 2t in the low nibble of byte t) times
+// 2^(s-127) -> 8 BF16 values, exactly while the scaled values stay normal,
+// finite BF16 numbers (scale codes 2..252).
+__device__ __forceinline__ bf16x8 decode8_scaled_fp4(uint32_t codes, float scale)
+{
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Deterministic compaction: slots[0..count) = the indices t < n (in increasing
+// order) with pred(t). All threads of the workgroup must call it.
+template <typename Pred>
+__device__ __forceinline__ int compact_slots(int n, int* slots, int* wave_cnt, Pred pred)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    int total = 0;
+    for (int base = 0; base < n; base += kGroupWaves * kWave) {
+        const int t = base + tid;
+        const bool f = t < n && pred(t);
+        const unsigned long long m = __ballot(f);
+        const int before = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wave_cnt[w] = __popcll(m);
+        __syncthreads();
+        int off = total;
+        for (int q = 0; q < w; ++q)
+            off += wave_cnt[q];
+        if (f)
+            slots[off + before] = t;
+        int sum = 0;
+        for (int q = 0; q < kGroupWaves; ++q)
+            sum += wave_cnt[q];
+        __syncthreads();
+        total += sum;
+    }
+    return total;
+}
+
+}  // namespace moed

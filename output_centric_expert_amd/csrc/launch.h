@@ -13,10 +13,11 @@ struct Tuning {
     int gu_npw = 1;     // gate/up (per-slot kernel): neurons per wavefront (1 or 2; 2 shares x)
     int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
-    int dn_group = 0;   // down: 0 = one wavefront per output; 1 = MFMA tiles of 16 outputs x
-                        // 16 tokens (rows decoded once per 16 tokens); 2 = choose by batch size.
-                        // 0 by default: the tiled kernel has not beaten the per-output one
-                        // (hidden-major order, cached loads) on any measured batch
+    int dn_group = 2;   // down inside moe_decode: 0 = one wavefront per output; 1 = expert-major
+                        // MFMA tiles writing per-slot partials to the workspace, then a combine
+                        // (each routed row decoded once per 64 slots); 2 = choose by batch size
+    int dn_tiles = 0;   // expert-major down: 16-slot tiles per pass over a row (1..4; 0 = as many
+                        // as fit in 64 KiB of LDS)
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
                         // except in the down kernel once B*k >= E (tokens then share rows)
@@ -66,8 +67,11 @@ size_t gate_up_grouped_lds(int B, int k);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
-hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
-bool down_grouped_fits(int E, int k);
+// Expert-major down (y: B*k*H float32 per-slot partials, then out).
+hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
+                               hipStream_t s);
+size_t down_grouped_lds(int B, int k, bool a_bf16, int max_tiles);
+int down_grouped_tiles(int B, int k, bool a_bf16, int requested);   // 0: does not fit
 // Router front-end (router.hip): top-k of float32 logits with renormalised
 // softmax weights, plus shared-expert slots.
 constexpr int kRouteMaxE = 2048;

@@ -70,21 +70,27 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
     return moed::launch_gate_up(p, a_bf16, t, s);
 }
 
-bool use_down_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
+// Expert-major down: used inside moe_decode (which owns a workspace for the
+// per-slot partials) once tokens share experts, about two or more slots per
+// expert on average.
+int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16)
 {
-    if (wfmt != moed::kMXFP8 || !moed::down_grouped_fits(E, k) || t.dn_group == 0)
-        return false;
-    if (t.dn_group == 1)
-        return true;
-    return (long)B * k >= 2L * E;
+    if (t.dn_group == 0 || (t.dn_group == 2 && (long)B * k < 2L * E))
+        return 0;
+    return moed::down_grouped_tiles(B, k, a_bf16, t.dn_tiles);
 }
 
-hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, hipStream_t s)
+hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, float* y,
+                       hipStream_t s)
 {
-    if (use_down_grouped(t, p.B, p.E, p.k, p.wfmt))
-        return moed::launch_down_grouped(p, a_bf16, out_bf16, t, s);
+    if (y) {
+        if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16))
+            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, s);
+    }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
                               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
@@ -116,11 +122,13 @@ moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, cons
 
 extern "C" {
 
-size_t moed_workspace_bytes(int B, int k, int I, int inter_dtype)
+size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype)
 {
-    if (B < 0 || k < 1 || I < 1 || !dtype_ok(inter_dtype))
+    if (B < 0 || k < 1 || H < 1 || I < 1 || !dtype_ok(inter_dtype))
         return 0;
-    return (size_t)B * (size_t)k * (size_t)I * (inter_dtype == MOED_F32 ? 4u : 2u);
+    const size_t inter = (size_t)B * (size_t)k * (size_t)I * (inter_dtype == MOED_F32 ? 4u : 2u);
+    const size_t partials = (size_t)B * (size_t)k * (size_t)H * 4u;
+    return B == 0 ? 0 : align256(inter) + partials;
 }
 
 int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg_q,
@@ -145,7 +153,7 @@ int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg
 
 int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
                     const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
-                    int B, int E, int k, int H, int I, void* stream)
+                    int B, int E, int k, int H, int I, float* partials, size_t partials_bytes, void* stream)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
@@ -155,12 +163,14 @@ int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, con
         return MOED_OK;
     if (!a || !topk_ids || !topk_w || !wd_q || !wd_s || !out)
         return MOED_ERR_NULL;
-    if (!aligned16(a) || !aligned16(wd_q))
+    if (partials && partials_bytes < (size_t)B * (size_t)k * (size_t)H * 4u)
+        return MOED_ERR_WORKSPACE;
+    if (!aligned16(a) || !aligned16(wd_q) || (partials && !aligned16(partials)))
         return MOED_ERR_ALIGN;
     const moed::Tuning t = pick(B, H, I);
     return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I),
-                                        inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t,
-                                        static_cast<hipStream_t>(stream)));
+                                  inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t, partials,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
@@ -177,7 +187,7 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         return MOED_OK;
     if (!x || !topk_ids || !topk_w || !wg_q || !wg_s || !wu_q || !wu_s || !wd_q || !wd_s || !out || !workspace)
         return MOED_ERR_NULL;
-    if (workspace_bytes < moed_workspace_bytes(B, k, I, inter_dtype))
+    if (workspace_bytes < moed_workspace_bytes(B, k, H, I, inter_dtype))
         return MOED_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(wd_q) || !aligned16(workspace))
         return MOED_ERR_ALIGN;
@@ -188,9 +198,11 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, workspace, B, E, k, H, I), a_bf16, t, s));
     if (st)
         return st;
+    const size_t inter = (size_t)B * (size_t)k * (size_t)I * (a_bf16 ? 2u : 4u);
+    float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256(inter));
     return hip_status(down_launch(
         down_args(workspace, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I), a_bf16,
-        out_dtype == MOED_BF16, t, s));
+        out_dtype == MOED_BF16, t, partials, s));
 }
 
 int moe_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* topk_ids,
@@ -286,6 +298,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_wpb") && v >= 1 && v <= 8) t.dn_wpb = (int)v;
         else if (!strcmp(tok, "dn_stage") && (v == 0 || v == 1)) t.dn_stage = (int)v;
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
+        else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;

@@ -46,13 +46,13 @@ def load() -> ctypes.CDLL:
                               "(or python -m output_centric_expert_amd.build)")
         lib = ctypes.CDLL(LIB_PATH)
         P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        lib.moed_workspace_bytes.argtypes = [I, I, I, I]
+        lib.moed_workspace_bytes.argtypes = [I, I, I, I, I]
         lib.moed_workspace_bytes.restype = Z
         lib.moe_decode.argtypes = [P] * 9 + [I, P] + [I] * 7 + [P, Z, P]
         lib.moe_decode.restype = I
         lib.moe_decode_gate_up.argtypes = [P] * 6 + [I, P] + [I] * 6 + [P]
         lib.moe_decode_gate_up.restype = I
-        lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P]
+        lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P, Z, P]
         lib.moe_decode_down.restype = I
         lib.moe_route.argtypes = [P, I, I, I, I, ctypes.c_float, P, P, P]
         lib.moe_route.restype = I
@@ -100,8 +100,9 @@ def _check(st: int, where: str):
         raise MoedError(st, where)
 
 
-def moed_workspace_bytes(B: int, k: int, I: int, inter_dtype=torch.float32) -> int:
-    return int(load().moed_workspace_bytes(B, k, I, _DT[inter_dtype]))
+def moed_workspace_bytes(B: int, k: int, H: int, I: int, inter_dtype=torch.float32) -> int:
+    """Workspace of moe_decode: the intermediate (256-byte aligned), then B*k*H float32 partials."""
+    return int(load().moed_workspace_bytes(B, k, H, I, _DT[inter_dtype]))
 
 
 _WF = {"mxfp8": 0, "mxfp4": 1}          # moed_wformat
@@ -125,7 +126,7 @@ def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None
     HB, IB = _kb(H, wformat), _kb(I, wformat)
     if out is None:
         out = torch.empty((B, H), dtype=out_dtype, device=x.device)
-    need = moed_workspace_bytes(B, k, I, inter_dtype)
+    need = moed_workspace_bytes(B, k, H, I, inter_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     st = load().moe_decode(
@@ -160,18 +161,25 @@ def moe_decode_gate_up(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a=None, inter_dtype=
 
 
 def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.bfloat16, stream=None,
-                    wformat="mxfp8"):
-    """Down step alone: returns out [B, H] from a [B, k, I]."""
+                    wformat="mxfp8", partials=None):
+    """Down step alone: returns out [B, H] from a [B, k, I]. partials: None (one wavefront per
+    output) or a float32 CUDA tensor of at least B*k*H elements, which lets batches whose
+    tokens share experts take the expert-major form."""
     B, k, I = a.shape
     E, H = wd_q.shape[0], wd_q.shape[1]
     IB = _kb(I, wformat)
     if out is None:
         out = torch.empty((B, H), dtype=out_dtype, device=a.device)
+    pp, pn = None, 0
+    if partials is not None:
+        pp = _ptr(partials, "partials", torch.float32)
+        pn = partials.numel() * 4
     st = load().moe_decode_down(
         _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(topk_w, "topk_w", torch.float32, (B, k)),
         _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
-        _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, _stream(stream))
+        _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, pp, pn,
+        _stream(stream))
     _check(st, "moe_decode_down")
     return out
 

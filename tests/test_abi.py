@@ -48,10 +48,13 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.moed_workspace_bytes(1, 8, 768, md.MOED_F32) == 8 * 768 * 4
-    assert lib.moed_workspace_bytes(64, 8, 2048, md.MOED_BF16) == 64 * 8 * 2048 * 2
-    assert lib.moed_workspace_bytes(0, 8, 768, md.MOED_F32) == 0
-    assert lib.moed_workspace_bytes(1, 8, 768, 7) == 0
+    # the intermediate rounded up to 256 bytes, then B*k*H float32 partials
+    assert lib.moed_workspace_bytes(1, 8, 2048, 768, md.MOED_F32) == 8 * 768 * 4 + 8 * 2048 * 4
+    assert lib.moed_workspace_bytes(64, 8, 7168, 2048, md.MOED_BF16) == 64 * 8 * 2048 * 2 + 64 * 8 * 7168 * 4
+    assert lib.moed_workspace_bytes(1, 2, 256, 48, md.MOED_BF16) == 256 + 2 * 256 * 4     # 192 -> 256
+    assert lib.moed_workspace_bytes(0, 8, 2048, 768, md.MOED_F32) == 0
+    assert lib.moed_workspace_bytes(1, 8, 2048, 768, 7) == 0
+    assert lib.moed_workspace_bytes(1, 8, 0, 768, md.MOED_F32) == 0
 
 
 P = ctypes.c_void_p
@@ -81,6 +84,7 @@ def test_decode_rejects_before_launch(lib):
     assert call_decode(lib, wf=-1) == md.MOED_ERR_DTYPE
     assert call_decode(lib, wf=1, x=None) == md.MOED_ERR_NULL   # MXFP4 goes through the same checks
     assert call_decode(lib, wsb=1 * 2 * 128 * 4 - 1) == md.MOED_ERR_WORKSPACE
+    assert call_decode(lib, wsb=1 * 2 * 128 * 4 + 1 * 2 * 256 * 4 - 1) == md.MOED_ERR_WORKSPACE   # no room for the partials
     assert call_decode(lib, x=MIS) == md.MOED_ERR_ALIGN
     assert call_decode(lib, wq=MIS) == md.MOED_ERR_ALIGN
     assert call_decode(lib, wsp=MIS) == md.MOED_ERR_ALIGN
@@ -98,8 +102,11 @@ def test_step_entry_points_reject_before_launch(lib):
     assert gu(k=0) == md.MOED_ERR_SHAPE
     assert gu(B=0, x=None) == md.MOED_OK
     dn = lambda **kw: lib.moe_decode_down(kw.get("a", A), 1, A, A, kw.get("wq", A), A, kw.get("wf", 0),
-                                          kw.get("out", A), kw.get("od", 0), 1, 8, 2, 256, 128, None)
+                                          kw.get("out", A), kw.get("od", 0), 1, 8, 2, 256, 128,
+                                          kw.get("y", None), kw.get("yb", 0), None)
     assert dn(out=None) == md.MOED_ERR_NULL
+    assert dn(y=A, yb=2 * 256 * 4 - 4) == md.MOED_ERR_WORKSPACE       # partials below B*k*H floats
+    assert dn(y=MIS, yb=2 * 256 * 4) == md.MOED_ERR_ALIGN
     assert dn(wq=MIS) == md.MOED_ERR_ALIGN
     assert dn(od=3) == md.MOED_ERR_DTYPE
     assert dn(wf=7) == md.MOED_ERR_DTYPE
@@ -130,6 +137,9 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"gu_group=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_group=1") == md.MOED_OK
     assert lib.moed_set_tuning(b"dn_group=-1") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"dn_group=1,dn_tiles=4") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_tiles=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_tiles=5") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_order=2") == md.MOED_OK
     assert lib.moed_set_tuning(b"dn_order=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"nt=2") == md.MOED_OK

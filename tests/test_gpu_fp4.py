@@ -128,10 +128,10 @@ def test_fp4_workload_sampled_parity(name):
     assert torch.equal(run(L), out), "not deterministic"
     ref, _ = oracle_tokens(L, toks)
     check_f32(out[toks], ref, "mxfp4 " + name)
-    # batch = concatenation of single-token calls, bit for bit, on each gate/up kernel
-    # (the per-slot and the grouped kernels accumulate in different orders)
+    # batch = concatenation of single-token calls, bit for bit, on each kernel pair
+    # (the per-slot/per-output and the expert-grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for spec in ("gu_group=0", "gu_group=1"):
+    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1"):
         md.moed_set_tuning(spec)
         try:
             full = run(L)
@@ -230,3 +230,27 @@ def test_fp4_grouped_gate_up(shape):
         assert torch.equal(run(L), out)
     finally:
         md.moed_set_tuning(None)
+
+
+@pytest.mark.parametrize("shape", [(80, 2, 2, 96, 160), (64, 4, 2, 2080, 288)],
+                         ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_fp4_expert_major_down(shape):
+    """The expert-major down on MXFP4 rows: more slots per expert than one pass takes, H % 64 = 32,
+    a leftover MX block; through moe_decode and through moe_decode_down with partials."""
+    B, E, k, H, I = shape
+    L = small(*shape, seed=sum(shape) + 31)
+    ref, _ = oracle_tokens(L, list(range(B)))
+    for tiles in (0, 1):
+        md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles}")
+        try:
+            out = run(L)
+            check_f32(out, ref, f"mxfp4 expert-major tiles={tiles} {shape}")
+            x, ids, w = md.layer_device_inputs(L)
+            a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF)
+            y = torch.full((B * k * H,), float("nan"), dtype=torch.float32, device="cuda")
+            out2 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32, wformat=WF,
+                                      partials=y)
+            torch.cuda.synchronize()
+            assert torch.equal(out2, out)
+        finally:
+            md.moed_set_tuning(None)

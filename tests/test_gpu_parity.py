@@ -390,7 +390,7 @@ def test_graph_replays_match_eager(name, wformat):
     x, ids, w = md.layer_device_inputs(L)
     sh = L.shape
     logits = torch.from_numpy(synth.make_router_logits(sh.B, sh.E, L.seed, sh.zipf_s).astype(np.float32)).cuda()
-    ws = torch.empty(md.moed_workspace_bytes(sh.B, sh.k, sh.I), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(md.moed_workspace_bytes(sh.B, sh.k, sh.H, sh.I), dtype=torch.uint8, device="cuda")
     rid = torch.empty_like(ids)
     rw = torch.empty_like(w)
     outs = [torch.empty((sh.B, sh.H), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -421,3 +421,67 @@ def test_graph_replays_match_eager(name, wformat):
                               out_dtype=torch.bfloat16, wformat=wformat)      # eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(other.float()).all()
+
+
+# --------------------------------------------------------------------------------------
+# expert-major down (per-slot partials in the workspace, then a slot-order sum)
+# --------------------------------------------------------------------------------------
+
+EXPERT_MAJOR = [
+    (80, 2, 2, 96, 160),      # 80 slots per expert: several passes; H % 64 = 32; a leftover MX block
+    (64, 4, 2, 2080, 288),    # wavefronts past H in the last row block; 2 K groups + 1 leftover block
+    (33, 8, 8, 256, 64),      # k = E: every token on every expert; no full K group
+    (6, 40, 5, 512, 128),     # mostly single-slot experts, many empty workgroups
+]
+
+
+@pytest.mark.parametrize("tiles", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", EXPERT_MAJOR, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_expert_major_down(shape, tiles):
+    B, E, k, H, I = shape
+    L = small(*shape, seed=sum(shape) + 5)
+    ref, _ = oracle_tokens(L, list(range(B)))
+    md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles}")
+    try:
+        out = run(L)
+        check_f32(out, ref, f"expert-major tiles={tiles} {shape}")
+        check_bf16(run(L, torch.bfloat16), out, ref, f"expert-major bf16 {shape}")
+        assert torch.equal(run(L), out)
+        # the down step alone with caller-owned partials: the same kernels, the same result;
+        # the output is the float32 slot-order sum of the partials
+        x, ids, w = md.layer_device_inputs(L)
+        a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+        y = torch.full((B * k * H,), float("nan"), dtype=torch.float32, device="cuda")
+        out2 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32, partials=y)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, out)
+        yv = y.view(B, k, H)
+        acc = torch.zeros((B, H), dtype=torch.float32, device="cuda")
+        for j in range(k):
+            acc = acc + yv[:, j]
+        assert torch.equal(acc, out)
+        # bf16 intermediates (the B operand is then the bf16 value itself): close to the
+        # per-output kernel on the same intermediate
+        o16 = run(L, inter_dtype=torch.bfloat16)
+        md.moed_set_tuning("dn_group=0")
+        p16 = run(L, inter_dtype=torch.bfloat16)
+        rms = math.sqrt(float(np.mean(ref ** 2)))
+        assert float((o16 - p16).abs().max()) <= 1e-4 * rms
+    finally:
+        md.moed_set_tuning(None)
+
+
+def test_expert_major_down_without_partials_is_per_output():
+    """moe_decode_down without partials keeps the per-output kernel: equal to dn_group=0."""
+    L = small(40, 3, 2, 96, 160, seed=9)
+    x, ids, w = md.layer_device_inputs(L)
+    a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+    md.moed_set_tuning("dn_group=1")
+    try:
+        o1 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32)
+        md.moed_set_tuning("dn_group=0")
+        o0 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1)
+    finally:
+        md.moed_set_tuning(None)
