@@ -47,28 +47,48 @@ __device__ __forceinline__ void split8(const f32x4& v0, const f32x4& v1, u32x4& 
 }
 
 // a[s][i0 .. i0+7] (i0 a multiple of 8) from the chunk-interleaved
-// intermediate, as hi / lo bf16 (a bf16 intermediate: hi only).
+// intermediate, as loaded: one 16-byte unit of bf16, or two of float32.
 template <bool A_BF16>
-__device__ __forceinline__ void load_a8_split(const void* a, int s, int i0, int I, u32x4& hi, u32x4& lo)
+struct ARaw {
+    static constexpr int N = A_BF16 ? 1 : 2;
+    u32x4 v[N];
+};
+
+template <bool A_BF16>
+__device__ __forceinline__ ARaw<A_BF16> load_a8(const void* a, int s, int i0, int I)
 {
     const size_t cpr16 = (size_t)(I / 16);
     const size_t o = (size_t)(i0 / 16);
+    const u32x4* a16 = static_cast<const u32x4*>(a);
+    ARaw<A_BF16> r;
     if constexpr (A_BF16) {
-        const u32x4* a16 = static_cast<const u32x4*>(a);
-        hi = a16[((size_t)s * 2 + (size_t)((i0 / 8) % 2)) * cpr16 + o];
+        r.v[0] = a16[((size_t)s * 2 + (size_t)((i0 / 8) % 2)) * cpr16 + o];
+    } else {
+        const size_t t = (size_t)((i0 / 4) % 4);  // 0 or 2
+        r.v[0] = a16[((size_t)s * 4 + t) * cpr16 + o];
+        r.v[1] = a16[((size_t)s * 4 + t + 1) * cpr16 + o];
+    }
+    return r;
+}
+
+// The B operand pieces of those 8 values: hi (and lo for float32 a).
+template <bool A_BF16>
+__device__ __forceinline__ void split_a8(const ARaw<A_BF16>& r, u32x4& hi, u32x4& lo)
+{
+    if constexpr (A_BF16) {
+        hi = r.v[0];
         lo = u32x4{0u, 0u, 0u, 0u};
     } else {
-        const f32x4* a32 = static_cast<const f32x4*>(a);
-        const size_t t = (size_t)((i0 / 4) % 4);  // 0 or 2
-        const f32x4 v0 = a32[((size_t)s * 4 + t) * cpr16 + o];
-        const f32x4 v1 = a32[((size_t)s * 4 + t + 1) * cpr16 + o];
-        split8(v0, v1, hi, lo);
+        split8(__builtin_bit_cast(f32x4, r.v[0]), __builtin_bit_cast(f32x4, r.v[1]), hi, lo);
     }
 }
 
+// The lane's rows: row tile t of the wavefront is rows h0 + 16t .. +15, the
+// lane supplying row h0 + 16t + col.
+template <int RT>
 struct DnRow {
-    const uint8_t* q;       // this lane's down row (codes)
-    const uint8_t* s;       // its scales
+    const uint8_t* q[RT];   // codes
+    const uint8_t* s[RT];   // scales
     int nsteps;             // MX blocks per row (I/32) = MFMA K steps
     int kb;                 // lane / 16
     int col;                // lane % 16
@@ -79,16 +99,17 @@ struct DnGroupW {
     float sc;
 };
 
-template <bool FP4>
-__device__ __forceinline__ DnGroupW load_dn_w(const DnRow& r, int g)
+template <bool FP4, int RT>
+__device__ __forceinline__ void load_dn_w(const DnRow<RT>& r, int g, DnGroupW (&w)[RT])
 {
-    DnGroupW w;
     const int kbase = g * 128 + 32 * r.kb;
     const int bbase = FP4 ? kbase / 2 : kbase;
-    w.c0 = *reinterpret_cast<const u32x4*>(r.q + bbase);
-    w.c1 = FP4 ? w.c0 : *reinterpret_cast<const u32x4*>(r.q + bbase + 16);
-    w.sc = ue8m0_to_f32(r.s[4 * g + r.kb]);
-    return w;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        w[t].c0 = *reinterpret_cast<const u32x4*>(r.q[t] + bbase);
+        w[t].c1 = FP4 ? w[t].c0 : *reinterpret_cast<const u32x4*>(r.q[t] + bbase + 16);
+        w[t].sc = ue8m0_to_f32(r.s[t][4 * g + r.kb]);
+    }
 }
 
 // MFMA step q of the group: codes 8q .. 8q+7 of the lane's block.
@@ -105,14 +126,20 @@ __device__ __forceinline__ bf16x8 dn_decode(const DnGroupW& w, int q)
 
 // One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1).
 // Every thread of the workgroup calls it (it has barriers); `store` is false
-// for wavefronts whose rows lie past H (they compute on a clamped row and
+// for wavefronts whose rows lie past H (they compute on clamped rows and
 // write nothing). Inside a K group lane (row, kb) supplies block kb's 32
 // codes over the 4 MFMA steps and the B operand uses the same k order;
 // leftover blocks (I/32 not a multiple of 4) take a from global memory in
-// plain k order.
-template <int NTL, bool A_BF16, bool FP4>
-__device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow& r, const int* slots, int count,
-                                                 int t0, u32x4* xs, bool store, int h0, float* y)
+// plain k order. Each B operand read from LDS serves the RT row tiles.
+//
+// Loads in flight: the weight codes of a group are requested two groups
+// ahead (two register sets, used alternately, so the loop carries no register
+// copies that would wait for them); the slots' a for the next group is
+// requested at the start of a group and split into its LDS buffer after the
+// group's MFMAs.
+template <int NTL, int RT, bool A_BF16, bool FP4>
+__device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<RT>& r, const int* slots,
+                                                 int count, int t0, u32x4* xs, bool store, int h0, float* y)
 {
     const int I = p.I;
     const int tid = threadIdx.x;
@@ -129,102 +156,130 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow&
         const int si = (t0 + tt) * 16 + r.col;
         bj[tt] = slots[si < count ? si : count - 1];  // extra columns repeat a slot
     }
-    f32x4 d[NTL];
+    f32x4 d[RT][NTL];
 #pragma unroll
-    for (int tt = 0; tt < NTL; ++tt)
-        d[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            d[t][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int ngroups = r.nsteps / 4;
-    u32x4 hreg[NTL], lreg[NTL];
-    DnGroupW wc{};
+    ARaw<A_BF16> raw[NTL];
+    auto put_a = [&](u32x4* buf) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            u32x4 hi, lo;
+            split_a8<A_BF16>(raw[tt], hi, lo);
+            const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
+            buf[u] = hi;
+            if constexpr (!A_BF16)
+                buf[kHalf + u] = lo;
+        }
+    };
+    DnGroupW wA[RT], wB[RT];
     if (ngroups > 0) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt)
-            load_a8_split<A_BF16>(p.a, ls[tt], 8 * lc, I, hreg[tt], lreg[tt]);
-        wc = load_dn_w<FP4>(r, 0);
-#pragma unroll
-        for (int tt = 0; tt < NTL; ++tt) {
-            const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
-            xs[u] = hreg[tt];
-            if constexpr (!A_BF16)
-                xs[kHalf + u] = lreg[tt];
-        }
+            raw[tt] = load_a8<A_BF16>(p.a, ls[tt], 8 * lc, I);
+        load_dn_w<FP4>(r, 0, wA);
+        load_dn_w<FP4>(r, ngroups > 1 ? 1 : 0, wB);
+        put_a(xs);
     }
     __syncthreads();
-    for (int g = 0; g < ngroups; ++g) {
+    auto group = [&](int g, DnGroupW (&w)[RT]) {
         const u32x4* xb = xs + (g & 1) * kBuf;
         const bool more = g + 1 < ngroups;
-        DnGroupW wn = wc;
-        if (more) {                               // next group's loads, ahead of this group's MFMAs
+        if (more) {
 #pragma unroll
             for (int tt = 0; tt < NTL; ++tt)
-                load_a8_split<A_BF16>(p.a, ls[tt], (g + 1) * 128 + 8 * lc, I, hreg[tt], lreg[tt]);
-            wn = load_dn_w<FP4>(r, g + 1);
+                raw[tt] = load_a8<A_BF16>(p.a, ls[tt], (g + 1) * 128 + 8 * lc, I);
         }
+        bf16x8 aw[RT][4];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                aw[t][q] = dn_decode<FP4>(w[t], q);
+        load_dn_w<FP4>(r, g + 2 < ngroups ? g + 2 : ngroups - 1, w);   // two groups ahead
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const bf16x8 aw = dn_decode<FP4>(wc, q);
             const int c = 4 * r.kb + q;
 #pragma unroll
             for (int tt = 0; tt < NTL; ++tt) {
                 const int u = (tt * 16 + r.col) * 16 + (c ^ r.col);
-                d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, xb[u]), d[tt], 0, 0,
-                                                                0);
-                if constexpr (!A_BF16)
-                    d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        aw, __builtin_bit_cast(bf16x8, xb[kHalf + u]), d[tt], 0, 0, 0);
-            }
-        }
-        if (more) {
-            u32x4* xn = xs + ((g + 1) & 1) * kBuf;
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, xb[u]);
 #pragma unroll
-            for (int tt = 0; tt < NTL; ++tt) {
-                const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
-                xn[u] = hreg[tt];
-                if constexpr (!A_BF16)
-                    xn[kHalf + u] = lreg[tt];
+                for (int t = 0; t < RT; ++t)
+                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bh, d[t][tt], 0, 0, 0);
+                if constexpr (!A_BF16) {
+                    const bf16x8 bl = __builtin_bit_cast(bf16x8, xb[kHalf + u]);
+#pragma unroll
+                    for (int t = 0; t < RT; ++t)
+                        d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bl, d[t][tt], 0, 0, 0);
+                }
             }
         }
+        if (more)
+            put_a(xs + ((g + 1) & 1) * kBuf);
         __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
-        wc = wn;
+    };
+    for (int g = 0; g < ngroups; g += 2) {
+        group(g, wA);
+        if (g + 1 < ngroups)
+            group(g + 1, wB);
     }
     for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
         const int k0 = st * 32 + 8 * r.kb;
-        bf16x8 aw;
-        if constexpr (FP4)
-            aw = decode8_scaled_fp4(*reinterpret_cast<const uint32_t*>(r.q + k0 / 2), ue8m0_to_f32(r.s[st]));
-        else
-            aw = decode8_scaled(*reinterpret_cast<const u32x2*>(r.q + k0), ue8m0_to_f32(r.s[st]));
+        bf16x8 aw[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            if constexpr (FP4)
+                aw[t] = decode8_scaled_fp4(*reinterpret_cast<const uint32_t*>(r.q[t] + k0 / 2),
+                                           ue8m0_to_f32(r.s[t][st]));
+            else
+                aw[t] = decode8_scaled(*reinterpret_cast<const u32x2*>(r.q[t] + k0), ue8m0_to_f32(r.s[t][st]));
+        }
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt) {
             u32x4 hi, lo;
-            load_a8_split<A_BF16>(p.a, bj[tt], k0, I, hi, lo);
-            d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, hi), d[tt], 0, 0, 0);
-            if constexpr (!A_BF16)
-                d[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, __builtin_bit_cast(bf16x8, lo), d[tt], 0, 0, 0);
+            split_a8<A_BF16>(load_a8<A_BF16>(p.a, bj[tt], k0, I), hi, lo);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, hi), d[t][tt],
+                                                                   0, 0, 0);
+                if constexpr (!A_BF16)
+                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, lo),
+                                                                       d[t][tt], 0, 0, 0);
+            }
         }
     }
     if (!store)
         return;
-    // lane holds D rows 4*kb .. +3 (outputs h, H a multiple of 16) of column col (slot)
+    // lane holds D rows 4*kb .. +3 (outputs h) of column col (slot) of each tile
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
         if ((t0 + tt) * 16 + r.col < count) {
             const int s = bj[tt];
             const float wgt = p.w[s];
-            *reinterpret_cast<f32x4*>(y + (size_t)s * (size_t)p.H + (size_t)(h0 + 4 * r.kb)) = wgt * d[tt];
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                *reinterpret_cast<f32x4*>(y + (size_t)s * (size_t)p.H + (size_t)(h0 + 16 * t + 4 * r.kb)) =
+                    wgt * d[t][tt];
         }
     }
 }
 
-template <bool A_BF16, bool FP4>
-__global__ void __launch_bounds__(kGroupWaves * kWave)
+// A workgroup owns (expert e, RT*64 rows); wavefront w the rows
+// hb + 16*RT*w .. +16*RT-1. H is a multiple of 16*RT.
+template <int RT, bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
 moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
 {
     extern __shared__ int slots[];                // B*k entries, then the a tiles
     __shared__ int wave_cnt[kGroupWaves];
-    const int nblk = (p.H + kGroupNeurons - 1) / kGroupNeurons;
+    constexpr int kRows = 16 * RT * kGroupWaves;
+    const int nblk = (p.H + kRows - 1) / kRows;
     const int e = blockIdx.x / nblk;
-    const int hb = (blockIdx.x % nblk) * kGroupNeurons;
+    const int hb = (blockIdx.x % nblk) * kRows;
     const int nslots = p.B * p.k;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
@@ -233,21 +288,32 @@ moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
     if (count == 0)
         return;                                   // whole workgroup: no barrier follows
     u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));
-    const int h0 = hb + 16 * w;                   // this wavefront's 16 rows
+    const int h0 = hb + 16 * RT * w;              // this wavefront's rows
     const bool store = h0 < p.H;                  // wavefronts past H still take part in the barriers
     const int col = lane % 16;
-    const int hr = h0 + col < p.H ? h0 + col : p.H - 1;
-    const size_t row = (size_t)e * (size_t)p.H + (size_t)hr;
     const size_t row_bytes = FP4 ? (size_t)(p.I / 2) : (size_t)p.I;
-    const DnRow r{p.wd_q + row * row_bytes, p.wd_s + row * (size_t)(p.I / 32), p.I / 32, lane / 16, col};
+    DnRow<RT> r;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int hr = h0 + 16 * t + col < p.H ? h0 + 16 * t + col : p.H - 1;
+        const size_t row = (size_t)e * (size_t)p.H + (size_t)hr;
+        r.q[t] = p.wd_q + row * row_bytes;
+        r.s[t] = p.wd_s + row * (size_t)(p.I / 32);
+    }
+    r.nsteps = p.I / 32;
+    r.kb = lane / 16;
+    r.col = col;
     const int ntiles = (count + 15) / 16;
     for (int t0 = 0; t0 < ntiles; t0 += max_tiles) {
         const int nt = ntiles - t0 < max_tiles ? ntiles - t0 : max_tiles;
         switch (nt) {
-        case 1: expert_down_pass<1, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
-        case 2: expert_down_pass<2, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
-        case 3: expert_down_pass<3, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
-        default: expert_down_pass<4, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        case 1: expert_down_pass<1, RT, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        case 2: expert_down_pass<2, RT, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        case 3: expert_down_pass<3, RT, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y); break;
+        default:                                  // 4 tiles of float32 a do not fit in 64 KiB of LDS
+            if constexpr (A_BF16)
+                expert_down_pass<4, RT, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y);
+            break;
         }
     }
 }
@@ -302,27 +368,27 @@ int down_grouped_tiles(int B, int k, bool a_bf16, int requested)
 }
 
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               hipStream_t s)
+                               int row_tiles, hipStream_t s)
 {
     if ((long)p.B * p.k == 0)
         return hipSuccess;
-    if (max_tiles < 1 || max_tiles > kTiles || (p.H % 16) != 0)
+    if (max_tiles < 1 || max_tiles > (a_bf16 ? kTiles : 3) || (row_tiles != 1 && row_tiles != 2) ||
+        (p.H % (16 * row_tiles)) != 0)
         return hipErrorInvalidValue;
-    const int nblk = (p.H + kGroupNeurons - 1) / kGroupNeurons;
+    const int nblk = (p.H + 16 * row_tiles * kGroupWaves - 1) / (16 * row_tiles * kGroupWaves);
     const dim3 grid((unsigned)((long)p.E * nblk)), block(kGroupWaves * kWave);
     const size_t lds = down_grouped_lds(p.B, p.k, a_bf16, max_tiles);
     const bool fp4 = p.wfmt == kMXFP4;
-    if (fp4) {
-        if (a_bf16)
-            hipLaunchKernelGGL((moe_down_expert_kernel<true, true>), grid, block, lds, s, p, y, max_tiles);
-        else
-            hipLaunchKernelGGL((moe_down_expert_kernel<false, true>), grid, block, lds, s, p, y, max_tiles);
+#define MOED_DX(RT, A, F) \
+    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F>), grid, block, lds, s, p, y, max_tiles)
+    if (row_tiles == 2) {
+        if (fp4) { if (a_bf16) MOED_DX(2, true, true); else MOED_DX(2, false, true); }
+        else { if (a_bf16) MOED_DX(2, true, false); else MOED_DX(2, false, false); }
     } else {
-        if (a_bf16)
-            hipLaunchKernelGGL((moe_down_expert_kernel<true, false>), grid, block, lds, s, p, y, max_tiles);
-        else
-            hipLaunchKernelGGL((moe_down_expert_kernel<false, false>), grid, block, lds, s, p, y, max_tiles);
+        if (fp4) { if (a_bf16) MOED_DX(1, true, true); else MOED_DX(1, false, true); }
+        else { if (a_bf16) MOED_DX(1, true, false); else MOED_DX(1, false, false); }
     }
+#undef MOED_DX
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

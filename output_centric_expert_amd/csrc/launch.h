@@ -18,6 +18,8 @@ struct Tuning {
                         // (each routed row decoded once per 64 slots); 2 = choose by batch size
     int dn_tiles = 0;   // expert-major down: 16-slot tiles per pass over a row (1..4; 0 = as many
                         // as fit in 64 KiB of LDS)
+    int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
+                        // of the slots' a serve two MFMAs)
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
                         // except in the down kernel once B*k >= E (tokens then share rows)
@@ -69,7 +71,7 @@ hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStrea
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Expert-major down (y: B*k*H float32 per-slot partials, then out).
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               hipStream_t s);
+                               int row_tiles, hipStream_t s);
 size_t down_grouped_lds(int B, int k, bool a_bf16, int max_tiles);
 int down_grouped_tiles(int B, int k, bool a_bf16, int requested);   // 0: does not fit
 // Router front-end (router.hip): top-k of float32 logits with renormalised

@@ -85,7 +85,7 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
 {
     if (y) {
         if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16))
-            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, s);
+            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, s);
     }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
@@ -299,6 +299,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_stage") && (v == 0 || v == 1)) t.dn_stage = (int)v;
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
+        else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;

@@ -240,11 +240,11 @@ def test_fp4_expert_major_down(shape):
     B, E, k, H, I = shape
     L = small(*shape, seed=sum(shape) + 31)
     ref, _ = oracle_tokens(L, list(range(B)))
-    for tiles in (0, 1):
-        md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles}")
+    for tiles, rt in ((0, 1), (0, 2), (1, 2)):
+        md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
         try:
             out = run(L)
-            check_f32(out, ref, f"mxfp4 expert-major tiles={tiles} {shape}")
+            check_f32(out, ref, f"mxfp4 expert-major tiles={tiles} rt={rt} {shape}")
             x, ids, w = md.layer_device_inputs(L)
             a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF)
             y = torch.full((B * k * H,), float("nan"), dtype=torch.float32, device="cuda")

@@ -435,16 +435,16 @@ EXPERT_MAJOR = [
 ]
 
 
-@pytest.mark.parametrize("tiles", [0, 1, 2, 3])
+@pytest.mark.parametrize("tiles,rt", [(0, 1), (0, 2), (1, 1), (1, 2), (2, 2), (3, 1), (3, 2)])
 @pytest.mark.parametrize("shape", EXPERT_MAJOR, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
-def test_expert_major_down(shape, tiles):
+def test_expert_major_down(shape, tiles, rt):
     B, E, k, H, I = shape
     L = small(*shape, seed=sum(shape) + 5)
     ref, _ = oracle_tokens(L, list(range(B)))
-    md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles}")
+    md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
     try:
         out = run(L)
-        check_f32(out, ref, f"expert-major tiles={tiles} {shape}")
+        check_f32(out, ref, f"expert-major tiles={tiles} rt={rt} {shape}")
         check_bf16(run(L, torch.bfloat16), out, ref, f"expert-major bf16 {shape}")
         assert torch.equal(run(L), out)
         # the down step alone with caller-owned partials: the same kernels, the same result;
