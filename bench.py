@@ -76,6 +76,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--all", action="store_true",
                     help="time every decode workload (one JSON line each); not the driver's line")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="labelled diagnostics, not the driver's line: adjacent vs scattered expert ids, "
+                         "warm cache (one weight copy), contiguous hot experts on the skewed workload")
     ap.add_argument("--counters", action="store_true",
                     help="eager launches for rocprofv3 --pmc passes (copy kernel of known size, "
                          "then the two layer kernels); prints the launch plan, no timing")
@@ -100,6 +103,9 @@ def main():
 
     if args.all:
         all_workloads(md, synth, args)
+        return
+    if args.diagnostics:
+        diagnostics(md, synth, args)
         return
 
     shape = synth.WORKLOADS[args.workload]
@@ -337,6 +343,44 @@ def all_workloads(md, synth, args):
         print(json.dumps(line), flush=True)
         del L
         torch.cuda.empty_cache()
+
+
+def diagnostics(md, synth, args):
+    """Labelled measurements beside the metric (none of them is the default line):
+    - the single-token layer with its 8 experts at adjacent ids 0..7 against the recipe's
+      scattered ids (same weights, same bytes);
+    - every workload with one weight copy, so the L2 and the 256 MB MALL keep what fits
+      (the metric's runs cycle through copies so that they cannot);
+    - the skewed workload with its hot experts at adjacent ids (Zipf ranks r_e = e + 1)."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    def emit(label, L, R, K):
+        t = measure_layer(md, L, R, K, min(args.warmup, 10))
+        gbs = L.unique_weight_bytes / (t["ms_per_step"] * 1e-3) / 1e9
+        print(json.dumps({"diagnostic": label, "workload": L.shape.name, "wformat": L.wformat,
+                          "weight_copies": R, "steps": K, "unique_experts": L.unique_experts,
+                          "gbs": round(gbs, 1), **timing_fields(L, t)}), flush=True)
+
+    name = "wide_B1_E128_k8_H2048_I768"
+    R, K = ALL_PLAN[name]
+    L = synth.make_layer(name, device="cuda", wformat=args.wformat)
+    emit("scattered expert ids (the recipe)", L, R, K)
+    adj = dataclasses.replace(L, ids=np.arange(L.shape.k, dtype=np.int32)[None, :].repeat(L.shape.B, 0))
+    emit("adjacent expert ids 0..k-1", adj, R, K)
+    del L, adj
+    torch.cuda.empty_cache()
+    for name in synth.WORKLOAD_ORDER:
+        _, K = ALL_PLAN[name]
+        L = synth.make_layer(name, device="cuda", wformat=args.wformat)
+        emit("warm cache (one weight copy)", L, 1, K)
+        del L
+        torch.cuda.empty_cache()
+    name = "skewed_B64_E256_k8_H7168_I2048"
+    R, K = ALL_PLAN[name]
+    L = synth.make_layer(name, device="cuda", wformat=args.wformat, contiguous_hot=True)
+    emit("hot experts at adjacent ids", L, R, K)
 
 
 def counters_run(md, x, ids, w, copies, out, a, workload, wformat="mxfp8"):

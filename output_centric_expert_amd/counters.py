@@ -40,6 +40,27 @@ def pick(per: dict, needle: str):
     return sum(vals) / len(vals), len(vals)
 
 
+# The kernels one call of each layer step launches: the per-slot or the expert-grouped gate/up;
+# the per-output down (staged or direct), or the expert-major down plus its combine.
+STEP_KERNELS = {"gate_up": ("moe_gate_up_kernel", "moe_gate_up_grouped_kernel"),
+                "down": ("moe_down_kernel", "moe_down_staged_kernel", "moe_down_rows_kernel",
+                         "moe_down_expert_kernel", "moe_down_combine_kernel")}
+
+
+def step_counter(per: dict, step: str):
+    """Per-call value of one layer step: the mean per dispatch of each of its kernels that ran,
+    summed over those kernels. Also returns {kernel: (mean, dispatches)}."""
+    parts = {}
+    for needle in STEP_KERNELS[step]:
+        names = [k for k in per if f"{needle}<" in k or f"{needle}(" in k]
+        if names:
+            vals = [v for k in names for v in per[k]]
+            parts[needle] = (sum(vals) / len(vals), len(vals))
+    if not parts:
+        raise KeyError(f"no dispatch of a {step} kernel")
+    return sum(m for m, _ in parts.values()), parts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--fetch", required=True)
@@ -62,12 +83,12 @@ def main():
            "copy_kernel": {"bytes_read": args.copy_bytes, "bytes_written": args.copy_bytes,
                            "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
                            "fetch_scale": f_fetch, "write_scale": f_write}}
-    for key, needle, alg in (("gate_up", "moe_gate_up_kernel", args.gate_up_bytes),
-                             ("down", "moe_down", args.down_bytes)):
-        fv, n = pick(fetch, needle)
-        wv, _ = pick(write, needle)
+    for key, alg in (("gate_up", args.gate_up_bytes), ("down", args.down_bytes)):
+        fv, fparts = step_counter(fetch, key)
+        wv, _ = step_counter(write, key)
         hbm = fv * 1024.0 * f_fetch + wv * 1024.0 * f_write
-        res[key] = {"dispatches": n, "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv,
+        res[key] = {"kernels": {k: {"dispatches": n, "FETCH_SIZE_KiB": m} for k, (m, n) in fparts.items()},
+                    "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv,
                     "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
                     "traffic_over_algorithmic": hbm / alg}
     res["hbm_bytes_per_launch"] = res["gate_up"]["hbm_bytes_per_launch"]

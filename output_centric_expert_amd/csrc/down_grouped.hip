@@ -329,15 +329,18 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
         return;
     const int b = (int)(q / hq);
     const int h = (int)(q % hq) * 4;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ids first, then every partial unconditionally (in bounds; the partial of a
+    // slot with an invalid id was never written and is masked below), so the k
+    // loads are all in flight at once; added in slot order
+    const int32_t* idb = ids + (size_t)b * (size_t)k;
     bool bad = false;
-    for (int j = 0; j < k; ++j) {
-        const size_t s = (size_t)b * (size_t)k + (size_t)j;
-        if ((unsigned)ids[s] >= (unsigned)E)
-            bad = true;
-        else
-            acc += *reinterpret_cast<const f32x4*>(y + s * (size_t)H + (size_t)h);
-    }
+    for (int j = 0; j < k; ++j)
+        bad |= (unsigned)idb[j] >= (unsigned)E;
+    const float* yb = y + (size_t)b * (size_t)k * (size_t)H + (size_t)h;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int j = 0; j < k; ++j)
+        acc += *reinterpret_cast<const f32x4*>(yb + (size_t)j * (size_t)H);
     if (bad)
         acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     const size_t o = (size_t)b * (size_t)H + (size_t)h;
