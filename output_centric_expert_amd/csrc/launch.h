@@ -15,7 +15,7 @@ struct Tuning {
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
     int dn_group = 2;   // down inside moe_decode: 0 = one wavefront per output; 1 = expert-major
                         // MFMA tiles writing per-slot partials to the workspace, then a combine
-                        // (each routed row decoded once per 64 slots); 2 = choose by batch size
+                        // (each routed row decoded once per 64 slots); 2 = expert-major once B*k >= 2E
     int dn_tiles = 0;   // expert-major down: 16-slot tiles per pass over a row (1..4; 0 = as many
                         // as fit in 64 KiB of LDS)
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
@@ -25,7 +25,7 @@ struct Tuning {
                         // except in the down kernel once B*k >= E (tokens then share rows)
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
-                        // MFMA tiles (rows decoded once per 16 slots); 2 = choose by batch size
+                        // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once 2*B*k >= 3E
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
     int dn_rows = 0;    // down (staged): outputs per wavefront, 1, 2 or 4; 0 = by batch (4 once
                         // B*k >= E, 2 for B >= 2, 1 for B = 1)

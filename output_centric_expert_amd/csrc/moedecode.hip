@@ -50,9 +50,10 @@ moed::Tuning pick(int B, int H, int I)
     return t;
 }
 
-// Expert-grouped gate/up pays off once there are about two or more slots per
-// expert on average (each routed row then serves several tokens); its slot
-// list must fit in 64 KiB of LDS.
+// Expert-grouped gate/up pays off once there are about 1.5 or more slots per
+// expert on average (each routed row then serves several tokens; measured
+// crossovers at 1.0-1.5 slots per expert for E = 128 and 256); its slot list
+// must fit in 64 KiB of LDS.
 bool use_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel
@@ -60,7 +61,7 @@ bool use_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
         return false;
     if (t.gu_group == 1)
         return true;
-    return (long)B * k >= 2L * E;
+    return 2L * B * k >= 3L * E;
 }
 
 hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tuning& t, hipStream_t s)
@@ -72,7 +73,7 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
 
 // Expert-major down: used inside moe_decode (which owns a workspace for the
 // per-slot partials) once tokens share experts, about two or more slots per
-// expert on average.
+// expert on average (measured crossovers at 1.5-2 slots per expert).
 int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16)
 {
     if (t.dn_group == 0 || (t.dn_group == 2 && (long)B * k < 2L * E))
