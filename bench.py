@@ -19,10 +19,10 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -39,15 +39,26 @@ def log(*a):
 
 
 # The sources the per-slot gate/up kernel (the dominant kernel of the single-token layer) is
-# compiled from, plus the entry point that selects its launch shape. Its committed HBM counters
-# stay valid while these are unchanged.
-GATE_UP_SOURCES = ("gate_up.hip", "gate_up_body.h", "launch.h", "mx_device.h", "moedecode.hip")
+# compiled from, with its launch-shape defaults. Its committed HBM counters stay valid while the
+# code in these files (comments and blank lines removed) is unchanged.
+GATE_UP_SOURCES = ("gate_up.hip", "gate_up_body.h", "launch.h", "mx_device.h")
 
 
-def source_digest() -> str:
+def _code_only(src: str) -> str:
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.strip() for line in src.splitlines() if line.strip())
+
+
+# ... and those of the expert-grouped gate/up and the expert-major down (the large-batch kernels).
+GROUPED_SOURCES = ("gate_up_grouped.hip", "down_grouped.hip", "grouped_common.h", "launch.h", "mx_device.h")
+
+
+def source_digest(files=GATE_UP_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in GATE_UP_SOURCES:
-        h.update(open(os.path.join(ROOT, "output_centric_expert_amd", "csrc", name), "rb").read())
+    for name in files:
+        with open(os.path.join(ROOT, "output_centric_expert_amd", "csrc", name)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
