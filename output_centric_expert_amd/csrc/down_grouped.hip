@@ -1,9 +1,10 @@
 // Down for large decode batches (tokens sharing experts): expert-major, so
-// each routed down row is read and decoded once per workgroup pass (up to 64
-// slots) instead of once per (token, slot).
+// each routed down row is read and decoded once per workgroup pass (up to 48
+// slots with a float32 intermediate, 64 with bf16) instead of once per
+// (token, slot).
 //
-// Step 1, moe_down_expert_kernel: a workgroup owns (expert e, 64 output rows
-// hb .. hb+63), four wavefronts of 16 rows each. It compacts the list of slots
+// Step 1, moe_down_expert_kernel: a workgroup owns (expert e, RT*64 output
+// rows), four wavefronts of RT tiles of 16 rows each. It compacts the list of slots
 // s = (b, j) routed to e (in slot order, from topk_ids) and computes, for
 // tiles of 16 of those slots, the MFMA product
 //   A = Wd[e][h][:], decoded exactly from MXFP8 / MXFP4 to BF16 with the
@@ -15,8 +16,9 @@
 // and writes the slot's weighted partial y[s][h] = w[s] * D[h][s]. The slots'
 // a is split once per workgroup and shared by its wavefronts through
 // double-buffered LDS tiles (the unit layout of the grouped gate/up kernel);
-// K is walked in groups of 4 MX blocks, the next group's loads issued before
-// the current group's MFMAs.
+// each B operand read from LDS serves the wavefront's RT row tiles. K is
+// walked in groups of 4 MX blocks with the weight codes requested two groups
+// ahead.
 //
 // Step 2, moe_down_combine_kernel: out[b][h] = sum over j of y[(b, j)][h], the
 // token's k slots added in slot order and stored once; a token with an

@@ -1,8 +1,8 @@
 // Helpers shared by the expert-grouped kernels (large decode batches): exact
 // MXFP8 / MXFP4 -> BF16 decode with the block scale folded in (the MFMA A
-// operand), the deterministic slot-list compaction, and the launch shape
-// (workgroups of 4 wavefronts, 16 rows each; up to 4 tiles of 16 slots per
-// pass over a row).
+// operand), the deterministic slot-list compaction, and the common launch
+// shape (workgroups of 4 wavefronts, 16-row MFMA tiles, up to 4 tiles of 16
+// slots per pass over a row).
 #pragma once
 
 #include "launch.h"
