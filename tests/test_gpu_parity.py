@@ -485,3 +485,46 @@ def test_expert_major_down_without_partials_is_per_output():
         assert torch.equal(o0, o1)
     finally:
         md.moed_set_tuning(None)
+
+
+def test_long_slot_list_takes_fewer_tiles():
+    """B*k = 4800 slots: the slot list takes 19 KB of LDS, so the expert-major down takes two
+    tiles of float32 a per pass instead of three."""
+    L = small(600, 8, 8, 64, 64, seed=31)
+    toks = [0, 1, 299, 599]
+    out = run(L)
+    ref, _ = oracle_tokens(L, toks)
+    check_f32(out[toks], ref, "B=600")
+    md.moed_set_tuning("dn_tiles=2")
+    try:
+        assert torch.equal(run(L), out)
+    finally:
+        md.moed_set_tuning(None)
+
+
+def test_slot_list_beyond_lds_falls_back():
+    """B*k = 12800 slots: the slot list alone takes 50 KB of LDS, so neither grouped kernel fits
+    and the layer keeps the per-slot gate/up and the per-output down."""
+    L = small(1600, 8, 8, 64, 64, seed=33)
+    toks = [0, 1, 800, 1599]
+    out = run(L)
+    md.moed_set_tuning("gu_group=0,dn_group=0")
+    try:
+        assert torch.equal(run(L), out)
+    finally:
+        md.moed_set_tuning(None)
+    ref, _ = oracle_tokens(L, toks)
+    check_f32(out[toks], ref, "B=1600 fallback")
+
+
+def test_partials_untouched_below_threshold():
+    """Below B*k >= 2E moe_decode_down keeps the per-output form and never writes the partials."""
+    L = small(2, 16, 4, 256, 128, seed=32)                # B*k = 8 < 2E
+    x, ids, w = md.layer_device_inputs(L)
+    a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+    y = torch.full((2 * 4 * 256,), 7.0, dtype=torch.float32, device="cuda")
+    out = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32, partials=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    ref, _ = oracle_tokens(L, [0, 1])
+    check_f32(out, ref, "below threshold with partials")
