@@ -144,10 +144,15 @@ def main():
     gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
 
     traffic = load_traffic("gate_up", args.workload) if L.wformat == "mxfp8" else None
+    _, dn_bytes = kernel_bytes(L)
+    floor = same_size_reads(md, gu_bytes, dn_bytes, K=min(K, 2000)) if L.unique_weight_bytes < (1 << 30) else None
     roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
                 "avg_launch_us": round(ms_gu * 1e3, 3)}
+    if floor:
+        roofline["same_size_read_us"] = floor["gate_up_bytes_us"]
+        roofline["frac_of_same_size_read"] = round(floor["gate_up_bytes_us"] / (ms_gu * 1e3), 4)
 
     cpu = None
     if not args.no_cpu:
@@ -174,6 +179,7 @@ def main():
         **timing_fields(L, t),
         "measured_read_peak_gbs": round(peak, 1),
         "frac_of_measured_read_peak": round(gbs / peak, 4),
+        "same_size_reads_us": floor,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "tuning": args.tune or "built-in",
@@ -349,6 +355,8 @@ def all_workloads(md, synth, args):
                 "unique_weight_bytes": L.unique_weight_bytes, "gbs": round(gbs, 1),
                 **timing_fields(L, t), "frac_of_measured_read_peak": round(gbs / peak, 4),
                 "measured_read_peak_gbs": round(peak, 1)}
+        if L.unique_weight_bytes < (1 << 30):
+            line["same_size_reads_us"] = same_size_reads(md, *kernel_bytes(L), K=min(K, 2000))
         if not args.no_cpu:
             line["cpu_baseline"] = cpu_baseline(L, L.unique_weight_bytes, min(args.cpu_seconds, 10.0))
         print(json.dumps(line), flush=True)
@@ -436,6 +444,48 @@ def measured_read_peak(md, nbytes=2 << 30, launches=20):
     del bufs
     torch.cuda.empty_cache()
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def same_size_reads(md, gu_bytes, dn_bytes, K=2000, min_total=1 << 30):
+    """What a pure streaming read of the same byte counts takes with the same launch mechanism
+    (a HIP graph of K back-to-back launches over rotating buffers, so the 256 MB cache cannot
+    serve them): µs per launch for the gate/up bytes alone, the down bytes alone, and the two as
+    a dependent pair (the layer's shape)."""
+    import numpy as np
+    import torch
+
+    R = max(2, -(-min_total // (gu_bytes + dn_bytes)))
+    bufs = [(torch.empty(gu_bytes, dtype=torch.uint8, device="cuda"),
+             torch.empty(dn_bytes, dtype=torch.uint8, device="cuda")) for _ in range(R)]
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(K):
+                fn(r)
+        g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / K)
+        del g
+        return float(np.median(res))
+
+    out = {"gate_up_bytes_us": timed(lambda r: md.moed_bench_read(bufs[r % R][0], sink)),
+           "down_bytes_us": timed(lambda r: md.moed_bench_read(bufs[r % R][1], sink)),
+           "pair_us": timed(lambda r: (md.moed_bench_read(bufs[r % R][0], sink),
+                                       md.moed_bench_read(bufs[r % R][1], sink)))}
+    del bufs
+    torch.cuda.empty_cache()
+    return {k: round(v, 3) for k, v in out.items()}
 
 
 def cpu_baseline(L, uniq, seconds):
