@@ -43,6 +43,15 @@
  *  - Expert ids outside [0, E) are not an error: every output of the affected
  *    token becomes NaN (no out-of-bounds read is made). NaN codes or scales
  *    in the weights propagate as NaN.
+ *  - Opt-in check: with MOED_CHECK=1 in the environment (read on every call)
+ *    moe_decode, moe_decode_gate_up and moe_decode_down first run a check
+ *    kernel on `stream` and return MOED_ERR_SHAPE, launching nothing else,
+ *    if an expert id lies outside [0, E) or a routed expert's rows (of the
+ *    matrices the call uses) hold a NaN code (E4M3 S.1111.111) or a NaN scale
+ *    (UE8M0 0xFF). This mode synchronises the stream (so it cannot be used
+ *    under graph capture) and, on its first use per device, allocates a
+ *    4-byte flag that it keeps until the process ends. Concurrent checked
+ *    calls on one device share that flag and race.
  *  - Duplicate ids within a token's row are legal and their terms add; the
  *    routing weights need not sum to 1.
  *  - Results are deterministic run to run (fixed reduction order).

@@ -80,6 +80,14 @@ constexpr int kRouteMaxE = 2048;
 constexpr int kRouteMaxK = 64;
 hipError_t launch_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* ids,
                         float* w, hipStream_t s);
+// Opt-in input check (check.hip). Pointers not used by a step may be null:
+// the gate/up step passes no down matrix and the down step no gate/up ones.
+struct CheckArgs {
+    const int32_t* ids;
+    const uint8_t *wg_q, *wg_s, *wu_q, *wu_s, *wd_q, *wd_s;
+    int B, E, k, H, I, wfmt;
+};
+hipError_t launch_check(const CheckArgs& c, uint32_t* flag, hipStream_t s);
 hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
                                   int path, hipStream_t s);
 

@@ -4,6 +4,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+
 #include "moedecode.h"
 #include "launch.h"
 
@@ -93,6 +96,60 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Opt-in input check (MOED_CHECK=1 in the environment, read on every call):
+// a check kernel on the caller's stream, then a synchronisation and a read of
+// its flag word. The flag lives in a 4-byte device buffer allocated on the
+// first checked call per device and kept for the process; nothing is
+// allocated when the check is off.
+bool check_enabled()
+{
+    const char* v = getenv("MOED_CHECK");
+    return v && v[0] == '1' && v[1] == '\0';
+}
+
+int run_check(const moed::CheckArgs& c, hipStream_t s)
+{
+    static std::mutex mu;
+    static std::map<int, uint32_t*> flags;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    uint32_t* flag = nullptr;
+    if (err == hipSuccess) {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = flags.find(dev);
+        if (it == flags.end()) {
+            err = hipMalloc(reinterpret_cast<void**>(&flag), sizeof(uint32_t));
+            if (err == hipSuccess)
+                flags[dev] = flag;
+        } else {
+            flag = it->second;
+        }
+    }
+    uint32_t host = 0;
+    if (err == hipSuccess)
+        err = moed::launch_check(c, flag, s);
+    if (err == hipSuccess)
+        err = hipStreamSynchronize(s);
+    if (err == hipSuccess)
+        err = hipMemcpy(&host, flag, sizeof(host), hipMemcpyDeviceToHost);
+    if (err != hipSuccess) {
+        g_last_hip = (int)err;
+        return MOED_ERR_HIP;
+    }
+    return host ? MOED_ERR_SHAPE : MOED_OK;
+}
+
+moed::CheckArgs check_args(const int32_t* ids, const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q,
+                           const uint8_t* wu_s, const uint8_t* wd_q, const uint8_t* wd_s, int B, int E, int k,
+                           int H, int I, int wfmt)
+{
+    moed::CheckArgs c;
+    c.ids = ids;
+    c.wg_q = wg_q; c.wg_s = wg_s; c.wu_q = wu_q; c.wu_s = wu_s; c.wd_q = wd_q; c.wd_s = wd_s;
+    c.B = B; c.E = E; c.k = k; c.H = H; c.I = I; c.wfmt = wfmt;
+    return c;
+}
+
 moed::GateUpArgs gate_up_args(const void* x, const int32_t* ids, const uint8_t* wg_q,
                               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
                               int wfmt, void* a, int B, int E, int k, int H, int I)
@@ -146,6 +203,12 @@ int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg
         return MOED_ERR_NULL;
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(a))
         return MOED_ERR_ALIGN;
+    if (check_enabled()) {
+        if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, nullptr, nullptr, B, E, k, H, I,
+                                          weight_format),
+                               static_cast<hipStream_t>(stream)))
+            return st;
+    }
     const moed::Tuning t = pick(B, H, I);
     return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, a,
                                                   B, E, k, H, I),
@@ -168,6 +231,12 @@ int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, con
         return MOED_ERR_WORKSPACE;
     if (!aligned16(a) || !aligned16(wd_q) || (partials && !aligned16(partials)))
         return MOED_ERR_ALIGN;
+    if (check_enabled()) {
+        if (int st = run_check(check_args(topk_ids, nullptr, nullptr, nullptr, nullptr, wd_q, wd_s, B, E, k, H, I,
+                                          weight_format),
+                               static_cast<hipStream_t>(stream)))
+            return st;
+    }
     const moed::Tuning t = pick(B, H, I);
     return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I),
                                   inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t, partials,
@@ -192,8 +261,13 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         return MOED_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(wd_q) || !aligned16(workspace))
         return MOED_ERR_ALIGN;
-    const moed::Tuning t = pick(B, H, I);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
+                               s))
+            return st;
+    }
+    const moed::Tuning t = pick(B, H, I);
     const bool a_bf16 = inter_dtype == MOED_BF16;
     int st = hip_status(gate_up_launch(
         gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, workspace, B, E, k, H, I), a_bf16, t, s));

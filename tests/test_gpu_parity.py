@@ -528,3 +528,54 @@ def test_partials_untouched_below_threshold():
     assert torch.all(y == 7.0)
     ref, _ = oracle_tokens(L, [0, 1])
     check_f32(out, ref, "below threshold with partials")
+
+
+def test_check_mode(monkeypatch):
+    """MOED_CHECK=1: ids outside [0, E) and NaN codes or scales in a routed expert's rows are
+    reported as MOED_ERR_SHAPE before anything else is launched; valid inputs give the same
+    result as without the check; NaNs in experts nobody is routed to are not an error."""
+    L = small(3, 6, 2, 256, 128, seed=41)
+    base = run(L)
+    monkeypatch.setenv("MOED_CHECK", "1")
+    assert torch.equal(run(L), base)
+
+    def expect_shape_error(fn):
+        with pytest.raises(md.MoedError) as ei:
+            fn()
+        assert ei.value.status == md.MOED_ERR_SHAPE
+
+    ids = L.ids.copy()
+    ids[1, 1] = 6
+    expect_shape_error(lambda: run(L, ids=ids))
+    routed = sorted(set(L.ids.ravel().tolist()))
+    unrouted = [e for e in range(6) if e not in routed]
+    e = routed[0]
+    for t, idx, bad in ((L.wd_q, (e, 5, 7), 0x7F), (L.wg_q, (e, 3, 100), 0xFF), (L.wu_s, (e, 2, 1), 0xFF)):
+        saved = t[idx].item()
+        t[idx] = bad
+        try:
+            expect_shape_error(lambda: run(L))
+        finally:
+            t[idx] = saved
+    assert torch.equal(run(L), base)
+    if unrouted:
+        u = unrouted[0]
+        saved = L.wg_s[u, 0, 0].item()
+        L.wg_s[u, 0, 0] = 0xFF
+        try:
+            assert torch.equal(run(L), base)
+        finally:
+            L.wg_s[u, 0, 0] = saved
+    # the step entry points check the matrices they use
+    x, idd, wd = md.layer_device_inputs(L)
+    bad_ids = torch.as_tensor(ids, dtype=torch.int32).cuda()
+    expect_shape_error(lambda: md.moe_decode_gate_up(x, bad_ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+    a_ws = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+    saved = L.wd_s[e, 0, 0].item()
+    L.wd_s[e, 0, 0] = 0xFF
+    try:
+        expect_shape_error(lambda: md.moe_decode_down(a_ws, idd, wd, L.wd_q, L.wd_s, out_dtype=torch.float32))
+        md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s)     # gate/up does not read Wd
+    finally:
+        L.wd_s[e, 0, 0] = saved
+    torch.cuda.synchronize()
