@@ -9,7 +9,13 @@ one-kernel graph. This splits each layer kernel's dispatches by the layer
 kernel that ran just before it, so the trace can be compared context by
 context.
 
-    python -m output_centric_expert_amd.trace_contexts gpurun_out/prof_ktrace/bench_kernel_trace.csv
+It also measures layers the way a trace sees them: for every gate/up dispatch
+followed directly by the down step (the down kernel, plus the combine kernel
+of the expert-major form), the span from the start of the gate/up to the end
+of the down step, reported as median, p10 and p90 per preceding kernel (the
+layer graph: after the down step; the routed layer: after the router).
+
+    python -m output_centric_expert_amd.trace_contexts <out>/prof_ktrace/bench_kernel_trace.csv
 """
 from __future__ import annotations
 
@@ -19,9 +25,10 @@ import json
 import statistics
 import sys
 
-KINDS = (("moe_gate_up_grouped_kernel", "gate_up_grouped"), ("moe_gate_up_kernel", "gate_up"),
+KINDS = (("moe_gate_up_grouped_kernel", "gate_up"), ("moe_gate_up_kernel", "gate_up"),
          ("moe_down_rows_kernel", "down"), ("moe_down_staged_kernel", "down"), ("moe_down_kernel", "down"),
-         ("moe_down_grouped_kernel", "down"), ("moe_route_kernel", "route"))
+         ("moe_down_expert_kernel", "down"), ("moe_down_combine_kernel", "combine"),
+         ("moe_route_kernel", "route"))
 
 
 def kind(name: str):
@@ -31,7 +38,7 @@ def kind(name: str):
     return None
 
 
-def contexts(path: str) -> dict:
+def read_rows(path: str):
     rows = []
     with open(path) as fh:
         for r in csv.DictReader(fh):
@@ -39,6 +46,34 @@ def contexts(path: str) -> dict:
             if k is not None:
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), k))
     rows.sort()
+    return rows
+
+
+def percentile(v, q):
+    v = sorted(v)
+    x = q * (len(v) - 1)
+    lo = int(x)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
+def layer_spans(rows) -> dict:
+    spans = collections.defaultdict(list)
+    for n, (start, _, k) in enumerate(rows):
+        if k != "gate_up" or n + 1 >= len(rows) or rows[n + 1][2] != "down":
+            continue
+        end = rows[n + 1][1]
+        if n + 2 < len(rows) and rows[n + 2][2] == "combine":
+            end = rows[n + 2][1]
+        prev = rows[n - 1][2] if n > 0 else None
+        spans["after " + ("the down step" if prev in ("down", "combine") else str(prev))].append(end - start)
+    return {ctx: {"layers": len(v), "median_ns": round(statistics.median(v), 1),
+                  "p10_ns": round(percentile(v, 0.1), 1), "p90_ns": round(percentile(v, 0.9), 1)}
+            for ctx, v in sorted(spans.items())}
+
+
+def contexts(path: str) -> dict:
+    rows = read_rows(path)
     per = collections.defaultdict(list)
     prev = None
     for start, end, k in rows:
@@ -49,4 +84,5 @@ def contexts(path: str) -> dict:
 
 
 if __name__ == "__main__":
-    print(json.dumps(contexts(sys.argv[1]), indent=1))
+    print(json.dumps({"kernels": contexts(sys.argv[1]), "layer_spans": layer_spans(read_rows(sys.argv[1]))},
+                     indent=1))
