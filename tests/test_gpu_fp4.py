@@ -252,5 +252,12 @@ def test_fp4_expert_major_down(shape):
                                       partials=y)
             torch.cuda.synchronize()
             assert torch.equal(out2, out)
+            # bf16 intermediate (the B operand is the bf16 value itself): close to the per-output
+            # kernel on the same intermediate
+            o16 = run(L, inter_dtype=torch.bfloat16)
+            md.moed_set_tuning("dn_group=0")
+            p16 = run(L, inter_dtype=torch.bfloat16)
+            rms = float(np.sqrt(np.mean(ref ** 2)))
+            assert float((o16 - p16).abs().max()) <= 1e-4 * rms
         finally:
             md.moed_set_tuning(None)
