@@ -19,9 +19,16 @@
 // SiLU(g) * u into the chunk-interleaved intermediate. There is no gather of
 // activations and no per-expert buffer: the slot list is an index list in LDS.
 //
+// Experts with only a few slots (at most row_slots) take a row path instead:
+// whole rows per wavefront with the per-slot kernel's contiguous loads, each
+// row applied to all of the expert's slots (their x staged in LDS). A 16-row
+// MFMA tile keeps only 128 bytes of each row in flight per group; a whole-row
+// wavefront keeps the full 2*H bytes.
+//
 // MFMA lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies A row l%16 and
 // B column l%16, both for k = 8*(l/16) .. +7, and receives D rows
 // 4*(l/16) .. +3 of column l%16.
+#include "gate_up_body.h"
 #include "grouped_common.h"
 
 namespace moed {
@@ -202,9 +209,92 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
     }
 }
 
+// Row path, for experts with few slots (at most kRowSlots, and their x rows fit
+// in the LDS of the x tiles): the slots' x rows are staged once in LDS and
+// each wavefront streams whole gate and up rows, one neuron at a time, with
+// the per-slot kernel's load pattern (16-byte chunk c of a row on lane c % 64,
+// U chunks per lane per pass) and its arithmetic for every slot, so that each
+// row is read once for all the expert's slots and each output is the float
+// the per-slot kernel computes. x of slot s is kept piece-major in LDS
+// (16-byte unit (s*NX + t)*nch + c holds piece t of chunk c) so the lanes'
+// reads are contiguous.
+constexpr int kRowSlots = 4;
+
+template <int U, bool A_BF16, bool FP4>
+__device__ __forceinline__ void rowwise_neurons(const GateUpArgs& p, int e, int n_first, int n_count,
+                                                const int* slots, int count, const u32x4* xs16, int lane)
+{
+    constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
+    const int H = p.H;
+    const int I = p.I;
+    const int nch = FP4 ? H / 32 : H / 16;
+    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
+    for (int n = 0; n < n_count; ++n) {
+        const int i = n_first + n;
+        const size_t row = (size_t)e * (size_t)I + (size_t)i;
+        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
+        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
+        const uint8_t* gsc = p.wg_s + row * (size_t)(H / 32);
+        const uint8_t* usc = p.wu_s + row * (size_t)(H / 32);
+        float g[kRowSlots], u[kRowSlots];
+#pragma unroll
+        for (int sl = 0; sl < kRowSlots; ++sl) {
+            g[sl] = 0.0f;
+            u[sl] = 0.0f;
+        }
+        for (int base = 0; base < nch; base += kWave * U) {
+            u32x4 wg[U], wu[U];
+            uint32_t sg[U], su[U];
+            float live[U];
+            int cc[U];
+#pragma unroll
+            for (int m = 0; m < U; ++m) {
+                const int c = base + lane + kWave * m;
+                cc[m] = c < nch ? c : nch - 1;
+                wg[m] = gq[cc[m]];
+                wu[m] = uq[cc[m]];
+                sg[m] = gsc[FP4 ? cc[m] : cc[m] >> 1];
+                su[m] = usc[FP4 ? cc[m] : cc[m] >> 1];
+                live[m] = c < nch ? 1.0f : 0.0f;
+            }
+#pragma unroll
+            for (int sl = 0; sl < kRowSlots; ++sl) {
+                if (sl < count) {                 // wave-uniform
+#pragma unroll
+                    for (int m = 0; m < U; ++m) {
+                        u32x4 xv[NX];
+#pragma unroll
+                        for (int t = 0; t < NX; ++t)
+                            xv[t] = xs16[(size_t)(sl * NX + t) * nch + cc[m]];
+                        const float pg = gu_chunk_dot<FP4, true, NX>(wg[m], xv);
+                        const float pu = gu_chunk_dot<FP4, true, NX>(wu[m], xv);
+                        g[sl] = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g[sl]);
+                        u[sl] = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u[sl]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < kRowSlots; ++sl) {
+            if (sl < count) {
+                const float gt = wave_sum(g[sl]);
+                const float ut = wave_sum(u[sl]);
+                if (lane == 0) {
+                    const float v = swiglu(gt, ut);
+                    const size_t idx = inter_index<A_BF16>(slots[sl], i, I);
+                    if constexpr (A_BF16)
+                        static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
+                    else
+                        static_cast<float*>(p.a)[idx] = v;
+                }
+            }
+        }
+    }
+}
+
 template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
-moe_gate_up_grouped_kernel(GateUpArgs p)
+moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u)
 {
     extern __shared__ int slots[];               // B*k entries
     __shared__ int wave_cnt[kGroupWaves];
@@ -242,6 +332,30 @@ moe_gate_up_grouped_kernel(GateUpArgs p)
     u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list
     const int n0 = n_block + 16 * w;              // this wavefront's 16 neurons
     const bool store = n0 < I;                    // wavefronts past I still take part in the barriers
+
+    if (count <= row_slots) {                     // workgroup-uniform: the row path
+        constexpr int NX = FP4 ? 4 : 2;
+        const int nch = FP4 ? H / 32 : H / 16;
+        const int units = count * NX * nch;
+        for (int v = threadIdx.x; v < units; v += blockDim.x) {
+            const int sl = v / (NX * nch);
+            const int t = (v % (NX * nch)) / nch;
+            const int c = v % nch;
+            const u32x4* xrow = reinterpret_cast<const u32x4*>(p.x + (size_t)(slots[sl] / p.k) * (size_t)H);
+            xs[v] = xrow[NX * c + t];
+        }
+        __syncthreads();
+        if (!store)
+            return;                               // after the only barrier
+        const int n_count = I - n0 < 16 ? I - n0 : 16;
+        if (row_u == 1)
+            rowwise_neurons<1, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
+        else if (row_u == 2)
+            rowwise_neurons<2, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
+        else if constexpr (!FP4)
+            rowwise_neurons<4, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
+        return;
+    }
 
     const int kb = lane / 16;                     // which quarter of a k group
     const int col = lane % 16;                    // A row (neuron) / B column (slot)
@@ -285,18 +399,30 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const dim3 grid((unsigned)((long)p.E * nblk));
     const dim3 block(kGroupWaves * kWave);
     const size_t lds = gate_up_grouped_lds(p.B, p.k);
-    (void)t;                                      // rows are re-read per pass: cached loads
     const bool fp4 = p.wfmt == kMXFP4;
+    // row path: experts with at most row_slots slots whose x rows fit in the
+    // x-tile space (2 * kTiles * kXUnitsPerTile units of 16 bytes)
+    const int nch = fp4 ? p.H / 32 : p.H / 16;
+    const int nx = fp4 ? 4 : 2;
+    int row_slots = t.gu_rowslots < kRowSlots ? t.gu_rowslots : kRowSlots;
+    while (row_slots > 0 && (long)row_slots * nx * nch > 2L * kTiles * kXUnitsPerTile)
+        --row_slots;
+    // chunks per lane per pass: 1, 2 or 4 (longer rows take several passes; the
+    // chunks still enter each lane's sums in increasing order, as in the
+    // per-slot kernel)
+    int row_u = 1;
+    while (row_u < (fp4 ? 2 : 4) && row_u * kWave < nch)
+        row_u *= 2;
     if (fp4) {
         if (a_bf16)
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p);
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p, row_slots, row_u);
         else
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p);
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p, row_slots, row_u);
     } else {
         if (a_bf16)
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p);
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p, row_slots, row_u);
         else
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p);
+            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p, row_slots, row_u);
     }
     return hipGetLastError();
 }

@@ -18,6 +18,8 @@ struct Tuning {
                         // (each routed row decoded once per 64 slots); 2 = expert-major once B*k >= 2E
     int dn_tiles = 0;   // expert-major down: 16-slot tiles per pass over a row (1..4; 0 = as many
                         // as fit in 64 KiB of LDS)
+    int gu_rowslots = 2; // expert-grouped gate/up: experts with at most this many slots (up to 4) take
+                         // the row path (whole rows per wavefront, x of the slots in LDS)
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
@@ -25,7 +27,8 @@ struct Tuning {
                         // except in the down kernel once B*k >= E (tokens then share rows)
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
-                        // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once 2*B*k >= 3E
+                        // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once
+                        // B*k*H >= 2458*E (about 1.2 slots per expert at H = 2048)
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
     int dn_rows = 0;    // down (staged): outputs per wavefront, 1, 2 or 4; 0 = by batch (4 once
                         // B*k >= E, 2 for B >= 2, 1 for B = 1)

@@ -53,23 +53,24 @@ moed::Tuning pick(int B, int H, int I)
     return t;
 }
 
-// Expert-grouped gate/up pays off once there are about 1.5 or more slots per
-// expert on average (each routed row then serves several tokens; measured
-// crossovers at 1.0-1.5 slots per expert for E = 128 and 256); its slot list
-// must fit in 64 KiB of LDS.
-bool use_grouped(const moed::Tuning& t, int B, int E, int k, int wfmt)
+// Expert-grouped gate/up pays off once tokens share experts: measured
+// crossovers (uniform routing, E = 128 and 256, k = 8) at about 1.2 slots per
+// expert for H = 2048, 0.6 for H = 4096 and below 0.5 for H = 7168 -- longer
+// rows amortise the workgroup's fixed costs sooner -- hence the rule
+// B*k*H >= 2458*E. Its slot list must fit in 64 KiB of LDS.
+bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel
     if (moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
-    return 2L * B * k >= 3L * E;
+    return (long long)B * k * H >= 2458LL * E;
 }
 
 hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tuning& t, hipStream_t s)
 {
-    if (use_grouped(t, p.B, p.E, p.k, p.wfmt))
+    if (use_grouped(t, p.B, p.E, p.k, p.H, p.wfmt))
         return moed::launch_gate_up_grouped(p, a_bf16, t, s);
     return moed::launch_gate_up(p, a_bf16, t, s);
 }
@@ -375,6 +376,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
+        else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;

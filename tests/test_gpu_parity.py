@@ -170,7 +170,7 @@ def test_workload_sampled_parity(name):
     # batch = concatenation of single-token calls, bit for bit, on each kernel pair
     # (the per-slot/per-output and the grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1"):
+    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1,gu_rowslots=0"):
         md.moed_set_tuning(spec)
         try:
             full = run(L, torch.float32)
@@ -579,3 +579,38 @@ def test_check_mode(monkeypatch):
     finally:
         L.wd_s[e, 0, 0] = saved
     torch.cuda.synchronize()
+
+
+ROW_PATH = [
+    (24, 16, 2, 2080, 64),    # ~3 slots per expert (some above 4: MFMA path); a ragged second chunk per lane
+    (12, 8, 3, 4096, 128),    # four chunks per lane per pass
+    (40, 6, 1, 96, 160),      # short rows (6 chunks), more than 4 slots on most experts
+    (16, 64, 8, 7168, 64),    # 7168-value rows: x of at most 2 slots fits, several passes per row
+]
+
+
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", ROW_PATH, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_grouped_row_path(shape, wformat):
+    """Experts with at most 4 slots in the expert-grouped gate/up take the row path: the same
+    float for every output as the per-slot kernel; the rest (MFMA path) within tolerance."""
+    B, E, k, H, I = shape
+    L = synth.make_layer(synth.LayerShape("rp", B, E, k, H, I), seed=sum(shape) + 9, device="cuda", wformat=wformat)
+    x, ids, _ = md.layer_device_inputs(L)
+    md.moed_set_tuning("gu_group=0")
+    try:
+        a_slot = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
+        md.moed_set_tuning("gu_group=1,gu_rowslots=4")
+        a_row = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
+        torch.cuda.synchronize()
+    finally:
+        md.moed_set_tuning(None)
+    counts = np.bincount(L.ids.ravel(), minlength=E)
+    slot_x = 2 * H if wformat == "mxfp8" else 2 * H    # bf16 x row bytes per slot
+    fits = max(0, min(4, 32768 // slot_x))
+    light = counts[L.ids] <= fits                       # [B, k]: slot's expert takes the row path
+    light_t = torch.from_numpy(light).cuda()
+    assert torch.equal(a_row[light_t], a_slot[light_t])
+    rms = float(a_slot.double().pow(2).mean().sqrt())
+    assert float((a_row - a_slot).abs().max()) <= 1e-5 * rms
+    assert light.any()
