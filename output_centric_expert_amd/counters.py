@@ -40,9 +40,10 @@ def pick(per: dict, needle: str):
     return sum(vals) / len(vals), len(vals)
 
 
-# The kernels one call of each layer step launches: the per-slot or the expert-grouped gate/up;
+# The kernels one call of each layer step launches: the per-slot or the expert-grouped gate/up
+# (128-byte tile slices or wide loads);
 # the per-output down (staged or direct), or the expert-major down plus its combine.
-STEP_KERNELS = {"gate_up": ("moe_gate_up_kernel", "moe_gate_up_grouped_kernel"),
+STEP_KERNELS = {"gate_up": ("moe_gate_up_kernel", "moe_gate_up_grouped_kernel", "moe_gate_up_grouped_wide_kernel"),
                 "down": ("moe_down_kernel", "moe_down_staged_kernel", "moe_down_rows_kernel",
                          "moe_down_expert_kernel", "moe_down_combine_kernel")}
 

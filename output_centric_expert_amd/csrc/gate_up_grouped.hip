@@ -28,6 +28,8 @@
 // MFMA lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies A row l%16 and
 // B column l%16, both for k = 8*(l/16) .. +7, and receives D rows
 // 4*(l/16) .. +3 of column l%16.
+#include <type_traits>
+
 #include "gate_up_body.h"
 #include "grouped_common.h"
 
@@ -52,6 +54,7 @@ struct GroupedRow {
 // each) and the MFMA reads (16 lanes, one per slot) free of LDS bank
 // conflicts.
 constexpr int kXUnitsPerTile = 16 * 16;          // 16-byte units per tile and group
+constexpr int kWideUnitsPerWave = 2 * 16 * 16;   // wide loads: 16-byte units of one step, per wavefront
 
 struct GroupW {
     u32x4 g0, g1, u0, u1;                        // this lane's codes of the group (g1/u1: MXFP8 only)
@@ -76,6 +79,89 @@ __device__ __forceinline__ GroupW load_group_w(const GroupedRow& r, int g)
     w.gsc = ue8m0_to_f32(r.gs[4 * g + r.kb]);
     w.usc = ue8m0_to_f32(r.us[4 * g + r.kb]);
     return w;
+}
+
+// The four MFMA steps of one 128-code group for NTL tiles: decode this lane's
+// codes of the group (wc) and multiply them with the slots' x pieces in LDS
+// (xb, the unit layout above).
+template <int NTL, bool FP4>
+__device__ __forceinline__ void group_mfma(const GroupW& wc, const u32x4* xb, const GroupedRow& r,
+                                           f32x4 (&dg)[NTL], f32x4 (&du)[NTL])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        bf16x8 ag, au;
+        if constexpr (FP4) {                      // dword q = codes 8q .. 8q+7
+            ag = decode8_scaled_fp4(wc.g0[q], wc.gsc);
+            au = decode8_scaled_fp4(wc.u0[q], wc.usc);
+        } else {
+            const u32x4 gsrc = q < 2 ? wc.g0 : wc.g1;
+            const u32x4 usrc = q < 2 ? wc.u0 : wc.u1;
+            const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
+            const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
+            ag = decode8_scaled(cgq, wc.gsc);
+            au = decode8_scaled(cuq, wc.usc);
+        }
+        const int c = 4 * r.kb + q;
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            const bf16x8 bx = __builtin_bit_cast(bf16x8, xb[(tt * 16 + r.col) * 16 + (c ^ r.col)]);
+            dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
+            du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
+        }
+    }
+}
+
+// MX blocks after the last whole 128-code group (H/32 not a multiple of 4):
+// x straight from global memory, plain k order.
+template <int NTL, bool FP4>
+__device__ __forceinline__ void leftover_blocks(const GroupedRow& r, const uint16_t* const (&xr)[NTL],
+                                                f32x4 (&dg)[NTL], f32x4 (&du)[NTL])
+{
+    for (int st = 4 * (r.nsteps / 4); st < r.nsteps; ++st) {
+        const int k0 = st * 32 + 8 * r.kb;
+        bf16x8 ag, au;
+        if constexpr (FP4) {
+            const uint32_t cg = *reinterpret_cast<const uint32_t*>(r.gq + k0 / 2);
+            const uint32_t cu = *reinterpret_cast<const uint32_t*>(r.uq + k0 / 2);
+            ag = decode8_scaled_fp4(cg, ue8m0_to_f32(r.gs[st]));
+            au = decode8_scaled_fp4(cu, ue8m0_to_f32(r.us[st]));
+        } else {
+            const u32x2 cg = *reinterpret_cast<const u32x2*>(r.gq + k0);
+            const u32x2 cu = *reinterpret_cast<const u32x2*>(r.uq + k0);
+            ag = decode8_scaled(cg, ue8m0_to_f32(r.gs[st]));
+            au = decode8_scaled(cu, ue8m0_to_f32(r.us[st]));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr[tt] + k0));
+            dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
+            du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
+        }
+    }
+}
+
+// SiLU(g) * u of the tiles' real slots: lane holds D rows 4*kb .. +3 (neurons)
+// of column col of each tile.
+template <int NTL, bool A_BF16>
+__device__ __forceinline__ void store_tiles(const GateUpArgs& p, const GroupedRow& r, const int (&bj)[NTL],
+                                            int count, int t0, const f32x4 (&dg)[NTL], const f32x4 (&du)[NTL])
+{
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        if ((t0 + tt) * 16 + r.col < count) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = r.n0 + 4 * r.kb + q;
+                const float v = swiglu(dg[tt][q], du[tt][q]);
+                const size_t idx = inter_index<A_BF16>(bj[tt], i, p.I);
+                if constexpr (A_BF16)
+                    static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
+                else
+                    static_cast<float*>(p.a)[idx] = v;
+            }
+        }
+    }
 }
 
 // One pass over the rows for NTL tiles of 16 slots (tiles t0 .. t0+NTL-1),
@@ -137,28 +223,7 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
                 xreg[tt] = *reinterpret_cast<const u32x4*>(xl[tt] + (g + 1) * 128 + 8 * lc);
             wn = load_group_w<FP4>(r, g + 1);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf16x8 ag, au;
-            if constexpr (FP4) {                  // dword q = codes 8q .. 8q+7
-                ag = decode8_scaled_fp4(wc.g0[q], wc.gsc);
-                au = decode8_scaled_fp4(wc.u0[q], wc.usc);
-            } else {
-                const u32x4 gsrc = q < 2 ? wc.g0 : wc.g1;
-                const u32x4 usrc = q < 2 ? wc.u0 : wc.u1;
-                const u32x2 cgq = (q & 1) ? u32x2{gsrc.z, gsrc.w} : u32x2{gsrc.x, gsrc.y};
-                const u32x2 cuq = (q & 1) ? u32x2{usrc.z, usrc.w} : u32x2{usrc.x, usrc.y};
-                ag = decode8_scaled(cgq, wc.gsc);
-                au = decode8_scaled(cuq, wc.usc);
-            }
-            const int c = 4 * r.kb + q;
-#pragma unroll
-            for (int tt = 0; tt < NTL; ++tt) {
-                const bf16x8 bx = __builtin_bit_cast(bf16x8, xb[(tt * 16 + r.col) * 16 + (c ^ r.col)]);
-                dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
-                du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
-            }
-        }
+        group_mfma<NTL, FP4>(wc, xb, r, dg, du);
         if (more) {
             u32x4* xn = xs + ((g + 1) & 1) * kBuf;
 #pragma unroll
@@ -168,45 +233,191 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
         __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
         wc = wn;
     }
-    for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
-        const int k0 = st * 32 + 8 * r.kb;
-        bf16x8 ag, au;
-        if constexpr (FP4) {
-            const uint32_t cg = *reinterpret_cast<const uint32_t*>(r.gq + k0 / 2);
-            const uint32_t cu = *reinterpret_cast<const uint32_t*>(r.uq + k0 / 2);
-            ag = decode8_scaled_fp4(cg, ue8m0_to_f32(r.gs[st]));
-            au = decode8_scaled_fp4(cu, ue8m0_to_f32(r.us[st]));
-        } else {
-            const u32x2 cg = *reinterpret_cast<const u32x2*>(r.gq + k0);
-            const u32x2 cu = *reinterpret_cast<const u32x2*>(r.uq + k0);
-            ag = decode8_scaled(cg, ue8m0_to_f32(r.gs[st]));
-            au = decode8_scaled(cu, ue8m0_to_f32(r.us[st]));
-        }
+    leftover_blocks<NTL, FP4>(r, xr, dg, du);
+    if (store)
+        store_tiles<NTL, A_BF16>(p, r, bj, count, t0, dg, du);
+}
+
+// Wide weight loads (the default MFMA path). The 128-byte row slices of a
+// 16-row tile, one per lane group, cap the weight stream near 4.8 TB/s on
+// MI355X; runs of 256 bytes per row reach about 6 TB/s. So the wavefront reads
+// its 16 gate and 16 up rows in steps of 256 bytes per row (two 128-code
+// groups of MXFP8, four of MXFP4): load i of lane L takes the 16-byte piece
+// L % 16 of row L / 16 + 4i, and each load instruction covers four whole
+// 256-byte runs. A step is moved into the MFMA operand layout through a
+// wavefront-private LDS region of 2 x 16 rows x 16 pieces (piece b of row n at
+// unit 16n + (b ^ n), which keeps both the writes and the operand reads free
+// of bank conflicts), and lane (col, kb) reads for group h of the step the
+// pieces holding MX block 4h + kb of row col: the codes the 128-byte slices
+// give it, in the same order, so the results are the same floats.
+template <bool FP4>
+struct StepW {
+    static constexpr int kGroups = FP4 ? 4 : 2;  // 128-code groups per 256-byte step
+    u32x4 g[4], u[4];                            // pieces of rows L/16 + 4i
+    uint32_t gs[kGroups], us[kGroups];           // scale bytes of this lane's row and block, per group
+};
+
+template <bool FP4>
+__device__ __forceinline__ StepW<FP4> load_step(const uint8_t* gq0, const uint8_t* uq0, size_t rstride,
+                                                const GroupedRow& r, int step, int lane)
+{
+    StepW<FP4> w;
+    const size_t off = (size_t)step * 256 + 16 * (size_t)(lane % 16);
 #pragma unroll
-        for (int tt = 0; tt < NTL; ++tt) {
-            const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr[tt] + k0));
-            dg[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bx, dg[tt], 0, 0, 0);
-            du[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, bx, du[tt], 0, 0, 0);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const size_t o = (size_t)(lane / 16 + 4 * i) * rstride + off;
+        w.g[i] = *reinterpret_cast<const u32x4*>(gq0 + o);
+        w.u[i] = *reinterpret_cast<const u32x4*>(uq0 + o);
     }
-    if (!store)
-        return;
-    // lane holds D rows 4*kb .. +3 (neurons) of column col of each tile
+#pragma unroll
+    for (int h = 0; h < StepW<FP4>::kGroups; ++h) {
+        const int blk = 4 * (step * StepW<FP4>::kGroups + h) + r.kb;
+        w.gs[h] = r.gs[blk];
+        w.us[h] = r.us[blk];
+    }
+    return w;
+}
+
+template <bool FP4>
+__device__ __forceinline__ void stage_step(const StepW<FP4>& w, u32x4* tb, int lane)
+{
+    const int b = lane % 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = lane / 16 + 4 * i;
+        tb[n * 16 + (b ^ n)] = w.g[i];
+        tb[256 + n * 16 + (b ^ n)] = w.u[i];
+    }
+}
+
+template <bool FP4>
+__device__ __forceinline__ GroupW staged_group(const u32x4* tb, const GroupedRow& r, int h, float gsc, float usc)
+{
+    GroupW w;
+    const u32x4* row = tb + r.col * 16;
+    if constexpr (FP4) {                         // block 4h + kb = piece 4h + kb
+        const int q = (4 * h + r.kb) ^ r.col;
+        w.g0 = row[q];
+        w.u0 = row[256 + q];
+        w.g1 = w.g0;
+        w.u1 = w.u0;
+    } else {                                     // block 4h + kb = pieces 8h + 2kb, +1
+        const int q0 = (8 * h + 2 * r.kb) ^ r.col;
+        const int q1 = (8 * h + 2 * r.kb + 1) ^ r.col;
+        w.g0 = row[q0];
+        w.g1 = row[q1];
+        w.u0 = row[256 + q0];
+        w.u1 = row[256 + q1];
+    }
+    w.gsc = gsc;
+    w.usc = usc;
+    return w;
+}
+
+// grouped_pass with the wide weight loads. One step of weights is in flight
+// ahead (issued during the step's second-to-last group), and the slots' x two
+// groups ahead in two register sets (group g's set is refilled with x of group
+// g+2 once it is in LDS), so neither the L2 latency of x nor that of the rows
+// is paid once per group. Each group's wait for its x never waits for weight
+// loads issued after it. Groups after the last whole step take the 128-byte
+// slices; leftover blocks as in grouped_pass. tb = this wavefront's LDS
+// region (512 units).
+template <int NTL, bool A_BF16, bool FP4>
+__device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const GroupedRow& r, const uint8_t* gq0,
+                                                  const uint8_t* uq0, size_t rstride, const int* slots, int count,
+                                                  int t0, u32x4* xs, u32x4* tb, bool store)
+{
+    constexpr int GPS = StepW<FP4>::kGroups;
+    const int H = p.H;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int lcol = tid / 16;
+    const int lc = tid % 16;
+    const uint16_t* xl[NTL];
+    int bj[NTL];
+    const uint16_t* xr[NTL];
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
-        if ((t0 + tt) * 16 + r.col < count) {
+        const int sl = (t0 + tt) * 16 + lcol;
+        xl[tt] = p.x + (size_t)(slots[sl < count ? sl : count - 1] / p.k) * (size_t)H;
+        const int si = (t0 + tt) * 16 + r.col;
+        bj[tt] = slots[si < count ? si : count - 1];
+        xr[tt] = p.x + (size_t)(bj[tt] / p.k) * (size_t)H;
+    }
+    f32x4 dg[NTL], du[NTL];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = r.n0 + 4 * r.kb + q;
-                const float v = swiglu(dg[tt][q], du[tt][q]);
-                const size_t idx = inter_index<A_BF16>(bj[tt], i, p.I);
-                if constexpr (A_BF16)
-                    static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
-                else
-                    static_cast<float*>(p.a)[idx] = v;
-            }
+    for (int tt = 0; tt < NTL; ++tt) {
+        dg[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        du[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int ngroups = r.nsteps / 4;
+    const int nst = ngroups / GPS;                // whole 256-byte steps
+    constexpr int kBuf = NTL * kXUnitsPerTile;
+    u32x4 xq[2][NTL];                             // x of groups g+1 and g+2, by group parity
+    StepW<FP4> sw{};
+    auto load_x = [&](u32x4 (&dst)[NTL], int g) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            dst[tt] = *reinterpret_cast<const u32x4*>(xl[tt] + g * 128 + 8 * lc);
+    };
+    auto put_x = [&](const u32x4 (&src)[NTL], int g) {
+        u32x4* xn = xs + (g & 1) * kBuf;
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            xn[(tt * 16 + lcol) * 16 + (lc ^ lcol)] = src[tt];
+    };
+    if (ngroups > 0) {
+        load_x(xq[0], 0);
+        if (ngroups > 1)
+            load_x(xq[1], 1);
+        if (nst > 0)
+            sw = load_step<FP4>(gq0, uq0, rstride, r, 0, lane);
+        put_x(xq[0], 0);
+    }
+    __syncthreads();
+    // group g (parity P): x of g+2 into set P, the MFMAs on buffer g&1, x of
+    // g+1 (set 1-P) into the other buffer
+    auto group = [&](auto par, int g, const GroupW& wc) {
+        constexpr int P = decltype(par)::value;
+        if (g + 2 < ngroups)
+            load_x(xq[P], g + 2);
+        group_mfma<NTL, FP4>(wc, xs + (g & 1) * kBuf, r, dg, du);
+        if (g + 1 < ngroups)
+            put_x(xq[1 - P], g + 1);
+        __syncthreads();
+    };
+    for (int s = 0; s < nst; ++s) {
+        stage_step<FP4>(sw, tb, lane);
+        float gsc[GPS], usc[GPS];
+#pragma unroll
+        for (int h = 0; h < GPS; ++h) {
+            gsc[h] = ue8m0_to_f32(sw.gs[h]);
+            usc[h] = ue8m0_to_f32(sw.us[h]);
+        }
+        const int g0 = s * GPS;                   // even: the parity of group g0 + h is that of h
+        {
+            if (GPS == 2 && s + 1 < nst)          // MXFP8: next step during the first group
+                sw = load_step<FP4>(gq0, uq0, rstride, r, s + 1, lane);
+            group(std::integral_constant<int, 0>{}, g0, staged_group<FP4>(tb, r, 0, gsc[0], usc[0]));
+        }
+        {
+            group(std::integral_constant<int, 1>{}, g0 + 1, staged_group<FP4>(tb, r, 1, gsc[1], usc[1]));
+        }
+        if constexpr (GPS == 4) {                 // MXFP4: next step during the third group
+            if (s + 1 < nst)
+                sw = load_step<FP4>(gq0, uq0, rstride, r, s + 1, lane);
+            group(std::integral_constant<int, 0>{}, g0 + 2, staged_group<FP4>(tb, r, 2, gsc[2], usc[2]));
+            group(std::integral_constant<int, 1>{}, g0 + 3, staged_group<FP4>(tb, r, 3, gsc[3], usc[3]));
         }
     }
+    for (int g = nst * GPS; g < ngroups; g += 2) {   // groups after the last whole step (g even)
+        group(std::integral_constant<int, 0>{}, g, load_group_w<FP4>(r, g));
+        if (g + 1 < ngroups)
+            group(std::integral_constant<int, 1>{}, g + 1, load_group_w<FP4>(r, g + 1));
+    }
+    leftover_blocks<NTL, FP4>(r, xr, dg, du);
+    if (store)
+        store_tiles<NTL, A_BF16>(p, r, bj, count, t0, dg, du);
 }
 
 // Row path, for experts with few slots (at most kRowSlots, and their x rows fit
@@ -292,9 +503,8 @@ __device__ __forceinline__ void rowwise_neurons(const GateUpArgs& p, int e, int 
     }
 }
 
-template <bool A_BF16, bool FP4>
-__global__ void __launch_bounds__(kGroupWaves * kWave)
-moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u)
+template <bool A_BF16, bool FP4, bool WIDE>
+__device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int row_slots, int row_u)
 {
     extern __shared__ int slots[];               // B*k entries
     __shared__ int wave_cnt[kGroupWaves];
@@ -372,23 +582,80 @@ moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u)
     // Each pass covers up to kTiles tiles of 16 slots, so a row is decoded once
     // per 16*kTiles slots; the tile count of a pass is a template argument, so
     // the hot loop has no per-tile branches.
-    for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
-        const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
-        const GroupedRow r{gq, uq, gs, us, nsteps, n0, kb, col};
-        switch (nt) {
-        case 1: grouped_pass<1, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
-        case 2: grouped_pass<2, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
-        case 3: grouped_pass<3, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
-        default: grouped_pass<4, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+    const GroupedRow r{gq, uq, gs, us, nsteps, n0, kb, col};
+    if constexpr (WIDE) {
+        // the wavefront's first row (all 16 rows clamped to I-1 past I), its
+        // row stride, and its LDS region for the wide loads
+        const size_t wrow = (size_t)e * (size_t)I + (size_t)(store ? n0 : I - 1);
+        const size_t rstride = store ? row_bytes : 0;
+        const uint8_t* gq0 = p.wg_q + wrow * row_bytes;
+        const uint8_t* uq0 = p.wu_q + wrow * row_bytes;
+        u32x4* tb = xs + 2 * kTiles * kXUnitsPerTile + w * kWideUnitsPerWave;
+        for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
+            const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
+            switch (nt) {
+            case 1: grouped_pass_wide<1, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
+            case 2: grouped_pass_wide<2, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
+            case 3: grouped_pass_wide<3, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
+            default: grouped_pass_wide<4, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
+            }
+        }
+    } else {
+        for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
+            const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
+            switch (nt) {
+            case 1: grouped_pass<1, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+            case 2: grouped_pass<2, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+            case 3: grouped_pass<3, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+            default: grouped_pass<4, A_BF16, FP4>(p, r, slots, count, t0, xs, store); break;
+            }
         }
     }
 }
 
-size_t gate_up_grouped_lds(int B, int k)
+template <bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(kGroupWaves * kWave)
+moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u)
 {
-    // slot list (rounded up to 16 bytes), then two buffers of x tiles
+    gate_up_grouped_body<A_BF16, FP4, false>(p, row_slots, row_u);
+}
+
+// The wide loads need 8 KiB of LDS per wavefront, so two workgroups share a CU;
+// the register budget is set to match (two wavefronts per SIMD).
+template <bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(kGroupWaves * kWave, 2)
+moe_gate_up_grouped_wide_kernel(GateUpArgs p, int row_slots, int row_u)
+{
+    gate_up_grouped_body<A_BF16, FP4, true>(p, row_slots, row_u);
+}
+
+size_t gate_up_grouped_lds(int B, int k, bool wide)
+{
+    // slot list (rounded up to 16 bytes), two buffers of x tiles, and with the
+    // wide loads one 8 KiB region per wavefront
     const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
-    return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4);
+    return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) +
+           (wide ? (size_t)kGroupWaves * kWideUnitsPerWave * sizeof(u32x4) : 0);
+}
+
+template <bool A_BF16, bool FP4, bool WIDE>
+hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int row_slots,
+                          int row_u)
+{
+    if constexpr (WIDE) {
+        // allow dynamic LDS beyond the default 64 KiB, once per process: up to
+        // 64 KiB for the slot list and x tiles plus the 32 KiB of wide-load regions
+        static const hipError_t attr =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                65536 + kGroupWaves * kWideUnitsPerWave * (int)sizeof(u32x4));
+        if (attr != hipSuccess)
+            return attr;
+        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u);
+    } else {
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s)
@@ -398,7 +665,8 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
     const dim3 grid((unsigned)((long)p.E * nblk));
     const dim3 block(kGroupWaves * kWave);
-    const size_t lds = gate_up_grouped_lds(p.B, p.k);
+    const bool wide = t.gu_wide != 0;
+    const size_t lds = gate_up_grouped_lds(p.B, p.k, wide);
     const bool fp4 = p.wfmt == kMXFP4;
     // row path: experts with at most row_slots slots whose x rows fit in the
     // x-tile space (2 * kTiles * kXUnitsPerTile units of 16 bytes)
@@ -415,16 +683,16 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
         row_u *= 2;
     if (fp4) {
         if (a_bf16)
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, true>), grid, block, lds, s, p, row_slots, row_u);
-        else
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, true>), grid, block, lds, s, p, row_slots, row_u);
-    } else {
-        if (a_bf16)
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<true, false>), grid, block, lds, s, p, row_slots, row_u);
-        else
-            hipLaunchKernelGGL((moe_gate_up_grouped_kernel<false, false>), grid, block, lds, s, p, row_slots, row_u);
+            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, row_slots, row_u)
+                        : launch_grouped<true, true, false>(grid, block, lds, s, p, row_slots, row_u);
+        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, row_slots, row_u)
+                    : launch_grouped<false, true, false>(grid, block, lds, s, p, row_slots, row_u);
     }
-    return hipGetLastError();
+    if (a_bf16)
+        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, row_slots, row_u)
+                    : launch_grouped<true, false, false>(grid, block, lds, s, p, row_slots, row_u);
+    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, row_slots, row_u)
+                : launch_grouped<false, false, false>(grid, block, lds, s, p, row_slots, row_u);
 }
 
 }  // namespace moed

@@ -20,6 +20,8 @@ struct Tuning {
                         // as fit in 64 KiB of LDS)
     int gu_rowslots = 2; // expert-grouped gate/up: experts with at most this many slots (up to 4) take
                          // the row path (whole rows per wavefront, x of the slots in LDS)
+    int gu_wide = 1;    // expert-grouped gate/up, MFMA path: 1 = weight rows read in 256-byte runs per
+                        // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
@@ -68,7 +70,7 @@ struct DownArgs {
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
-size_t gate_up_grouped_lds(int B, int k);
+size_t gate_up_grouped_lds(int B, int k, bool wide);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -57,11 +57,12 @@ moed::Tuning pick(int B, int H, int I)
 // crossovers (uniform routing, E = 128 and 256, k = 8) at about 1.2 slots per
 // expert for H = 2048, 0.6 for H = 4096 and below 0.5 for H = 7168 -- longer
 // rows amortise the workgroup's fixed costs sooner -- hence the rule
-// B*k*H >= 2458*E. Its slot list must fit in 64 KiB of LDS.
+// B*k*H >= 2458*E. Its slot list must fit in 64 KiB of LDS with the x tiles
+// (the wide loads add 32 KiB, within the 160 KiB of a workgroup).
 bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel
-    if (moed::gate_up_grouped_lds(B, k) > 65536 || t.gu_group == 0)
+    if (moed::gate_up_grouped_lds(B, k, false) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
@@ -377,6 +378,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
         else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
+        else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
         else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;

@@ -144,6 +144,9 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"gu_rowslots=0") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_rowslots=4") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_rowslots=5") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_wide=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_wide=1") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_wide=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_rt=0") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_rt=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_order=2") == md.MOED_OK

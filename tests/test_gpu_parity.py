@@ -62,7 +62,7 @@ def run(L, out_dtype=torch.float32, inter_dtype=torch.float32, ids=None, w=None,
     return out
 
 
-def oracle_tokens(L, tokens, ids=None, w=None):
+def oracle_tokens(L, tokens, ids=None, w=None, wformat="mxfp8"):
     """Oracle output (and intermediate) for a subset of tokens, from the same weight bytes."""
     ids = L.ids if ids is None else np.asarray(ids, np.int32)
     w = L.w if w is None else np.asarray(w, np.float32)
@@ -75,7 +75,7 @@ def oracle_tokens(L, tokens, ids=None, w=None):
     pick = lambda t: t.index_select(0, idx).cpu()
     return oracle.moe_decode(np.ascontiguousarray(L.x[tokens]), np.ascontiguousarray(ids_c.astype(np.int32)),
                              np.ascontiguousarray(w[tokens]), pick(L.wg_q), pick(L.wg_s), pick(L.wu_q),
-                             pick(L.wu_s), pick(L.wd_q), pick(L.wd_s), return_inter=True)
+                             pick(L.wu_s), pick(L.wd_q), pick(L.wd_s), return_inter=True, wformat=wformat)
 
 
 def check_f32(gpu_out, ref, label, tol=TOL):
@@ -614,3 +614,45 @@ def test_grouped_row_path(shape, wformat):
     rms = float(a_slot.double().pow(2).mean().sqrt())
     assert float((a_row - a_slot).abs().max()) <= 1e-5 * rms
     assert light.any()
+
+
+WIDE = [
+    (40, 3, 2, 640, 160),     # ~27 slots per expert (2 tiles); 5 groups: whole steps + 1 group; waves past I
+    (72, 2, 2, 640, 96),      # 72 slots per expert: a 4-tile pass, then a 1-tile pass
+    (24, 6, 4, 2080, 64),     # 65 MX blocks: 16 groups and a leftover block
+    (20, 4, 3, 448, 128),     # 3 groups and 2 leftover blocks: no whole MXFP4 step
+    (16, 8, 8, 7168, 64),     # 56 groups of 7168-value rows
+]
+
+
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_grouped_wide_loads(shape, wformat):
+    """The MFMA path's wide weight loads (256-byte runs per row, moved to the operand layout
+    through LDS) feed every MFMA the codes the 128-byte tile slices do, in the same order:
+    the intermediate is the same floats (float32 and bf16), and the layer within tolerance of
+    the oracle."""
+    B, E, k, H, I = shape
+    L = synth.make_layer(synth.LayerShape("wide", B, E, k, H, I), seed=sum(shape) + 21, device="cuda",
+                         wformat=wformat)
+    x, ids, _ = md.layer_device_inputs(L)
+    got = {}
+    try:
+        for wide in (0, 1):
+            md.moed_set_tuning(f"gu_group=1,gu_rowslots=0,gu_wide={wide}")
+            for dt in (torch.float32, torch.bfloat16):
+                got[wide, dt] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
+                                                      inter_dtype=dt, wformat=wformat)
+            torch.cuda.synchronize()
+        say(f"wide loads {shape} {wformat}: comparing")
+        for dt in (torch.float32, torch.bfloat16):
+            assert torch.equal(got[1, dt], got[0, dt]), f"{shape} {wformat} {dt}"
+        md.moed_set_tuning("gu_group=1,gu_rowslots=0,gu_wide=1")
+        ref, _ = oracle_tokens(L, [0, B - 1], wformat=wformat)
+        xd, idd, wd = md.layer_device_inputs(L)
+        out = md.moe_decode(xd, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                            out_dtype=torch.float32, wformat=wformat)
+        torch.cuda.synchronize()
+        check_f32(out[[0, B - 1]], ref, f"wide {shape} {wformat}")
+    finally:
+        md.moed_set_tuning(None)
