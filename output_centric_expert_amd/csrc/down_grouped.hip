@@ -26,6 +26,8 @@
 //
 // The per-slot partials are the price of reading each routed row once: they
 // take B*k*H*4 bytes of workspace and a second, small HBM-bound launch.
+#include <type_traits>
+
 #include "grouped_common.h"
 
 namespace moed {
@@ -134,11 +136,10 @@ __device__ __forceinline__ bf16x8 dn_decode(const DnGroupW& w, int q)
 // leftover blocks (I/32 not a multiple of 4) take a from global memory in
 // plain k order. Each B operand read from LDS serves the RT row tiles.
 //
-// Loads in flight: the weight codes of a group are requested two groups
-// ahead (two register sets, used alternately, so the loop carries no register
-// copies that would wait for them); the slots' a for the next group is
-// requested at the start of a group and split into its LDS buffer after the
-// group's MFMAs.
+// Loads in flight: the weight codes and the slots' a of a group are both
+// requested two groups ahead (two register sets each, used alternately, so
+// the loop carries no register copies that would wait for them); a group's a
+// is split into its LDS buffer after the previous group's MFMAs.
 template <int NTL, int RT, bool A_BF16, bool FP4>
 __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<RT>& r, const int* slots,
                                                  int count, int t0, u32x4* xs, bool store, int h0, float* y)
@@ -165,12 +166,17 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
         for (int tt = 0; tt < NTL; ++tt)
             d[t][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int ngroups = r.nsteps / 4;
-    ARaw<A_BF16> raw[NTL];
-    auto put_a = [&](u32x4* buf) {
+    ARaw<A_BF16> raw[2][NTL];                     // a of groups g+1 and g+2, by group parity
+    auto load_a = [&](ARaw<A_BF16> (&dst)[NTL], int g) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            dst[tt] = load_a8<A_BF16>(p.a, ls[tt], g * 128 + 8 * lc, I);
+    };
+    auto put_a = [&](const ARaw<A_BF16> (&src)[NTL], u32x4* buf) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt) {
             u32x4 hi, lo;
-            split_a8<A_BF16>(raw[tt], hi, lo);
+            split_a8<A_BF16>(src[tt], hi, lo);
             const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
             buf[u] = hi;
             if constexpr (!A_BF16)
@@ -179,22 +185,21 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
     };
     DnGroupW wA[RT], wB[RT];
     if (ngroups > 0) {
-#pragma unroll
-        for (int tt = 0; tt < NTL; ++tt)
-            raw[tt] = load_a8<A_BF16>(p.a, ls[tt], 8 * lc, I);
+        load_a(raw[0], 0);
+        if (ngroups > 1)
+            load_a(raw[1], 1);
         load_dn_w<FP4>(r, 0, wA);
         load_dn_w<FP4>(r, ngroups > 1 ? 1 : 0, wB);
-        put_a(xs);
+        put_a(raw[0], xs);
     }
     __syncthreads();
-    auto group = [&](int g, DnGroupW (&w)[RT]) {
+    // group g (parity P): a of g+2 into set P, the MFMAs on buffer g&1, a of
+    // g+1 (set 1-P) split into the other buffer
+    auto group = [&](auto par, int g, DnGroupW (&w)[RT]) {
+        constexpr int P = decltype(par)::value;
         const u32x4* xb = xs + (g & 1) * kBuf;
-        const bool more = g + 1 < ngroups;
-        if (more) {
-#pragma unroll
-            for (int tt = 0; tt < NTL; ++tt)
-                raw[tt] = load_a8<A_BF16>(p.a, ls[tt], (g + 1) * 128 + 8 * lc, I);
-        }
+        if (g + 2 < ngroups)
+            load_a(raw[P], g + 2);
         bf16x8 aw[RT][4];
 #pragma unroll
         for (int t = 0; t < RT; ++t)
@@ -220,14 +225,14 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
                 }
             }
         }
-        if (more)
-            put_a(xs + ((g + 1) & 1) * kBuf);
+        if (g + 1 < ngroups)
+            put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
         __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
     };
     for (int g = 0; g < ngroups; g += 2) {
-        group(g, wA);
+        group(std::integral_constant<int, 0>{}, g, wA);
         if (g + 1 < ngroups)
-            group(g + 1, wB);
+            group(std::integral_constant<int, 1>{}, g + 1, wB);
     }
     for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
         const int k0 = st * 32 + 8 * r.kb;
