@@ -291,7 +291,7 @@ moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
     const int* ids = p.ids;
-    const int count = compact_slots(nslots, slots, wave_cnt, [&](int t) { return ids[t] == e; });
+    const int count = compact_slots(nslots, ids, slots, wave_cnt, [&](int v) { return v == e; });
     if (count == 0)
         return;                                   // whole workgroup: no barrier follows
     u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));

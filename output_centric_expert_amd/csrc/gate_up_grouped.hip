@@ -521,8 +521,8 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int ro
 
     // slots routed to an id outside [0, E) get NaN, written by expert 0's workgroups
     if (e == 0) {
-        const int nbad = compact_slots(nslots, slots, wave_cnt,
-                                       [&](int t) { return (unsigned)ids[t] >= (unsigned)E; });
+        const int nbad = compact_slots(nslots, ids, slots, wave_cnt,
+                                       [&](int v) { return (unsigned)v >= (unsigned)E; });
         for (int q = threadIdx.x; q < nbad * kGroupNeurons; q += blockDim.x) {
             const int bj = slots[q / kGroupNeurons];
             const int i = n_block + q % kGroupNeurons;
@@ -536,7 +536,7 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int ro
         }
         __syncthreads();                          // the list is reused below
     }
-    const int count = compact_slots(nslots, slots, wave_cnt, [&](int t) { return ids[t] == e; });
+    const int count = compact_slots(nslots, ids, slots, wave_cnt, [&](int v) { return v == e; });
     if (count == 0)
         return;                                   // whole workgroup: no barrier follows
     u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list

@@ -46,32 +46,48 @@ __device__ __forceinline__ bf16x8 decode8_scaled_fp4(uint32_t codes, float scale
 }
 
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing
-// order) with pred(t). All threads of the workgroup must call it.
+// order) with pred(ids[t]). All threads of the workgroup must call it. The ids
+// of up to four 256-slot chunks are loaded together, so the list costs one
+// round trip to L2 per 1024 slots.
 template <typename Pred>
-__device__ __forceinline__ int compact_slots(int n, int* slots, int* wave_cnt, Pred pred)
+__device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, int* wave_cnt, Pred pred)
 {
+    constexpr int kChunk = kGroupWaves * kWave;
+    constexpr int kBatch = 4;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     int total = 0;
-    for (int base = 0; base < n; base += kGroupWaves * kWave) {
-        const int t = base + tid;
-        const bool f = t < n && pred(t);
-        const unsigned long long m = __ballot(f);
-        const int before = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0)
-            wave_cnt[w] = __popcll(m);
-        __syncthreads();
-        int off = total;
-        for (int q = 0; q < w; ++q)
-            off += wave_cnt[q];
-        if (f)
-            slots[off + before] = t;
-        int sum = 0;
-        for (int q = 0; q < kGroupWaves; ++q)
-            sum += wave_cnt[q];
-        __syncthreads();
-        total += sum;
+    for (int base0 = 0; base0 < n; base0 += kBatch * kChunk) {
+        int v[kBatch];
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int t = base0 + c * kChunk + tid;
+            v[c] = t < n ? ids[t] : 0;
+        }
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int base = base0 + c * kChunk;
+            if (base >= n)                        // workgroup-uniform
+                break;
+            const int t = base + tid;
+            const bool f = t < n && pred(v[c]);
+            const unsigned long long m = __ballot(f);
+            const int before = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == 0)
+                wave_cnt[w] = __popcll(m);
+            __syncthreads();
+            int off = total;
+            for (int q = 0; q < w; ++q)
+                off += wave_cnt[q];
+            if (f)
+                slots[off + before] = t;
+            int sum = 0;
+            for (int q = 0; q < kGroupWaves; ++q)
+                sum += wave_cnt[q];
+            __syncthreads();
+            total += sum;
+        }
     }
     return total;
 }
