@@ -41,6 +41,89 @@ moe_gate_up_kernel(GateUpArgs p)
     }
 }
 
+// Exact-fit form for rows of exactly 64*U chunks (MXFP8: H a multiple of
+// 1024; MXFP4: of 2048), one neuron per wavefront, BF16 dot route, streaming
+// loads: every lane holds U whole chunks, so there is no clamping or lane
+// factor, and the routed id is requested ahead of the activations so that its
+// round trip overlaps theirs. The per-lane products, the order of the FMAs
+// and the reduction are those of moe_gate_up_kernel (whose lane factor is 1
+// here), so the values are the same floats.
+template <int U, bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(256)
+moe_gate_up_exact_kernel(GateUpArgs p)
+{
+    constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int n_out = p.B * p.k * p.I;
+    const int n_raw = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (int)(threadIdx.x / kWave));
+    const int n0 = n_raw < n_out ? n_raw : n_out - 1;   // no early exit; the extra waves store nothing
+    const int i0 = n0 % p.I;
+    const int bj = n0 / p.I;
+    const int b = bj / p.k;
+    const int H = p.H;
+    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
+    const int e_raw = p.ids[bj];
+    const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
+    u32x4 xv[U][NX];
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+#pragma unroll
+        for (int t = 0; t < NX; ++t)
+            xv[m][t] = xq[NX * (lane + kWave * m) + t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool bad_id = (unsigned)e_raw >= (unsigned)p.E;   // expert 0's rows are read, result NaN
+    const int e = bad_id ? 0 : e_raw;
+    const size_t row = (size_t)e * (size_t)p.I + (size_t)i0;
+    const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
+    const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
+    const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+    const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+    u32x4 wg[U], wu[U];
+    uint32_t sg[U], su[U];
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+        const int c = lane + kWave * m;
+        wg[m] = __builtin_nontemporal_load(gq + c);
+        wu[m] = __builtin_nontemporal_load(uq + c);
+        sg[m] = gs[FP4 ? c : c >> 1];
+        su[m] = us[FP4 ? c : c >> 1];
+    }
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+        const float pg = gu_chunk_dot<FP4, true, NX>(wg[m], xv[m]);
+        const float pu = gu_chunk_dot<FP4, true, NX>(wu[m], xv[m]);
+        g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]), g);
+        u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]), u);
+    }
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == 0 && n_raw < n_out) {
+        const float v = bad_id ? __builtin_nanf("") : swiglu(g, u);
+        const size_t a_idx = inter_index<A_BF16>(bj, i0, p.I);
+        if constexpr (A_BF16)
+            static_cast<uint16_t*>(p.a)[a_idx] = f32_to_bf16_rne(v);
+        else
+            static_cast<float*>(p.a)[a_idx] = v;
+    }
+}
+
+template <bool A_BF16, bool FP4>
+static hipError_t dispatch_exact(int U, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
+{
+    switch (U) {
+#define MOED_GUX_CASE(N) \
+    case N: hipLaunchKernelGGL((moe_gate_up_exact_kernel<N, A_BF16, FP4>), grid, block, 0, s, p); break;
+        MOED_GUX_CASE(1) MOED_GUX_CASE(2) MOED_GUX_CASE(3) MOED_GUX_CASE(4)
+        MOED_GUX_CASE(5) MOED_GUX_CASE(6) MOED_GUX_CASE(7) MOED_GUX_CASE(8)
+#undef MOED_GUX_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <bool DOT_BF16, bool A_BF16, bool NT, bool FP4>
 static hipError_t dispatch_u(int U, int npw, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
 {
@@ -85,6 +168,14 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
     const dim3 block(wpb * kWave);
     const dim3 grid((unsigned)((n_waves + wpb - 1) / wpb));
     const bool dot = t.gu_dot != 0, nt = t.nt != 0;
+    // rows of exactly 64*U chunks, U <= umax: the exact-fit kernel
+    if (t.gu_exact != 0 && npw == 1 && nt && (dot || fp4) && nch == kWave * U) {
+        if (fp4)
+            return a_bf16 ? dispatch_exact<true, true>(U, p, grid, block, s)
+                          : dispatch_exact<false, true>(U, p, grid, block, s);
+        return a_bf16 ? dispatch_exact<true, false>(U, p, grid, block, s)
+                      : dispatch_exact<false, false>(U, p, grid, block, s);
+    }
     if (fp4) {                                    // one decode route (BF16 dot2)
         if (a_bf16) return nt ? dispatch_u<true, true, true, true>(U, npw, p, grid, block, s)
                               : dispatch_u<true, true, false, true>(U, npw, p, grid, block, s);

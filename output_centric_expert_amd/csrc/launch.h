@@ -11,6 +11,8 @@ namespace moed {
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
     int gu_npw = 1;     // gate/up (per-slot kernel): neurons per wavefront (1 or 2; 2 shares x)
+    int gu_exact = 1;   // gate/up (per-slot kernel): 1 = exact-fit kernel when a row is exactly 64*U
+                        // chunks (U <= gu_umax), one neuron per wavefront, BF16 route, streaming
     int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)
     int dn_stage = 1;   // down: 1 = copy a[b] into LDS once per workgroup (when it fits)
     int dn_group = 2;   // down inside moe_decode: 0 = one wavefront per output; 1 = expert-major
@@ -35,6 +37,8 @@ struct Tuning {
     int dn_rows = 0;    // down (staged): outputs per wavefront, 1, 2 or 4; 0 = by batch (4 once
                         // B*k >= E, 2 for B >= 2, 1 for B = 1)
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
+    int dn_onepass = 1; // down (staged, one output per wavefront): 1 = straight-line kernel when the
+                        // token's slots form one group and a row is one chunk per lane
     int dn_order = 1;   // down workgroup order: 0 = token-major; 1 = hidden-major, each XCD
                         // taking a contiguous range; 2 = hidden-major, plain round robin
 };

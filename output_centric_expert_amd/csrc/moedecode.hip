@@ -388,6 +388,8 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "gu_npw") && (v == 1 || v == 2)) t.gu_npw = (int)v;
         else if (!strcmp(tok, "dn_rows") && (v == 0 || v == 1 || v == 2 || v == 4)) t.dn_rows = (int)v;
         else if (!strcmp(tok, "dn_lanegroups") && (v == 0 || v == 1)) t.dn_lanegroups = (int)v;
+        else if (!strcmp(tok, "dn_onepass") && (v == 0 || v == 1)) t.dn_onepass = (int)v;
+        else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;
         else return MOED_ERR_SHAPE;
     }
     g_tuning = t;

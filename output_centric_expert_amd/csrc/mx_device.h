@@ -155,9 +155,12 @@ __device__ __forceinline__ float wave_sum(float v)
 // logical indices then meets in one L2. It is a bijection of [0, n).
 __device__ __forceinline__ int xcd_contiguous(int i, int n)
 {
+    // XCD x starts at x*q + min(x, r): the first r XCDs take q + 1 indices,
+    // the others q (written without a branch, so a kernel's argument loads
+    // are not split around it)
     const int x = i % 8, slot = i / 8;
     const int q = n / 8, r = n % 8;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+    return x * q + (x < r ? x : r) + slot;
 }
 
 // float32 -> bfloat16 bits, round to nearest even; NaN stays a (quiet) NaN.

@@ -160,6 +160,10 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"dn_rows=2") == md.MOED_OK
     assert lib.moed_set_tuning(b"dn_rows=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"dn_rows=4") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_onepass=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_onepass=2") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_exact=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_exact=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(None) == md.MOED_OK

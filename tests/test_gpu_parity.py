@@ -235,7 +235,8 @@ def test_ragged_shapes(shape):
                                   "dn_order=1", "dn_order=2", "dn_order=1,dn_stage=0,dn_wpb=3",
                                   "dn_order=2,dn_wpb=5,nt=0", "dn_lanegroups=0", "dn_lanegroups=1,dn_umax=1",
                                   "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0",
-                                  "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5"])
+                                  "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5",
+                                  "dn_onepass=0", "gu_exact=0", "gu_exact=0,dn_onepass=0,dn_rows=1"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
@@ -656,3 +657,50 @@ def test_grouped_wide_loads(shape, wformat):
         check_f32(out[[0, B - 1]], ref, f"wide {shape} {wformat}")
     finally:
         md.moed_set_tuning(None)
+
+
+# (B, E, k, H, I): which straight-line kernels each shape takes --
+#   one-pass down: k = G*JB slots in one group, a row of at most 64/G chunks
+#   exact-fit gate/up: a row of exactly 64*U chunks
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(1, 128, 8, 2048, 768),     # G=1 JB=8 (mxfp8), G=2 JB=4 (mxfp4); U=2 / U=1
+                                   (1, 8, 2, 256, 128),        # lane groups, one slot each
+                                   (3, 12, 4, 1024, 1024),     # G=1 JB=4 at B=3 (rows kernel for B>1 under mxfp8)
+                                   (2, 9, 1, 4096, 544),       # k=1; U=4 / U=2
+                                   (5, 64, 8, 2048, 256),      # four lane groups at B=5
+                                   (1, 6, 6, 1024, 640)])      # k=6: not a power-of-two group (generic kernels)
+def test_straight_line_kernels_match_generic(shape, wformat):
+    """The one-pass down and exact-fit gate/up kernels compute the same floats as the generic
+    staged / per-slot kernels they replace (same products, FMA order and reduction), so the
+    intermediate and both output dtypes agree bit for bit; both also meet the oracle gate.
+    The ids include an invalid one when B > 1 (its token's outputs NaN on both sides)."""
+    B, E, k, H, I = shape
+    L = synth.make_layer(synth.LayerShape("sl", B, E, k, H, I), seed=sum(shape) + 5, device="cuda", wformat=wformat)
+    ids = L.ids.copy()
+    if B > 1:
+        ids[B - 1, 0] = E                     # out of range: that token's outputs are NaN
+    x, _, wd = md.layer_device_inputs(L)
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    got = {}
+    for spec in ["gu_exact=0,dn_onepass=0", None]:
+        md.moed_set_tuning(spec)
+        try:
+            say(f"straight-line {shape} {wformat} spec={spec}")
+            a = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat)
+            outs = [md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                                  out_dtype=dt, wformat=wformat) for dt in (torch.float32, torch.bfloat16)]
+            torch.cuda.synchronize()
+            got[spec] = [a.clone()] + [o.clone() for o in outs]
+        finally:
+            md.moed_set_tuning(None)
+    for t0, t1, what in zip(got["gu_exact=0,dn_onepass=0"], got[None], ["a", "out f32", "out bf16"]):
+        nan0, nan1 = torch.isnan(t0.float()), torch.isnan(t1.float())
+        assert torch.equal(nan0, nan1), f"{shape} {wformat}: {what} NaN positions differ"
+        bits = torch.int32 if t0.dtype == torch.float32 else torch.int16
+        assert torch.equal(t0.view(bits)[~nan0], t1.view(bits)[~nan1]), \
+            f"{shape} {wformat}: {what} differs between the straight-line and the generic kernels"
+    good = list(range(B - 1)) if B > 1 else [0]
+    ref, _ = oracle_tokens(L, good, ids=ids, wformat=wformat)
+    check_f32(got[None][1][good], ref, f"straight-line {shape} {wformat}")
+    if B > 1:
+        assert torch.isnan(got[None][1][B - 1]).all()
