@@ -146,7 +146,7 @@ def main():
     traffic = load_traffic("gate_up", args.workload) if L.wformat == "mxfp8" else None
     _, dn_bytes = kernel_bytes(L)
     floor = same_size_reads(md, gu_bytes, dn_bytes, K=min(K, 2000)) if L.unique_weight_bytes < (1 << 30) else None
-    roofline = {"bound": "hbm", "kernel": "moe_gate_up_kernel", "achieved": round(gu_gbs, 1),
+    roofline = {"bound": "hbm", "kernel": gate_up_kernel_name(L), "achieved": round(gu_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
                 "avg_launch_us": round(ms_gu * 1e3, 3)}
@@ -312,6 +312,17 @@ def synth_router_logits(L):
 
 
 WEIGHT_DESC = {"mxfp8": "mxfp8 (e4m3 + ue8m0 per 32)", "mxfp4": "mxfp4 (e2m1 two per byte + ue8m0 per 32)"}
+
+
+def gate_up_kernel_name(L):
+    """The gate/up kernel the library's built-in launch table picks for this layer: the
+    expert-grouped one once B*k*H >= 2458*E, else the per-slot exact-fit kernel when a row is
+    exactly 64*U 16-byte chunks (U <= 8), else the generic per-slot kernel."""
+    sh = L.shape
+    if sh.B * sh.k * sh.H >= 2458 * sh.E:
+        return "moe_gate_up_grouped_wide_kernel"
+    nch = sh.H // 32 if L.wformat == "mxfp4" else sh.H // 16
+    return "moe_gate_up_exact_kernel" if nch % 64 == 0 and nch // 64 <= 8 else "moe_gate_up_kernel"
 
 
 def kernel_bytes(L):

@@ -26,8 +26,9 @@ import statistics
 import sys
 
 KINDS = (("moe_gate_up_grouped_wide_kernel", "gate_up"), ("moe_gate_up_grouped_kernel", "gate_up"),
-         ("moe_gate_up_kernel", "gate_up"),
-         ("moe_down_rows_kernel", "down"), ("moe_down_staged_kernel", "down"), ("moe_down_kernel", "down"),
+         ("moe_gate_up_exact_kernel", "gate_up"), ("moe_gate_up_kernel", "gate_up"),
+         ("moe_down_rows_kernel", "down"), ("moe_down_staged_kernel", "down"), ("moe_down_onepass_kernel", "down"),
+         ("moe_down_kernel", "down"),
          ("moe_down_expert_kernel", "down"), ("moe_down_combine_kernel", "combine"),
          ("moe_route_kernel", "route"))
 
