@@ -188,139 +188,6 @@ moe_down_staged_kernel(DownArgs p)
     }
 }
 
-// One-pass form of the staged kernel for the usual decode shape: the token's
-// k slots are exactly one group (k = G*JB: JB slots for each of G lane
-// groups) and a row is at most one chunk per lane (cpr <= 64/G); float32 a,
-// streaming weight loads, 8 wavefronts per workgroup. Everything a wave needs
-// is requested in straight-line code before its first wait: the copy of a[b]
-// (at most NCP units per thread), the k routed ids and weights (compile-time
-// offsets, so one wide scalar load each when G = 1), then every weight chunk
-// and scale byte. No loop, no branch and no wait sits among these loads, so
-// the weights of all k experts are in flight together from the kernel's
-// first memory round trip on. Per output the FMAs, their operands and their
-// order are those of moe_down_staged_kernel with the same lane groups, so the
-// results are the same floats. The workgroup order is always hidden-major and
-// XCD-contiguous (the default order of the other kernels).
-template <int JB, int G, bool OUT_BF16, bool FP4>
-__global__ void __launch_bounds__(512)
-moe_down_onepass_kernel(DownArgs p)
-{
-    extern __shared__ u32x4 a_lds[];
-    constexpr int WPB = 8;
-    constexpr int NTH = WPB * kWave;
-    constexpr int KS = G * JB;                    // slots per token (= p.k)
-    // a[b] is KS * 4 * (I/16) units with I/16 <= 64/G (MXFP8) or 128/G (MXFP4)
-    constexpr int NCP = FP4 ? JB : (JB >= 2 ? JB / 2 : 1);
-    using LG = LaneGroups<G>;
-    const int lane = threadIdx.x & (kWave - 1);
-    // always the hidden-major, XCD-contiguous workgroup order (no branch on
-    // the order argument ahead of the loads)
-    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
-    const int b = blk % p.B;
-    const int h = (blk / p.B) * WPB + (int)(threadIdx.x / kWave);
-    const bool active = h < p.H;                  // idle waves still help copy a[b]
-    const int cpr16 = p.I / 16;
-    const int cpr = FP4 ? p.I / 32 : cpr16;
-    const int nunits = KS * 4 * cpr16;
-    const int* ids = p.ids + (size_t)b * KS;
-    const float* wts = p.w + (size_t)b * KS;
-    const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
-
-    // 1) the copy of a[b]: NCP unconditional loads per thread from clamped
-    // addresses (surplus ones re-read the last unit; a guard here would make
-    // the compiler wait for each copy before issuing the next)
-    u32x4 cp[NCP];
-#pragma unroll
-    for (int q = 0; q < NCP; ++q) {
-        const int u = (int)threadIdx.x + q * NTH;
-        cp[q] = asrc[u < nunits ? u : nunits - 1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 2) ids and routing weights of the lane's slots j = g + G*jj: all k of
-    // them by scalar loads at compile-time offsets, then picked per lane group
-    // (a per-lane load here would be counted with the copy loads, so the
-    // weight loads would wait for the copy as well)
-    const int g = LG::group(lane);
-    const int lc = LG::chunk(lane);
-    int id_all[KS];
-    float w_all[KS];
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-        id_all[t] = ids[t];
-        w_all[t] = wts[t];
-    }
-    // both arrive in one wait, before the weight loads (left alone, the
-    // compiler sinks the weights' scalar load towards its use, where it costs
-    // a memory round trip of its own)
-#pragma unroll
-    for (int t = 0; t < KS; ++t)
-        asm volatile("" ::"s"(id_all[t]), "s"(w_all[t]));
-    int eid[JB];
-    float wt[JB];
-#pragma unroll
-    for (int jj = 0; jj < JB; ++jj) {
-        eid[jj] = id_all[G * jj];
-        wt[jj] = w_all[G * jj];
-#pragma unroll
-        for (int gg = 1; gg < G; ++gg) {
-            eid[jj] = g == gg ? id_all[gg + G * jj] : eid[jj];
-            wt[jj] = g == gg ? w_all[gg + G * jj] : wt[jj];
-        }
-    }
-    // 3) every weight chunk and scale byte (an invalid id reads expert 0's row
-    // and makes the output NaN; lanes past the row end re-read its last chunk
-    // with factor 0)
-    const size_t row_bytes = FP4 ? (size_t)(p.I / 2) : (size_t)p.I;
-    const int hc = active ? h : 0;
-    const int oc = lc < cpr ? lc : cpr - 1;
-    const bool lane_live = active && lc < cpr;
-    u32x4 wq[JB][1];
-    uint32_t ws[JB][1];
-    float mask[JB][1];
-#pragma unroll
-    for (int jj = 0; jj < JB; ++jj) {
-        const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
-        const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
-        wq[jj][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes) + oc);
-        ws[jj][0] = p.wd_s[row * (size_t)(p.I / 32) + (FP4 ? oc : oc >> 1)];
-        mask[jj][0] = lane_live ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < NCP; ++q) {
-        const int u = (int)threadIdx.x + q * NTH;
-        if (u < nunits)
-            a_lds[u] = cp[q];
-    }
-    __syncthreads();
-    if (!active)
-        return;                                   // after the only barrier
-    float acc = down_group_dot<1, JB, false, FP4, G>(a_lds, KS, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
-    acc = wave_sum(acc);
-    if (lane == 0) {
-        if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h] = f32_to_bf16_rne(acc);
-        else
-            static_cast<float*>(p.out)[(size_t)b * p.H + h] = acc;
-    }
-}
-
-template <int G>
-static hipError_t launch_onepass_g(int jb, bool fp4, bool out_bf16, const DownArgs& p, dim3 grid, dim3 block,
-                                   size_t lds, hipStream_t s)
-{
-#define MOED_OP(J, F, O) \
-    if (jb == J && fp4 == F && out_bf16 == O) { \
-        hipLaunchKernelGGL((moe_down_onepass_kernel<J, G, O, F>), grid, block, lds, s, p); \
-        return hipGetLastError(); \
-    }
-#define MOED_OP_J(J) MOED_OP(J, false, false) MOED_OP(J, false, true) MOED_OP(J, true, false) MOED_OP(J, true, true)
-    MOED_OP_J(1) MOED_OP_J(2) MOED_OP_J(4) MOED_OP_J(8)
-#undef MOED_OP_J
-#undef MOED_OP
-    return hipErrorInvalidValue;
-}
-
 // LDS-staged variant with R consecutive outputs per wavefront (used once
 // tokens share experts, B*k >= E, where the copy of a[b] and the LDS reads of
 // it, not the weight stream, bound the kernel): each piece of a read from LDS
@@ -524,11 +391,7 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     if (staged && t.dn_onepass != 0 && !a_bf16 && nt && wpb == 8 && p.k == groups * per_group &&
         (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups &&
         (groups > 1 || rows == 1)) {
-        if (groups == 1)
-            return launch_onepass_g<1>(per_group, fp4, out_bf16, q, grid, block, lds, s);
-        if (groups == 2)
-            return launch_onepass_g<2>(per_group, fp4, out_bf16, q, grid, block, lds, s);
-        return launch_onepass_g<4>(per_group, fp4, out_bf16, q, grid, block, lds, s);
+        return launch_down_onepass(q, per_group, groups, out_bf16, grid, block, lds, s);
     }
     if (groups > 1) {
         const int per = (p.k + groups - 1) / groups;   // slots per group

@@ -1,0 +1,195 @@
+// One-pass down kernel for single-token and small-batch decode (one wavefront
+// per output out[b][h]; warp-decode post, "How the two kernels work", third
+// and fourth paragraphs): the staged kernel's arithmetic in straight-line code
+// for the case where a token's k slots form one slot group and a routed row is
+// at most one 16-byte chunk per lane.
+#include "down_body.h"
+
+namespace moed {
+
+// One-pass form of the staged kernel for the usual decode shape: the token's
+// k slots are exactly one group (k = G*JB: JB slots for each of G lane
+// groups) and a row is at most one chunk per lane (cpr <= 64/G); float32 a,
+// streaming weight loads, 8 wavefronts per workgroup. Everything a wave needs
+// is requested in straight-line code before its first wait: the copy of a[b]
+// (at most NCP units per thread), the k routed ids and weights (compile-time
+// offsets, so one wide scalar load each when G = 1), then every weight chunk
+// and scale byte. No loop, no branch and no wait sits among these loads, so
+// the weights of all k experts are in flight together from the kernel's
+// first memory round trip on. Per output the FMAs, their operands and their
+// order are those of moe_down_staged_kernel with the same lane groups, so the
+// results are the same floats. The workgroup order is always hidden-major and
+// XCD-contiguous (the default order of the other kernels). ONE_TOKEN: B = 1,
+// so the token index needs no division.
+template <int JB, int G, bool OUT_BF16, bool FP4, int NCP, bool ONE_TOKEN>
+__global__ void __launch_bounds__(512)
+moe_down_onepass_kernel(DownArgs p)
+{
+    extern __shared__ u32x4 a_lds[];
+    constexpr int WPB = 8;
+    constexpr int NTH = WPB * kWave;
+    constexpr int KS = G * JB;                    // slots per token (= p.k)
+    using LG = LaneGroups<G>;
+    const int lane = threadIdx.x & (kWave - 1);
+    // always the hidden-major, XCD-contiguous workgroup order (no branch on
+    // the order argument ahead of the loads)
+    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    const int b = ONE_TOKEN ? 0 : blk % p.B;
+    const int h = (ONE_TOKEN ? blk : blk / p.B) * WPB + (int)(threadIdx.x / kWave);
+    const bool active = h < p.H;                  // idle waves still help copy a[b]
+    const int cpr16 = p.I / 16;
+    const int cpr = FP4 ? p.I / 32 : cpr16;
+    const int nunits = KS * 4 * cpr16;
+    const int* ids = p.ids + (size_t)b * KS;
+    const float* wts = p.w + (size_t)b * KS;
+    const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
+
+    // 1) the copy of a[b]: NCP unconditional loads per thread from clamped
+    // addresses (surplus ones re-read the last unit; a guard here would make
+    // the compiler wait for each copy before issuing the next). NCP is the
+    // exact count ceil(units / 512) for single-token calls with k = 8, else the
+    // largest count the shape limits allow.
+    u32x4 cp[NCP];
+#pragma unroll
+    for (int q = 0; q < NCP; ++q) {
+        const int u = (int)threadIdx.x + q * NTH;
+        cp[q] = asrc[u < nunits ? u : nunits - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2) ids and routing weights of the lane's slots j = g + G*jj: all k of
+    // them by scalar loads at compile-time offsets, then picked per lane group
+    // (a per-lane load here would be counted with the copy loads, so the
+    // weight loads would wait for the copy as well)
+    const int g = LG::group(lane);
+    const int lc = LG::chunk(lane);
+    int id_all[KS];
+    float w_all[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        id_all[t] = ids[t];
+        w_all[t] = wts[t];
+    }
+    // both arrive in one wait, before the weight loads (left alone, the
+    // compiler sinks the weights' scalar load towards its use, where it costs
+    // a memory round trip of its own)
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+        asm volatile("" ::"s"(id_all[t]), "s"(w_all[t]));
+    int eid[JB];
+    float wt[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        eid[jj] = id_all[G * jj];
+        wt[jj] = w_all[G * jj];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) {
+            eid[jj] = g == gg ? id_all[gg + G * jj] : eid[jj];
+            wt[jj] = g == gg ? w_all[gg + G * jj] : wt[jj];
+        }
+    }
+    // 3) every weight chunk and scale byte (an invalid id reads expert 0's row
+    // and makes the output NaN; lanes past the row end re-read its last chunk
+    // with factor 0)
+    const size_t row_bytes = FP4 ? (size_t)(p.I / 2) : (size_t)p.I;
+    const int hc = active ? h : 0;
+    const int oc = lc < cpr ? lc : cpr - 1;
+    const bool lane_live = active && lc < cpr;
+    u32x4 wq[JB][1];
+    uint32_t ws[JB][1];
+    float mask[JB][1];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
+        const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
+        wq[jj][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes) + oc);
+        ws[jj][0] = p.wd_s[row * (size_t)(p.I / 32) + (FP4 ? oc : oc >> 1)];
+        mask[jj][0] = lane_live ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < NCP; ++q) {
+        const int u = (int)threadIdx.x + q * NTH;
+        if (u < nunits)
+            a_lds[u] = cp[q];
+    }
+    __syncthreads();
+    if (!active)
+        return;                                   // after the only barrier
+    float acc = down_group_dot<1, JB, false, FP4, G>(a_lds, KS, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+        if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h] = f32_to_bf16_rne(acc);
+        else
+            static_cast<float*>(p.out)[(size_t)b * p.H + h] = acc;
+    }
+}
+
+// Copy loads per thread that cover a[b] (KS*4*(I/16) units) for any shape the
+// kernel takes: I/16 <= 64/G for MXFP8 and <= 128/G for MXFP4.
+constexpr int onepass_max_ncp(int jb, bool fp4) { return fp4 ? jb : (jb >= 2 ? jb / 2 : 1); }
+
+template <int JB, int G, bool FP4>
+static hipError_t launch_jg(const DownArgs& p, bool out_bf16, int ncp, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t s)
+{
+    constexpr int MAXN = onepass_max_ncp(JB, FP4);
+#define MOED_OP(O, N, ONE) \
+    hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, O, FP4, N, ONE>), grid, block, lds, s, p)
+    // single-token calls of k = 8 slots: the exact copy count (one to four loads)
+    if constexpr (JB * G == 8) {
+        if (p.B == 1 && ncp <= 4) {
+            switch (ncp * 2 + (out_bf16 ? 1 : 0)) {
+            case 2: MOED_OP(false, 1, true); break;
+            case 3: MOED_OP(true, 1, true); break;
+            case 4: MOED_OP(false, 2, true); break;
+            case 5: MOED_OP(true, 2, true); break;
+            case 6: MOED_OP(false, 3, true); break;
+            case 7: MOED_OP(true, 3, true); break;
+            case 8: MOED_OP(false, 4, true); break;
+            default: MOED_OP(true, 4, true); break;
+            }
+            return hipGetLastError();
+        }
+    }
+    if (out_bf16)
+        MOED_OP(true, MAXN, false);
+    else
+        MOED_OP(false, MAXN, false);
+#undef MOED_OP
+    return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_g(const DownArgs& p, int jb, bool out_bf16, int ncp, dim3 grid, dim3 block, size_t lds,
+                           hipStream_t s)
+{
+    const bool fp4 = p.wfmt == kMXFP4;
+    switch (jb * 2 + (fp4 ? 1 : 0)) {
+    case 1 * 2 + 0: return launch_jg<1, G, false>(p, out_bf16, ncp, grid, block, lds, s);
+    case 1 * 2 + 1: return launch_jg<1, G, true>(p, out_bf16, ncp, grid, block, lds, s);
+    case 2 * 2 + 0: return launch_jg<2, G, false>(p, out_bf16, ncp, grid, block, lds, s);
+    case 2 * 2 + 1: return launch_jg<2, G, true>(p, out_bf16, ncp, grid, block, lds, s);
+    case 4 * 2 + 0: return launch_jg<4, G, false>(p, out_bf16, ncp, grid, block, lds, s);
+    case 4 * 2 + 1: return launch_jg<4, G, true>(p, out_bf16, ncp, grid, block, lds, s);
+    case 8 * 2 + 0: return launch_jg<8, G, false>(p, out_bf16, ncp, grid, block, lds, s);
+    case 8 * 2 + 1: return launch_jg<8, G, true>(p, out_bf16, ncp, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, dim3 grid, dim3 block,
+                               size_t lds, hipStream_t s)
+{
+    const int units = p.k * 4 * (p.I / 16);       // float32 a[b] in 16-byte units
+    const int ncp = (units + 511) / 512;
+    if (groups == 1)
+        return launch_g<1>(p, jb, out_bf16, ncp, grid, block, lds, s);
+    if (groups == 2)
+        return launch_g<2>(p, jb, out_bf16, ncp, grid, block, lds, s);
+    if (groups == 4)
+        return launch_g<4>(p, jb, out_bf16, ncp, grid, block, lds, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moed

@@ -76,6 +76,10 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
 size_t gate_up_grouped_lds(int B, int k, bool wide);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
+// One-pass down (float32 a, streaming loads, 8 wavefronts per workgroup): k = groups * jb slots,
+// rows of at most 64/groups chunks; hipErrorInvalidValue for a (jb, groups) it has no kernel for.
+hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, dim3 grid, dim3 block,
+                               size_t lds, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Expert-major down (y: B*k*H float32 per-slot partials, then out).

@@ -668,7 +668,9 @@ def test_grouped_wide_loads(shape, wformat):
                                    (3, 12, 4, 1024, 1024),     # G=1 JB=4 at B=3 (rows kernel for B>1 under mxfp8)
                                    (2, 9, 1, 4096, 544),       # k=1; U=4 / U=2
                                    (5, 64, 8, 2048, 256),      # four lane groups at B=5
-                                   (1, 6, 6, 1024, 640)])      # k=6: not a power-of-two group (generic kernels)
+                                   (1, 6, 6, 1024, 640),       # k=6: not a power-of-two group (generic kernels)
+                                   (1, 64, 8, 2048, 256),      # single token, four lane groups of two slots
+                                   (1, 32, 8, 1024, 1024)])    # single token, four copy loads per thread
 def test_straight_line_kernels_match_generic(shape, wformat):
     """The one-pass down and exact-fit gate/up kernels compute the same floats as the generic
     staged / per-slot kernels they replace (same products, FMA order and reduction), so the
