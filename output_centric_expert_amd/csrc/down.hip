@@ -385,12 +385,15 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     // (several outputs per wavefront once tokens share experts, with the same
     // arithmetic per output as one output per wavefront: 4 once B*k >= E, 2 for
     // smaller batches, 1 for a single token, where halving the workgroup count
-    // would leave CUs idle -- measured; lane groups keep one output per wavefront)
+    // would leave CUs idle -- measured; lane groups keep one output per
+    // wavefront, and so does the one-pass kernel, which also replaces the
+    // two-row default where it applies: B=4 down 12.7 -> 10.7 us, B=8 18.6 ->
+    // 17.7 us at k=8, I=768; at B*k >= E four rows stay faster)
     const int rows = t.dn_rows != 0 ? t.dn_rows : ((long)p.B * p.k >= (long)p.E ? 4 : (p.B >= 2 ? 2 : 1));
     const int per_group = p.k / groups;
     if (staged && t.dn_onepass != 0 && !a_bf16 && nt && wpb == 8 && p.k == groups * per_group &&
         (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups &&
-        (groups > 1 || rows == 1)) {
+        (groups > 1 || rows == 1 || (t.dn_rows == 0 && rows == 2))) {
         return launch_down_onepass(q, per_group, groups, out_bf16, grid, block, lds, s);
     }
     if (groups > 1) {
