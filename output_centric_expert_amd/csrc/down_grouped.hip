@@ -275,26 +275,17 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
     }
 }
 
-// A workgroup owns (expert e, RT*64 rows); wavefront w the rows
-// hb + 16*RT*w .. +16*RT-1. H is a multiple of 16*RT.
+// An item is (expert e, RT*64 rows); wavefront w takes the rows
+// hb + 16*RT*w .. +16*RT-1. H is a multiple of 16*RT. wl_off >= 0: the work
+// list sits wl_off ints into the dynamic LDS and the workgroups walk the
+// items of the routed experts with a stride of the grid size; wl_off < 0: one
+// item per workgroup over all E experts (the grid is E * blocks).
 template <int RT, bool A_BF16, bool FP4>
-__global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
-moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
+__device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, int max_tiles, int e, int hb,
+                                                 int count, const int* slots, u32x4* xs)
 {
-    extern __shared__ int slots[];                // B*k entries, then the a tiles
-    __shared__ int wave_cnt[kGroupWaves];
-    constexpr int kRows = 16 * RT * kGroupWaves;
-    const int nblk = (p.H + kRows - 1) / kRows;
-    const int e = blockIdx.x / nblk;
-    const int hb = (blockIdx.x % nblk) * kRows;
-    const int nslots = p.B * p.k;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int* ids = p.ids;
-    const int count = compact_slots(nslots, ids, slots, wave_cnt, [&](int v) { return v == e; });
-    if (count == 0)
-        return;                                   // whole workgroup: no barrier follows
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));
     const int h0 = hb + 16 * RT * w;              // this wavefront's rows
     const bool store = h0 < p.H;                  // wavefronts past H still take part in the barriers
     const int col = lane % 16;
@@ -322,6 +313,35 @@ moe_down_expert_kernel(DownArgs p, float* y, int max_tiles)
                 expert_down_pass<4, RT, A_BF16, FP4>(p, r, slots, count, t0, xs, store, h0, y);
             break;
         }
+    }
+}
+
+template <int RT, bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
+moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
+{
+    extern __shared__ int slots[];                // B*k entries, the a tiles, then the work list
+    __shared__ int wave_cnt[kGroupWaves];
+    constexpr int kRows = 16 * RT * kGroupWaves;
+    const int nblk = (p.H + kRows - 1) / kRows;
+    const int nslots = p.B * p.k;
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));
+    const int* act = nullptr;
+    int n_items = p.E * nblk;
+    if (wl_off >= 0) {
+        int* mark = slots + wl_off;
+        int* list = mark + p.E;
+        n_items = routed_experts(nslots, p.ids, p.E, mark, list, wave_cnt) * nblk;
+        act = list;
+    }
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int e = act ? act[item / nblk] : item / nblk;
+        const int hb = (item % nblk) * kRows;
+        const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
+        if (count == 0)
+            continue;                             // whole workgroup (only without the work list)
+        expert_down_item<RT, A_BF16, FP4>(p, y, max_tiles, e, hb, count, slots, xs);
+        __syncthreads();                          // the next item rewrites the slot list and the a tiles
     }
 }
 
@@ -360,25 +380,26 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
     }
 }
 
-size_t down_grouped_lds(int B, int k, bool a_bf16, int max_tiles)
+size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles)
 {
-    // slot list (rounded up to 16 bytes), then two buffers of hi (and lo) tiles
+    // slot list (rounded up to 16 bytes), two buffers of hi (and lo) tiles,
+    // then the work list
     const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
-    return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4);
+    return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4) + worklist_lds(E);
 }
 
-int down_grouped_tiles(int B, int k, bool a_bf16, int requested)
+int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested)
 {
     if (requested > 0)
-        return down_grouped_lds(B, k, a_bf16, requested) <= 65536 ? requested : 0;
+        return down_grouped_lds(B, k, E, a_bf16, requested) <= 65536 ? requested : 0;
     for (int mt = kTiles; mt >= 1; --mt)
-        if (down_grouped_lds(B, k, a_bf16, mt) <= 65536)
+        if (down_grouped_lds(B, k, E, a_bf16, mt) <= 65536)
             return mt;
     return 0;
 }
 
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               int row_tiles, hipStream_t s)
+                               int row_tiles, int grid_cap, hipStream_t s)
 {
     if ((long)p.B * p.k == 0)
         return hipSuccess;
@@ -386,11 +407,16 @@ hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, fl
         (p.H % (16 * row_tiles)) != 0)
         return hipErrorInvalidValue;
     const int nblk = (p.H + 16 * row_tiles * kGroupWaves - 1) / (16 * row_tiles * kGroupWaves);
-    const dim3 grid((unsigned)((long)p.E * nblk)), block(kGroupWaves * kWave);
-    const size_t lds = down_grouped_lds(p.B, p.k, a_bf16, max_tiles);
+    const long items = (long)p.E * nblk;
+    const size_t lds = down_grouped_lds(p.B, p.k, p.E, a_bf16, max_tiles);
+    const size_t wl = worklist_lds(p.E);
+    // with the work list: at most grid_cap workgroups walk the routed experts' items
+    const bool use_wl = wl > 0 && grid_cap > 0;
+    const int wl_off = use_wl ? (int)((lds - wl) / sizeof(int)) : -1;
+    const dim3 grid((unsigned)(use_wl && items > grid_cap ? grid_cap : items)), block(kGroupWaves * kWave);
     const bool fp4 = p.wfmt == kMXFP4;
 #define MOED_DX(RT, A, F) \
-    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F>), grid, block, lds, s, p, y, max_tiles)
+    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F>), grid, block, lds, s, p, y, max_tiles, wl_off)
     if (row_tiles == 2) {
         if (fp4) { if (a_bf16) MOED_DX(2, true, true); else MOED_DX(2, false, true); }
         else { if (a_bf16) MOED_DX(2, true, false); else MOED_DX(2, false, false); }

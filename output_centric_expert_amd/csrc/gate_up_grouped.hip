@@ -503,43 +503,16 @@ __device__ __forceinline__ void rowwise_neurons(const GateUpArgs& p, int e, int 
     }
 }
 
+// One item: expert e, neurons n_block .. n_block+63, the count >= 1 slots
+// routed to e in slots[] (slot order). Every thread of the workgroup calls it.
 template <bool A_BF16, bool FP4, bool WIDE>
-__device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int row_slots, int row_u)
+__device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const int* slots,
+                                             u32x4* xs, int row_slots, int row_u)
 {
-    extern __shared__ int slots[];               // B*k entries
-    __shared__ int wave_cnt[kGroupWaves];
-    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
-    const int e = blockIdx.x / nblk;
-    const int n_block = (blockIdx.x % nblk) * kGroupNeurons;
-    const int nslots = p.B * p.k;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int* ids = p.ids;
-    const int E = p.E;
     const int I = p.I;
     const int H = p.H;
-
-    // slots routed to an id outside [0, E) get NaN, written by expert 0's workgroups
-    if (e == 0) {
-        const int nbad = compact_slots(nslots, ids, slots, wave_cnt,
-                                       [&](int v) { return (unsigned)v >= (unsigned)E; });
-        for (int q = threadIdx.x; q < nbad * kGroupNeurons; q += blockDim.x) {
-            const int bj = slots[q / kGroupNeurons];
-            const int i = n_block + q % kGroupNeurons;
-            if (i < I) {
-                const size_t idx = inter_index<A_BF16>(bj, i, I);
-                if constexpr (A_BF16)
-                    static_cast<uint16_t*>(p.a)[idx] = 0x7FC0u;
-                else
-                    static_cast<float*>(p.a)[idx] = __builtin_nanf("");
-            }
-        }
-        __syncthreads();                          // the list is reused below
-    }
-    const int count = compact_slots(nslots, ids, slots, wave_cnt, [&](int v) { return v == e; });
-    if (count == 0)
-        return;                                   // whole workgroup: no barrier follows
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list
     const int n0 = n_block + 16 * w;              // this wavefront's 16 neurons
     const bool store = n0 < I;                    // wavefronts past I still take part in the barriers
 
@@ -613,34 +586,85 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int ro
     }
 }
 
+// The grouped gate/up: invalid slots first (workgroup q < blocks writes NaN
+// for neuron block q of every slot whose id is outside [0, E)), then the
+// items (expert, block of 64 neurons): with the work list (wl_off >= 0, its
+// place in the dynamic LDS) the routed experts' items with a stride of the
+// grid size, else one item per workgroup over all E experts.
+template <bool A_BF16, bool FP4, bool WIDE>
+__device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int row_slots, int row_u, int wl_off)
+{
+    extern __shared__ int slots[];               // B*k entries, the x tiles, then the work list
+    __shared__ int wave_cnt[kGroupWaves];
+    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
+    const int nslots = p.B * p.k;
+    const int E = p.E;
+    const int I = p.I;
+
+    if ((int)blockIdx.x < nblk) {
+        const int n_block = (int)blockIdx.x * kGroupNeurons;
+        const int nbad = compact_slots(nslots, p.ids, slots, wave_cnt,
+                                       [&](int v) { return (unsigned)v >= (unsigned)E; });
+        for (int q = threadIdx.x; q < nbad * kGroupNeurons; q += blockDim.x) {
+            const int bj = slots[q / kGroupNeurons];
+            const int i = n_block + q % kGroupNeurons;
+            if (i < I) {
+                const size_t idx = inter_index<A_BF16>(bj, i, I);
+                if constexpr (A_BF16)
+                    static_cast<uint16_t*>(p.a)[idx] = 0x7FC0u;
+                else
+                    static_cast<float*>(p.a)[idx] = __builtin_nanf("");
+            }
+        }
+        __syncthreads();                          // the list is reused below
+    }
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list
+    const int* act = nullptr;
+    int n_items = E * nblk;
+    if (wl_off >= 0) {
+        int* mark = slots + wl_off;
+        int* list = mark + E;
+        n_items = routed_experts(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
+        act = list;
+    }
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int e = act ? act[item / nblk] : item / nblk;
+        const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
+        if (count == 0)
+            continue;                             // whole workgroup (only without the work list)
+        gate_up_item<A_BF16, FP4, WIDE>(p, e, (item % nblk) * kGroupNeurons, count, slots, xs, row_slots, row_u);
+        __syncthreads();                          // the next item rewrites the slot list and the x tiles
+    }
+}
+
 template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
-moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u)
+moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, false>(p, row_slots, row_u);
+    gate_up_grouped_body<A_BF16, FP4, false>(p, row_slots, row_u, wl_off);
 }
 
 // The wide loads need 8 KiB of LDS per wavefront, so two workgroups share a CU;
 // the register budget is set to match (two wavefronts per SIMD).
 template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave, 2)
-moe_gate_up_grouped_wide_kernel(GateUpArgs p, int row_slots, int row_u)
+moe_gate_up_grouped_wide_kernel(GateUpArgs p, int row_slots, int row_u, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, true>(p, row_slots, row_u);
+    gate_up_grouped_body<A_BF16, FP4, true>(p, row_slots, row_u, wl_off);
 }
 
-size_t gate_up_grouped_lds(int B, int k, bool wide)
+size_t gate_up_grouped_lds(int B, int k, int E, bool wide)
 {
-    // slot list (rounded up to 16 bytes), two buffers of x tiles, and with the
-    // wide loads one 8 KiB region per wavefront
+    // slot list (rounded up to 16 bytes), two buffers of x tiles, with the
+    // wide loads one 8 KiB region per wavefront, then the work list
     const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
     return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) +
-           (wide ? (size_t)kGroupWaves * kWideUnitsPerWave * sizeof(u32x4) : 0);
+           (wide ? (size_t)kGroupWaves * kWideUnitsPerWave * sizeof(u32x4) : 0) + worklist_lds(E);
 }
 
 template <bool A_BF16, bool FP4, bool WIDE>
 hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int row_slots,
-                          int row_u)
+                          int row_u, int wl_off)
 {
     if constexpr (WIDE) {
         // allow dynamic LDS beyond the default 64 KiB, once per process: up to
@@ -651,9 +675,10 @@ hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, cons
                                 65536 + kGroupWaves * kWideUnitsPerWave * (int)sizeof(u32x4));
         if (attr != hipSuccess)
             return attr;
-        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u);
+        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u,
+                           wl_off);
     } else {
-        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u);
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u, wl_off);
     }
     return hipGetLastError();
 }
@@ -663,10 +688,19 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     if ((long)p.B * p.k == 0)
         return hipSuccess;
     const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
-    const dim3 grid((unsigned)((long)p.E * nblk));
-    const dim3 block(kGroupWaves * kWave);
+    const long items = (long)p.E * nblk;
     const bool wide = t.gu_wide != 0;
-    const size_t lds = gate_up_grouped_lds(p.B, p.k, wide);
+    const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide);
+    const size_t wl = worklist_lds(p.E);
+    // with the work list: at most gu_grid workgroups (and at least one per
+    // neuron block, for the invalid-slot pass) walk the routed experts' items
+    const bool use_wl = wl > 0 && t.gu_grid > 0;
+    const int wl_off = use_wl ? (int)((lds - wl) / sizeof(int)) : -1;
+    long nwg = use_wl && items > t.gu_grid ? t.gu_grid : items;
+    if (nwg < nblk)
+        nwg = nblk;
+    const dim3 grid((unsigned)nwg);
+    const dim3 block(kGroupWaves * kWave);
     const bool fp4 = p.wfmt == kMXFP4;
     // row path: experts with at most row_slots slots whose x rows fit in the
     // x-tile space (2 * kTiles * kXUnitsPerTile units of 16 bytes)
@@ -683,16 +717,16 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
         row_u *= 2;
     if (fp4) {
         if (a_bf16)
-            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, row_slots, row_u)
-                        : launch_grouped<true, true, false>(grid, block, lds, s, p, row_slots, row_u);
-        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, row_slots, row_u)
-                    : launch_grouped<false, true, false>(grid, block, lds, s, p, row_slots, row_u);
+            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
+                        : launch_grouped<true, true, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
+        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
+                    : launch_grouped<false, true, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
     }
     if (a_bf16)
-        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, row_slots, row_u)
-                    : launch_grouped<true, false, false>(grid, block, lds, s, p, row_slots, row_u);
-    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, row_slots, row_u)
-                : launch_grouped<false, false, false>(grid, block, lds, s, p, row_slots, row_u);
+        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
+                    : launch_grouped<true, false, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
+    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
+                : launch_grouped<false, false, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
 }
 
 }  // namespace moed

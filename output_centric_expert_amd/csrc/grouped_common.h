@@ -92,4 +92,45 @@ __device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, 
     return total;
 }
 
+// Work list of the grouped kernels. Without it the grid has one workgroup
+// per (expert, block) for all E experts, and a workgroup whose expert got no
+// slot still pays for the slot compaction before it leaves -- at batch 64 of
+// 256 experts most of the grid. With it, every workgroup builds the same list
+// of the routed experts in its LDS and walks the items (routed-expert rank,
+// block) with a stride of the grid size. Used when E <= kWorklistMaxE.
+constexpr int kWorklistMaxE = 1024;
+
+// LDS bytes of the work list: E marks and the list of routed experts (at
+// most E).
+inline size_t worklist_lds(int E)
+{
+    return E <= kWorklistMaxE ? ((size_t)2 * (size_t)E + 3) / 4 * 16 : 0;
+}
+
+// act[0..n) = the experts with at least one slot routed to them (ids in
+// [0, E)), in increasing order; mark is E ints of scratch. Returns n. All
+// threads of the workgroup must call it.
+__device__ __forceinline__ int routed_experts(int n_slots, const int* ids, int E, int* mark, int* act, int* wave_cnt)
+{
+    constexpr int kChunk = kGroupWaves * kWave;
+    const int tid = threadIdx.x;
+    for (int t = tid; t < E; t += kChunk)
+        mark[t] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_slots; base += 4 * kChunk) {
+        int v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {             // four ids per thread in flight at once
+            const int t = base + c * kChunk + tid;
+            v[c] = t < n_slots ? ids[t] : -1;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if ((unsigned)v[c] < (unsigned)E)
+                mark[v[c]] = 1;                   // equal values: any order of the stores
+    }
+    __syncthreads();
+    return compact_slots(E, mark, act, wave_cnt, [](int v) { return v != 0; });
+}
+
 }  // namespace moed

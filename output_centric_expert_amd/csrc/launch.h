@@ -39,6 +39,9 @@ struct Tuning {
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
     int dn_onepass = 1; // down (staged, one output per wavefront): 1 = straight-line kernel when the
                         // token's slots form one group and a row is one chunk per lane
+    int gu_grid = 1024; // grouped gate/up: at most this many workgroups walk the items of the routed
+                        // experts (0 = one workgroup per item of all E experts, empty ones included)
+    int dn_grid = 2048; // expert-major down: the same for its items
     int dn_order = 1;   // down workgroup order: 0 = token-major; 1 = hidden-major, each XCD
                         // taking a contiguous range; 2 = hidden-major, plain round robin
 };
@@ -74,7 +77,7 @@ struct DownArgs {
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
-size_t gate_up_grouped_lds(int B, int k, bool wide);
+size_t gate_up_grouped_lds(int B, int k, int E, bool wide);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 // One-pass down (float32 a, streaming loads, 8 wavefronts per workgroup): k = groups * jb slots,
 // rows of at most 64/groups chunks; hipErrorInvalidValue for a (jb, groups) it has no kernel for.
@@ -84,9 +87,9 @@ hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStrea
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Expert-major down (y: B*k*H float32 per-slot partials, then out).
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               int row_tiles, hipStream_t s);
-size_t down_grouped_lds(int B, int k, bool a_bf16, int max_tiles);
-int down_grouped_tiles(int B, int k, bool a_bf16, int requested);   // 0: does not fit
+                               int row_tiles, int grid_cap, hipStream_t s);
+size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles);
+int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested);   // 0: does not fit
 // Router front-end (router.hip): top-k of float32 logits with renormalised
 // softmax weights, plus shared-expert slots.
 constexpr int kRouteMaxE = 2048;

@@ -62,7 +62,7 @@ moed::Tuning pick(int B, int H, int I)
 bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel
-    if (moed::gate_up_grouped_lds(B, k, false) > 65536 || t.gu_group == 0)
+    if (moed::gate_up_grouped_lds(B, k, E, false) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
@@ -83,7 +83,7 @@ int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16)
 {
     if (t.dn_group == 0 || (t.dn_group == 2 && (long)B * k < 2L * E))
         return 0;
-    return moed::down_grouped_tiles(B, k, a_bf16, t.dn_tiles);
+    return moed::down_grouped_tiles(B, k, E, a_bf16, t.dn_tiles);
 }
 
 hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, float* y,
@@ -91,7 +91,7 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
 {
     if (y) {
         if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16))
-            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, s);
+            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, t.dn_grid, s);
     }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
@@ -390,6 +390,8 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_lanegroups") && (v == 0 || v == 1)) t.dn_lanegroups = (int)v;
         else if (!strcmp(tok, "dn_onepass") && (v == 0 || v == 1)) t.dn_onepass = (int)v;
         else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;
+        else if (!strcmp(tok, "gu_grid") && v >= 0 && v <= 65536) t.gu_grid = (int)v;
+        else if (!strcmp(tok, "dn_grid") && v >= 0 && v <= 65536) t.dn_grid = (int)v;
         else return MOED_ERR_SHAPE;
     }
     g_tuning = t;

@@ -164,6 +164,9 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"dn_onepass=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_exact=0") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_exact=2") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_grid=0,dn_grid=65536") == md.MOED_OK
+    assert lib.moed_set_tuning(b"dn_grid=-1") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"grp_grid=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(None) == md.MOED_OK

@@ -236,7 +236,8 @@ def test_ragged_shapes(shape):
                                   "dn_order=2,dn_wpb=5,nt=0", "dn_lanegroups=0", "dn_lanegroups=1,dn_umax=1",
                                   "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0",
                                   "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5",
-                                  "dn_onepass=0", "gu_exact=0", "gu_exact=0,dn_onepass=0,dn_rows=1"])
+                                  "dn_onepass=0", "gu_exact=0", "gu_exact=0,dn_onepass=0,dn_rows=1",
+                                  "gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_grid=3,dn_grid=5,gu_group=1,dn_group=1"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
@@ -706,3 +707,38 @@ def test_straight_line_kernels_match_generic(shape, wformat):
     check_f32(got[None][1][good], ref, f"straight-line {shape} {wformat}")
     if B > 1:
         assert torch.isnan(got[None][1][B - 1]).all()
+
+
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(64, 40, 8, 512, 256, 1.1),    # skewed: a few hot experts, many empty ones
+                                   (24, 16, 4, 1024, 384, 0.0),   # every expert routed
+                                   (48, 300, 8, 256, 128, 1.1)])  # E beyond one item per routed expert
+def test_grouped_work_list_matches_full_grid(shape, wformat):
+    """The grouped gate/up and the expert-major down give the same bits whether the grid has one
+    workgroup per item of all E experts (gu_grid=dn_grid=0) or a few workgroups walk the routed experts'
+    items (the work list, at the built-in grid cap and at a cap of 5); an invalid id on the last
+    token gives NaN there on every form."""
+    B, E, k, H, I, zipf = shape
+    L = synth.make_layer(synth.LayerShape("wl", B, E, k, H, I, zipf), seed=B + E, device="cuda", wformat=wformat)
+    ids = L.ids.copy()
+    ids[B - 1, 1] = -3
+    x, _, wd = md.layer_device_inputs(L)
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    got = []
+    for spec in ["gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_group=1,dn_group=1",
+                 "gu_grid=5,dn_grid=3,gu_group=1,dn_group=1"]:
+        md.moed_set_tuning(spec)
+        try:
+            say(f"work list {shape} {wformat} {spec}")
+            out = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                                out_dtype=torch.float32, wformat=wformat)
+            torch.cuda.synchronize()
+            got.append(out.clone())
+        finally:
+            md.moed_set_tuning(None)
+    for g in got[1:]:
+        assert torch.equal(torch.isnan(g), torch.isnan(got[0]))
+        assert torch.equal(g[:B - 1].view(torch.int32), got[0][:B - 1].view(torch.int32)), f"{shape} {wformat}"
+    assert torch.isnan(got[0][B - 1]).all()
+    ref, _ = oracle_tokens(L, [0, B // 2, B - 2], ids=ids, wformat=wformat)
+    check_f32(got[1][[0, B // 2, B - 2]], ref, f"work list {shape} {wformat}")
