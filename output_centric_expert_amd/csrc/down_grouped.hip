@@ -36,18 +36,19 @@ namespace {
 
 constexpr int kDnUnits = 16 * 16;                // 16-byte units per tile and K group (one of hi / lo)
 
-// 8 float32 values -> 8 bf16 hi and 8 bf16 lo (hi + lo = v to about 2^-17 relative).
+// 8 float32 values -> 8 bf16 hi and 8 bf16 lo (hi + lo = v to about 2^-17
+// relative): hi = RNE(v), lo = RNE(v - hi), two values per conversion.
 __device__ __forceinline__ void split8(const f32x4& v0, const f32x4& v1, u32x4& hi, u32x4& lo)
 {
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        h[t] = f32_to_bf16_rne(v[t]);
-        l[t] = f32_to_bf16_rne(v[t] - __uint_as_float(h[t] << 16));
+    for (int t = 0; t < 4; ++t) {
+        h[t] = f32x2_to_bf16x2_rne(v[2 * t], v[2 * t + 1]);
+        l[t] = f32x2_to_bf16x2_rne(v[2 * t] - bf16_lo(h[t]), v[2 * t + 1] - bf16_hi(h[t]));
     }
-    hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 // a[s][i0 .. i0+7] (i0 a multiple of 8) from the chunk-interleaved
@@ -372,8 +373,8 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
         acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     const size_t o = (size_t)b * (size_t)H + (size_t)h;
     if constexpr (OUT_BF16) {
-        const uint32_t lo = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-        const uint32_t hi = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+        const uint32_t lo = f32x2_to_bf16x2_rne(acc.x, acc.y);
+        const uint32_t hi = f32x2_to_bf16x2_rne(acc.z, acc.w);
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = u32x2{lo, hi};
     } else {
         *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc;

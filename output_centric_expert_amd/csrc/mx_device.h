@@ -163,14 +163,19 @@ __device__ __forceinline__ int xcd_contiguous(int i, int n)
     return x * q + (x < r ? x : r) + slot;
 }
 
-// float32 -> bfloat16 bits, round to nearest even; NaN stays a (quiet) NaN.
+// Two float32 -> two bfloat16, round to nearest even (v_cvt_pk_bf16_f32), a
+// in the low half. NaN stays NaN. Over all 2^32 float32 inputs it gives the
+// same bits as rounding the bit pattern (add 0x7FFF plus the kept lsb, keep
+// the high half) for every non-NaN input, and a NaN exactly for NaN inputs.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// float32 -> bfloat16 bits, round to nearest even; NaN stays a NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return (uint16_t)(f32x2_to_bf16x2_rne(f, 0.0f) & 0xFFFFu);
 }
 
 // Position of a[b][j][i] (bj = b*k + j) in the intermediate buffer. The
