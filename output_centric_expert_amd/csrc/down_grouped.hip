@@ -101,7 +101,8 @@ struct DnRow {
 
 struct DnGroupW {
     u32x4 c0, c1;           // codes of the lane's MX block in the group (c1: MXFP8 only)
-    float sc;
+    uint32_t sb;            // its UE8M0 scale byte, as loaded (turned into a float only when
+                            // decoded: converting at the load would wait for it there)
 };
 
 template <bool FP4, int RT>
@@ -113,7 +114,7 @@ __device__ __forceinline__ void load_dn_w(const DnRow<RT>& r, int g, DnGroupW (&
     for (int t = 0; t < RT; ++t) {
         w[t].c0 = *reinterpret_cast<const u32x4*>(r.q[t] + bbase);
         w[t].c1 = FP4 ? w[t].c0 : *reinterpret_cast<const u32x4*>(r.q[t] + bbase + 16);
-        w[t].sc = ue8m0_to_f32(r.s[t][4 * g + r.kb]);
+        w[t].sb = r.s[t][4 * g + r.kb];
     }
 }
 
@@ -121,10 +122,11 @@ __device__ __forceinline__ void load_dn_w(const DnRow<RT>& r, int g, DnGroupW (&
 template <bool FP4>
 __device__ __forceinline__ bf16x8 dn_decode(const DnGroupW& w, int q)
 {
+    const float sc = ue8m0_to_f32(w.sb);
     if constexpr (FP4)
-        return decode8_scaled_fp4(w.c0[q], w.sc);
+        return decode8_scaled_fp4(w.c0[q], sc);
     const u32x4 src = q < 2 ? w.c0 : w.c1;
-    return decode8_scaled((q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y}, w.sc);
+    return decode8_scaled((q & 1) ? u32x2{src.z, src.w} : u32x2{src.x, src.y}, sc);
 }
 
 }  // namespace
@@ -199,8 +201,11 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
     auto group = [&](auto par, int g, DnGroupW (&w)[RT]) {
         constexpr int P = decltype(par)::value;
         const u32x4* xb = xs + (g & 1) * kBuf;
-        if (g + 2 < ngroups)
-            load_a(raw[P], g + 2);
+        // unconditional (the last two groups re-read the last one): a load
+        // behind a branch makes the compiler wait for every load at the join,
+        // the ones just issued two groups ahead included
+        load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 aw[RT][4];
 #pragma unroll
         for (int t = 0; t < RT; ++t)
@@ -208,6 +213,9 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
             for (int q = 0; q < 4; ++q)
                 aw[t][q] = dn_decode<FP4>(w[t], q);
         load_dn_w<FP4>(r, g + 2 < ngroups ? g + 2 : ngroups - 1, w);   // two groups ahead
+        // the group's loads stay ahead of its other work (the split of the next
+        // group's a would otherwise be hoisted above them, waiting for older loads first)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = 4 * r.kb + q;
@@ -226,15 +234,19 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
                 }
             }
         }
-        if (g + 1 < ngroups)
-            put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
+        // (after the last group this fills the other buffer with a copy nobody reads)
+        put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
         __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
     };
-    for (int g = 0; g < ngroups; g += 2) {
+    // pairs of groups with no branch inside the loop body, so the wait before
+    // each group's decode covers exactly that group's weights and not the loads
+    // in flight behind them
+    for (int g = 0; g + 1 < ngroups; g += 2) {
         group(std::integral_constant<int, 0>{}, g, wA);
-        if (g + 1 < ngroups)
-            group(std::integral_constant<int, 1>{}, g + 1, wB);
+        group(std::integral_constant<int, 1>{}, g + 1, wB);
     }
+    if (ngroups & 1)
+        group(std::integral_constant<int, 0>{}, ngroups - 1, wA);
     for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
         const int k0 = st * 32 + 8 * r.kb;
         bf16x8 aw[RT];
