@@ -377,15 +377,26 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
     __syncthreads();
     // group g (parity P): x of g+2 into set P, the MFMAs on buffer g&1, x of
     // g+1 (set 1-P) into the other buffer
+    // No branch around a load in the step loop (the last groups re-read the last
+    // group's x, the last step re-reads the last step): a load behind a branch
+    // makes the compiler wait for every load at the join, the ones issued a
+    // group or a step ahead included. After the last group put_x fills the
+    // other buffer with a copy nobody reads.
+    // group g uses x set P = g&1: the caller first requests x of g+2 into it
+    // (xload) -- before a step's rows, so that waiting for that x later never
+    // waits for rows issued behind it
+    auto xload = [&](auto par, int g) {
+        constexpr int P = decltype(par)::value;
+        load_x(xq[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
+    };
     auto group = [&](auto par, int g, const GroupW& wc) {
         constexpr int P = decltype(par)::value;
-        if (g + 2 < ngroups)
-            load_x(xq[P], g + 2);
         group_mfma<NTL, FP4>(wc, xs + (g & 1) * kBuf, r, dg, du);
-        if (g + 1 < ngroups)
-            put_x(xq[1 - P], g + 1);
+        put_x(xq[1 - P], g + 1 < ngroups ? g + 1 : ngroups - 1);
         __syncthreads();
     };
+    constexpr auto P0 = std::integral_constant<int, 0>{};
+    constexpr auto P1 = std::integral_constant<int, 1>{};
     for (int s = 0; s < nst; ++s) {
         stage_step<FP4>(sw, tb, lane);
         float gsc[GPS], usc[GPS];
@@ -395,25 +406,28 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
             usc[h] = ue8m0_to_f32(sw.us[h]);
         }
         const int g0 = s * GPS;                   // even: the parity of group g0 + h is that of h
-        {
-            if (GPS == 2 && s + 1 < nst)          // MXFP8: next step during the first group
-                sw = load_step<FP4>(gq0, uq0, rstride, r, s + 1, lane);
-            group(std::integral_constant<int, 0>{}, g0, staged_group<FP4>(tb, r, 0, gsc[0], usc[0]));
-        }
-        {
-            group(std::integral_constant<int, 1>{}, g0 + 1, staged_group<FP4>(tb, r, 1, gsc[1], usc[1]));
-        }
+        const int snext = s + 1 < nst ? s + 1 : s;
+        xload(P0, g0);
+        if constexpr (GPS == 2)                   // MXFP8: next step during the first group
+            sw = load_step<FP4>(gq0, uq0, rstride, r, snext, lane);
+        group(P0, g0, staged_group<FP4>(tb, r, 0, gsc[0], usc[0]));
+        xload(P1, g0 + 1);
+        group(P1, g0 + 1, staged_group<FP4>(tb, r, 1, gsc[1], usc[1]));
         if constexpr (GPS == 4) {                 // MXFP4: next step during the third group
-            if (s + 1 < nst)
-                sw = load_step<FP4>(gq0, uq0, rstride, r, s + 1, lane);
-            group(std::integral_constant<int, 0>{}, g0 + 2, staged_group<FP4>(tb, r, 2, gsc[2], usc[2]));
-            group(std::integral_constant<int, 1>{}, g0 + 3, staged_group<FP4>(tb, r, 3, gsc[3], usc[3]));
+            xload(P0, g0 + 2);
+            sw = load_step<FP4>(gq0, uq0, rstride, r, snext, lane);
+            group(P0, g0 + 2, staged_group<FP4>(tb, r, 2, gsc[2], usc[2]));
+            xload(P1, g0 + 3);
+            group(P1, g0 + 3, staged_group<FP4>(tb, r, 3, gsc[3], usc[3]));
         }
     }
     for (int g = nst * GPS; g < ngroups; g += 2) {   // groups after the last whole step (g even)
-        group(std::integral_constant<int, 0>{}, g, load_group_w<FP4>(r, g));
-        if (g + 1 < ngroups)
-            group(std::integral_constant<int, 1>{}, g + 1, load_group_w<FP4>(r, g + 1));
+        xload(P0, g);
+        group(P0, g, load_group_w<FP4>(r, g));
+        if (g + 1 < ngroups) {
+            xload(P1, g + 1);
+            group(P1, g + 1, load_group_w<FP4>(r, g + 1));
+        }
     }
     leftover_blocks<NTL, FP4>(r, xr, dg, du);
     if (store)
