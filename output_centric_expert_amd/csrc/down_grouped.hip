@@ -288,12 +288,273 @@ __device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<
     }
 }
 
+// Wide weight loads. The 128-byte row slices above (lane group kb of a 16-row
+// tile reads 32 bytes of each row per group) keep the weight stream near
+// 4.5 TB/s; runs of 256 bytes per row go faster (the same change in the
+// grouped gate/up). The wavefront reads its 16*RT rows in steps of 256 bytes
+// per row (two 128-code groups of MXFP8, four of MXFP4): load i of lane L
+// takes the 16-byte piece L % 16 of row L / 16 + 4i, so each load instruction
+// covers four whole 256-byte runs. A step goes through a wavefront-private LDS
+// region of 16*RT rows x 16 pieces (piece b of row n at unit 16n + (b ^ (n % 16)),
+// free of bank conflicts for the writes and the operand reads), and lane
+// (col, kb) reads for group h of the step the pieces holding MX block 4h + kb
+// of its rows: the codes load_dn_w gives it, so the results are the same floats.
+template <bool FP4, int RT>
+struct DnStep {
+    static constexpr int kGroups = FP4 ? 4 : 2;  // 128-code groups per 256-byte step
+    u32x4 v[4 * RT];                             // pieces of rows L/16 + 4i
+    uint32_t sb[kGroups][RT];                    // scale bytes (as loaded) of the lane's rows, block kb
+};
+
+// 16-byte LDS units of one step, per wavefront
+template <int RT>
+constexpr int kDnWideUnits = 16 * RT * 16;
+
+template <bool FP4, int RT>
+__device__ __forceinline__ void load_dn_step(const uint8_t* q0, size_t rstride, const DnRow<RT>& r, int step,
+                                             int lane, DnStep<FP4, RT>& w)
+{
+    const size_t off = (size_t)step * 256 + 16 * (size_t)(lane % 16);
+#pragma unroll
+    for (int i = 0; i < 4 * RT; ++i)
+        w.v[i] = *reinterpret_cast<const u32x4*>(q0 + (size_t)(lane / 16 + 4 * i) * rstride + off);
+#pragma unroll
+    for (int h = 0; h < DnStep<FP4, RT>::kGroups; ++h)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            w.sb[h][t] = r.s[t][4 * (step * DnStep<FP4, RT>::kGroups + h) + r.kb];
+}
+
+template <bool FP4, int RT>
+__device__ __forceinline__ void stage_dn_step(const DnStep<FP4, RT>& w, u32x4* tb, int lane)
+{
+    const int b = lane % 16;
+#pragma unroll
+    for (int i = 0; i < 4 * RT; ++i) {
+        const int n = lane / 16 + 4 * i;
+        tb[n * 16 + (b ^ (n & 15))] = w.v[i];
+    }
+}
+
+// Group h of the staged step, row tile t: the lane's codes of MX block 4h + kb.
+template <bool FP4, int RT>
+__device__ __forceinline__ DnGroupW staged_dn_group(const u32x4* tb, const DnRow<RT>& r, int h, int t,
+                                                    uint32_t sb)
+{
+    const u32x4* row = tb + (16 * t + r.col) * 16;
+    DnGroupW w;
+    if constexpr (FP4) {                         // block 4h + kb = piece 4h + kb
+        w.c0 = row[(4 * h + r.kb) ^ r.col];
+        w.c1 = w.c0;
+    } else {                                     // block 4h + kb = pieces 8h + 2kb, +1
+        w.c0 = row[(8 * h + 2 * r.kb) ^ r.col];
+        w.c1 = row[(8 * h + 2 * r.kb + 1) ^ r.col];
+    }
+    w.sb = sb;
+    return w;
+}
+
+// expert_down_pass with the wide weight loads: one step of weights in flight
+// ahead (requested once the group before the step's last two has taken its a
+// loads), the slots' a two groups ahead as before; each wait for a group's a
+// therefore never waits for rows issued behind it. Groups after the last whole
+// step load their 128-byte slices directly; leftover blocks as in
+// expert_down_pass. q0 / rstride: the wavefront's first row and its row stride
+// (0 for a wavefront past H, which reads row H-1 throughout); tb: its LDS region.
+template <int NTL, int RT, bool A_BF16, bool FP4>
+__device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const DnRow<RT>& r, const uint8_t* q0,
+                                                      size_t rstride, const int* slots, int count, int t0,
+                                                      u32x4* xs, u32x4* tb, bool store, int h0, float* y)
+{
+    constexpr int GPS = DnStep<FP4, RT>::kGroups;
+    const int I = p.I;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int lcol = tid / 16;
+    const int lc = tid % 16;
+    constexpr int kHalf = NTL * kDnUnits;
+    constexpr int kBuf = (A_BF16 ? 1 : 2) * kHalf;
+    int ls[NTL];
+    int bj[NTL];
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        const int sl = (t0 + tt) * 16 + lcol;
+        ls[tt] = slots[sl < count ? sl : count - 1];
+        const int si = (t0 + tt) * 16 + r.col;
+        bj[tt] = slots[si < count ? si : count - 1];
+    }
+    f32x4 d[RT][NTL];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            d[t][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ngroups = r.nsteps / 4;
+    const int nst = ngroups / GPS;                // whole 256-byte steps
+    ARaw<A_BF16> raw[2][NTL];                     // a of groups g+1 and g+2, by group parity
+    auto load_a = [&](ARaw<A_BF16> (&dst)[NTL], int g) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            dst[tt] = load_a8<A_BF16>(p.a, ls[tt], g * 128 + 8 * lc, I);
+    };
+    auto put_a = [&](const ARaw<A_BF16> (&src)[NTL], u32x4* buf) {
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            u32x4 hi, lo;
+            split_a8<A_BF16>(src[tt], hi, lo);
+            const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
+            buf[u] = hi;
+            if constexpr (!A_BF16)
+                buf[kHalf + u] = lo;
+        }
+    };
+    DnStep<FP4, RT> sw{};
+    if (ngroups > 0) {
+        load_a(raw[0], 0);
+        if (ngroups > 1)
+            load_a(raw[1], 1);
+        if (nst > 0)
+            load_dn_step<FP4, RT>(q0, rstride, r, 0, lane, sw);
+        put_a(raw[0], xs);
+    }
+    __syncthreads();
+    // a of group g+2 into set P = g & 1 (unconditional: the last groups re-read
+    // the last group's a, so no load sits behind a branch)
+    // (the scheduling barrier keeps the loads issued ahead of the group's other
+    // work: the split of the next group's a would otherwise be hoisted above
+    // them and wait for every older load first)
+    auto aload = [&](auto par, int g) {
+        constexpr int P = decltype(par)::value;
+        load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // group g: the MFMAs on buffer g&1, then a of g+1 (set 1-P) split into the other buffer
+    auto group = [&](auto par, int g, const DnGroupW (&w)[RT]) {
+        constexpr int P = decltype(par)::value;
+        const u32x4* xb = xs + (g & 1) * kBuf;
+        bf16x8 aw[RT][4];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                aw[t][q] = dn_decode<FP4>(w[t], q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 4 * r.kb + q;
+#pragma unroll
+            for (int tt = 0; tt < NTL; ++tt) {
+                const int u = (tt * 16 + r.col) * 16 + (c ^ r.col);
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, xb[u]);
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bh, d[t][tt], 0, 0, 0);
+                if constexpr (!A_BF16) {
+                    const bf16x8 bl = __builtin_bit_cast(bf16x8, xb[kHalf + u]);
+#pragma unroll
+                    for (int t = 0; t < RT; ++t)
+                        d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bl, d[t][tt], 0, 0, 0);
+                }
+            }
+        }
+        put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
+        __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
+    };
+    constexpr auto P0 = std::integral_constant<int, 0>{};
+    constexpr auto P1 = std::integral_constant<int, 1>{};
+    for (int s = 0; s < nst; ++s) {
+        stage_dn_step<FP4, RT>(sw, tb, lane);
+        const int g0 = s * GPS;                   // even: the parity of group g0 + h is that of h
+        const int snext = s + 1 < nst ? s + 1 : s;
+        DnGroupW w[RT];
+        uint32_t sbk[GPS][RT];                    // this step's scale bytes (sw is refilled below)
+#pragma unroll
+        for (int h = 0; h < GPS; ++h)
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                sbk[h][t] = sw.sb[h][t];
+        auto staged_k = [&](int h) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, sbk[h][t]);
+        };
+        aload(P0, g0);
+        if constexpr (GPS == 2) {                 // MXFP8: next step during the first group
+            load_dn_step<FP4, RT>(q0, rstride, r, snext, lane, sw);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        staged_k(0);
+        group(P0, g0, w);
+        aload(P1, g0 + 1);
+        staged_k(1);
+        group(P1, g0 + 1, w);
+        if constexpr (GPS == 4) {                 // MXFP4: next step during the third group
+            aload(P0, g0 + 2);
+            load_dn_step<FP4, RT>(q0, rstride, r, snext, lane, sw);
+            __builtin_amdgcn_sched_barrier(0);
+            staged_k(2);
+            group(P0, g0 + 2, w);
+            aload(P1, g0 + 3);
+            staged_k(3);
+            group(P1, g0 + 3, w);
+        }
+    }
+    for (int g = nst * GPS; g < ngroups; g += 2) {   // groups after the last whole step (g even)
+        DnGroupW w[RT];
+        aload(P0, g);
+        load_dn_w<FP4>(r, g, w);
+        group(P0, g, w);
+        if (g + 1 < ngroups) {
+            aload(P1, g + 1);
+            load_dn_w<FP4>(r, g + 1, w);
+            group(P1, g + 1, w);
+        }
+    }
+    for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
+        const int k0 = st * 32 + 8 * r.kb;
+        bf16x8 aw[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            if constexpr (FP4)
+                aw[t] = decode8_scaled_fp4(*reinterpret_cast<const uint32_t*>(r.q[t] + k0 / 2),
+                                           ue8m0_to_f32(r.s[t][st]));
+            else
+                aw[t] = decode8_scaled(*reinterpret_cast<const u32x2*>(r.q[t] + k0), ue8m0_to_f32(r.s[t][st]));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt) {
+            u32x4 hi, lo;
+            split_a8<A_BF16>(load_a8<A_BF16>(p.a, bj[tt], k0, I), hi, lo);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, hi), d[t][tt],
+                                                                   0, 0, 0);
+                if constexpr (!A_BF16)
+                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, lo),
+                                                                       d[t][tt], 0, 0, 0);
+            }
+        }
+    }
+    if (!store)
+        return;
+#pragma unroll
+    for (int tt = 0; tt < NTL; ++tt) {
+        if ((t0 + tt) * 16 + r.col < count) {
+            const int s = bj[tt];
+            const float wgt = p.w[s];
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                *reinterpret_cast<f32x4*>(y + (size_t)s * (size_t)p.H + (size_t)(h0 + 16 * t + 4 * r.kb)) =
+                    wgt * d[t][tt];
+        }
+    }
+}
+
 // An item is (expert e, RT*64 rows); wavefront w takes the rows
 // hb + 16*RT*w .. +16*RT-1. H is a multiple of 16*RT. wl_off >= 0: the work
 // list sits wl_off ints into the dynamic LDS and the workgroups walk the
 // items of the routed experts with a stride of the grid size; wl_off < 0: one
 // item per workgroup over all E experts (the grid is E * blocks).
-template <int RT, bool A_BF16, bool FP4>
+template <int RT, bool A_BF16, bool FP4, bool WIDE>
 __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, int max_tiles, int e, int hb,
                                                  int count, const int* slots, u32x4* xs)
 {
@@ -315,6 +576,29 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
     r.kb = lane / 16;
     r.col = col;
     const int ntiles = (count + 15) / 16;
+    if constexpr (WIDE) {
+        // the wavefront's first row (all rows clamped to H-1 past H), its row
+        // stride, and its LDS region after the a tiles
+        const uint8_t* q0 = p.wd_q + ((size_t)e * (size_t)p.H + (size_t)(store ? h0 : p.H - 1)) * row_bytes;
+        const size_t rstride = store ? row_bytes : 0;
+        u32x4* tb = xs + 2 * (A_BF16 ? 1 : 2) * max_tiles * kDnUnits + w * kDnWideUnits<RT>;
+        // at most 2 tiles of float32 a (3 of bf16) per pass here: the step
+        // registers take the place of the last tile's (the launcher sizes the
+        // LDS for the same)
+        constexpr int kCap = A_BF16 ? 3 : 2;
+        const int mt = max_tiles < kCap ? max_tiles : kCap;
+        for (int t0 = 0; t0 < ntiles; t0 += mt) {
+            const int nt = ntiles - t0 < mt ? ntiles - t0 : mt;
+            if (nt == 1) {
+                expert_down_pass_wide<1, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+            } else if (nt == 2) {
+                expert_down_pass_wide<2, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+            } else if constexpr (A_BF16) {
+                expert_down_pass_wide<3, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+            }
+        }
+        return;
+    }
     for (int t0 = 0; t0 < ntiles; t0 += max_tiles) {
         const int nt = ntiles - t0 < max_tiles ? ntiles - t0 : max_tiles;
         switch (nt) {
@@ -329,7 +613,7 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
     }
 }
 
-template <int RT, bool A_BF16, bool FP4>
+template <int RT, bool A_BF16, bool FP4, bool WIDE>
 __global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
 moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
 {
@@ -353,7 +637,7 @@ moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
         const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
         if (count == 0)
             continue;                             // whole workgroup (only without the work list)
-        expert_down_item<RT, A_BF16, FP4>(p, y, max_tiles, e, hb, count, slots, xs);
+        expert_down_item<RT, A_BF16, FP4, WIDE>(p, y, max_tiles, e, hb, count, slots, xs);
         __syncthreads();                          // the next item rewrites the slot list and the a tiles
     }
 }
@@ -393,26 +677,53 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
     }
 }
 
-size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles)
+size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles, int row_tiles, bool wide)
 {
     // slot list (rounded up to 16 bytes), two buffers of hi (and lo) tiles,
-    // then the work list
+    // with the wide loads one step region per wavefront, then the work list
     const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
-    return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4) + worklist_lds(E);
+    const size_t stage = wide ? (size_t)kGroupWaves * 16 * (size_t)row_tiles * 16 * sizeof(u32x4) : 0;
+    return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4) + stage + worklist_lds(E);
 }
 
-int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested)
+// Dynamic LDS limits: without the wide loads the default 64 KiB; with them up
+// to 96 KiB may be requested, and the automatic choice keeps two workgroups
+// per CU (80 KiB each).
+constexpr size_t kDnLdsMax = 65536;
+constexpr size_t kDnLdsMaxWide = 98304;
+constexpr size_t kDnLdsAutoWide = 81920;
+
+int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested, int row_tiles, bool wide)
 {
-    if (requested > 0)
-        return down_grouped_lds(B, k, E, a_bf16, requested) <= 65536 ? requested : 0;
-    for (int mt = kTiles; mt >= 1; --mt)
-        if (down_grouped_lds(B, k, E, a_bf16, mt) <= 65536)
+    const int cap = wide ? (a_bf16 ? 3 : 2) : kTiles;   // wide loads: 2 tiles of float32 a, 3 of bf16
+    if (requested > 0) {
+        const int mt = requested < cap ? requested : cap;
+        return down_grouped_lds(B, k, E, a_bf16, mt, row_tiles, wide) <= (wide ? kDnLdsMaxWide : kDnLdsMax) ? mt : 0;
+    }
+    for (int mt = cap; mt >= 1; --mt)
+        if (down_grouped_lds(B, k, E, a_bf16, mt, row_tiles, wide) <= (wide ? kDnLdsAutoWide : kDnLdsMax))
             return mt;
     return 0;
 }
 
+template <int RT, bool A, bool F, bool W>
+hipError_t launch_expert(dim3 grid, dim3 block, size_t lds, hipStream_t s, const DownArgs& p, float* y,
+                         int max_tiles, int wl_off)
+{
+    if constexpr (W) {
+        // allow dynamic LDS beyond the default 64 KiB, once per process
+        static const hipError_t attr =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_down_expert_kernel<RT, A, F, W>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDnLdsMaxWide);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F, W>), grid, block, lds, s, p, y, max_tiles, wl_off);
+    return hipGetLastError();
+}
+
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               int row_tiles, int grid_cap, hipStream_t s)
+                               int row_tiles, bool wide, int grid_cap, hipStream_t s)
 {
     if ((long)p.B * p.k == 0)
         return hipSuccess;
@@ -421,24 +732,27 @@ hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, fl
         return hipErrorInvalidValue;
     const int nblk = (p.H + 16 * row_tiles * kGroupWaves - 1) / (16 * row_tiles * kGroupWaves);
     const long items = (long)p.E * nblk;
-    const size_t lds = down_grouped_lds(p.B, p.k, p.E, a_bf16, max_tiles);
+    const size_t lds = down_grouped_lds(p.B, p.k, p.E, a_bf16, max_tiles, row_tiles, wide);
+    if (lds > (wide ? kDnLdsMaxWide : kDnLdsMax))
+        return hipErrorInvalidValue;
     const size_t wl = worklist_lds(p.E);
     // with the work list: at most grid_cap workgroups walk the routed experts' items
     const bool use_wl = wl > 0 && grid_cap > 0;
     const int wl_off = use_wl ? (int)((lds - wl) / sizeof(int)) : -1;
     const dim3 grid((unsigned)(use_wl && items > grid_cap ? grid_cap : items)), block(kGroupWaves * kWave);
     const bool fp4 = p.wfmt == kMXFP4;
-#define MOED_DX(RT, A, F) \
-    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F>), grid, block, lds, s, p, y, max_tiles, wl_off)
+    hipError_t err;
+#define MOED_DX(RT, W)                                                                                   \
+    err = fp4 ? (a_bf16 ? launch_expert<RT, true, true, W>(grid, block, lds, s, p, y, max_tiles, wl_off)  \
+                        : launch_expert<RT, false, true, W>(grid, block, lds, s, p, y, max_tiles, wl_off)) \
+              : (a_bf16 ? launch_expert<RT, true, false, W>(grid, block, lds, s, p, y, max_tiles, wl_off) \
+                        : launch_expert<RT, false, false, W>(grid, block, lds, s, p, y, max_tiles, wl_off))
     if (row_tiles == 2) {
-        if (fp4) { if (a_bf16) MOED_DX(2, true, true); else MOED_DX(2, false, true); }
-        else { if (a_bf16) MOED_DX(2, true, false); else MOED_DX(2, false, false); }
+        if (wide) MOED_DX(2, true); else MOED_DX(2, false);
     } else {
-        if (fp4) { if (a_bf16) MOED_DX(1, true, true); else MOED_DX(1, false, true); }
-        else { if (a_bf16) MOED_DX(1, true, false); else MOED_DX(1, false, false); }
+        if (wide) MOED_DX(1, true); else MOED_DX(1, false);
     }
 #undef MOED_DX
-    hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
     const long n = (long)p.B * (p.H / 4);

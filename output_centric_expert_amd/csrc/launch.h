@@ -26,6 +26,8 @@ struct Tuning {
                         // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
+    int dn_wide = 1;    // expert-major down: 1 = weight rows read in 256-byte runs per row and moved to
+                        // the operand layout through LDS; 0 = 128-byte slices per row and group
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
                         // except in the down kernel once B*k >= E (tokens then share rows)
@@ -87,9 +89,10 @@ hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStrea
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Expert-major down (y: B*k*H float32 per-slot partials, then out).
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
-                               int row_tiles, int grid_cap, hipStream_t s);
-size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles);
-int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested);   // 0: does not fit
+                               int row_tiles, bool wide, int grid_cap, hipStream_t s);
+size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles, int row_tiles, bool wide);
+// 0: does not fit
+int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested, int row_tiles, bool wide);
 // Router front-end (router.hip): top-k of float32 logits with renormalised
 // softmax weights, plus shared-expert slots.
 constexpr int kRouteMaxE = 2048;

@@ -83,7 +83,7 @@ int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16)
 {
     if (t.dn_group == 0 || (t.dn_group == 2 && (long)B * k < 2L * E))
         return 0;
-    return moed::down_grouped_tiles(B, k, E, a_bf16, t.dn_tiles);
+    return moed::down_grouped_tiles(B, k, E, a_bf16, t.dn_tiles, t.dn_rt, t.dn_wide != 0);
 }
 
 hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, float* y,
@@ -91,7 +91,7 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
 {
     if (y) {
         if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16))
-            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, t.dn_grid, s);
+            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, t.dn_wide != 0, t.dn_grid, s);
     }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
@@ -377,6 +377,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
+        else if (!strcmp(tok, "dn_wide") && v >= 0 && v <= 1) t.dn_wide = (int)v;
         else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;

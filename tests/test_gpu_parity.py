@@ -237,7 +237,8 @@ def test_ragged_shapes(shape):
                                   "gu_npw=2", "gu_npw=2,gu_umax=1,gu_wpb=3", "gu_npw=2,gu_dot=0",
                                   "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5",
                                   "dn_onepass=0", "gu_exact=0", "gu_exact=0,dn_onepass=0,dn_rows=1",
-                                  "gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_grid=3,dn_grid=5,gu_group=1,dn_group=1"])
+                                  "gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_grid=3,dn_grid=5,gu_group=1,dn_group=1",
+                                  "dn_group=1,dn_wide=0", "dn_group=1,dn_wide=1,dn_tiles=3"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
@@ -742,3 +743,49 @@ def test_grouped_work_list_matches_full_grid(shape, wformat):
     assert torch.isnan(got[0][B - 1]).all()
     ref, _ = oracle_tokens(L, [0, B // 2, B - 2], ids=ids, wformat=wformat)
     check_f32(got[1][[0, B // 2, B - 2]], ref, f"work list {shape} {wformat}")
+
+
+# (B, E, k, H, I) for the expert-major down's wide weight loads
+DOWN_WIDE = [
+    (40, 3, 2, 96, 640),      # ~27 slots per expert (2 tiles); 5 groups: whole steps + 1 group; waves past H
+    (72, 2, 2, 64, 768),      # 72 slots per expert: passes of 2 + 2 + 1 tiles (float32 a)
+    (24, 6, 4, 2080, 544),    # 17 MX blocks: 4 groups and a leftover block; waves past H in the last block
+    (20, 4, 3, 128, 448),     # 3 groups and 2 leftover blocks: no whole MXFP4 step
+    (16, 8, 8, 64, 7168),     # 56 groups per row
+]
+
+
+@pytest.mark.parametrize("rt", [2, 1])
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("shape", DOWN_WIDE, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_expert_major_down_wide_loads(shape, wformat, rt):
+    """The expert-major down's wide weight loads (256-byte runs per row, moved to the operand
+    layout through LDS) feed every MFMA the codes the 128-byte slices do, in the same order:
+    the layer output is the same floats for float32 and bf16 intermediates (an invalid id on
+    the last token gives NaN there on both), and within tolerance of the oracle."""
+    B, E, k, H, I = shape
+    L = synth.make_layer(synth.LayerShape("dwide", B, E, k, H, I), seed=sum(shape) + 41, device="cuda",
+                         wformat=wformat)
+    ids = L.ids.copy()
+    ids[B - 1, 0] = E + 2
+    x, _, wd = md.layer_device_inputs(L)
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    got = {}
+    try:
+        for wide in (0, 1):
+            md.moed_set_tuning(f"dn_group=1,dn_rt={rt},dn_wide={wide}")
+            say(f"down wide loads {shape} {wformat} rt={rt} wide={wide}")
+            for dt in (torch.float32, torch.bfloat16):
+                got[wide, dt] = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                                              out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
+            torch.cuda.synchronize()
+    finally:
+        md.moed_set_tuning(None)
+    for dt in (torch.float32, torch.bfloat16):
+        o0, o1 = got[0, dt], got[1, dt]
+        assert torch.equal(torch.isnan(o0), torch.isnan(o1))
+        assert torch.equal(o0[:B - 1].view(torch.int32), o1[:B - 1].view(torch.int32)), f"{shape} {wformat} {dt}"
+        assert torch.isnan(o1[B - 1]).all()
+    toks = [0, B // 2, B - 2]
+    ref, _ = oracle_tokens(L, toks, ids=ids, wformat=wformat)
+    check_f32(got[1, torch.float32][toks], ref, f"down wide {shape} {wformat}")
