@@ -26,8 +26,9 @@ struct Tuning {
                         // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
-    int dn_wide = 1;    // expert-major down: 1 = weight rows read in 256-byte runs per row and moved to
-                        // the operand layout through LDS; 0 = 128-byte slices per row and group
+    int dn_wide = 1;    // expert-major down: weight rows read in 256-byte runs per row and moved to the
+                        // operand layout through LDS (1 = for MXFP8 weights, 2 = for both formats),
+                        // or 0 = 128-byte slices per row and group
     int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
     int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
                         // except in the down kernel once B*k >= E (tokens then share rows)

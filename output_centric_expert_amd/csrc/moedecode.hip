@@ -79,19 +79,27 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
 // Expert-major down: used inside moe_decode (which owns a workspace for the
 // per-slot partials) once tokens share experts, about two or more slots per
 // expert on average (measured crossovers at 1.5-2 slots per expert).
-int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16)
+// The expert-major down's wide loads: dn_wide 1 = for MXFP8 weights (measured faster there, and
+// slower for MXFP4), 2 = for both formats, 0 = never.
+bool down_wide(const moed::Tuning& t, int wfmt)
+{
+    return t.dn_wide == 2 || (t.dn_wide == 1 && wfmt == moed::kMXFP8);
+}
+
+int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16, bool wide)
 {
     if (t.dn_group == 0 || (t.dn_group == 2 && (long)B * k < 2L * E))
         return 0;
-    return moed::down_grouped_tiles(B, k, E, a_bf16, t.dn_tiles, t.dn_rt, t.dn_wide != 0);
+    return moed::down_grouped_tiles(B, k, E, a_bf16, t.dn_tiles, t.dn_rt, wide);
 }
 
 hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, const moed::Tuning& t, float* y,
                        hipStream_t s)
 {
     if (y) {
-        if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16))
-            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, t.dn_wide != 0, t.dn_grid, s);
+        const bool wide = down_wide(t, p.wfmt);
+        if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16, wide))
+            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, wide, t.dn_grid, s);
     }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
@@ -377,7 +385,7 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
-        else if (!strcmp(tok, "dn_wide") && v >= 0 && v <= 1) t.dn_wide = (int)v;
+        else if (!strcmp(tok, "dn_wide") && v >= 0 && v <= 2) t.dn_wide = (int)v;
         else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
