@@ -11,6 +11,9 @@ namespace moed {
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
     int gu_npw = 1;     // gate/up (per-slot kernel): neurons per wavefront (1 or 2; 2 shares x)
+    int gu_order = 1;   // exact-fit gate/up at B > 1: neuron-block order with XCD-contiguous workgroups
+                        // (slots sharing an expert meet in one L2) for MXFP8 (1) or both formats (2);
+                        // 0 = slot-major
     int gu_exact = 1;   // gate/up (per-slot kernel): 1 = exact-fit kernel when a row is exactly 64*U
                         // chunks (U <= gu_umax), one neuron per wavefront, BF16 route, streaming
     int dn_wpb = 8;     // down: wavefronts per workgroup (1..8; at most 4 unstaged)

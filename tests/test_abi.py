@@ -166,6 +166,9 @@ def test_tuning_spec_parser(lib):
     assert lib.moed_set_tuning(b"dn_wide=1") == md.MOED_OK
     assert lib.moed_set_tuning(b"dn_wide=2") == md.MOED_OK
     assert lib.moed_set_tuning(b"dn_wide=3") == md.MOED_ERR_SHAPE
+    assert lib.moed_set_tuning(b"gu_order=0") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_order=2") == md.MOED_OK
+    assert lib.moed_set_tuning(b"gu_order=3") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_exact=0") == md.MOED_OK
     assert lib.moed_set_tuning(b"gu_exact=2") == md.MOED_ERR_SHAPE
     assert lib.moed_set_tuning(b"gu_grid=0,dn_grid=65536") == md.MOED_OK

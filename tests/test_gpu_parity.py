@@ -238,7 +238,7 @@ def test_ragged_shapes(shape):
                                   "dn_rows=2", "dn_rows=2,dn_umax=2,dn_wpb=3", "dn_rows=1", "dn_rows=4", "dn_rows=4,dn_wpb=5",
                                   "dn_onepass=0", "gu_exact=0", "gu_exact=0,dn_onepass=0,dn_rows=1",
                                   "gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_grid=3,dn_grid=5,gu_group=1,dn_group=1",
-                                  "dn_group=1,dn_wide=0", "dn_group=1,dn_wide=2,dn_tiles=3"])
+                                  "dn_group=1,dn_wide=0", "dn_group=1,dn_wide=2,dn_tiles=3", "gu_order=0", "gu_order=2"])
 def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
