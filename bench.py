@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--wformat", default="mxfp8", choices=["mxfp8", "mxfp4"],
                     help="routed-weight format (the headline metric is quoted on mxfp8)")
     ap.add_argument("--copies", type=int, default=32, help="distinct HBM copies of the layer weights")
-    ap.add_argument("--tune", default=None, help="launch-shape override (moed_set_tuning spec)")
+    ap.add_argument("--tune", default=None, help="launch-shape override (a moed_tuning_init spec)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--all", action="store_true",
@@ -110,7 +110,7 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     md.load()
     if args.tune:
-        md.moed_set_tuning(args.tune)
+        md.set_default_tuning(args.tune)
 
     if args.all:
         all_workloads(md, synth, args)

@@ -36,8 +36,10 @@
  *    memory) on the current device, C-contiguous, no strides. The caller owns
  *    every buffer; the library allocates nothing on these paths.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *    stream) and never synchronise. They are stateless and thread-safe;
- *    concurrent calls need distinct workspaces/outputs.
+ *    stream) and never synchronise. They keep no state between calls: the
+ *    launch shape comes from a built-in table, or from the moed_tuning a
+ *    *_tuned call is handed. Calls may be made from any number of host
+ *    threads at once; concurrent calls need distinct workspaces/outputs.
  *  - Argument errors are reported before anything is launched. A launch
  *    failure returns MOED_ERR_HIP; moed_last_hip_error() gives the raw code.
  *  - Expert ids outside [0, E) are not an error: every output of the affected
@@ -48,10 +50,12 @@
  *    kernel on `stream` and return MOED_ERR_SHAPE, launching nothing else,
  *    if an expert id lies outside [0, E) or a routed expert's rows (of the
  *    matrices the call uses) hold a NaN code (E4M3 S.1111.111) or a NaN scale
- *    (UE8M0 0xFF). This mode synchronises the stream (so it cannot be used
- *    under graph capture) and, on its first use per device, allocates a
- *    4-byte flag that it keeps until the process ends. Concurrent checked
- *    calls on one device share that flag and race.
+ *    (UE8M0 0xFF), and MOED_ERR_SCALE if the call takes a large-batch kernel
+ *    (see moe_decode) and a routed block scale of the matrices it decodes
+ *    lies outside the range that kernel decodes exactly. This mode
+ *    synchronises the stream (so it cannot be used under graph capture). Its
+ *    flag word is a device array of the library (no allocation); checked
+ *    calls that overlap on one device share it and race.
  *  - Duplicate ids within a token's row are legal and their terms add; the
  *    routing weights need not sum to 1.
  *  - Results are deterministic run to run (fixed reduction order).
@@ -74,7 +78,10 @@ typedef enum {
     MOED_ERR_DTYPE = 3,      /* unknown moed_dtype or moed_wformat                */
     MOED_ERR_WORKSPACE = 4,  /* workspace smaller than moed_workspace_bytes()     */
     MOED_ERR_ALIGN = 5,      /* x, a, workspace or a weight-code base not 16-byte aligned */
-    MOED_ERR_HIP = 6         /* a HIP launch failed; see moed_last_hip_error()    */
+    MOED_ERR_HIP = 6,        /* a HIP launch failed; see moed_last_hip_error()    */
+    MOED_ERR_SCALE = 7,      /* (MOED_CHECK only) a routed block scale outside the exact
+                                range of the large-batch kernel the call takes     */
+    MOED_ERR_TUNING = 8      /* a moed_tuning not filled by moed_tuning_init()    */
 } moed_status;
 
 typedef enum {
@@ -90,7 +97,11 @@ typedef enum {
 /* Size limits (checked): B*k*I and B*H below 2^31, k*I/16 below 2^22. */
 
 /*
- * Bytes of workspace moe_decode() needs: the intermediate a[B][k][I]
+ * Bytes of workspace moe_decode() needs. The post's two kernels hand over one
+ * intermediate value per (token, slot, neuron) ("How the two kernels work":
+ * the gate/up kernel writes one intermediate value, the down kernel reads the
+ * row it needs); it is the only buffer between them ("Buffer removal"). So:
+ * the intermediate a[B][k][I]
  * (B*k*I*4 bytes for inter_dtype MOED_F32, the accuracy-gated path; *2 for
  * MOED_BF16), rounded up to 256 bytes, then B*k*H float32 per-slot partials
  * y[b][j][h] = topk_w[b][j] * (Wd^[e]·a[b][j])_h, which the expert-major down
@@ -100,7 +111,15 @@ typedef enum {
 size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype);
 
 /*
- * The whole layer (steps gate/up then down on `stream`).
+ * The whole layer (steps gate/up then down on `stream`): the routed SwiGLU
+ * expert block of the warp-decode post ("What changed": two kernels, the
+ * first one wavefront per intermediate neuron, the second one wavefront per
+ * output; "How the two kernels work": each output folds every routed
+ * expert's weighted contribution into one FP32 accumulator and is stored
+ * once):
+ *   out[b][h] = sum_j topk_w[b][j] * sum_i Wd^[e][h][i] * SiLU(g_i) * u_i,
+ *   g_i = sum_h' Wg^[e][i][h'] x[b][h'],  u_i = sum_h' Wu^[e][i][h'] x[b][h'],
+ *   e = topk_ids[b][j], W^ the decoded MX weights.
  *   x         [B][H]  bfloat16 activations
  *   topk_ids  [B][k]  int32 routed expert ids
  *   topk_w    [B][k]  float32 routing weights (folded in the down kernel)
@@ -119,7 +138,16 @@ size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype);
  * decoded rows of each routed expert serve every slot routed to it, each slot's
  * weighted partial goes to the workspace, and a second launch adds each
  * token's k partials in slot order and stores the output once. Smaller batches
- * use the one-wavefront-per-output down of moe_decode_down().
+ * use the one-wavefront-per-output down of moe_decode_down(). Likewise the
+ * gate/up step runs expert-grouped (MFMA) once B*k*H >= 2458*E.
+ *
+ * Exact range of the large-batch kernels: they decode a weight to BF16 with
+ * its block scale folded into the conversion, which is exact while every
+ * scaled value is a normal, finite BF16 number -- scale codes 10..245 for
+ * MXFP8 and 2..252 for MXFP4 (weights quantized from real value ranges sit
+ * far inside; the synthetic ones use codes near 115). Outside that range
+ * those kernels flush tiny blocks to zero or overflow huge ones where the
+ * single-token kernels stay exact; MOED_CHECK=1 reports such scales.
  */
 int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
                const uint8_t *wg_q, const uint8_t *wg_s,
@@ -234,13 +262,41 @@ const char *moed_status_string(int status);
 int moed_last_hip_error(void);
 
 /*
- * Benchmark-only tuning override (NOT thread-safe; meant for launch-shape
- * sweeps). `spec` is a comma-separated list of key=value pairs, e.g.
- * "gu_wpb=4,dn_wpb=2,gu_dot=1,nt=0,gu_group=2"; NULL or "" restores the
- * built-in table.
- * Returns MOED_OK, or MOED_ERR_SHAPE for an unknown key or value.
+ * Launch-shape choice for one call, for launch-shape sweeps and for tests of
+ * the alternative kernels (every choice computes the same layer). A plain
+ * value owned by the caller; the library keeps no copy.
+ * moed_tuning_init fills *t with the built-in table, then applies `spec`, a
+ * comma-separated list of key=value pairs (e.g. "gu_group=0,dn_group=0");
+ * NULL or "" leaves the built-in table. Returns MOED_OK, MOED_ERR_NULL for a
+ * NULL t, or MOED_ERR_SHAPE for an unknown key or value (t is then left
+ * unfilled).
+ * The *_tuned calls are the calls above with a trailing `tuning` (NULL = the
+ * built-in table, as in the plain calls); MOED_ERR_TUNING if *tuning was not
+ * filled by moed_tuning_init.
  */
-int moed_set_tuning(const char *spec);
+typedef struct { int32_t words[48]; } moed_tuning;
+
+int moed_tuning_init(moed_tuning *t, const char *spec);
+int moe_decode_tuned(const void *x, const int32_t *topk_ids, const float *topk_w,
+                     const uint8_t *wg_q, const uint8_t *wg_s,
+                     const uint8_t *wu_q, const uint8_t *wu_s,
+                     const uint8_t *wd_q, const uint8_t *wd_s, int weight_format,
+                     void *out, int out_dtype, int inter_dtype,
+                     int B, int E, int k, int H, int I,
+                     void *workspace, size_t workspace_bytes, void *stream,
+                     const moed_tuning *tuning);
+int moe_decode_gate_up_tuned(const void *x, const int32_t *topk_ids,
+                             const uint8_t *wg_q, const uint8_t *wg_s,
+                             const uint8_t *wu_q, const uint8_t *wu_s, int weight_format,
+                             void *a, int inter_dtype,
+                             int B, int E, int k, int H, int I, void *stream,
+                             const moed_tuning *tuning);
+int moe_decode_down_tuned(const void *a, int inter_dtype, const int32_t *topk_ids,
+                          const float *topk_w, const uint8_t *wd_q, const uint8_t *wd_s,
+                          int weight_format, void *out, int out_dtype,
+                          int B, int E, int k, int H, int I,
+                          float *partials, size_t partials_bytes, void *stream,
+                          const moed_tuning *tuning);
 
 #ifdef __cplusplus
 }

@@ -78,9 +78,9 @@ def reference_dense(x: np.ndarray, ids: np.ndarray, w: np.ndarray, wg, wu, wd) -
     for b in range(B):
         for j in range(k):
             e = int(ids[b, j])
-            g = wg[e].astype(np.float64) @ x[b]
-            u = wu[e].astype(np.float64) @ x[b]
-            out[b] += float(w[b, j]) * (wd[e].astype(np.float64) @ (_silu(g) * u))
+            g = np.asarray(wg[e], np.float64) @ x[b]
+            u = np.asarray(wu[e], np.float64) @ x[b]
+            out[b] += float(w[b, j]) * (np.asarray(wd[e], np.float64) @ (_silu(g) * u))
     return out
 
 
@@ -96,8 +96,8 @@ def _cls_quantize_x(x):
 
 def _cls_gate_up(wg_e, wu_e, xq_b):
     """Stage 2: both projections with float32 accumulation, SwiGLU in float32."""
-    g = wg_e.astype(np.float32) @ xq_b
-    u = wu_e.astype(np.float32) @ xq_b
+    g = np.asarray(wg_e, np.float32) @ xq_b
+    u = np.asarray(wu_e, np.float32) @ xq_b
     return (g / (np.float32(1.0) + np.exp(-g)) * u).astype(np.float32)
 
 
@@ -108,7 +108,7 @@ def _cls_quantize_a(act):
 
 def _cls_down(wd_e, aq):
     """Stage 4: the down projection with float32 accumulation."""
-    return wd_e.astype(np.float32) @ aq
+    return np.asarray(wd_e, np.float32) @ aq
 
 
 def _cls_expert_round(y):

@@ -2,12 +2,61 @@
 // the layer does not check on its hot path -- every routed expert id in
 // [0, E), and no NaN code (E4M3 S.1111.111) or NaN scale (UE8M0 0xFF) in the
 // rows of the experts that are routed to. E2M1 has no NaN code; its scales
-// are checked. The result is a flag word in device memory: bit 0 = an id out
-// of range, bit 1 = a NaN code or scale in a routed expert.
+// are checked. It also flags block scales of routed experts outside the range
+// the large-batch kernels decode exactly (they fold the scale into the BF16
+// conversion), separately for the gate/up and the down matrices, so that the
+// caller can reject only the calls that take those kernels. The result is a
+// flag word (kCheck* bits) in a file-scope device array: no allocation.
+#include <map>
+#include <mutex>
+
 #include "launch.h"
 #include "mx_device.h"
 
 namespace moed {
+
+namespace {
+__device__ __align__(256) uint32_t check_flag_word[64];
+}
+
+hipError_t check_flag(uint32_t** flag)
+{
+    static std::mutex mu;
+    static std::map<int, uint32_t*> addr;         // per device: the array's address on it
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(check_flag_word));
+        if (err != hipSuccess)
+            return err;
+        it = addr.emplace(dev, static_cast<uint32_t*>(p)).first;
+    }
+    *flag = it->second;
+    return hipSuccess;
+}
+
+hipError_t set_max_dynamic_lds(const void* func, int bytes)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> done;    // (device, kernel) -> bytes set
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = done.find({dev, func});
+    if (it != done.end() && it->second >= bytes)
+        return hipSuccess;
+    err = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err == hipSuccess)
+        done[{dev, func}] = bytes;
+    return err;
+}
 
 __global__ void moe_check_clear_kernel(uint32_t* flag)
 {
@@ -38,11 +87,14 @@ moe_check_kernel(const int32_t* ids, int nslots, int E, const uint8_t* wg_q, con
         bad_id |= (unsigned)v >= (unsigned)E;
     }
     if (bad_id && e == 0 && part == 0)
-        atomicOr(flag, 1u);
+        atomicOr(flag, kCheckBadId);
     __syncthreads();
     if (!routed)
         return;                                       // whole block
     bool bad = false;
+    bool range_gu = false, range_dn = false;
+    const uint32_t lo = fp4 ? kExactScaleLoFP4 : kExactScaleLoFP8;
+    const uint32_t hi = fp4 ? kExactScaleHiFP4 : kExactScaleHiFP8;
     // codes: rows of K bytes (K/2 for E2M1, which has no NaN code)
     auto scan_codes = [&](const uint8_t* q, int rows, int K) {
         if (fp4 || !q)
@@ -52,22 +104,29 @@ moe_check_kernel(const int32_t* ids, int nslots, int E, const uint8_t* wg_q, con
             for (int c = threadIdx.x; c < K; c += blockDim.x)
                 bad |= (q[base + (size_t)r * K + c] & 0x7Fu) == 0x7Fu;
     };
-    auto scan_scales = [&](const uint8_t* s, int rows, int K) {
+    auto scan_scales = [&](const uint8_t* s, int rows, int K, bool& range) {
         if (!s)
             return;
         const size_t base = (size_t)e * (size_t)rows * (size_t)(K / 32);
         for (int r = part; r < rows; r += parts)
-            for (int c = threadIdx.x; c < K / 32; c += blockDim.x)
-                bad |= s[base + (size_t)r * (K / 32) + c] == 0xFFu;
+            for (int c = threadIdx.x; c < K / 32; c += blockDim.x) {
+                const uint32_t v = s[base + (size_t)r * (K / 32) + c];
+                bad |= v == 0xFFu;
+                range |= v != 0xFFu && (v < lo || v > hi);
+            }
     };
     scan_codes(wg_q, I, H);
     scan_codes(wu_q, I, H);
     scan_codes(wd_q, H, I);
-    scan_scales(wg_s, I, H);
-    scan_scales(wu_s, I, H);
-    scan_scales(wd_s, H, I);
+    scan_scales(wg_s, I, H, range_gu);
+    scan_scales(wu_s, I, H, range_gu);
+    scan_scales(wd_s, H, I, range_dn);
     if (bad)
-        atomicOr(flag, 2u);
+        atomicOr(flag, kCheckNaN);
+    if (range_gu)
+        atomicOr(flag, kCheckScaleGateUp);
+    if (range_dn)
+        atomicOr(flag, kCheckScaleDown);
 }
 
 hipError_t launch_check(const CheckArgs& c, uint32_t* flag, hipStream_t s)

@@ -711,10 +711,9 @@ hipError_t launch_expert(dim3 grid, dim3 block, size_t lds, hipStream_t s, const
                          int max_tiles, int wl_off)
 {
     if constexpr (W) {
-        // allow dynamic LDS beyond the default 64 KiB, once per process
-        static const hipError_t attr =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_down_expert_kernel<RT, A, F, W>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDnLdsMaxWide);
+        // allow dynamic LDS beyond the default 64 KiB, once per device
+        const hipError_t attr = set_max_dynamic_lds(
+            reinterpret_cast<const void*>(&moe_down_expert_kernel<RT, A, F, W>), (int)kDnLdsMaxWide);
         if (attr != hipSuccess)
             return attr;
     }

@@ -681,11 +681,10 @@ hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, cons
                           int row_u, int wl_off)
 {
     if constexpr (WIDE) {
-        // allow dynamic LDS beyond the default 64 KiB, once per process: up to
+        // allow dynamic LDS beyond the default 64 KiB, once per device: up to
         // 64 KiB for the slot list and x tiles plus the 32 KiB of wide-load regions
-        static const hipError_t attr =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
+        const hipError_t attr =
+            set_max_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4>),
                                 65536 + kGroupWaves * kWideUnitsPerWave * (int)sizeof(u32x4));
         if (attr != hipSuccess)
             return attr;

@@ -110,7 +110,21 @@ struct CheckArgs {
     const uint8_t *wg_q, *wg_s, *wu_q, *wu_s, *wd_q, *wd_s;
     int B, E, k, H, I, wfmt;
 };
+// Bits of the check flag word.
+constexpr uint32_t kCheckBadId = 1u;          // an expert id outside [0, E)
+constexpr uint32_t kCheckNaN = 2u;            // a NaN code or scale in a routed expert's rows
+constexpr uint32_t kCheckScaleGateUp = 4u;    // a routed gate/up block scale the grouped gate/up does not decode exactly
+constexpr uint32_t kCheckScaleDown = 8u;      // a routed down block scale the expert-major down does not decode exactly
+// Block-scale codes the large-batch kernels decode exactly (the scale folded
+// into the BF16 conversion keeps every scaled value a normal, finite BF16).
+constexpr int kExactScaleLoFP8 = 10, kExactScaleHiFP8 = 245;
+constexpr int kExactScaleLoFP4 = 2, kExactScaleHiFP4 = 252;
 hipError_t launch_check(const CheckArgs& c, uint32_t* flag, hipStream_t s);
+// Device address of the check flag word of the current device (a file-scope
+// device array; its address is taken once per device).
+hipError_t check_flag(uint32_t** flag);
+// hipFuncAttributeMaxDynamicSharedMemorySize for `func`, set once per device.
+hipError_t set_max_dynamic_lds(const void* func, int bytes);
 hipError_t launch_selftest_decode(const uint8_t* codes, const uint8_t* scales, float* out, int n,
                                   int path, hipStream_t s);
 

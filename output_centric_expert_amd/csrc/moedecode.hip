@@ -1,20 +1,25 @@
 // C ABI of libmoedecode: argument checks, launch-shape choice, two launches.
 // Everything here runs on the host; all arithmetic of the layer runs in the
-// kernels of gate_up.hip and down.hip.
+// kernels of gate_up.hip and down.hip. No call keeps state between calls: the
+// launch shape comes from the built-in table or from the caller's
+// moed_tuning, passed with the call.
 #include <stdlib.h>
 #include <string.h>
 
-#include <map>
 #include <mutex>
+#include <set>
+#include <tuple>
 
 #include "moedecode.h"
 #include "launch.h"
 
+static_assert(sizeof(moed::Tuning) <= sizeof(moed_tuning), "moed_tuning too small for the launch table");
+static_assert(sizeof(moed::Tuning) % sizeof(int) == 0, "moed::Tuning holds ints only");
+
 namespace {
 
 thread_local int g_last_hip = 0;
-moed::Tuning g_tuning;          // built-in table unless moed_set_tuning() overrode it
-bool g_tuning_overridden = false;
+constexpr uint32_t kTuningMagic = 0x6D6F6564u;   // "moed": marks an initialised moed_tuning
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -42,15 +47,18 @@ int hip_status(hipError_t e)
     return MOED_ERR_HIP;
 }
 
-// The built-in launch table. Waves per workgroup and the decode route were
-// picked by sweeps on MI355X (see the benchmark's tuning mode).
-moed::Tuning pick(int B, int H, int I)
+// The launch table of one call: the built-in choice (picked by sweeps on
+// MI355X), or the caller's moed_tuning. Returns false for a moed_tuning that
+// moed_tuning_init() did not fill.
+bool pick(const moed_tuning* user, moed::Tuning* t)
 {
-    if (g_tuning_overridden)
-        return g_tuning;
-    moed::Tuning t;
-    (void)B; (void)H; (void)I;
-    return t;
+    *t = moed::Tuning();
+    if (!user)
+        return true;
+    if ((uint32_t)user->words[0] != kTuningMagic)
+        return false;
+    memcpy(static_cast<void*>(t), &user->words[1], sizeof(moed::Tuning));
+    return true;
 }
 
 // Expert-grouped gate/up pays off once tokens share experts: measured
@@ -108,33 +116,21 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Opt-in input check (MOED_CHECK=1 in the environment, read on every call):
 // a check kernel on the caller's stream, then a synchronisation and a read of
-// its flag word. The flag lives in a 4-byte device buffer allocated on the
-// first checked call per device and kept for the process; nothing is
-// allocated when the check is off.
+// its flag word, which lives in a file-scope device array (one per device,
+// allocated with the code object). Nothing is allocated.
 bool check_enabled()
 {
     const char* v = getenv("MOED_CHECK");
     return v && v[0] == '1' && v[1] == '\0';
 }
 
-int run_check(const moed::CheckArgs& c, hipStream_t s)
+// grouped: the call takes the expert-grouped gate/up (its block scales are
+// folded into the BF16 conversion); expert_down: the expert-major down (the
+// same for the down scales).
+int run_check(const moed::CheckArgs& c, bool grouped, bool expert_down, hipStream_t s)
 {
-    static std::mutex mu;
-    static std::map<int, uint32_t*> flags;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
     uint32_t* flag = nullptr;
-    if (err == hipSuccess) {
-        std::lock_guard<std::mutex> lock(mu);
-        auto it = flags.find(dev);
-        if (it == flags.end()) {
-            err = hipMalloc(reinterpret_cast<void**>(&flag), sizeof(uint32_t));
-            if (err == hipSuccess)
-                flags[dev] = flag;
-        } else {
-            flag = it->second;
-        }
-    }
+    hipError_t err = moed::check_flag(&flag);
     uint32_t host = 0;
     if (err == hipSuccess)
         err = moed::launch_check(c, flag, s);
@@ -146,7 +142,11 @@ int run_check(const moed::CheckArgs& c, hipStream_t s)
         g_last_hip = (int)err;
         return MOED_ERR_HIP;
     }
-    return host ? MOED_ERR_SHAPE : MOED_OK;
+    if (host & (moed::kCheckBadId | moed::kCheckNaN))
+        return MOED_ERR_SHAPE;
+    if ((grouped && (host & moed::kCheckScaleGateUp)) || (expert_down && (host & moed::kCheckScaleDown)))
+        return MOED_ERR_SCALE;
+    return MOED_OK;
 }
 
 moed::CheckArgs check_args(const int32_t* ids, const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q,
@@ -186,6 +186,31 @@ moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, cons
     return p;
 }
 
+// Both steps of the layer on `s`, arguments already checked; `workspace`
+// holds the intermediate, then (256-byte aligned) the per-slot partials.
+int layer(const void* x, const int32_t* topk_ids, const float* topk_w, const uint8_t* wg_q, const uint8_t* wg_s,
+          const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wd_q, const uint8_t* wd_s, int weight_format,
+          void* out, int out_dtype, int inter_dtype, int B, int E, int k, int H, int I, void* workspace,
+          const moed::Tuning& t, hipStream_t s)
+{
+    const bool a_bf16 = inter_dtype == MOED_BF16;
+    if (check_enabled()) {
+        const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, weight_format)) != 0;
+        if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
+                               use_grouped(t, B, E, k, H, weight_format), expert_down, s))
+            return st;
+    }
+    int st = hip_status(gate_up_launch(
+        gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, workspace, B, E, k, H, I), a_bf16, t, s));
+    if (st)
+        return st;
+    const size_t inter = (size_t)B * (size_t)k * (size_t)I * (a_bf16 ? 2u : 4u);
+    float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256(inter));
+    return hip_status(down_launch(
+        down_args(workspace, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I), a_bf16,
+        out_dtype == MOED_BF16, t, partials, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,40 +224,55 @@ size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype)
     return B == 0 ? 0 : align256(inter) + partials;
 }
 
-int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg_q,
-                       const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, int weight_format,
-                       void* a, int inter_dtype, int B, int E, int k, int H, int I, void* stream)
+int moe_decode_gate_up_tuned(const void* x, const int32_t* topk_ids, const uint8_t* wg_q, const uint8_t* wg_s,
+                             const uint8_t* wu_q, const uint8_t* wu_s, int weight_format, void* a, int inter_dtype,
+                             int B, int E, int k, int H, int I, void* stream, const moed_tuning* tuning)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
     if (!dtype_ok(inter_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
+    moed::Tuning t;
+    if (!pick(tuning, &t))
+        return MOED_ERR_TUNING;
     if (B == 0)
         return MOED_OK;
     if (!x || !topk_ids || !wg_q || !wg_s || !wu_q || !wu_s || !a)
         return MOED_ERR_NULL;
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(a))
         return MOED_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
     if (check_enabled()) {
         if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, nullptr, nullptr, B, E, k, H, I,
                                           weight_format),
-                               static_cast<hipStream_t>(stream)))
+                               use_grouped(t, B, E, k, H, weight_format), false, s))
             return st;
     }
-    const moed::Tuning t = pick(B, H, I);
     return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, a,
                                                   B, E, k, H, I),
-                                     inter_dtype == MOED_BF16, t, static_cast<hipStream_t>(stream)));
+                                     inter_dtype == MOED_BF16, t, s));
 }
 
-int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
-                    const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
-                    int B, int E, int k, int H, int I, float* partials, size_t partials_bytes, void* stream)
+int moe_decode_gate_up(const void* x, const int32_t* topk_ids, const uint8_t* wg_q, const uint8_t* wg_s,
+                       const uint8_t* wu_q, const uint8_t* wu_s, int weight_format, void* a, int inter_dtype,
+                       int B, int E, int k, int H, int I, void* stream)
+{
+    return moe_decode_gate_up_tuned(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, a, inter_dtype, B, E, k, H,
+                                    I, stream, nullptr);
+}
+
+int moe_decode_down_tuned(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
+                          const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
+                          int B, int E, int k, int H, int I, float* partials, size_t partials_bytes, void* stream,
+                          const moed_tuning* tuning)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
     if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
+    moed::Tuning t;
+    if (!pick(tuning, &t))
+        return MOED_ERR_TUNING;
     if (B == 0)
         return MOED_OK;
     if (!a || !topk_ids || !topk_w || !wd_q || !wd_s || !out)
@@ -241,28 +281,41 @@ int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, con
         return MOED_ERR_WORKSPACE;
     if (!aligned16(a) || !aligned16(wd_q) || (partials && !aligned16(partials)))
         return MOED_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool a_bf16 = inter_dtype == MOED_BF16;
     if (check_enabled()) {
+        const bool expert_down =
+            partials && pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, weight_format)) != 0;
         if (int st = run_check(check_args(topk_ids, nullptr, nullptr, nullptr, nullptr, wd_q, wd_s, B, E, k, H, I,
                                           weight_format),
-                               static_cast<hipStream_t>(stream)))
+                               false, expert_down, s))
             return st;
     }
-    const moed::Tuning t = pick(B, H, I);
     return hip_status(down_launch(down_args(a, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I),
-                                  inter_dtype == MOED_BF16, out_dtype == MOED_BF16, t, partials,
-                                  static_cast<hipStream_t>(stream)));
+                                  a_bf16, out_dtype == MOED_BF16, t, partials, s));
 }
 
-int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
-               const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
-               const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
-               int inter_dtype, int B, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
-               void* stream)
+int moe_decode_down(const void* a, int inter_dtype, const int32_t* topk_ids, const float* topk_w,
+                    const uint8_t* wd_q, const uint8_t* wd_s, int weight_format, void* out, int out_dtype,
+                    int B, int E, int k, int H, int I, float* partials, size_t partials_bytes, void* stream)
+{
+    return moe_decode_down_tuned(a, inter_dtype, topk_ids, topk_w, wd_q, wd_s, weight_format, out, out_dtype, B, E,
+                                 k, H, I, partials, partials_bytes, stream, nullptr);
+}
+
+int moe_decode_tuned(const void* x, const int32_t* topk_ids, const float* topk_w, const uint8_t* wg_q,
+                     const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wd_q,
+                     const uint8_t* wd_s, int weight_format, void* out, int out_dtype, int inter_dtype, int B, int E,
+                     int k, int H, int I, void* workspace, size_t workspace_bytes, void* stream,
+                     const moed_tuning* tuning)
 {
     if (int st = check_shape(B, E, k, H, I))
         return st;
     if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype) || !wformat_ok(weight_format))
         return MOED_ERR_DTYPE;
+    moed::Tuning t;
+    if (!pick(tuning, &t))
+        return MOED_ERR_TUNING;
     if (B == 0)
         return MOED_OK;
     if (!x || !topk_ids || !topk_w || !wg_q || !wg_s || !wu_q || !wu_s || !wd_q || !wd_s || !out || !workspace)
@@ -271,23 +324,17 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w,
         return MOED_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(wd_q) || !aligned16(workspace))
         return MOED_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (check_enabled()) {
-        if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
-                               s))
-            return st;
-    }
-    const moed::Tuning t = pick(B, H, I);
-    const bool a_bf16 = inter_dtype == MOED_BF16;
-    int st = hip_status(gate_up_launch(
-        gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, workspace, B, E, k, H, I), a_bf16, t, s));
-    if (st)
-        return st;
-    const size_t inter = (size_t)B * (size_t)k * (size_t)I * (a_bf16 ? 2u : 4u);
-    float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256(inter));
-    return hip_status(down_launch(
-        down_args(workspace, topk_ids, topk_w, wd_q, wd_s, weight_format, out, B, E, k, H, I), a_bf16,
-        out_dtype == MOED_BF16, t, partials, s));
+    return layer(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, weight_format, out, out_dtype, inter_dtype,
+                 B, E, k, H, I, workspace, t, static_cast<hipStream_t>(stream));
+}
+
+int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w, const uint8_t* wg_q,
+               const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wd_q,
+               const uint8_t* wd_s, int weight_format, void* out, int out_dtype, int inter_dtype, int B, int E, int k,
+               int H, int I, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return moe_decode_tuned(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, weight_format, out, out_dtype,
+                            inter_dtype, B, E, k, H, I, workspace, workspace_bytes, stream, nullptr);
 }
 
 int moe_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* topk_ids,
@@ -353,24 +400,26 @@ const char* moed_status_string(int status)
     case MOED_ERR_WORKSPACE: return "MOED_ERR_WORKSPACE: workspace too small";
     case MOED_ERR_ALIGN: return "MOED_ERR_ALIGN: pointer not 16-byte aligned";
     case MOED_ERR_HIP: return "MOED_ERR_HIP: HIP launch failed";
+    case MOED_ERR_SCALE: return "MOED_ERR_SCALE: a routed block scale outside the range the large-batch kernels decode exactly";
+    case MOED_ERR_TUNING: return "MOED_ERR_TUNING: moed_tuning not filled by moed_tuning_init";
     default: return "unknown moed_status";
     }
 }
 
 int moed_last_hip_error(void) { return g_last_hip; }
 
-int moed_set_tuning(const char* spec)
+int moed_tuning_init(moed_tuning* out, const char* spec)
 {
+    if (!out)
+        return MOED_ERR_NULL;
     moed::Tuning t;
-    if (!spec || !*spec) {
-        g_tuning = t;
-        g_tuning_overridden = false;
-        return MOED_OK;
-    }
-    char buf[512];
-    strncpy(buf, spec, sizeof buf - 1);
-    buf[sizeof buf - 1] = 0;
-    for (char* tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+    if (spec && strlen(spec) >= 512)
+        return MOED_ERR_SHAPE;
+    char buf[512] = {0};
+    if (spec)
+        strncpy(buf, spec, sizeof buf - 1);
+    char* save = nullptr;
+    for (char* tok = strtok_r(buf, ",", &save); tok; tok = strtok_r(nullptr, ",", &save)) {
         char* eq = strchr(tok, '=');
         if (!eq)
             return MOED_ERR_SHAPE;
@@ -404,8 +453,9 @@ int moed_set_tuning(const char* spec)
         else if (!strcmp(tok, "dn_grid") && v >= 0 && v <= 65536) t.dn_grid = (int)v;
         else return MOED_ERR_SHAPE;
     }
-    g_tuning = t;
-    g_tuning_overridden = true;
+    memset(out, 0, sizeof(*out));
+    out->words[0] = (int32_t)kTuningMagic;
+    memcpy(&out->words[1], &t, sizeof(t));
     return MOED_OK;
 }
 

@@ -8,20 +8,29 @@ functions raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoedecode.so")
 
-MOED_OK, MOED_ERR_NULL, MOED_ERR_SHAPE, MOED_ERR_DTYPE, MOED_ERR_WORKSPACE, MOED_ERR_ALIGN, MOED_ERR_HIP = range(7)
+(MOED_OK, MOED_ERR_NULL, MOED_ERR_SHAPE, MOED_ERR_DTYPE, MOED_ERR_WORKSPACE, MOED_ERR_ALIGN, MOED_ERR_HIP,
+ MOED_ERR_SCALE, MOED_ERR_TUNING) = range(9)
 MOED_BF16, MOED_F32 = 0, 1
 
 EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down", "moe_route",
            "moed_selftest_decode", "moed_bench_read", "moed_bench_copy", "moed_status_string",
-           "moed_last_hip_error", "moed_set_tuning")
+           "moed_last_hip_error", "moed_tuning_init", "moe_decode_tuned", "moe_decode_gate_up_tuned",
+           "moe_decode_down_tuned")
+
+
+class MoedTuning(ctypes.Structure):
+    """moed_tuning of the header: a launch-shape choice handed to one call."""
+    _fields_ = [("words", ctypes.c_int32 * 48)]
 
 
 class MoedError(RuntimeError):
@@ -54,6 +63,15 @@ def load() -> ctypes.CDLL:
         lib.moe_decode_gate_up.restype = I
         lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P, Z, P]
         lib.moe_decode_down.restype = I
+        TP = ctypes.POINTER(MoedTuning)
+        lib.moed_tuning_init.argtypes = [TP, ctypes.c_char_p]
+        lib.moed_tuning_init.restype = I
+        lib.moe_decode_tuned.argtypes = lib.moe_decode.argtypes + [TP]
+        lib.moe_decode_tuned.restype = I
+        lib.moe_decode_gate_up_tuned.argtypes = lib.moe_decode_gate_up.argtypes + [TP]
+        lib.moe_decode_gate_up_tuned.restype = I
+        lib.moe_decode_down_tuned.argtypes = lib.moe_decode_down.argtypes + [TP]
+        lib.moe_decode_down_tuned.restype = I
         lib.moe_route.argtypes = [P, I, I, I, I, ctypes.c_float, P, P, P]
         lib.moe_route.restype = I
         lib.moed_selftest_decode.argtypes = [P, P, P, I, I, P]
@@ -66,8 +84,6 @@ def load() -> ctypes.CDLL:
         lib.moed_status_string.restype = ctypes.c_char_p
         lib.moed_last_hip_error.argtypes = []
         lib.moed_last_hip_error.restype = I
-        lib.moed_set_tuning.argtypes = [ctypes.c_char_p]
-        lib.moed_set_tuning.restype = I
         _lib = lib
     return _lib
 
@@ -100,6 +116,43 @@ def _check(st: int, where: str):
         raise MoedError(st, where)
 
 
+def moed_tuning_init(spec: str | None) -> MoedTuning:
+    """A moed_tuning filled from the built-in table and `spec` ("key=value,...")."""
+    t = MoedTuning()
+    _check(load().moed_tuning_init(ctypes.byref(t), spec.encode() if spec else None), "moed_tuning_init")
+    return t
+
+
+_default = threading.local()
+
+
+def set_default_tuning(spec: str | None):
+    """Later calls made by this Python thread without a tuning argument pass a moed_tuning
+    filled from `spec` (None: the built-in table). A convenience of the binding for tests and
+    sweeps; the library itself keeps no state between calls."""
+    _default.tuning = moed_tuning_init(spec) if spec else None
+
+
+@contextlib.contextmanager
+def tuned(spec: str | None):
+    """set_default_tuning(spec) for the calls inside the block."""
+    prev = getattr(_default, "tuning", None)
+    set_default_tuning(spec)
+    try:
+        yield
+    finally:
+        _default.tuning = prev
+
+
+def _tuning(tuning):
+    """tuning argument -> (use the _tuned entry point?, pointer)."""
+    if tuning is None:
+        tuning = getattr(_default, "tuning", None)
+    elif isinstance(tuning, str):
+        tuning = moed_tuning_init(tuning)
+    return (tuning is not None), (ctypes.byref(tuning) if tuning is not None else None)
+
+
 def moed_workspace_bytes(B: int, k: int, H: int, I: int, inter_dtype=torch.float32) -> int:
     """Workspace of moe_decode: the intermediate (256-byte aligned), then B*k*H float32 partials."""
     return int(load().moed_workspace_bytes(B, k, H, I, _DT[inter_dtype]))
@@ -117,9 +170,10 @@ def _kb(K: int, wformat: str) -> int:
 
 def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None,
                out_dtype=torch.bfloat16, inter_dtype=torch.float32, workspace=None, stream=None,
-               wformat="mxfp8"):
+               wformat="mxfp8", tuning=None):
     """The whole layer: returns out [B, H] (out_dtype). wformat: "mxfp8" or "mxfp4"
-    (codes [E, I, H/2] and [E, H, I/2], two per byte, low nibble first)."""
+    (codes [E, I, H/2] and [E, H, I/2], two per byte, low nibble first). tuning: None (the
+    built-in table, or the one of an enclosing tuned() block), a spec string or a MoedTuning."""
     B, H = x.shape
     k = topk_ids.shape[1]
     E, I = wg_q.shape[0], wg_q.shape[1]
@@ -129,7 +183,9 @@ def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None
     need = moed_workspace_bytes(B, k, H, I, inter_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    st = load().moe_decode(
+    use, tp = _tuning(tuning)
+    lib = load()
+    args = (
         _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(topk_w, "topk_w", torch.float32, (B, k)),
         _ptr(wg_q, "wg_q", torch.uint8, (E, I, HB)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
@@ -137,12 +193,13 @@ def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None
         _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
         _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], _DT[inter_dtype],
         B, E, k, H, I, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    st = lib.moe_decode_tuned(*args, tp) if use else lib.moe_decode(*args)
     _check(st, "moe_decode")
     return out
 
 
 def moe_decode_gate_up(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a=None, inter_dtype=torch.float32,
-                       stream=None, wformat="mxfp8"):
+                       stream=None, wformat="mxfp8", tuning=None):
     """Gate/up step alone: returns a = SiLU(gate) * up, shape [B, k, I] in the
     library's chunk-interleaved element order (inter_to_bki() gives plain order)."""
     B, H = x.shape
@@ -151,17 +208,20 @@ def moe_decode_gate_up(x, topk_ids, wg_q, wg_s, wu_q, wu_s, a=None, inter_dtype=
     HB = _kb(H, wformat)
     if a is None:
         a = torch.empty((B, k, I), dtype=inter_dtype, device=x.device)
-    st = load().moe_decode_gate_up(
+    use, tp = _tuning(tuning)
+    lib = load()
+    args = (
         _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(wg_q, "wg_q", torch.uint8, (E, I, HB)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
         _ptr(wu_q, "wu_q", torch.uint8, (E, I, HB)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
         _WF[wformat], _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], B, E, k, H, I, _stream(stream))
+    st = lib.moe_decode_gate_up_tuned(*args, tp) if use else lib.moe_decode_gate_up(*args)
     _check(st, "moe_decode_gate_up")
     return a
 
 
 def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.bfloat16, stream=None,
-                    wformat="mxfp8", partials=None):
+                    wformat="mxfp8", partials=None, tuning=None):
     """Down step alone: returns out [B, H] from a [B, k, I]. partials: None (one wavefront per
     output) or a float32 CUDA tensor of at least B*k*H elements, which lets batches whose
     tokens share experts take the expert-major form."""
@@ -174,12 +234,15 @@ def moe_decode_down(a, topk_ids, topk_w, wd_q, wd_s, out=None, out_dtype=torch.b
     if partials is not None:
         pp = _ptr(partials, "partials", torch.float32)
         pn = partials.numel() * 4
-    st = load().moe_decode_down(
+    use, tp = _tuning(tuning)
+    lib = load()
+    args = (
         _ptr(a, "a", None, (B, k, I)), _DT[a.dtype], _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
         _ptr(topk_w, "topk_w", torch.float32, (B, k)),
         _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
         _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], B, E, k, H, I, pp, pn,
         _stream(stream))
+    st = lib.moe_decode_down_tuned(*args, tp) if use else lib.moe_decode_down(*args)
     _check(st, "moe_decode_down")
     return out
 
@@ -223,10 +286,6 @@ def moed_bench_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int | None = N
     if n > dst.numel() * dst.element_size():
         raise ValueError("moed_bench_copy: dst too small")
     _check(load().moed_bench_copy(_ptr(src, "src"), _ptr(dst, "dst"), n, _stream(stream)), "moed_bench_copy")
-
-
-def moed_set_tuning(spec: str | None):
-    _check(load().moed_set_tuning(spec.encode() if spec else None), "moed_set_tuning")
 
 
 def moed_status_string(status: int) -> str:

@@ -41,7 +41,7 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(9):
         assert md.moed_status_string(s).startswith("MOED_")
     assert "unknown" in md.moed_status_string(99)
     assert md.moed_last_hip_error() == 0
@@ -130,53 +130,96 @@ def test_route_rejects_before_launch(lib):
     assert rt(B=0, lg=None, ids=None, w=None) == md.MOED_OK
 
 
+def _init(lib, spec):
+    t = md.MoedTuning()
+    return lib.moed_tuning_init(ctypes.byref(t), spec)
+
+
 def test_tuning_spec_parser(lib):
-    assert lib.moed_set_tuning(b"gu_wpb=2,dn_wpb=1,gu_dot=0,nt=1") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_wpb=9") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_group=1,dn_stage=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_group=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_group=1") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_group=-1") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_group=1,dn_tiles=4") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_tiles=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_tiles=5") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_rt=1") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_rowslots=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_rowslots=4") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_rowslots=5") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_wide=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_wide=1") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_wide=2") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_rt=0") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_rt=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_order=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_order=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"nt=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"nt=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_lanegroups=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_lanegroups=2") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_npw=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_npw=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_rows=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_rows=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_rows=4") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_onepass=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_onepass=2") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"dn_wide=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_wide=1") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_wide=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_wide=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_order=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_order=2") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_order=3") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_exact=0") == md.MOED_OK
-    assert lib.moed_set_tuning(b"gu_exact=2") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_grid=0,dn_grid=65536") == md.MOED_OK
-    assert lib.moed_set_tuning(b"dn_grid=-1") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"grp_grid=1") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"bogus=1") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(b"gu_wpb") == md.MOED_ERR_SHAPE
-    assert lib.moed_set_tuning(None) == md.MOED_OK
+    """moed_tuning_init: the built-in table plus key=value overrides, filled into the caller's struct."""
+    assert _init(lib, b"gu_wpb=2,dn_wpb=1,gu_dot=0,nt=1") == md.MOED_OK
+    assert _init(lib, b"gu_wpb=9") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_group=1,dn_stage=0") == md.MOED_OK
+    assert _init(lib, b"gu_group=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_group=1") == md.MOED_OK
+    assert _init(lib, b"dn_group=-1") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_group=1,dn_tiles=4") == md.MOED_OK
+    assert _init(lib, b"dn_tiles=0") == md.MOED_OK
+    assert _init(lib, b"dn_tiles=5") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_rt=1") == md.MOED_OK
+    assert _init(lib, b"gu_rowslots=0") == md.MOED_OK
+    assert _init(lib, b"gu_rowslots=4") == md.MOED_OK
+    assert _init(lib, b"gu_rowslots=5") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_wide=0") == md.MOED_OK
+    assert _init(lib, b"gu_wide=1") == md.MOED_OK
+    assert _init(lib, b"gu_wide=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_rt=0") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_rt=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_order=2") == md.MOED_OK
+    assert _init(lib, b"dn_order=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"nt=2") == md.MOED_OK
+    assert _init(lib, b"nt=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_lanegroups=0") == md.MOED_OK
+    assert _init(lib, b"dn_lanegroups=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_npw=2") == md.MOED_OK
+    assert _init(lib, b"gu_npw=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_rows=2") == md.MOED_OK
+    assert _init(lib, b"dn_rows=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_rows=4") == md.MOED_OK
+    assert _init(lib, b"dn_onepass=0") == md.MOED_OK
+    assert _init(lib, b"dn_onepass=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_wide=0") == md.MOED_OK
+    assert _init(lib, b"dn_wide=1") == md.MOED_OK
+    assert _init(lib, b"dn_wide=2") == md.MOED_OK
+    assert _init(lib, b"dn_wide=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_order=0") == md.MOED_OK
+    assert _init(lib, b"gu_order=2") == md.MOED_OK
+    assert _init(lib, b"gu_order=3") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_exact=0") == md.MOED_OK
+    assert _init(lib, b"gu_exact=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_grid=0,dn_grid=65536") == md.MOED_OK
+    assert _init(lib, b"dn_grid=-1") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"grp_grid=1") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"bogus=1") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_wpb") == md.MOED_ERR_SHAPE
+    assert _init(lib, None) == md.MOED_OK
+
+
+def test_tuning_struct_is_per_call(lib):
+    """A moed_tuning is the caller's value: filled only by moed_tuning_init, checked by the *_tuned
+    calls before anything else is looked at (MOED_ERR_TUNING for one it did not fill), and NULL
+    means the built-in table. Nothing is launched here (argument errors come first)."""
+    assert lib.moed_tuning_init(None, b"gu_group=0") == md.MOED_ERR_NULL
+    t = md.MoedTuning()
+    assert lib.moed_tuning_init(ctypes.byref(t), None) == md.MOED_OK
+    u = md.MoedTuning()
+    assert lib.moed_tuning_init(ctypes.byref(u), b"") == md.MOED_OK
+    assert bytes(t) == bytes(u)                       # NULL and "" both give the built-in table
+    v = md.MoedTuning()
+    assert lib.moed_tuning_init(ctypes.byref(v), b"gu_group=0") == md.MOED_OK
+    assert bytes(v) != bytes(t)
+    bad = md.MoedTuning()                             # never initialised
+    Z = ctypes.c_size_t
+    # B = 0 launches nothing, but the tuning is checked first
+    args = [None] * 9 + [0, None, 0, 0, 0, 8, 2, 256, 128, None, Z(0), None]
+    assert lib.moe_decode_tuned(*args, ctypes.byref(bad)) == md.MOED_ERR_TUNING
+    assert lib.moe_decode_tuned(*args, ctypes.byref(t)) == md.MOED_OK
+    assert lib.moe_decode_tuned(*args, None) == md.MOED_OK
+    gu = [None] * 6 + [0, None, 1, 0, 8, 2, 256, 128, None]
+    assert lib.moe_decode_gate_up_tuned(*gu, ctypes.byref(bad)) == md.MOED_ERR_TUNING
+    assert lib.moe_decode_gate_up_tuned(*gu, ctypes.byref(v)) == md.MOED_OK
+    dn = [None, 1, None, None, None, None, 0, None, 1, 0, 8, 2, 256, 128, None, Z(0), None]
+    assert lib.moe_decode_down_tuned(*dn, ctypes.byref(bad)) == md.MOED_ERR_TUNING
+    assert lib.moe_decode_down_tuned(*dn, None) == md.MOED_OK
+    # a shape error is still reported for a good tuning
+    args_bad_shape = [None] * 9 + [0, None, 0, 0, 1, 8, 2, 100, 128, None, Z(0), None]
+    assert lib.moe_decode_tuned(*args_bad_shape, ctypes.byref(t)) == md.MOED_ERR_SHAPE
+
+
+def test_no_process_wide_tuning_state(lib):
+    """The library exports no setter of process-wide launch state."""
+    out = os.popen(f"nm -D --defined-only {md.LIB_PATH}").read()
+    assert "moed_set_tuning" not in out
 
 
 def test_inter_layout_roundtrip():

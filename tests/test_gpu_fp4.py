@@ -28,7 +28,7 @@ def gpu():
     md.load()
     oracle.build(force=False)
     yield
-    md.moed_set_tuning(None)
+    md.set_default_tuning(None)
 
 
 def layer(shape, seed=None):
@@ -94,8 +94,7 @@ def test_e2m1_decode_nan_scale():
 # --------------------------------------------------------------------------------------
 
 FULL = ["tiny_B1_E8_k2_H256_I128", "wide_B1_E128_k8_H2048_I768", "batch_B8_E128_k8_H2048_I768"]
-SAMPLED = {"batch_B32_E128_k8_H4096_I1536": [0, 13, 31],
-           "skewed_B64_E256_k8_H7168_I2048": [0, 40, 63]}
+LARGE = ["batch_B32_E128_k8_H4096_I1536", "skewed_B64_E256_k8_H7168_I2048"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -118,31 +117,55 @@ def test_fp4_workload_full_parity(name):
     assert torch.equal(out, out32)
 
 
-@pytest.mark.parametrize("name", list(SAMPLED))
-def test_fp4_workload_sampled_parity(name):
-    say(f"mxfp4 workload {name}: sampled parity")
+@pytest.mark.parametrize("name", LARGE)
+def test_fp4_workload_large_full_parity(name):
+    """Every output of every token against the oracle, on the default and on the pure
+    output-centric kernel pair; determinism and batch = concatenation of tokens."""
+    say(f"mxfp4 workload {name}: full parity, both kernel pairs")
     L = layer(name)
-    toks = SAMPLED[name]
+    B = L.shape.B
     out = run(L)
     assert torch.isfinite(out).all()
     assert torch.equal(run(L), out), "not deterministic"
-    ref, _ = oracle_tokens(L, toks)
-    check_f32(out[toks], ref, "mxfp4 " + name)
+    ref, _ = oracle_tokens(L, list(range(B)))
+    check_f32(out, ref, "mxfp4 " + name)
+    with md.tuned("gu_group=0,dn_group=0"):
+        check_f32(run(L), ref, "mxfp4 output-centric pair " + name)
     # batch = concatenation of single-token calls, bit for bit, on each kernel pair
     # (the per-slot/per-output and the expert-grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
     for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1,gu_rowslots=0"):
-        md.moed_set_tuning(spec)
-        try:
+        with md.tuned(spec):
             full = run(L)
-            for b in toks[:2]:
+            for b in (0, B - 1):
                 one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
                                     L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32,
                                     wformat=WF)
                 torch.cuda.synchronize()
                 assert torch.equal(one[0], full[b]), spec
-        finally:
-            md.moed_set_tuning(None)
+
+
+@pytest.mark.parametrize("shape", [(3, 12, 4, 2048, 256), (2, 9, 1, 4096, 544), (4, 16, 8, 2048, 768)],
+                         ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_fp4_exact_fit_neuron_block_order(shape):
+    """B > 1 with MXFP4 rows of exactly 64*U chunks: the exact-fit gate/up in neuron-block order
+    (gu_order=2) computes the same floats as in slot-major order (gu_order=0), and matches the
+    oracle."""
+    B = shape[0]
+    L = small(*shape, seed=sum(shape) + 21)
+    x, ids, _ = md.layer_device_inputs(L)
+    got = {}
+    for order in (0, 2):
+        with md.tuned(f"gu_group=0,gu_order={order}"):
+            got[order] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF)
+            torch.cuda.synchronize()
+    assert torch.equal(got[0], got[2])
+    _, a_ref = oracle_tokens(L, list(range(B)))
+    check_f32(md.inter_to_bki(got[2]).reshape(B, -1), a_ref.reshape(B, -1), f"mxfp4 gu_order=2 a {shape}")
+    with md.tuned("gu_group=0,gu_order=2"):
+        out = run(L)
+    ref, _ = oracle_tokens(L, list(range(B)))
+    check_f32(out, ref, f"mxfp4 gu_order=2 {shape}")
 
 
 SHAPES = [
@@ -176,11 +199,11 @@ def test_fp4_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 16448, 64)]:
         L = small(*shape, seed=3)
         ref, _ = oracle_tokens(L, list(range(shape[0])))
-        md.moed_set_tuning(spec)
+        md.set_default_tuning(spec)
         try:
             check_f32(run(L), ref, f"mxfp4 {spec} {shape}")
         finally:
-            md.moed_set_tuning(None)
+            md.set_default_tuning(None)
 
 
 def test_fp4_duplicate_and_invalid_ids():
@@ -218,7 +241,7 @@ def test_fp4_grouped_gate_up(shape):
     B = shape[0]
     L = small(*shape, seed=sum(shape) + 21)
     ref, a_ref = oracle_tokens(L, list(range(B)))
-    md.moed_set_tuning("gu_group=1")
+    md.set_default_tuning("gu_group=1")
     try:
         out = run(L)
         check_f32(out, ref, f"mxfp4 grouped {shape}")
@@ -229,7 +252,7 @@ def test_fp4_grouped_gate_up(shape):
         check_f32(a.reshape(B, -1), a_ref.reshape(B, -1), f"mxfp4 grouped a {shape}")
         assert torch.equal(run(L), out)
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 @pytest.mark.parametrize("shape", [(80, 2, 2, 96, 160), (64, 4, 2, 2080, 288)],
@@ -241,7 +264,7 @@ def test_fp4_expert_major_down(shape):
     L = small(*shape, seed=sum(shape) + 31)
     ref, _ = oracle_tokens(L, list(range(B)))
     for tiles, rt in ((0, 1), (0, 2), (1, 2)):
-        md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
+        md.set_default_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
         try:
             out = run(L)
             check_f32(out, ref, f"mxfp4 expert-major tiles={tiles} rt={rt} {shape}")
@@ -255,9 +278,9 @@ def test_fp4_expert_major_down(shape):
             # bf16 intermediate (the B operand is the bf16 value itself): close to the per-output
             # kernel on the same intermediate
             o16 = run(L, inter_dtype=torch.bfloat16)
-            md.moed_set_tuning("dn_group=0")
+            md.set_default_tuning("dn_group=0")
             p16 = run(L, inter_dtype=torch.bfloat16)
             rms = float(np.sqrt(np.mean(ref ** 2)))
             assert float((o16 - p16).abs().max()) <= 1e-4 * rms
         finally:
-            md.moed_set_tuning(None)
+            md.set_default_tuning(None)

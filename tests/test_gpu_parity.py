@@ -6,9 +6,8 @@ outputs must be the round-to-nearest-even of the float32 result, bit for bit,
 and within that bound plus half a bf16 ulp of the oracle value.
 
 The five decode workloads run in the launch configuration the benchmark
-times. The three smaller ones are compared on every output; the two large
-ones on every output of four sampled tokens (the oracle is run on just those
-tokens, which is exact because tokens are independent) plus properties that
+times, and every output of every token is compared with the oracle; the two
+large ones also on the pure output-centric kernel pair, plus properties that
 hold at any size (determinism, finiteness, batch = concatenation of tokens).
 """
 import math
@@ -32,7 +31,7 @@ def gpu():
     md.load()                                   # raises if the HIP library is missing
     oracle.build(force=False)
     yield
-    md.moed_set_tuning(None)
+    md.set_default_tuning(None)
 
 
 def say(*a):
@@ -134,8 +133,7 @@ def test_decode_nan_scale():
 # --------------------------------------------------------------------------------------
 
 FULL = ["tiny_B1_E8_k2_H256_I128", "wide_B1_E128_k8_H2048_I768", "batch_B8_E128_k8_H2048_I768"]
-SAMPLED = {"batch_B32_E128_k8_H4096_I1536": [0, 7, 19, 31],
-           "skewed_B64_E256_k8_H7168_I2048": [0, 21, 42, 63]}
+LARGE = ["batch_B32_E128_k8_H4096_I1536", "skewed_B64_E256_k8_H7168_I2048"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -154,33 +152,46 @@ def test_workload_full_parity(name):
     check_f32(a.reshape(L.shape.B, -1), a_ref.reshape(L.shape.B, -1), name + " a")
 
 
-@pytest.mark.parametrize("name", list(SAMPLED))
-def test_workload_sampled_parity(name):
-    say(f"workload {name}: sampled parity")
+@pytest.mark.parametrize("name", LARGE)
+def test_workload_large_full_parity(name):
+    """The two large workloads, every output of every token against the oracle (run on all
+    tokens, all host threads), on the default kernel pair (expert-grouped gate/up, expert-major
+    down) and on the pure output-centric pair (per-slot gate/up, per-output down); plus
+    determinism, the bf16 store, the intermediate, and batch = concatenation of tokens."""
+    say(f"workload {name}: full parity, both kernel pairs")
     L = layer(name)
-    toks = SAMPLED[name]
+    B = L.shape.B
     out32 = run(L, torch.float32)
     out32b = run(L, torch.float32)
     assert torch.equal(out32, out32b), "not deterministic"
     assert torch.isfinite(out32).all()
-    ref, _ = oracle_tokens(L, toks)
-    check_f32(out32[toks], ref, name)
+    say(f"workload {name}: oracle on all {B} tokens")
+    ref, a_ref = oracle_tokens(L, list(range(B)))
+    check_f32(out32, ref, name + " default pair")
     out16 = run(L, torch.bfloat16)
-    check_bf16(out16[toks], out32[toks], ref, name)
+    check_bf16(out16, out32, ref, name + " default pair")
+    x, ids, w = md.layer_device_inputs(L)
+    a = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+    torch.cuda.synchronize()
+    check_f32(a.reshape(B, -1), a_ref.reshape(B, -1), name + " default a")
+    with md.tuned("gu_group=0,dn_group=0"):
+        oc32 = run(L, torch.float32)
+        check_f32(oc32, ref, name + " output-centric pair")
+        oc16 = run(L, torch.bfloat16)
+        check_bf16(oc16, oc32, ref, name + " output-centric pair")
+        a0 = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s))
+        torch.cuda.synchronize()
+        check_f32(a0.reshape(B, -1), a_ref.reshape(B, -1), name + " output-centric a")
     # batch = concatenation of single-token calls, bit for bit, on each kernel pair
     # (the per-slot/per-output and the grouped kernels accumulate in different orders)
-    x, ids, w = md.layer_device_inputs(L)
     for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1,gu_rowslots=0"):
-        md.moed_set_tuning(spec)
-        try:
+        with md.tuned(spec):
             full = run(L, torch.float32)
-            for b in toks[:2]:
+            for b in (0, B // 3, B - 1):
                 one = md.moe_decode(x[b:b + 1].contiguous(), ids[b:b + 1].contiguous(), w[b:b + 1].contiguous(),
                                     L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32)
                 torch.cuda.synchronize()
                 assert torch.equal(one[0], full[b]), spec
-        finally:
-            md.moed_set_tuning(None)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -243,11 +254,11 @@ def test_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 8224, 64)]:
         L = small(*shape, seed=3)
         ref, _ = oracle_tokens(L, list(range(shape[0])))
-        md.moed_set_tuning(spec)
+        md.set_default_tuning(spec)
         try:
             check_f32(run(L), ref, f"{spec} {shape}")
         finally:
-            md.moed_set_tuning(None)
+            md.set_default_tuning(None)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -346,7 +357,7 @@ def test_grouped_gate_up(shape):
     B = shape[0]
     L = small(*shape, seed=sum(shape) + 1)
     ref, a_ref = oracle_tokens(L, list(range(B)))
-    md.moed_set_tuning("gu_group=1,dn_group=1")
+    md.set_default_tuning("gu_group=1,dn_group=1")
     try:
         check_f32(run(L), ref, f"grouped {shape}")
         check_bf16(run(L, torch.bfloat16), run(L), ref, f"grouped bf16 {shape}")
@@ -361,7 +372,7 @@ def test_grouped_gate_up(shape):
         # bit-exact agreement between repeated runs
         assert torch.equal(run(L), run(L))
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 def test_grouped_duplicates_and_invalid_ids():
@@ -370,11 +381,11 @@ def test_grouped_duplicates_and_invalid_ids():
     ids[:, 1] = ids[:, 0]                 # duplicate slot in every token
     ids[3, 2] = 5                         # out of range
     ids[7, 0] = -1
-    md.moed_set_tuning("gu_group=1,dn_group=1")
+    md.set_default_tuning("gu_group=1,dn_group=1")
     try:
         out = run(L, ids=ids).cpu()
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
     assert torch.isnan(out[3]).all() and torch.isnan(out[7]).all()
     good = [b for b in range(20) if b not in (3, 7)]
     ref, _ = oracle_tokens(L, good, ids=ids)
@@ -444,7 +455,7 @@ def test_expert_major_down(shape, tiles, rt):
     B, E, k, H, I = shape
     L = small(*shape, seed=sum(shape) + 5)
     ref, _ = oracle_tokens(L, list(range(B)))
-    md.moed_set_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
+    md.set_default_tuning(f"dn_group=1,dn_tiles={tiles},dn_rt={rt}")
     try:
         out = run(L)
         check_f32(out, ref, f"expert-major tiles={tiles} rt={rt} {shape}")
@@ -466,12 +477,12 @@ def test_expert_major_down(shape, tiles, rt):
         # bf16 intermediates (the B operand is then the bf16 value itself): close to the
         # per-output kernel on the same intermediate
         o16 = run(L, inter_dtype=torch.bfloat16)
-        md.moed_set_tuning("dn_group=0")
+        md.set_default_tuning("dn_group=0")
         p16 = run(L, inter_dtype=torch.bfloat16)
         rms = math.sqrt(float(np.mean(ref ** 2)))
         assert float((o16 - p16).abs().max()) <= 1e-4 * rms
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 def test_expert_major_down_without_partials_is_per_output():
@@ -479,15 +490,15 @@ def test_expert_major_down_without_partials_is_per_output():
     L = small(40, 3, 2, 96, 160, seed=9)
     x, ids, w = md.layer_device_inputs(L)
     a_ws = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
-    md.moed_set_tuning("dn_group=1")
+    md.set_default_tuning("dn_group=1")
     try:
         o1 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32)
-        md.moed_set_tuning("dn_group=0")
+        md.set_default_tuning("dn_group=0")
         o0 = md.moe_decode_down(a_ws, ids, w, L.wd_q, L.wd_s, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(o0, o1)
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 def test_long_slot_list_takes_fewer_tiles():
@@ -498,11 +509,11 @@ def test_long_slot_list_takes_fewer_tiles():
     out = run(L)
     ref, _ = oracle_tokens(L, toks)
     check_f32(out[toks], ref, "B=600")
-    md.moed_set_tuning("dn_tiles=2")
+    md.set_default_tuning("dn_tiles=2")
     try:
         assert torch.equal(run(L), out)
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 def test_slot_list_beyond_lds_falls_back():
@@ -511,11 +522,11 @@ def test_slot_list_beyond_lds_falls_back():
     L = small(1600, 8, 8, 64, 64, seed=33)
     toks = [0, 1, 800, 1599]
     out = run(L)
-    md.moed_set_tuning("gu_group=0,dn_group=0")
+    md.set_default_tuning("gu_group=0,dn_group=0")
     try:
         assert torch.equal(run(L), out)
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
     ref, _ = oracle_tokens(L, toks)
     check_f32(out[toks], ref, "B=1600 fallback")
 
@@ -584,6 +595,59 @@ def test_check_mode(monkeypatch):
     torch.cuda.synchronize()
 
 
+
+def test_input_check_scale_range(monkeypatch):
+    """MOED_CHECK=1 also reports routed block scales outside the range the large-batch kernels
+    decode exactly (MXFP8 codes 10..245), as MOED_ERR_SCALE, and only for calls that take those
+    kernels: the expert-grouped gate/up for gate/up scales, the expert-major down for down scales."""
+    L = small(40, 4, 2, 256, 64, seed=43)            # B*k*H >= 2458*E and B*k >= 2E: both grouped
+    monkeypatch.setenv("MOED_CHECK", "1")
+    base = run(L)
+    routed = sorted(set(L.ids.ravel().tolist()))
+    e = routed[0]
+
+    def status(fn):
+        try:
+            fn()
+            torch.cuda.synchronize()
+            return md.MOED_OK
+        except md.MoedError as err:
+            return err.status
+
+    x, idd, wd = md.layer_device_inputs(L)
+    for t, idx, code, grouped_spec, plain_spec in (
+            (L.wg_s, (e, 1, 2), 5, "gu_group=1", "gu_group=0"),
+            (L.wu_s, (e, 0, 0), 250, "gu_group=1", "gu_group=0"),
+            (L.wd_s, (e, 3, 1), 9, "dn_group=1", "dn_group=0")):
+        saved = t[idx].item()
+        t[idx] = code
+        try:
+            assert status(lambda: run(L)) == md.MOED_ERR_SCALE
+            with md.tuned(grouped_spec):
+                assert status(lambda: run(L)) == md.MOED_ERR_SCALE
+            with md.tuned(plain_spec):
+                assert status(lambda: run(L)) == md.MOED_OK
+            if t is L.wd_s:
+                a_ws = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s)
+                y = torch.empty(40 * 2 * 256, dtype=torch.float32, device="cuda")
+                assert status(lambda: md.moe_decode_down(a_ws, idd, wd, L.wd_q, L.wd_s, partials=y)) == \
+                    md.MOED_ERR_SCALE
+                assert status(lambda: md.moe_decode_down(a_ws, idd, wd, L.wd_q, L.wd_s)) == md.MOED_OK
+            else:
+                assert status(lambda: md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s)) == \
+                    md.MOED_ERR_SCALE
+        finally:
+            t[idx] = saved
+    # the edges of the exact range are accepted
+    for code in (10, 245):
+        saved = L.wg_s[e, 0, 0].item()
+        L.wg_s[e, 0, 0] = code
+        try:
+            assert status(lambda: run(L)) == md.MOED_OK
+        finally:
+            L.wg_s[e, 0, 0] = saved
+    assert torch.equal(run(L), base)
+
 ROW_PATH = [
     (24, 16, 2, 2080, 64),    # ~3 slots per expert (some above 4: MFMA path); a ragged second chunk per lane
     (12, 8, 3, 4096, 128),    # four chunks per lane per pass
@@ -600,14 +664,14 @@ def test_grouped_row_path(shape, wformat):
     B, E, k, H, I = shape
     L = synth.make_layer(synth.LayerShape("rp", B, E, k, H, I), seed=sum(shape) + 9, device="cuda", wformat=wformat)
     x, ids, _ = md.layer_device_inputs(L)
-    md.moed_set_tuning("gu_group=0")
+    md.set_default_tuning("gu_group=0")
     try:
         a_slot = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
-        md.moed_set_tuning("gu_group=1,gu_rowslots=4")
+        md.set_default_tuning("gu_group=1,gu_rowslots=4")
         a_row = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
         torch.cuda.synchronize()
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
     counts = np.bincount(L.ids.ravel(), minlength=E)
     slot_x = 2 * H if wformat == "mxfp8" else 2 * H    # bf16 x row bytes per slot
     fits = max(0, min(4, 32768 // slot_x))
@@ -642,7 +706,7 @@ def test_grouped_wide_loads(shape, wformat):
     got = {}
     try:
         for wide in (0, 1):
-            md.moed_set_tuning(f"gu_group=1,gu_rowslots=0,gu_wide={wide}")
+            md.set_default_tuning(f"gu_group=1,gu_rowslots=0,gu_wide={wide}")
             for dt in (torch.float32, torch.bfloat16):
                 got[wide, dt] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
                                                       inter_dtype=dt, wformat=wformat)
@@ -650,7 +714,7 @@ def test_grouped_wide_loads(shape, wformat):
         say(f"wide loads {shape} {wformat}: comparing")
         for dt in (torch.float32, torch.bfloat16):
             assert torch.equal(got[1, dt], got[0, dt]), f"{shape} {wformat} {dt}"
-        md.moed_set_tuning("gu_group=1,gu_rowslots=0,gu_wide=1")
+        md.set_default_tuning("gu_group=1,gu_rowslots=0,gu_wide=1")
         ref, _ = oracle_tokens(L, [0, B - 1], wformat=wformat)
         xd, idd, wd = md.layer_device_inputs(L)
         out = md.moe_decode(xd, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
@@ -658,7 +722,7 @@ def test_grouped_wide_loads(shape, wformat):
         torch.cuda.synchronize()
         check_f32(out[[0, B - 1]], ref, f"wide {shape} {wformat}")
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
 
 
 # (B, E, k, H, I): which straight-line kernels each shape takes --
@@ -687,7 +751,7 @@ def test_straight_line_kernels_match_generic(shape, wformat):
     idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
     got = {}
     for spec in ["gu_exact=0,dn_onepass=0", None]:
-        md.moed_set_tuning(spec)
+        md.set_default_tuning(spec)
         try:
             say(f"straight-line {shape} {wformat} spec={spec}")
             a = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat)
@@ -696,7 +760,7 @@ def test_straight_line_kernels_match_generic(shape, wformat):
             torch.cuda.synchronize()
             got[spec] = [a.clone()] + [o.clone() for o in outs]
         finally:
-            md.moed_set_tuning(None)
+            md.set_default_tuning(None)
     for t0, t1, what in zip(got["gu_exact=0,dn_onepass=0"], got[None], ["a", "out f32", "out bf16"]):
         nan0, nan1 = torch.isnan(t0.float()), torch.isnan(t1.float())
         assert torch.equal(nan0, nan1), f"{shape} {wformat}: {what} NaN positions differ"
@@ -728,7 +792,7 @@ def test_grouped_work_list_matches_full_grid(shape, wformat):
     got = []
     for spec in ["gu_grid=0,dn_grid=0,gu_group=1,dn_group=1", "gu_group=1,dn_group=1",
                  "gu_grid=5,dn_grid=3,gu_group=1,dn_group=1"]:
-        md.moed_set_tuning(spec)
+        md.set_default_tuning(spec)
         try:
             say(f"work list {shape} {wformat} {spec}")
             out = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
@@ -736,7 +800,7 @@ def test_grouped_work_list_matches_full_grid(shape, wformat):
             torch.cuda.synchronize()
             got.append(out.clone())
         finally:
-            md.moed_set_tuning(None)
+            md.set_default_tuning(None)
     for g in got[1:]:
         assert torch.equal(torch.isnan(g), torch.isnan(got[0]))
         assert torch.equal(g[:B - 1].view(torch.int32), got[0][:B - 1].view(torch.int32)), f"{shape} {wformat}"
@@ -773,14 +837,14 @@ def test_expert_major_down_wide_loads(shape, wformat, rt):
     got = {}
     try:
         for wide in (0, 2):                        # 2: the wide loads for either weight format
-            md.moed_set_tuning(f"dn_group=1,dn_rt={rt},dn_wide={wide}")
+            md.set_default_tuning(f"dn_group=1,dn_rt={rt},dn_wide={wide}")
             say(f"down wide loads {shape} {wformat} rt={rt} wide={wide}")
             for dt in (torch.float32, torch.bfloat16):
                 got[wide, dt] = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
                                               out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
             torch.cuda.synchronize()
     finally:
-        md.moed_set_tuning(None)
+        md.set_default_tuning(None)
     for dt in (torch.float32, torch.bfloat16):
         o0, o1 = got[0, dt], got[2, dt]
         assert torch.equal(torch.isnan(o0), torch.isnan(o1))
