@@ -158,6 +158,28 @@ int moe_decode(const void *x, const int32_t *topk_ids, const float *topk_w,
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The whole layer without a workspace argument, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Arguments, results and errors as moe_decode() without
+ * its workspace; the intermediate and the per-slot partials go to a scratch
+ * array the library holds in device memory instead: 32 MiB per device, part of
+ * the library's code object, kept until the process ends (its address is
+ * taken on the first call on each device). Sizes whose
+ * moed_workspace_bytes(B, k, H, I, inter_dtype) exceeds 32 MiB return
+ * MOED_ERR_WORKSPACE before anything is launched (every workload of up to
+ * B = 64 tokens at H = 7168, I = 2048, k = 8 fits). Nothing in the array has
+ * to start at zero: every call writes what it reads. All calls on one device
+ * share the array, so calls that overlap on one device (from other streams
+ * or host threads) race; the caller serialises them. Allocates nothing.
+ */
+int moe_decode_noalloc(const void *x, const int32_t *topk_ids, const float *topk_w,
+                       const uint8_t *wg_q, const uint8_t *wg_s,
+                       const uint8_t *wu_q, const uint8_t *wu_s,
+                       const uint8_t *wd_q, const uint8_t *wd_s, int weight_format,
+                       void *out, int out_dtype, int inter_dtype,
+                       int B, int E, int k, int H, int I, void *stream);
+
+/*
  * Gate/up step alone: a[b][j][i] = SiLU(Wg^[e]·x[b])_i * (Wu^[e]·x[b])_i with
  * e = topk_ids[b][j], stored as inter_dtype into `a` (B*k*I elements).
  * SiLU(t) = t / (1 + exp(-t)).  (Warp-decode post, "How the two kernels work",

@@ -7,7 +7,6 @@
 // conversion), separately for the gate/up and the down matrices, so that the
 // caller can reject only the calls that take those kernels. The result is a
 // flag word (kCheck* bits) in a file-scope device array: no allocation.
-#include <map>
 #include <mutex>
 
 #include "launch.h"
@@ -19,43 +18,62 @@ namespace {
 __device__ __align__(256) uint32_t check_flag_word[64];
 }
 
+// Per-device facts are kept in fixed tables (no heap allocation, so that the
+// entry point for callers that cannot allocate may use them too).
 hipError_t check_flag(uint32_t** flag)
 {
     static std::mutex mu;
-    static std::map<int, uint32_t*> addr;         // per device: the array's address on it
+    static uint32_t* addr[kMaxDevices] = {};      // per device: the array's address on it
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
-    auto it = addr.find(dev);
-    if (it == addr.end()) {
+    if (!addr[dev]) {
         void* p = nullptr;
         err = hipGetSymbolAddress(&p, HIP_SYMBOL(check_flag_word));
         if (err != hipSuccess)
             return err;
-        it = addr.emplace(dev, static_cast<uint32_t*>(p)).first;
+        addr[dev] = static_cast<uint32_t*>(p);
     }
-    *flag = it->second;
+    *flag = addr[dev];
     return hipSuccess;
 }
 
 hipError_t set_max_dynamic_lds(const void* func, int bytes)
 {
+    struct Entry {
+        int dev;
+        const void* func;
+        int bytes;
+    };
+    constexpr int kSlots = 256;                   // (device, kernel) pairs: a handful of kernels per device
     static std::mutex mu;
-    static std::map<std::pair<int, const void*>, int> done;    // (device, kernel) -> bytes set
+    static Entry done[kSlots];
+    static int used = 0;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess)
         return err;
     std::lock_guard<std::mutex> lock(mu);
-    auto it = done.find({dev, func});
-    if (it != done.end() && it->second >= bytes)
-        return hipSuccess;
+    int slot = -1;
+    for (int i = 0; i < used; ++i) {
+        if (done[i].dev == dev && done[i].func == func) {
+            if (done[i].bytes >= bytes)
+                return hipSuccess;
+            slot = i;
+        }
+    }
     err = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (err == hipSuccess)
-        done[{dev, func}] = bytes;
-    return err;
+    if (err != hipSuccess)
+        return err;
+    if (slot < 0 && used < kSlots)
+        slot = used++;
+    if (slot >= 0)
+        done[slot] = Entry{dev, func, bytes};
+    return hipSuccess;
 }
 
 __global__ void moe_check_clear_kernel(uint32_t* flag)

@@ -120,6 +120,7 @@ constexpr uint32_t kCheckScaleDown = 8u;      // a routed down block scale the e
 constexpr int kExactScaleLoFP8 = 10, kExactScaleHiFP8 = 245;
 constexpr int kExactScaleLoFP4 = 2, kExactScaleHiFP4 = 252;
 hipError_t launch_check(const CheckArgs& c, uint32_t* flag, hipStream_t s);
+constexpr int kMaxDevices = 64;               // devices the per-device tables hold
 // Device address of the check flag word of the current device (a file-scope
 // device array; its address is taken once per device).
 hipError_t check_flag(uint32_t** flag);

@@ -211,6 +211,36 @@ int layer(const void* x, const int32_t* topk_ids, const float* topk_w, const uin
         out_dtype == MOED_BF16, t, partials, s));
 }
 
+// Scratch of moe_decode_noalloc(): the workspace (intermediate, then the
+// per-slot partials) in a file-scope device array, one per device, held until
+// the process ends. In host code `scratch` names a host-side stand-in, not the
+// device memory: host code only ever uses the address hipGetSymbolAddress
+// gives for the current device, taken once per device on its first call.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out)
+{
+    static std::mutex mu;
+    static void* addr[moed::kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= moed::kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,6 +365,30 @@ int moe_decode(const void* x, const int32_t* topk_ids, const float* topk_w, cons
 {
     return moe_decode_tuned(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, weight_format, out, out_dtype,
                             inter_dtype, B, E, k, H, I, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_decode_noalloc(const void* x, const int32_t* topk_ids, const float* topk_w, const uint8_t* wg_q,
+                       const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wd_q,
+                       const uint8_t* wd_s, int weight_format, void* out, int out_dtype, int inter_dtype, int B,
+                       int E, int k, int H, int I, void* stream)
+{
+    if (int st = check_shape(B, E, k, H, I))
+        return st;
+    if (!dtype_ok(inter_dtype) || !dtype_ok(out_dtype) || !wformat_ok(weight_format))
+        return MOED_ERR_DTYPE;
+    if (B == 0)
+        return MOED_OK;
+    if (!x || !topk_ids || !topk_w || !wg_q || !wg_s || !wu_q || !wu_s || !wd_q || !wd_s || !out)
+        return MOED_ERR_NULL;
+    if (moed_workspace_bytes(B, k, H, I, inter_dtype) > kScratchBytes)
+        return MOED_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(wg_q) || !aligned16(wu_q) || !aligned16(wd_q))
+        return MOED_ERR_ALIGN;
+    void* ws = nullptr;
+    if (int st = hip_status(scratch_address(&ws)))
+        return st;
+    return layer(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, weight_format, out, out_dtype, inter_dtype,
+                 B, E, k, H, I, ws, moed::Tuning(), static_cast<hipStream_t>(stream));
 }
 
 int moe_route(const float* logits, int B, int E, int k, int n_shared, float routed_scale, int32_t* topk_ids,

@@ -25,7 +25,7 @@ MOED_BF16, MOED_F32 = 0, 1
 EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down", "moe_route",
            "moed_selftest_decode", "moed_bench_read", "moed_bench_copy", "moed_status_string",
            "moed_last_hip_error", "moed_tuning_init", "moe_decode_tuned", "moe_decode_gate_up_tuned",
-           "moe_decode_down_tuned")
+           "moe_decode_down_tuned", "moe_decode_noalloc")
 
 
 class MoedTuning(ctypes.Structure):
@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
         lib.moe_decode_gate_up.restype = I
         lib.moe_decode_down.argtypes = [P, I, P, P, P, P, I, P, I] + [I] * 5 + [P, Z, P]
         lib.moe_decode_down.restype = I
+        lib.moe_decode_noalloc.argtypes = [P] * 9 + [I, P] + [I] * 7 + [P]
+        lib.moe_decode_noalloc.restype = I
         TP = ctypes.POINTER(MoedTuning)
         lib.moed_tuning_init.argtypes = [TP, ctypes.c_char_p]
         lib.moed_tuning_init.restype = I
@@ -195,6 +197,26 @@ def moe_decode(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out=None
         B, E, k, H, I, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     st = lib.moe_decode_tuned(*args, tp) if use else lib.moe_decode(*args)
     _check(st, "moe_decode")
+    return out
+
+
+def moe_decode_noalloc(x, topk_ids, topk_w, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, out,
+                       inter_dtype=torch.float32, stream=None, wformat="mxfp8"):
+    """The whole layer into the caller's `out` [B, H] (bf16 or float32) with the library's
+    device scratch array instead of a workspace: the call allocates nothing."""
+    B, H = x.shape
+    k = topk_ids.shape[1]
+    E, I = wg_q.shape[0], wg_q.shape[1]
+    HB, IB = _kb(H, wformat), _kb(I, wformat)
+    st = load().moe_decode_noalloc(
+        _ptr(x, "x", torch.bfloat16, (B, H)), _ptr(topk_ids, "topk_ids", torch.int32, (B, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (B, k)),
+        _ptr(wg_q, "wg_q", torch.uint8, (E, I, HB)), _ptr(wg_s, "wg_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wu_q, "wu_q", torch.uint8, (E, I, HB)), _ptr(wu_s, "wu_s", torch.uint8, (E, I, H // 32)),
+        _ptr(wd_q, "wd_q", torch.uint8, (E, H, IB)), _ptr(wd_s, "wd_s", torch.uint8, (E, H, I // 32)),
+        _WF[wformat], _ptr(out, "out", None, (B, H)), _DT[out.dtype], _DT[inter_dtype],
+        B, E, k, H, I, _stream(stream))
+    _check(st, "moe_decode_noalloc")
     return out
 
 
