@@ -38,23 +38,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The sources the per-slot gate/up kernel (the dominant kernel of the single-token layer) is
-# compiled from, with its launch-shape defaults. Its committed HBM counters stay valid while the
-# code in these files (comments and blank lines removed) is unchanged.
-GATE_UP_SOURCES = ("gate_up.hip", "gate_up_body.h", "launch.h", "mx_device.h")
-
-
 def _code_only(src: str) -> str:
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     return "\n".join(line.strip() for line in src.splitlines() if line.strip())
 
 
-# ... and those of the expert-grouped gate/up and the expert-major down (the large-batch kernels).
-GROUPED_SOURCES = ("gate_up_grouped.hip", "down_grouped.hip", "grouped_common.h", "launch.h", "mx_device.h")
+# The sources the kernels of the decode-batch layer (per-slot gate/up, per-output down) are
+# compiled from, with the launch table; and those of the large-batch kernels. A committed profile
+# of either set stays valid while the code in these files (comments and blank lines removed) is
+# unchanged.
+LAYER_SOURCES = ("gate_up.hip", "gate_up_body.h", "down.hip", "down_body.h", "down_onepass.hip", "launch.h",
+                 "mx_device.h", "moedecode.hip")
+GROUPED_SOURCES = ("gate_up_grouped.hip", "down_grouped.hip", "grouped_common.h", "launch.h", "mx_device.h",
+                   "moedecode.hip")
 
 
-def source_digest(files=GATE_UP_SOURCES) -> str:
+def source_digest(files=LAYER_SOURCES) -> str:
     h = hashlib.sha256()
     for name in files:
         with open(os.path.join(ROOT, "output_centric_expert_amd", "csrc", name)) as fh:
@@ -62,15 +62,18 @@ def source_digest(files=GATE_UP_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
-    p = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+def load_profile(prefix: str, workload: str, files=LAYER_SOURCES):
+    """A committed profile summary (profiles/<prefix>_<workload>.json), if it was taken from the
+    current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{prefix}_{workload}.json")
     if not os.path.exists(p):
         return None
-    d = json.load(open(p))
-    if d.get("source_digest") != source_digest():
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_digest") != source_digest(files):
         return None
-    return d.get("hbm_bytes_per_launch")
+    d["_file"] = os.path.relpath(p, ROOT)
+    return d
 
 
 def main():
@@ -85,6 +88,8 @@ def main():
     ap.add_argument("--tune", default=None, help="launch-shape override (a moed_tuning_init spec)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--single", action="store_true",
+                    help="time only --workload (no per-config list of every workload)")
     ap.add_argument("--all", action="store_true",
                     help="time every decode workload (one JSON line each); not the driver's line")
     ap.add_argument("--diagnostics", action="store_true",
@@ -133,29 +138,37 @@ def main():
         return
 
     K, W = args.steps, args.warmup
+    log("step: the timed layer graph")
     t = measure_layer(md, L, R, K, W)
-    peak = measured_read_peak(md)
     B, E, k, H, I = shape.B, shape.E, shape.k, shape.H, shape.I
     U = L.unique_experts
     uniq = L.unique_weight_bytes
-    gu_bytes, _ = kernel_bytes(L)
-    ms_per_step, ms_gu = t["ms_per_step"], t["ms_gate_up"]
+    gu_bytes, dn_bytes = kernel_bytes(L)
+    ms_per_step = t["ms_per_step"]
     gbs = uniq / (ms_per_step * 1e-3) / 1e9
-    gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
 
-    traffic = load_traffic("gate_up", args.workload) if L.wformat == "mxfp8" else None
-    _, dn_bytes = kernel_bytes(L)
-    floor = same_size_reads(md, gu_bytes, dn_bytes, K=min(K, 2000)) if L.unique_weight_bytes < (1 << 30) else None
-    roofline = {"bound": "hbm", "kernel": gate_up_kernel_name(L), "achieved": round(gu_gbs, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
-                "avg_launch_us": round(ms_gu * 1e3, 3)}
-    if floor:
-        roofline["same_size_read_us"] = floor["gate_up_bytes_us"]
-        roofline["frac_of_same_size_read"] = round(floor["gate_up_bytes_us"] / (ms_gu * 1e3), 4)
+    log("step: read floors")
+    peak = measured_read_peak(md)
+    floors = read_floors(md, (dn_bytes, gu_bytes, gu_bytes + dn_bytes)) if uniq < (1 << 30) else None
+    files = LAYER_SOURCES if gate_up_kernel_name(L) != "moe_gate_up_grouped_wide_kernel" else GROUPED_SOURCES
+    counters = load_profile("counters_layer", args.workload, files) if L.wformat == "mxfp8" else None
+    trace = load_profile("kernel_trace", args.workload, files) if L.wformat == "mxfp8" else None
+    roof = roofline(L, "gate_up", gu_bytes, t, counters, trace, floors)
+    roof_dn = roofline(L, "down", dn_bytes, t, counters, trace, floors)
+
+    per_config = None
+    if not args.single:
+        per_config = []
+        for name in synth.WORKLOAD_ORDER:
+            log(f"step: per-config {name}")
+            per_config.append(config_entry(md, synth, name, args.wformat,
+                                           reuse=(L, t) if name == args.workload else None,
+                                           cpu=not args.no_cpu))
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
+        log("step: cpu baseline")
         cpu = cpu_baseline(L, uniq, args.cpu_seconds)
 
     res = {
@@ -179,12 +192,270 @@ def main():
         **timing_fields(L, t),
         "measured_read_peak_gbs": round(peak, 1),
         "frac_of_measured_read_peak": round(gbs / peak, 4),
-        "same_size_reads_us": floor,
-        "roofline": roofline,
+        "read_floors": floors,
+        "roofline": roof,
+        "roofline_down": roof_dn,
+        "per_config": per_config,
         "cpu_baseline": cpu,
         "tuning": args.tune or "built-in",
     }
     print(json.dumps(res), flush=True)
+
+
+def down_kernel_name(L):
+    """The down kernel(s) the built-in launch table picks inside moe_decode: the expert-major
+    kernel plus its combine once B*k >= 2E, else the per-output one-pass kernel for float32 a when
+    the token's k slots form one lane-group set and a row is at most one chunk per lane, else the
+    staged per-output kernel."""
+    sh = L.shape
+    if sh.B * sh.k >= 2 * sh.E:
+        return "moe_down_expert_kernel + moe_down_combine_kernel"
+    cpr = sh.I // 32 if L.wformat == "mxfp4" else sh.I // 16
+    groups = 1
+    while groups < 4 and cpr <= 64 // (2 * groups) and 2 * groups <= sh.k:
+        groups *= 2
+    jb = sh.k // groups
+    if sh.k == groups * jb and jb & (jb - 1) == 0 and jb <= 8 and cpr <= 64 // groups and \
+            (groups > 1 or sh.B <= 2 or sh.B * sh.k < sh.E):
+        return "moe_down_onepass_kernel"
+    return "moe_down_staged_kernel"
+
+
+def roofline(L, step, alg_bytes, t, counters, trace, floors):
+    """Roofline entry of one layer step: algorithmic bytes per launch over the kernel's average
+    launch duration, against MI355X's 8 TB/s. The duration is measured live: HIP events on the
+    launch stream around a graph of K launches of the step alone (weights rotating through the
+    copies), divided by K. The entry also carries the mean duration the committed rocprofv3
+    kernel trace gives for the same launches (the one-step graph; tracing lengthens each
+    dispatch a little), when the trace was taken from the current sources, HBM traffic from the
+    committed counter runs, and the best same-size pure read."""
+    us = t["ms_" + step] * 1e3
+    achieved = alg_bytes / (us * 1e-6) / 1e9
+    e = {"bound": "hbm", "kernel": gate_up_kernel_name(L) if step == "gate_up" else down_kernel_name(L),
+         "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+         "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(us, 3),
+         "avg_launch_us_source": "HIP events around a graph of K launches of this step, / K"}
+    if counters and step in counters:
+        e["traffic"] = counters[step]["hbm_bytes_per_launch"]
+        e["traffic_over_algorithmic"] = round(counters[step]["traffic_over_algorithmic"], 4)
+        e["traffic_source"] = counters["_file"]
+    ctx = f"{step} after {step}"
+    if trace and ctx in trace.get("contexts", {}):
+        tr = trace["contexts"][ctx]
+        e["avg_launch_us_rocprof"] = round(tr["mean_ns"] * 1e-3, 3)
+        e["frac_rocprof"] = round(alg_bytes / (tr["mean_ns"] * 1e-9) / 1e9 / PEAK_HBM_GBS, 4)
+        e["rocprof_source"] = f"{trace['_file']} (context '{ctx}', {tr['dispatches']} dispatches)"
+    if floors and str(alg_bytes) in floors["single"]:
+        e["same_size_read_us"] = floors["single"][str(alg_bytes)]["us"]
+        e["frac_of_same_size_read"] = round(floors["single"][str(alg_bytes)]["us"] / us, 4)
+    return e
+
+
+# Launch shapes the read-floor probe tries: one-pass grids and persistent grids of 1-8
+# workgroups per CU (256 CUs), 1-16 chunks of 1 KiB per wavefront in flight.
+FLOOR_SHAPES = ([(u, wpg, 0) for u in (1, 2, 4, 8) for wpg in (4, 8)] +
+                [(u, wpg, 256 * m) for u in (2, 4, 8, 16) for wpg in (4, 8, 16) for m in (1, 2, 4, 8)
+                 if wpg * m <= 32])
+
+
+def read_floors(md, sizes, K=300, min_total=1 << 30):
+    """The fastest a pure streaming read of each byte count takes in one launch, over the launch
+    shapes in FLOOR_SHAPES (graph of K back-to-back launches over rotating buffers, so the 256 MB
+    cache cannot serve them), and the fastest two dependent launches of sizes[1] then sizes[0]
+    bytes (the layer's two steps), each with its own best shape. Microseconds per launch."""
+    import numpy as np
+    import torch
+
+    big = max(sizes)
+    R = max(2, -(-min_total // big))
+    bufs = [torch.empty(big + 256, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(K):
+                fn(r)
+        g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / K)
+        del g
+        return float(np.median(res))
+
+    single = {}
+    for nb in sizes:
+        best = None
+        for (u, wpg, groups) in FLOOR_SHAPES:
+            us = timed(lambda r: md.moed_bench_read_cfg(bufs[r % R], sink, nb, u, wpg, groups))
+            if best is None or us < best["us"]:
+                best = {"us": round(us, 3), "unroll": u, "waves_per_group": wpg, "groups": groups,
+                        "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
+        best["frac_of_8TBps"] = round(best["gbs"] / PEAK_HBM_GBS, 4)
+        single[str(nb)] = best
+    a, b = single[str(sizes[1])], single[str(sizes[0])]
+    pair = timed(lambda r: (md.moed_bench_read_cfg(bufs[r % R], sink, sizes[1], a["unroll"], a["waves_per_group"],
+                                                   a["groups"]),
+                            md.moed_bench_read_cfg(bufs[(r + 1) % R], sink, sizes[0], b["unroll"],
+                                                   b["waves_per_group"], b["groups"])))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"single": single, "pair_us": round(pair, 3),
+            "pair_bytes": [sizes[1], sizes[0]], "shapes_tried": len(FLOOR_SHAPES), "launches_per_graph": K}
+
+
+# weight copies and steps per workload when every workload is timed: copies * touched bytes
+# well above the 256 MB cache
+CONFIG_PLAN = {"tiny_B1_E8_k2_H256_I128": (32, 1000), "wide_B1_E128_k8_H2048_I768": (32, 1000),
+               "batch_B8_E128_k8_H2048_I768": (8, 500), "batch_B32_E128_k8_H4096_I1536": (2, 60),
+               "skewed_B64_E256_k8_H7168_I2048": (2, 30)}
+
+
+def config_entry(md, synth, name, wformat, reuse=None, cpu=True):
+    """One workload: µs per layer (graph of K layers over rotating weight copies; each step alone),
+    GB/s on unique routed-weight bytes and its fraction of 8 TB/s; accuracy against the float64
+    oracle on every token (float32 output: max|err|/rms, min cosine; bf16 output: max abs; the
+    FP32-accumulate path with BF16 intermediates: max|err|/rms), computed outside the timed
+    region; the oracle's own time for the layer on the host threads (and on one thread for the
+    three smaller workloads)."""
+    import torch
+
+    R, K = CONFIG_PLAN[name]
+    if reuse is not None:
+        L, t = reuse
+    else:
+        L = synth.make_layer(name, device="cuda", wformat=wformat)
+        t = measure_steps(md, L, R, K)
+    gu_bytes, dn_bytes = kernel_bytes(L)
+    us = t["ms_per_step"] * 1e3
+    gbs = L.unique_weight_bytes / (us * 1e-6) / 1e9
+    sh = L.shape
+    e = {"workload": name, "B": sh.B, "E": sh.E, "k": sh.k, "H": sh.H, "I": sh.I,
+         "unique_experts": L.unique_experts, "unique_weight_bytes": L.unique_weight_bytes,
+         "us_per_layer": round(us, 3), "gbs": round(gbs, 1), "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4),
+         "us_gate_up": round(t["ms_gate_up"] * 1e3, 3), "us_down": round(t["ms_down"] * 1e3, 3),
+         "kernels": {"gate_up": gate_up_kernel_name(L), "down": down_kernel_name(L)},
+         "steps": t.get("steps", K), "weight_copies": R if reuse is None else None}
+    e["accuracy"] = accuracy_entry(md, L, cpu_threads=oracle_threads(), one_thread=cpu and sh.B <= 8)
+    return e
+
+
+def measure_steps(md, L, R, K):
+    """Graph-timed µs per layer and per step (gate/up alone, down alone), K launches each."""
+    import numpy as np
+    import torch
+
+    sh = L.shape
+    x, ids, w = md.layer_device_inputs(L)
+    copies = weight_copies(L, R)
+    out = torch.empty((sh.B, sh.H), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((sh.B, sh.k, sh.I), dtype=torch.float32, device="cuda")
+    ws = torch.empty(md.moed_workspace_bytes(sh.B, sh.k, sh.H, sh.I), dtype=torch.uint8, device="cuda")
+    y = torch.empty(sh.B * sh.k * sh.H, dtype=torch.float32, device="cuda")
+    wf = L.wformat
+    fns = {"per_step": lambda r: md.moe_decode(x, ids, w, *copies[r % R], out=out, workspace=ws, wformat=wf),
+           "gate_up": lambda r: md.moe_decode_gate_up(x, ids, *copies[r % R][:4], a=a, wformat=wf),
+           "down": lambda r: md.moe_decode_down(a, ids, w, *copies[r % R][4:], out=out, wformat=wf, partials=y)}
+    res = {"steps": K}
+    for key, fn in fns.items():
+        for r in range(5):
+            fn(r)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(K):
+                fn(r)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / K)
+        res["ms_" + key] = float(np.median(ts))
+        del g
+    del copies
+    return res
+
+
+def oracle_threads():
+    """Host threads the oracle runs on: every CPU the process may use, capped by OMP_NUM_THREADS
+    when it is set (the GPU machine gives a one-GPU job a share of the host's cores that way)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def accuracy_entry(md, L, cpu_threads, one_thread=False):
+    """The HIP path against the float64 oracle on every token of the layer."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    oracle.build(force=False)
+    x, ids, w = md.layer_device_inputs(L)
+    args = (x, ids, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)
+    f32 = md.moe_decode(*args, out_dtype=torch.float32, wformat=L.wformat)
+    b16 = md.moe_decode(*args, out_dtype=torch.bfloat16, wformat=L.wformat)
+    i16 = md.moe_decode(*args, out_dtype=torch.float32, inter_dtype=torch.bfloat16, wformat=L.wformat)
+    torch.cuda.synchronize()
+    sel = sorted({int(e) for e in L.ids.ravel()})
+    remap = np.full(L.shape.E, -1, np.int64)
+    remap[sel] = np.arange(len(sel))
+    ids_c = np.ascontiguousarray(remap[L.ids].astype(np.int32))
+    idx = torch.tensor(sel, device=L.wg_q.device)
+    host = [t.index_select(0, idx).cpu() for t in (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
+    used = oracle.threads(cpu_threads)
+    t0 = time.perf_counter()
+    ref = oracle.moe_decode(np.ascontiguousarray(L.x), ids_c, np.ascontiguousarray(L.w), *host,
+                            nthreads=cpu_threads, wformat=L.wformat)
+    s_layer = time.perf_counter() - t0
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    g = f32.double().cpu().numpy()
+    d = g - ref
+    cos = np.sum(g * ref, axis=1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(ref, axis=1))
+    gi = i16.double().cpu().numpy()
+    gb = b16.double().cpu().numpy()
+    e = {"tokens": int(L.shape.B), "f32_max_err_over_rms": float(np.abs(d).max() / rms),
+         "f32_rms_err_over_rms": float(np.sqrt(np.mean(d ** 2)) / rms),
+         "f32_min_cosine": float(cos.min()), "f32_max_abs": float(np.abs(d).max()),
+         "bf16_out_max_abs": float(np.abs(gb - ref).max()),
+         "bf16_inter_max_err_over_rms": float(np.abs(gi - ref).max() / rms),
+         "bf16_inter_rms_err_over_rms": float(np.sqrt(np.mean((gi - ref) ** 2)) / rms),
+         "gate_f32_max_err_over_rms": 2e-3, "passes_gate": bool(np.abs(d).max() <= 2e-3 * rms),
+         "oracle_s_per_layer": round(s_layer, 5), "oracle_threads": used}
+    if one_thread:
+        t0 = time.perf_counter()
+        oracle.moe_decode(np.ascontiguousarray(L.x), ids_c, np.ascontiguousarray(L.w), *host, nthreads=1,
+                          wformat=L.wformat)
+        e["oracle_s_per_layer_1thread"] = round(time.perf_counter() - t0, 5)
+    return e
 
 
 COPY_BYTES = 256 << 20      # known-size reference for counter calibration
@@ -434,7 +705,8 @@ def counters_run(md, x, ids, w, copies, out, a, workload, wformat="mxfp8"):
         torch.cuda.synchronize()
     print(json.dumps({"counters_plan": {"workload": workload, "copy_bytes": COPY_BYTES,
                                         "launches_each": COUNTER_LAUNCHES,
-                                        "source_digest": source_digest()}}), flush=True)
+                                        "source_digest_layer": source_digest(LAYER_SOURCES),
+                                        "source_digest_grouped": source_digest(GROUPED_SOURCES)}}), flush=True)
 
 
 def measured_read_peak(md, nbytes=2 << 30, launches=20):
@@ -500,7 +772,8 @@ def same_size_reads(md, gu_bytes, dn_bytes, K=2000, min_total=1 << 30):
 
 
 def cpu_baseline(L, uniq, seconds):
-    """The float64 oracle, as it stands, on full layers of the same workload (host cores)."""
+    """The float64 oracle, as it stands, on full layers of the same workload: on the host threads
+    the process may use (oracle_threads), and on one thread."""
     import numpy as np
     import torch
 
@@ -517,21 +790,29 @@ def cpu_baseline(L, uniq, seconds):
     w_t = np.ascontiguousarray(L.w[toks])
     idx = torch.tensor(sel, device=L.wg_q.device)
     host = [t.index_select(0, idx).cpu() for t in (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)]
-    nthreads = min(os.cpu_count() or 1, 16)
+
+    def run(nthreads, budget):
+        oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)     # warm-up
+        n, t = 0, 0.0
+        while t < budget or n < 3:
+            t0 = time.perf_counter()
+            oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)
+            t += time.perf_counter() - t0
+            n += 1
+        return n, t / n / len(toks) * B          # the oracle's cost is linear in tokens
+
+    nthreads = oracle_threads()
     used = oracle.threads(nthreads)
-    oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)     # warm-up
-    n, t = 0, 0.0
-    while t < seconds or n < 3:
-        t0 = time.perf_counter()
-        oracle.moe_decode(x_t, ids_c, w_t, *host, nthreads=nthreads, wformat=L.wformat)
-        t += time.perf_counter() - t0
-        n += 1
-    per_tok = t / n / len(toks)
-    per = per_tok * B                       # the oracle's cost is linear in tokens
+    n, per = run(nthreads, seconds)
+    n1, per1 = run(1, min(seconds, 5.0))
     what = "full layers" if len(toks) == B else f"runs of {len(toks)} of the {B} tokens (cost per layer scaled by B/{len(toks)})"
     return {"value": round(uniq / per / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"{n} {what} of the same workload (touched experts copied to host)",
-            "s_per_layer": round(per, 6)}
+            "s_per_layer": round(per, 6),
+            "value_1thread": round(uniq / per1 / 1e9, 4), "s_per_layer_1thread": round(per1, 6),
+            "runs_1thread": n1, "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "threads_note": "threads = the CPUs this process may use, capped by OMP_NUM_THREADS "
+                            "(the GPU box gives a one-GPU job 16)"}
 
 
 if __name__ == "__main__":

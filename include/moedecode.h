@@ -276,6 +276,17 @@ int moed_selftest_decode(const uint8_t *codes, const uint8_t *scales, float *out
  */
 int moed_bench_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, void *stream);
 int moed_bench_copy(const void *src, void *dst, size_t bytes, void *stream);
+/*
+ * moed_bench_read_cfg: the same read with a chosen launch shape, to find the
+ *   fastest a single launch can stream a given byte count: workgroups of
+ *   waves_per_group (1..16) wavefronts, each wavefront reading chunks of
+ *   unroll (1, 2, 4, 8 or 16) 16-byte units per lane with all of a chunk's
+ *   loads in flight together; groups = 0 gives a grid that covers the bytes
+ *   in one pass, groups > 0 that many workgroups looping over the chunks.
+ *   Argument errors as moed_bench_read (MOED_ERR_SHAPE for a bad shape).
+ */
+int moed_bench_read_cfg(const void *src, size_t bytes, void *sink, size_t sink_bytes, int unroll,
+                        int waves_per_group, int groups, void *stream);
 
 /* Human-readable name of a moed_status value. Never NULL. */
 const char *moed_status_string(int status);

@@ -4,9 +4,12 @@ reports as roofline.traffic.
 
 The raw counters are scaled by what the same counters read for a copy kernel
 of known size (COPY_BYTES read + COPY_BYTES written), launched in the same run.
+With --extra DIR, a third pass (any counters, e.g. TCC_HIT_sum TCC_MISS_sum
+VALUBusy MfmaUtil) is reported per step as the mean per call, with the L2 hit
+rate TCC_HIT / (TCC_HIT + TCC_MISS) when both are there.
 
     python -m output_centric_expert_amd.counters --fetch DIR --write DIR \\
-        --workload NAME --digest HEX --out profiles/counters_gate_up_NAME.json
+        --workload NAME --digest HEX --out profiles/counters_layer_NAME.json
 """
 from __future__ import annotations
 
@@ -31,6 +34,16 @@ def read_counter(d: str, name: str):
                     continue
                 per[row["Kernel_Name"]][row.get("Dispatch_Id") or row.get("Correlation_Id")] += float(row["Counter_Value"])
     return {k: list(v.values()) for k, v in per.items()}
+
+
+def counter_names(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    names = set()
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                names.add(row.get("Counter_Name"))
+    return sorted(n for n in names if n)
 
 
 def pick(per: dict, needle: str):
@@ -73,6 +86,8 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--gate-up-bytes", type=int, required=True, help="algorithmic bytes per gate/up launch")
     ap.add_argument("--down-bytes", type=int, required=True, help="algorithmic bytes per down launch")
+    ap.add_argument("--command", default=None, help="the commands the counter runs came from")
+    ap.add_argument("--extra", default=None, help="directory of a third --pmc pass (any counters)")
     args = ap.parse_args()
 
     fetch = read_counter(args.fetch, "FETCH_SIZE")
@@ -81,7 +96,7 @@ def main():
     cw, _ = pick(write, "moe_bench_copy_kernel")
     f_fetch = args.copy_bytes / (cf * 1024.0)
     f_write = args.copy_bytes / (cw * 1024.0)
-    res = {"workload": args.workload, "source_digest": args.digest,
+    res = {"workload": args.workload, "source_digest": args.digest, "command": args.command,
            "copy_kernel": {"bytes_read": args.copy_bytes, "bytes_written": args.copy_bytes,
                            "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
                            "fetch_scale": f_fetch, "write_scale": f_write}}
@@ -93,6 +108,20 @@ def main():
                     "FETCH_SIZE_KiB": fv, "WRITE_SIZE_KiB": wv,
                     "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
                     "traffic_over_algorithmic": hbm / alg}
+    if args.extra:
+        for name in counter_names(args.extra):
+            per = read_counter(args.extra, name)
+            for key in ("gate_up", "down"):
+                try:
+                    v, parts = step_counter(per, key)
+                except KeyError:
+                    continue
+                res[key].setdefault("extra", {})[name] = v
+                res[key].setdefault("extra_per_kernel", {})[name] = {k: m for k, (m, _) in parts.items()}
+        for key in ("gate_up", "down"):
+            ex = res[key].get("extra", {})
+            if "TCC_HIT_sum" in ex and "TCC_MISS_sum" in ex and ex["TCC_HIT_sum"] + ex["TCC_MISS_sum"] > 0:
+                ex["L2_hit_rate"] = ex["TCC_HIT_sum"] / (ex["TCC_HIT_sum"] + ex["TCC_MISS_sum"])
     res["hbm_bytes_per_launch"] = res["gate_up"]["hbm_bytes_per_launch"]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as fh:

@@ -91,6 +91,8 @@ hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_b
                                size_t lds, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_bench_read_cfg(const void* src, size_t bytes, void* sink, int unroll, int waves_per_group,
+                                 int groups, hipStream_t s);
 // Expert-major down (y: B*k*H float32 per-slot partials, then out).
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
                                int row_tiles, bool wide, int grid_cap, hipStream_t s);

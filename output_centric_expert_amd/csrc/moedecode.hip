@@ -431,6 +431,25 @@ int moed_bench_read(const void* src, size_t bytes, void* sink, size_t sink_bytes
     return hip_status(moed::launch_bench_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int moed_bench_read_cfg(const void* src, size_t bytes, void* sink, size_t sink_bytes, int unroll,
+                        int waves_per_group, int groups, void* stream)
+{
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+        return MOED_ERR_SHAPE;
+    if (waves_per_group < 1 || waves_per_group > 16 || groups < 0)
+        return MOED_ERR_SHAPE;
+    if (bytes == 0)
+        return MOED_OK;
+    if (!src || !sink)
+        return MOED_ERR_NULL;
+    if (bytes % 16 != 0 || sink_bytes < 4096)
+        return MOED_ERR_SHAPE;
+    if (!aligned16(src))
+        return MOED_ERR_ALIGN;
+    return hip_status(moed::launch_bench_read_cfg(src, bytes, sink, unroll, waves_per_group, groups,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int moed_bench_copy(const void* src, void* dst, size_t bytes, void* stream)
 {
     if (bytes == 0)

@@ -25,7 +25,7 @@ MOED_BF16, MOED_F32 = 0, 1
 EXPORTS = ("moed_workspace_bytes", "moe_decode", "moe_decode_gate_up", "moe_decode_down", "moe_route",
            "moed_selftest_decode", "moed_bench_read", "moed_bench_copy", "moed_status_string",
            "moed_last_hip_error", "moed_tuning_init", "moe_decode_tuned", "moe_decode_gate_up_tuned",
-           "moe_decode_down_tuned", "moe_decode_noalloc")
+           "moe_decode_down_tuned", "moe_decode_noalloc", "moed_bench_read_cfg")
 
 
 class MoedTuning(ctypes.Structure):
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
         lib.moed_selftest_decode.restype = I
         lib.moed_bench_read.argtypes = [P, Z, P, Z, P]
         lib.moed_bench_read.restype = I
+        lib.moed_bench_read_cfg.argtypes = [P, Z, P, Z, I, I, I, P]
+        lib.moed_bench_read_cfg.restype = I
         lib.moed_bench_copy.argtypes = [P, P, Z, P]
         lib.moed_bench_copy.restype = I
         lib.moed_status_string.argtypes = [I]
@@ -301,6 +303,13 @@ def moed_bench_read(src: torch.Tensor, sink: torch.Tensor, nbytes: int | None = 
     n = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(load().moed_bench_read(_ptr(src, "src"), n, _ptr(sink, "sink"), sink.numel() * sink.element_size(),
                                   _stream(stream)), "moed_bench_read")
+
+
+def moed_bench_read_cfg(src: torch.Tensor, sink: torch.Tensor, nbytes: int, unroll: int, waves_per_group: int,
+                        groups: int = 0, stream=None):
+    """The read probe with a chosen launch shape (see the header)."""
+    _check(load().moed_bench_read_cfg(_ptr(src, "src"), nbytes, _ptr(sink, "sink"), sink.numel() * sink.element_size(),
+                                      unroll, waves_per_group, groups, _stream(stream)), "moed_bench_read_cfg")
 
 
 def moed_bench_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int | None = None, stream=None):

@@ -15,15 +15,21 @@ of the expert-major form), the span from the start of the gate/up to the end
 of the down step, reported as median, p10 and p90 per preceding kernel (the
 layer graph: after the down step; the routed layer: after the router).
 
-    python -m output_centric_expert_amd.trace_contexts <out>/prof_ktrace/bench_kernel_trace.csv
+With --workload, --digest and --out it writes the summary as the JSON the
+benchmark reads (profiles/kernel_trace_<workload>.json: its roofline entries
+take the mean of the "gate_up after gate_up" and "down after down" contexts,
+the one-step graphs they time), with the rocprofv3 --stats rows of the run.
+
+    python -m output_centric_expert_amd.trace_contexts <out>/prof_ktrace/bench_kernel_trace.csv \
+        [--stats <out>/prof_ktrace/bench_kernel_stats.csv --workload NAME --digest HEX --command CMD --out FILE]
 """
 from __future__ import annotations
 
+import argparse
 import collections
 import csv
 import json
 import statistics
-import sys
 
 KINDS = (("moe_gate_up_grouped_wide_kernel", "gate_up"), ("moe_gate_up_grouped_kernel", "gate_up"),
          ("moe_gate_up_exact_kernel", "gate_up"), ("moe_gate_up_kernel", "gate_up"),
@@ -85,6 +91,38 @@ def contexts(path: str) -> dict:
                   "median_ns": round(statistics.median(v), 1)} for ctx, v in sorted(per.items())}
 
 
+def stats_rows(path: str) -> list:
+    """The rocprofv3 --stats rows (kernel name, calls, average / min / max ns) of the layer kernels."""
+    out = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if kind(r["Name"]) is None:
+                continue
+            out.append({"kernel": r["Name"], "calls": int(r["Calls"]), "average_ns": float(r["AverageNs"]),
+                        "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])})
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace")
+    ap.add_argument("--stats")
+    ap.add_argument("--workload")
+    ap.add_argument("--digest")
+    ap.add_argument("--command")
+    ap.add_argument("--out")
+    args = ap.parse_args()
+    rows = read_rows(args.trace)
+    res = {"workload": args.workload, "source_digest": args.digest, "command": args.command,
+           "contexts": contexts(args.trace), "layer_spans": layer_spans(rows)}
+    if args.stats:
+        res["stats"] = stats_rows(args.stats)
+    text = json.dumps(res, indent=1)
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text + "\n")
+    print(text)
+
+
 if __name__ == "__main__":
-    print(json.dumps({"kernels": contexts(sys.argv[1]), "layer_spans": layer_spans(read_rows(sys.argv[1]))},
-                     indent=1))
+    main()

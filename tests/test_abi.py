@@ -245,6 +245,16 @@ def test_bench_kernels_reject_before_launch(lib):
     assert lib.moed_bench_read(A, 64, A, 1024, None) == md.MOED_ERR_SHAPE   # sink too small
     assert lib.moed_bench_read(MIS, 64, A, 4096, None) == md.MOED_ERR_ALIGN
     assert lib.moed_bench_read(None, 0, None, 0, None) == md.MOED_OK
+    rc = lib.moed_bench_read_cfg
+    assert rc(None, 64, A, 4096, 1, 4, 0, None) == md.MOED_ERR_NULL
+    assert rc(A, 64, A, 4096, 3, 4, 0, None) == md.MOED_ERR_SHAPE      # unroll not 1/2/4/8/16
+    assert rc(A, 64, A, 4096, 2, 17, 0, None) == md.MOED_ERR_SHAPE     # more than 16 waves per group
+    assert rc(A, 64, A, 4096, 2, 0, 0, None) == md.MOED_ERR_SHAPE
+    assert rc(A, 64, A, 4096, 2, 4, -1, None) == md.MOED_ERR_SHAPE
+    assert rc(A, 60, A, 4096, 2, 4, 0, None) == md.MOED_ERR_SHAPE
+    assert rc(A, 64, A, 1024, 2, 4, 0, None) == md.MOED_ERR_SHAPE
+    assert rc(MIS, 64, A, 4096, 2, 4, 0, None) == md.MOED_ERR_ALIGN
+    assert rc(None, 0, None, 0, 16, 16, 1024, None) == md.MOED_OK
     assert lib.moed_bench_copy(A, None, 64, None) == md.MOED_ERR_NULL
     assert lib.moed_bench_copy(A, A, 65, None) == md.MOED_ERR_SHAPE
     assert lib.moed_bench_copy(A, MIS, 64, None) == md.MOED_ERR_ALIGN

@@ -335,6 +335,10 @@ def test_bench_kernels():
     md.moed_bench_copy(src, dst)
     sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
     md.moed_bench_read(src, sink)
+    # the launch-shape read probe: one-pass and looping grids, a ragged last chunk
+    for unroll, wpg, groups, nbytes in ((1, 4, 0, 1 << 20), (16, 16, 3, 1 << 20), (4, 8, 0, (1 << 20) - 48),
+                                        (2, 1, 1, 4096)):
+        md.moed_bench_read_cfg(src, sink, nbytes, unroll, wpg, groups)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
 
