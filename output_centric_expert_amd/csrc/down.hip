@@ -27,14 +27,14 @@ moe_down_kernel(DownArgs p)
     constexpr int NP = APieces<FP4, A_BF16>::N;   // 16-byte pieces of a per weight chunk
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
     const int wave = __builtin_amdgcn_readfirstlane(blk * wpb + (int)(threadIdx.x / kWave));
     const int n_out = p.B * p.H;
     if (wave >= n_out)
         return;
-    // token-major (w = b*H + h) or hidden-major (w = h*B + b)
-    const int b = p.order == 0 ? wave / p.H : wave % p.B;
-    const int h = p.order == 0 ? wave % p.H : wave / p.B;
+    // hidden-major (w = h*B + b): the tokens of one output h are neighbours
+    const int b = wave % p.B;
+    const int h = wave / p.B;
     const int k = p.k;
     const int I = p.I;
     const int cpr16 = I / 16;                     // 16-value groups per row of a
@@ -128,11 +128,11 @@ moe_down_staged_kernel(DownArgs p)
     constexpr int NA = A_BF16 ? 2 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int nblk_h = (p.H + wpb - 1) / wpb;
-    // workgroup (b, hb): token-major (b*nblk_h + hb) or hidden-major (hb*B + b)
-    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
-    const int b = p.order == 0 ? blk / nblk_h : blk % p.B;
-    const int h = (p.order == 0 ? blk % nblk_h : blk / p.B) * wpb + (int)(threadIdx.x / kWave);
+    // workgroup hb*B + b (hidden-major, each XCD a contiguous range): the
+    // workgroups of one hidden block -- the same weight rows -- are neighbours
+    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    const int b = blk % p.B;
+    const int h = (blk / p.B) * wpb + (int)(threadIdx.x / kWave);
     const bool active = h < p.H;                  // idle waves still help copy a[b]
     const int k = p.k;
     const int cpr16 = p.I / 16;                   // 16-value groups per row of a
@@ -202,10 +202,9 @@ moe_down_rows_kernel(DownArgs p)
     constexpr int NA = A_BF16 ? 2 : 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int nblk_h = (p.H + wpb * R - 1) / (wpb * R);
-    const int blk = p.order == 1 ? xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
-    const int b = p.order == 0 ? blk / nblk_h : blk % p.B;
-    const int h0 = ((p.order == 0 ? blk % nblk_h : blk / p.B) * wpb + (int)(threadIdx.x / kWave)) * R;
+    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    const int b = blk % p.B;
+    const int h0 = ((blk / p.B) * wpb + (int)(threadIdx.x / kWave)) * R;
     const bool active = h0 < p.H;
     const int k = p.k;
     const int cpr16 = p.I / 16;
@@ -369,9 +368,9 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     const int wpb = t.dn_wpb > (staged ? 8 : 4) ? (staged ? 8 : 4) : t.dn_wpb;
     const dim3 block(wpb * kWave);
     const dim3 grid(staged ? (unsigned)((long)p.B * ((p.H + wpb - 1) / wpb)) : (unsigned)((n_out + wpb - 1) / wpb));
-    const bool nt = t.nt == 2 ? (long)p.B * p.k < (long)p.E : t.nt != 0;
-    DownArgs q = p;
-    q.order = t.dn_order;
+    // streaming weight loads unless tokens share rows (B*k >= E)
+    const bool nt = (long)p.B * p.k < (long)p.E;
+    const DownArgs& q = p;
     // lane groups (staged kernel): rows of at most 16 or 32 chunks share the
     // wavefront among 4 or 2 slots at a time (at most k groups)
     int groups = 1;
@@ -389,11 +388,11 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     // wavefront, and so does the one-pass kernel, which also replaces the
     // two-row default where it applies: B=4 down 12.7 -> 10.7 us, B=8 18.6 ->
     // 17.7 us at k=8, I=768; at B*k >= E four rows stay faster)
-    const int rows = t.dn_rows != 0 ? t.dn_rows : ((long)p.B * p.k >= (long)p.E ? 4 : (p.B >= 2 ? 2 : 1));
+    const int rows = (long)p.B * p.k >= (long)p.E ? 4 : (p.B >= 2 ? 2 : 1);
     const int per_group = p.k / groups;
     if (staged && t.dn_onepass != 0 && !a_bf16 && nt && wpb == 8 && p.k == groups * per_group &&
         (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups &&
-        (groups > 1 || rows == 1 || (t.dn_rows == 0 && rows == 2))) {
+        (groups > 1 || rows <= 2)) {
         return launch_down_onepass(q, per_group, groups, out_bf16, grid, block, lds, s);
     }
     if (groups > 1) {

@@ -9,41 +9,32 @@
 
 namespace moed {
 
-template <int U, bool DOT_BF16, bool A_BF16, bool NT, bool FP4, int NPW>
+template <int U, bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(256)
 moe_gate_up_kernel(GateUpArgs p)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wpb = blockDim.x / kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (int)(threadIdx.x / kWave));
-    const int n_out = p.B * p.k * p.I;
-    const int n0 = wave * NPW;                    // first of the wave's NPW neurons
-    if (n0 >= n_out)
+    const int n0 = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (int)(threadIdx.x / kWave));
+    if (n0 >= p.B * p.k * p.I)
         return;                                   // whole wavefront leaves together
-    float g[NPW], u[NPW];
+    float g, u;
     bool bad_id;
-    gate_up_wave<U, DOT_BF16, NT, FP4, NPW>(p, n0, lane, g, u, bad_id);
-#pragma unroll
-    for (int n = 0; n < NPW; ++n) {
-        g[n] = wave_sum(g[n]);
-        u[n] = wave_sum(u[n]);
-    }
+    gate_up_wave<U, FP4>(p, n0, lane, g, u, bad_id);
+    g = wave_sum(g);
+    u = wave_sum(u);
     if (lane == 0) {
-#pragma unroll
-        for (int n = 0; n < NPW; ++n) {
-            const float v = bad_id ? __builtin_nanf("") : swiglu(g[n], u[n]);
-            const size_t a_idx = inter_index<A_BF16>((n0 + n) / p.I, (n0 + n) % p.I, p.I);
-            if constexpr (A_BF16)
-                static_cast<uint16_t*>(p.a)[a_idx] = f32_to_bf16_rne(v);
-            else
-                static_cast<float*>(p.a)[a_idx] = v;
-        }
+        const float v = bad_id ? __builtin_nanf("") : swiglu(g, u);
+        const size_t a_idx = inter_index<A_BF16>(n0 / p.I, n0 % p.I, p.I);
+        if constexpr (A_BF16)
+            static_cast<uint16_t*>(p.a)[a_idx] = f32_to_bf16_rne(v);
+        else
+            static_cast<float*>(p.a)[a_idx] = v;
     }
 }
 
 // Exact-fit form for rows of exactly 64*U chunks (MXFP8: H a multiple of
-// 1024; MXFP4: of 2048), one neuron per wavefront, BF16 dot route, streaming
-// loads: every lane holds U whole chunks, so there is no clamping or lane
+// 1024; MXFP4: of 2048): every lane holds U whole chunks, so there is no clamping or lane
 // factor, and the routed id is requested ahead of the activations so that its
 // round trip overlaps theirs. The per-lane products, the order of the FMAs
 // and the reduction are those of moe_gate_up_kernel (whose lane factor is 1
@@ -108,8 +99,8 @@ moe_gate_up_exact_kernel(GateUpArgs p)
     float g = 0.0f, u = 0.0f;
 #pragma unroll
     for (int m = 0; m < U; ++m) {
-        const float pg = gu_chunk_dot<FP4, true, NX>(wg[m], xv[m]);
-        const float pu = gu_chunk_dot<FP4, true, NX>(wu[m], xv[m]);
+        const float pg = gu_chunk_dot<FP4, NX>(wg[m], xv[m]);
+        const float pu = gu_chunk_dot<FP4, NX>(wu[m], xv[m]);
         g = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]), g);
         u = __builtin_fmaf(pu, ue8m0_to_f32(su[m]), u);
     }
@@ -144,22 +135,12 @@ static hipError_t dispatch_exact(int U, bool nb, const GateUpArgs& p, dim3 grid,
     return hipGetLastError();
 }
 
-template <bool DOT_BF16, bool A_BF16, bool NT, bool FP4>
-static hipError_t dispatch_u(int U, int npw, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
+template <bool A_BF16, bool FP4>
+static hipError_t dispatch_u(int U, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
 {
-    if (npw == 2) {                               // two neurons per wave: U <= 4
-        switch (U) {
-#define MOED_GU2_CASE(N) \
-        case N: hipLaunchKernelGGL((moe_gate_up_kernel<N, DOT_BF16, A_BF16, NT, FP4, 2>), grid, block, 0, s, p); break;
-            MOED_GU2_CASE(1) MOED_GU2_CASE(2) MOED_GU2_CASE(3) MOED_GU2_CASE(4)
-#undef MOED_GU2_CASE
-        default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     switch (U) {
 #define MOED_GU_CASE(N) \
-    case N: hipLaunchKernelGGL((moe_gate_up_kernel<N, DOT_BF16, A_BF16, NT, FP4, 1>), grid, block, 0, s, p); break;
+    case N: hipLaunchKernelGGL((moe_gate_up_kernel<N, A_BF16, FP4>), grid, block, 0, s, p); break;
         MOED_GU_CASE(1) MOED_GU_CASE(2) MOED_GU_CASE(3) MOED_GU_CASE(4)
         MOED_GU_CASE(5) MOED_GU_CASE(6) MOED_GU_CASE(7) MOED_GU_CASE(8)
 #undef MOED_GU_CASE
@@ -175,21 +156,16 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
         return hipSuccess;
     const bool fp4 = p.wfmt == kMXFP4;
     const int nch = fp4 ? p.H / 32 : p.H / 16;    // 16-byte chunks per row
-    // neurons per wavefront: 2 shares each x load between two rows (decode route 1 only)
-    const int npw = (t.gu_npw == 2 && (t.gu_dot != 0 || fp4)) ? 2 : 1;
     int U = (nch + kWave - 1) / kWave;
-    const int umax = npw == 2 ? (t.gu_umax < 4 ? t.gu_umax : 4) : t.gu_umax;
-    if (U > umax)
-        U = umax;
+    if (U > t.gu_umax)
+        U = t.gu_umax;
     if (U < 1)
         U = 1;
     const int wpb = t.gu_wpb;
-    const long n_waves = (n_out + npw - 1) / npw;
     const dim3 block(wpb * kWave);
-    const dim3 grid((unsigned)((n_waves + wpb - 1) / wpb));
-    const bool dot = t.gu_dot != 0, nt = t.nt != 0;
-    // rows of exactly 64*U chunks, U <= umax: the exact-fit kernel
-    if (t.gu_exact != 0 && npw == 1 && nt && (dot || fp4) && nch == kWave * U) {
+    const dim3 grid((unsigned)((n_out + wpb - 1) / wpb));
+    // rows of exactly 64*U chunks, U <= gu_umax: the exact-fit kernel
+    if (t.gu_exact != 0 && nch == kWave * U) {
         // neuron-block order where slots may share experts (B > 1); by default for
         // MXFP8 only (measured 3-4% faster at B = 8-16 there, 2% slower for MXFP4)
         const bool nb = (t.gu_order == 2 || (t.gu_order == 1 && !fp4)) && p.B > 1 && p.I % 16 == 0;
@@ -199,22 +175,9 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
         return a_bf16 ? dispatch_exact<true, false>(U, nb, p, grid, block, s)
                       : dispatch_exact<false, false>(U, nb, p, grid, block, s);
     }
-    if (fp4) {                                    // one decode route (BF16 dot2)
-        if (a_bf16) return nt ? dispatch_u<true, true, true, true>(U, npw, p, grid, block, s)
-                              : dispatch_u<true, true, false, true>(U, npw, p, grid, block, s);
-        return nt ? dispatch_u<true, false, true, true>(U, npw, p, grid, block, s)
-                  : dispatch_u<true, false, false, true>(U, npw, p, grid, block, s);
-    }
-    if (dot) {
-        if (a_bf16) return nt ? dispatch_u<true, true, true, false>(U, npw, p, grid, block, s)
-                              : dispatch_u<true, true, false, false>(U, npw, p, grid, block, s);
-        return nt ? dispatch_u<true, false, true, false>(U, npw, p, grid, block, s)
-                  : dispatch_u<true, false, false, false>(U, npw, p, grid, block, s);
-    }
-    if (a_bf16) return nt ? dispatch_u<false, true, true, false>(U, 1, p, grid, block, s)
-                          : dispatch_u<false, true, false, false>(U, 1, p, grid, block, s);
-    return nt ? dispatch_u<false, false, true, false>(U, 1, p, grid, block, s)
-              : dispatch_u<false, false, false, false>(U, 1, p, grid, block, s);
+    if (fp4)
+        return a_bf16 ? dispatch_u<true, true>(U, p, grid, block, s) : dispatch_u<false, true>(U, p, grid, block, s);
+    return a_bf16 ? dispatch_u<true, false>(U, p, grid, block, s) : dispatch_u<false, false>(U, p, grid, block, s);
 }
 
 }  // namespace moed

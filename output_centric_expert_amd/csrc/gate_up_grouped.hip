@@ -491,8 +491,8 @@ __device__ __forceinline__ void rowwise_neurons(const GateUpArgs& p, int e, int 
 #pragma unroll
                         for (int t = 0; t < NX; ++t)
                             xv[t] = xs16[(size_t)(sl * NX + t) * nch + cc[m]];
-                        const float pg = gu_chunk_dot<FP4, true, NX>(wg[m], xv);
-                        const float pu = gu_chunk_dot<FP4, true, NX>(wu[m], xv);
+                        const float pg = gu_chunk_dot<FP4, NX>(wg[m], xv);
+                        const float pu = gu_chunk_dot<FP4, NX>(wu[m], xv);
                         g[sl] = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g[sl]);
                         u[sl] = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u[sl]);
                     }

@@ -10,7 +10,6 @@ namespace moed {
 // can override them for sweeps.
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
-    int gu_npw = 1;     // gate/up (per-slot kernel): neurons per wavefront (1 or 2; 2 shares x)
     int gu_order = 1;   // exact-fit gate/up at B > 1: neuron-block order with XCD-contiguous workgroups
                         // (slots sharing an expert meet in one L2) for MXFP8 (1) or both formats (2);
                         // 0 = slot-major
@@ -32,24 +31,17 @@ struct Tuning {
     int dn_wide = 1;    // expert-major down: weight rows read in 256-byte runs per row and moved to the
                         // operand layout through LDS (1 = for MXFP8 weights, 2 = for both formats),
                         // or 0 = 128-byte slices per row and group
-    int gu_dot = 1;     // gate/up decode route: 0 = FP8->FP32 + FMA, 1 = FP8->BF16 + dot2
-    int nt = 2;         // weight loads: 0 = cached; 1 = non-temporal (streaming); 2 = streaming,
-                        // except in the down kernel once B*k >= E (tokens then share rows)
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
                         // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once
                         // B*k*H >= 2458*E (about 1.2 slots per expert at H = 2048)
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
-    int dn_rows = 0;    // down (staged): outputs per wavefront, 1, 2 or 4; 0 = by batch (4 once
-                        // B*k >= E, 2 for B >= 2, 1 for B = 1)
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
     int dn_onepass = 1; // down (staged, one output per wavefront): 1 = straight-line kernel when the
                         // token's slots form one group and a row is one chunk per lane
     int gu_grid = 1024; // grouped gate/up: at most this many workgroups walk the items of the routed
                         // experts (0 = one workgroup per item of all E experts, empty ones included)
     int dn_grid = 2048; // expert-major down: the same for its items
-    int dn_order = 1;   // down workgroup order: 0 = token-major; 1 = hidden-major, each XCD
-                        // taking a contiguous range; 2 = hidden-major, plain round robin
 };
 
 // Weight formats (moed_wformat in the C ABI).
@@ -77,7 +69,6 @@ struct DownArgs {
     void* out;              // [B][H] f32 or bf16
     int B, E, k, H, I;
     float inv_cpr;          // 1 / (I/16), for the chunk -> (slot, offset) split
-    int order;              // workgroup order (Tuning::dn_order)
     int wfmt;               // kMXFP8 or kMXFP4 (codes [E][H][I/2])
 };
 

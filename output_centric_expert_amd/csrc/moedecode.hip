@@ -181,7 +181,6 @@ moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, cons
     p.a = a; p.ids = ids; p.w = w; p.wd_q = wd_q; p.wd_s = wd_s; p.out = out;
     p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
     p.inv_cpr = 1.0f / (float)(I / 16);
-    p.order = 0;
     p.wfmt = wfmt;
     return p;
 }
@@ -511,14 +510,9 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_order") && v >= 0 && v <= 2) t.gu_order = (int)v;
-        else if (!strcmp(tok, "gu_dot") && (v == 0 || v == 1)) t.gu_dot = (int)v;
-        else if (!strcmp(tok, "nt") && v >= 0 && v <= 2) t.nt = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
         else if (!strcmp(tok, "gu_group") && v >= 0 && v <= 2) t.gu_group = (int)v;
         else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;
-        else if (!strcmp(tok, "dn_order") && v >= 0 && v <= 2) t.dn_order = (int)v;
-        else if (!strcmp(tok, "gu_npw") && (v == 1 || v == 2)) t.gu_npw = (int)v;
-        else if (!strcmp(tok, "dn_rows") && (v == 0 || v == 1 || v == 2 || v == 4)) t.dn_rows = (int)v;
         else if (!strcmp(tok, "dn_lanegroups") && (v == 0 || v == 1)) t.dn_lanegroups = (int)v;
         else if (!strcmp(tok, "dn_onepass") && (v == 0 || v == 1)) t.dn_onepass = (int)v;
         else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;

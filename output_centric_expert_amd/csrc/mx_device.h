@@ -59,7 +59,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // acc + sum_{t<4} E4M3(codes.byte[t]) * x[t], with x[0..3] packed as two bf16 pairs.
-// Route 1: FP8 -> BF16 (v_cvt_scalef32_pk_bf16_fp8, scale 1) and a BF16 dot2
+// FP8 -> BF16 (v_cvt_scalef32_pk_bf16_fp8, scale 1; exact) and a BF16 dot2
 // with FP32 accumulation (v_dot2c_f32_bf16).
 __device__ __forceinline__ float dot4_bf16(uint32_t codes, uint32_t x01, uint32_t x23, float acc)
 {
@@ -67,18 +67,6 @@ __device__ __forceinline__ float dot4_bf16(uint32_t codes, uint32_t x01, uint32_
     const bf16x2 w23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
     acc = __builtin_amdgcn_fdot2_f32_bf16(w01, as_bf16x2(x01), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(w23, as_bf16x2(x23), acc, false);
-    return acc;
-}
-
-// Route 0: FP8 -> FP32 (v_cvt_pk_f32_fp8) and FP32 FMAs against the widened bf16.
-__device__ __forceinline__ float dot4_f32(uint32_t codes, uint32_t x01, uint32_t x23, float acc)
-{
-    const f32x2 w01 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
-    const f32x2 w23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
-    acc = __builtin_fmaf(w01.x, bf16_lo(x01), acc);
-    acc = __builtin_fmaf(w01.y, bf16_hi(x01), acc);
-    acc = __builtin_fmaf(w23.x, bf16_lo(x23), acc);
-    acc = __builtin_fmaf(w23.y, bf16_hi(x23), acc);
     return acc;
 }
 
