@@ -1,7 +1,7 @@
 // Per-wave body of the general per-slot gate/up kernel (one wavefront per
 // intermediate neuron of one (token, routed slot) pair; warp-decode post, "How
-// the two kernels work", first two paragraphs); the exact-fit kernel and the
-// expert-grouped kernel's row path use the same chunk dot.
+// the two kernels work", first two paragraphs); the exact-fit kernel uses the
+// same chunk dot.
 //
 // Wave w owns (b, j, i) with w = (b*k + j)*I + i. It first issues the loads
 // of its 16 bf16 activations per chunk, x[b][16c..16c+15] (used by both

@@ -19,11 +19,10 @@
 // SiLU(g) * u into the chunk-interleaved intermediate. There is no gather of
 // activations and no per-expert buffer: the slot list is an index list in LDS.
 //
-// Experts with only a few slots (at most row_slots) take a row path instead:
-// whole rows per wavefront with the per-slot kernel's contiguous loads, each
-// row applied to all of the expert's slots (their x staged in LDS). A 16-row
-// MFMA tile keeps only 128 bytes of each row in flight per group; a whole-row
-// wavefront keeps the full 2*H bytes.
+// Every routed expert takes the MFMA path, one slot or many: the weight rows
+// are read once per item either way, and with streaming loads the tiles keep
+// up with a whole-row wavefront even for single-slot experts (a row path for
+// experts with up to two slots measured 10-25% slower at batch 8-32).
 //
 // MFMA lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies A row l%16 and
 // B column l%16, both for k = 8*(l/16) .. +7, and receives D rows
@@ -67,14 +66,14 @@ __device__ __forceinline__ GroupW load_group_w(const GroupedRow& r, int g)
     GroupW w;
     const int kbase = g * 128 + 32 * r.kb;       // this lane's MX block (value index)
     const int bbase = FP4 ? kbase / 2 : kbase;   // its first code byte
-    w.g0 = *reinterpret_cast<const u32x4*>(r.gq + bbase);
-    w.u0 = *reinterpret_cast<const u32x4*>(r.uq + bbase);
+    w.g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(r.gq + bbase));
+    w.u0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(r.uq + bbase));
     if constexpr (FP4) {
         w.g1 = w.g0;
         w.u1 = w.u0;
     } else {
-        w.g1 = *reinterpret_cast<const u32x4*>(r.gq + bbase + 16);
-        w.u1 = *reinterpret_cast<const u32x4*>(r.uq + bbase + 16);
+        w.g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(r.gq + bbase + 16));
+        w.u1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(r.uq + bbase + 16));
     }
     w.gsc = ue8m0_to_f32(r.gs[4 * g + r.kb]);
     w.usc = ue8m0_to_f32(r.us[4 * g + r.kb]);
@@ -254,26 +253,23 @@ template <bool FP4>
 struct StepW {
     static constexpr int kGroups = FP4 ? 4 : 2;  // 128-code groups per 256-byte step
     u32x4 g[4], u[4];                            // pieces of rows L/16 + 4i
-    uint32_t gs[kGroups], us[kGroups];           // scale bytes of this lane's row and block, per group
 };
 
+// gq0 / uq0: the wavefront's first gate / up row (wave-uniform); lo: this
+// lane's byte offset (lane/16)*rstride + 16*(lane%16); rs4 = 4*rstride. Uniform
+// bases plus 32-bit lane offsets shared by both matrices keep the addresses of
+// the eight loads in four registers.
 template <bool FP4>
-__device__ __forceinline__ StepW<FP4> load_step(const uint8_t* gq0, const uint8_t* uq0, size_t rstride,
-                                                const GroupedRow& r, int step, int lane)
+__device__ __forceinline__ StepW<FP4> load_step(const uint8_t* gq0, const uint8_t* uq0, uint32_t lo, uint32_t rs4,
+                                                int step)
 {
     StepW<FP4> w;
-    const size_t off = (size_t)step * 256 + 16 * (size_t)(lane % 16);
+    const uint32_t base = lo + 256u * (uint32_t)step;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const size_t o = (size_t)(lane / 16 + 4 * i) * rstride + off;
-        w.g[i] = *reinterpret_cast<const u32x4*>(gq0 + o);
-        w.u[i] = *reinterpret_cast<const u32x4*>(uq0 + o);
-    }
-#pragma unroll
-    for (int h = 0; h < StepW<FP4>::kGroups; ++h) {
-        const int blk = 4 * (step * StepW<FP4>::kGroups + h) + r.kb;
-        w.gs[h] = r.gs[blk];
-        w.us[h] = r.us[blk];
+        const uint32_t o = base + (uint32_t)i * rs4;
+        w.g[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gq0 + o));
+        w.u[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(uq0 + o));
     }
     return w;
 }
@@ -314,18 +310,20 @@ __device__ __forceinline__ GroupW staged_group(const u32x4* tb, const GroupedRow
     return w;
 }
 
-// grouped_pass with the wide weight loads. One step of weights is in flight
-// ahead (issued during the step's second-to-last group), and the slots' x two
+// grouped_pass with the wide weight loads (H a multiple of 512, so a row is a
+// whole number of 256-byte steps and, for MXFP8, of two-step scale blocks).
+// One step of weights is in flight ahead (issued during the step's
+// second-to-last group), with it the next scale block, and the slots' x two
 // groups ahead in two register sets (group g's set is refilled with x of group
 // g+2 once it is in LDS), so neither the L2 latency of x nor that of the rows
 // is paid once per group. Each group's wait for its x never waits for weight
-// loads issued after it. Groups after the last whole step take the 128-byte
-// slices; leftover blocks as in grouped_pass. tb = this wavefront's LDS
-// region (512 units).
+// loads issued after it. tb = this wavefront's LDS region (512 units);
+// gs0 / us0 / sstride: the scale row of the lane's block-load row slot (gate
+// for lanes 0-31, up for 32-63; row (L % 32) / 2) and the scale row stride.
 template <int NTL, bool A_BF16, bool FP4>
 __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const GroupedRow& r, const uint8_t* gq0,
-                                                  const uint8_t* uq0, size_t rstride, const int* slots, int count,
-                                                  int t0, u32x4* xs, u32x4* tb, bool store)
+                                                  const uint8_t* uq0, size_t rstride, const uint8_t* sq0,
+                                                  const int* slots, int count, int t0, u32x4* xs, u32x4* tb, bool store)
 {
     constexpr int GPS = StepW<FP4>::kGroups;
     const int H = p.H;
@@ -333,16 +331,14 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
     const int lane = tid & (kWave - 1);
     const int lcol = tid / 16;
     const int lc = tid % 16;
-    const uint16_t* xl[NTL];
+    uint32_t xo[NTL];                             // element offset of this thread's x row, per tile
     int bj[NTL];
-    const uint16_t* xr[NTL];
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
         const int sl = (t0 + tt) * 16 + lcol;
-        xl[tt] = p.x + (size_t)(slots[sl < count ? sl : count - 1] / p.k) * (size_t)H;
+        xo[tt] = (uint32_t)(slots[sl < count ? sl : count - 1] / p.k) * (uint32_t)H + 8u * (uint32_t)lc;
         const int si = (t0 + tt) * 16 + r.col;
         bj[tt] = slots[si < count ? si : count - 1];
-        xr[tt] = p.x + (size_t)(bj[tt] / p.k) * (size_t)H;
     }
     f32x4 dg[NTL], du[NTL];
 #pragma unroll
@@ -351,14 +347,15 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         du[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     const int ngroups = r.nsteps / 4;
-    const int nst = ngroups / GPS;                // whole 256-byte steps
+    const int nst = ngroups / GPS;                // 256-byte steps (even for MXFP8)
+    const uint32_t lo = (uint32_t)(lane / 16) * (uint32_t)rstride + 16u * (uint32_t)(lane % 16);
+    const uint32_t rs4 = 4u * (uint32_t)rstride;
     constexpr int kBuf = NTL * kXUnitsPerTile;
     u32x4 xq[2][NTL];                             // x of groups g+1 and g+2, by group parity
-    StepW<FP4> sw{};
     auto load_x = [&](u32x4 (&dst)[NTL], int g) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt)
-            dst[tt] = *reinterpret_cast<const u32x4*>(xl[tt] + g * 128 + 8 * lc);
+            dst[tt] = *reinterpret_cast<const u32x4*>(p.x + (xo[tt] + 128u * (uint32_t)g));
     };
     auto put_x = [&](const u32x4 (&src)[NTL], int g) {
         u32x4* xn = xs + (g & 1) * kBuf;
@@ -366,17 +363,12 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         for (int tt = 0; tt < NTL; ++tt)
             xn[(tt * 16 + lcol) * 16 + (lc ^ lcol)] = src[tt];
     };
-    if (ngroups > 0) {
-        load_x(xq[0], 0);
-        if (ngroups > 1)
-            load_x(xq[1], 1);
-        if (nst > 0)
-            sw = load_step<FP4>(gq0, uq0, rstride, r, 0, lane);
-        put_x(xq[0], 0);
-    }
+    load_x(xq[0], 0);
+    load_x(xq[1], 1);
+    StepW<FP4> sw = load_step<FP4>(gq0, uq0, lo, rs4, 0);
+    u32x2 sb = load_scale_block(sq0, 0, lane);
+    put_x(xq[0], 0);
     __syncthreads();
-    // group g (parity P): x of g+2 into set P, the MFMAs on buffer g&1, x of
-    // g+1 (set 1-P) into the other buffer
     // No branch around a load in the step loop (the last groups re-read the last
     // group's x, the last step re-reads the last step): a load behind a branch
     // makes the compiler wait for every load at the join, the ones issued a
@@ -389,139 +381,76 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         constexpr int P = decltype(par)::value;
         load_x(xq[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
     };
-    auto group = [&](auto par, int g, const GroupW& wc) {
+    // group g = step group h, scale-block group GI: the scales of the lane's
+    // gate and up rows (col and 16 + col of the block load) taken from the
+    // block just before the decode, the MFMAs on x buffer g&1, then x of g+1
+    // (set 1-P) into the other buffer
+    auto group = [&](auto par, auto gi, int g, int h, const u32x2& blk) {
         constexpr int P = decltype(par)::value;
-        group_mfma<NTL, FP4>(wc, xs + (g & 1) * kBuf, r, dg, du);
+        constexpr int GI = decltype(gi)::value;
+        const float gsc = block_scale<GI>(blk, r.col, r.kb);
+        const float usc = block_scale<GI>(blk, 16 + r.col, r.kb);
+        group_mfma<NTL, FP4>(staged_group<FP4>(tb, r, h, gsc, usc), xs + (g & 1) * kBuf, r, dg, du);
         put_x(xq[1 - P], g + 1 < ngroups ? g + 1 : ngroups - 1);
         __syncthreads();
     };
     constexpr auto P0 = std::integral_constant<int, 0>{};
     constexpr auto P1 = std::integral_constant<int, 1>{};
-    for (int s = 0; s < nst; ++s) {
-        stage_step<FP4>(sw, tb, lane);
-        float gsc[GPS], usc[GPS];
-#pragma unroll
-        for (int h = 0; h < GPS; ++h) {
-            gsc[h] = ue8m0_to_f32(sw.gs[h]);
-            usc[h] = ue8m0_to_f32(sw.us[h]);
-        }
-        const int g0 = s * GPS;                   // even: the parity of group g0 + h is that of h
-        const int snext = s + 1 < nst ? s + 1 : s;
-        xload(P0, g0);
-        if constexpr (GPS == 2)                   // MXFP8: next step during the first group
-            sw = load_step<FP4>(gq0, uq0, rstride, r, snext, lane);
-        group(P0, g0, staged_group<FP4>(tb, r, 0, gsc[0], usc[0]));
-        xload(P1, g0 + 1);
-        group(P1, g0 + 1, staged_group<FP4>(tb, r, 1, gsc[1], usc[1]));
-        if constexpr (GPS == 4) {                 // MXFP4: next step during the third group
+    constexpr auto G0 = std::integral_constant<int, 0>{};
+    constexpr auto G1 = std::integral_constant<int, 1>{};
+    constexpr auto G2 = std::integral_constant<int, 2>{};
+    constexpr auto G3 = std::integral_constant<int, 3>{};
+    if constexpr (GPS == 2) {
+        // MXFP8: a scale block spans two steps, so steps go in pairs; the next
+        // step's rows (and, in the second step, the next block) are requested
+        // during each step's first group
+        for (int s = 0; s < nst; s += 2) {
+            const int g0 = 2 * s;
+            const u32x2 blk = sb;                 // this pair's block (sb is refilled below)
+            stage_step<FP4>(sw, tb, lane);
+            xload(P0, g0);
+            sw = load_step<FP4>(gq0, uq0, lo, rs4, s + 1);
+            group(P0, G0, g0, 0, blk);
+            xload(P1, g0 + 1);
+            group(P1, G1, g0 + 1, 1, blk);
+            stage_step<FP4>(sw, tb, lane);
+            const int sn = s + 2 < nst ? s + 2 : s + 1;
             xload(P0, g0 + 2);
-            sw = load_step<FP4>(gq0, uq0, rstride, r, snext, lane);
-            group(P0, g0 + 2, staged_group<FP4>(tb, r, 2, gsc[2], usc[2]));
+            sw = load_step<FP4>(gq0, uq0, lo, rs4, sn);
+            sb = load_scale_block(sq0, sn / 2, lane);
+            group(P0, G2, g0 + 2, 0, blk);
             xload(P1, g0 + 3);
-            group(P1, g0 + 3, staged_group<FP4>(tb, r, 3, gsc[3], usc[3]));
+            group(P1, G3, g0 + 3, 1, blk);
+        }
+    } else {
+        // MXFP4: one scale block per step; the next step and block are
+        // requested during the step's third group
+        for (int s = 0; s < nst; ++s) {
+            const int g0 = 4 * s;
+            const u32x2 blk = sb;
+            stage_step<FP4>(sw, tb, lane);
+            const int sn = s + 1 < nst ? s + 1 : s;
+            xload(P0, g0);
+            group(P0, G0, g0, 0, blk);
+            xload(P1, g0 + 1);
+            group(P1, G1, g0 + 1, 1, blk);
+            xload(P0, g0 + 2);
+            sw = load_step<FP4>(gq0, uq0, lo, rs4, sn);
+            sb = load_scale_block(sq0, sn, lane);
+            group(P0, G2, g0 + 2, 2, blk);
+            xload(P1, g0 + 3);
+            group(P1, G3, g0 + 3, 3, blk);
         }
     }
-    for (int g = nst * GPS; g < ngroups; g += 2) {   // groups after the last whole step (g even)
-        xload(P0, g);
-        group(P0, g, load_group_w<FP4>(r, g));
-        if (g + 1 < ngroups) {
-            xload(P1, g + 1);
-            group(P1, g + 1, load_group_w<FP4>(r, g + 1));
-        }
-    }
-    leftover_blocks<NTL, FP4>(r, xr, dg, du);
     if (store)
         store_tiles<NTL, A_BF16>(p, r, bj, count, t0, dg, du);
-}
-
-// Row path, for experts with few slots (at most kRowSlots, and their x rows fit
-// in the LDS of the x tiles): the slots' x rows are staged once in LDS and
-// each wavefront streams whole gate and up rows, one neuron at a time, with
-// the per-slot kernel's load pattern (16-byte chunk c of a row on lane c % 64,
-// U chunks per lane per pass) and its arithmetic for every slot, so that each
-// row is read once for all the expert's slots and each output is the float
-// the per-slot kernel computes. x of slot s is kept piece-major in LDS
-// (16-byte unit (s*NX + t)*nch + c holds piece t of chunk c) so the lanes'
-// reads are contiguous.
-constexpr int kRowSlots = 4;
-
-template <int U, bool A_BF16, bool FP4>
-__device__ __forceinline__ void rowwise_neurons(const GateUpArgs& p, int e, int n_first, int n_count,
-                                                const int* slots, int count, const u32x4* xs16, int lane)
-{
-    constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
-    const int H = p.H;
-    const int I = p.I;
-    const int nch = FP4 ? H / 32 : H / 16;
-    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
-    for (int n = 0; n < n_count; ++n) {
-        const int i = n_first + n;
-        const size_t row = (size_t)e * (size_t)I + (size_t)i;
-        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
-        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
-        const uint8_t* gsc = p.wg_s + row * (size_t)(H / 32);
-        const uint8_t* usc = p.wu_s + row * (size_t)(H / 32);
-        float g[kRowSlots], u[kRowSlots];
-#pragma unroll
-        for (int sl = 0; sl < kRowSlots; ++sl) {
-            g[sl] = 0.0f;
-            u[sl] = 0.0f;
-        }
-        for (int base = 0; base < nch; base += kWave * U) {
-            u32x4 wg[U], wu[U];
-            uint32_t sg[U], su[U];
-            float live[U];
-            int cc[U];
-#pragma unroll
-            for (int m = 0; m < U; ++m) {
-                const int c = base + lane + kWave * m;
-                cc[m] = c < nch ? c : nch - 1;
-                wg[m] = gq[cc[m]];
-                wu[m] = uq[cc[m]];
-                sg[m] = gsc[FP4 ? cc[m] : cc[m] >> 1];
-                su[m] = usc[FP4 ? cc[m] : cc[m] >> 1];
-                live[m] = c < nch ? 1.0f : 0.0f;
-            }
-#pragma unroll
-            for (int sl = 0; sl < kRowSlots; ++sl) {
-                if (sl < count) {                 // wave-uniform
-#pragma unroll
-                    for (int m = 0; m < U; ++m) {
-                        u32x4 xv[NX];
-#pragma unroll
-                        for (int t = 0; t < NX; ++t)
-                            xv[t] = xs16[(size_t)(sl * NX + t) * nch + cc[m]];
-                        const float pg = gu_chunk_dot<FP4, NX>(wg[m], xv);
-                        const float pu = gu_chunk_dot<FP4, NX>(wu[m], xv);
-                        g[sl] = __builtin_fmaf(pg, ue8m0_to_f32(sg[m]) * live[m], g[sl]);
-                        u[sl] = __builtin_fmaf(pu, ue8m0_to_f32(su[m]) * live[m], u[sl]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int sl = 0; sl < kRowSlots; ++sl) {
-            if (sl < count) {
-                const float gt = wave_sum(g[sl]);
-                const float ut = wave_sum(u[sl]);
-                if (lane == 0) {
-                    const float v = swiglu(gt, ut);
-                    const size_t idx = inter_index<A_BF16>(slots[sl], i, I);
-                    if constexpr (A_BF16)
-                        static_cast<uint16_t*>(p.a)[idx] = f32_to_bf16_rne(v);
-                    else
-                        static_cast<float*>(p.a)[idx] = v;
-                }
-            }
-        }
-    }
 }
 
 // One item: expert e, neurons n_block .. n_block+63, the count >= 1 slots
 // routed to e in slots[] (slot order). Every thread of the workgroup calls it.
 template <bool A_BF16, bool FP4, bool WIDE>
 __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const int* slots,
-                                             u32x4* xs, int row_slots, int row_u)
+                                             u32x4* xs)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
@@ -529,30 +458,6 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
     const int H = p.H;
     const int n0 = n_block + 16 * w;              // this wavefront's 16 neurons
     const bool store = n0 < I;                    // wavefronts past I still take part in the barriers
-
-    if (count <= row_slots) {                     // workgroup-uniform: the row path
-        constexpr int NX = FP4 ? 4 : 2;
-        const int nch = FP4 ? H / 32 : H / 16;
-        const int units = count * NX * nch;
-        for (int v = threadIdx.x; v < units; v += blockDim.x) {
-            const int sl = v / (NX * nch);
-            const int t = (v % (NX * nch)) / nch;
-            const int c = v % nch;
-            const u32x4* xrow = reinterpret_cast<const u32x4*>(p.x + (size_t)(slots[sl] / p.k) * (size_t)H);
-            xs[v] = xrow[NX * c + t];
-        }
-        __syncthreads();
-        if (!store)
-            return;                               // after the only barrier
-        const int n_count = I - n0 < 16 ? I - n0 : 16;
-        if (row_u == 1)
-            rowwise_neurons<1, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
-        else if (row_u == 2)
-            rowwise_neurons<2, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
-        else if constexpr (!FP4)
-            rowwise_neurons<4, A_BF16, FP4>(p, e, n0, n_count, slots, count, xs, lane);
-        return;
-    }
 
     const int kb = lane / 16;                     // which quarter of a k group
     const int col = lane % 16;                    // A row (neuron) / B column (slot)
@@ -573,18 +478,24 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
     if constexpr (WIDE) {
         // the wavefront's first row (all 16 rows clamped to I-1 past I), its
         // row stride, and its LDS region for the wide loads
-        const size_t wrow = (size_t)e * (size_t)I + (size_t)(store ? n0 : I - 1);
+        // (wave-uniform: readfirstlane lets the loads take them from SGPRs)
+        const int wrow_i = __builtin_amdgcn_readfirstlane(store ? n0 : I - 1);
+        const size_t wrow = (size_t)e * (size_t)I + (size_t)wrow_i;
         const size_t rstride = store ? row_bytes : 0;
         const uint8_t* gq0 = p.wg_q + wrow * row_bytes;
         const uint8_t* uq0 = p.wu_q + wrow * row_bytes;
+        // the lane's scale row for the block loads: gate rows for lanes 0-31,
+        // up rows for 32-63, row (lane % 32) / 2 of the wavefront's 16
+        const size_t srow = wrow + (store ? (size_t)((lane % 32) / 2) : 0);
+        const uint8_t* sq0 = (lane < 32 ? p.wg_s : p.wu_s) + srow * (size_t)(H / 32);
         u32x4* tb = xs + 2 * kTiles * kXUnitsPerTile + w * kWideUnitsPerWave;
         for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
             const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
             switch (nt) {
-            case 1: grouped_pass_wide<1, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
-            case 2: grouped_pass_wide<2, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
-            case 3: grouped_pass_wide<3, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
-            default: grouped_pass_wide<4, A_BF16, FP4>(p, r, gq0, uq0, rstride, slots, count, t0, xs, tb, store); break;
+            case 1: grouped_pass_wide<1, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            case 2: grouped_pass_wide<2, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            case 3: grouped_pass_wide<3, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            default: grouped_pass_wide<4, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
             }
         }
     } else {
@@ -606,7 +517,7 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
 // place in the dynamic LDS) the routed experts' items with a stride of the
 // grid size, else one item per workgroup over all E experts.
 template <bool A_BF16, bool FP4, bool WIDE>
-__device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int row_slots, int row_u, int wl_off)
+__device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl_off)
 {
     extern __shared__ int slots[];               // B*k entries, the x tiles, then the work list
     __shared__ int wave_cnt[kGroupWaves];
@@ -646,25 +557,25 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int ro
         const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
         if (count == 0)
             continue;                             // whole workgroup (only without the work list)
-        gate_up_item<A_BF16, FP4, WIDE>(p, e, (item % nblk) * kGroupNeurons, count, slots, xs, row_slots, row_u);
+        gate_up_item<A_BF16, FP4, WIDE>(p, e, (item % nblk) * kGroupNeurons, count, slots, xs);
         __syncthreads();                          // the next item rewrites the slot list and the x tiles
     }
 }
 
 template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
-moe_gate_up_grouped_kernel(GateUpArgs p, int row_slots, int row_u, int wl_off)
+moe_gate_up_grouped_kernel(GateUpArgs p, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, false>(p, row_slots, row_u, wl_off);
+    gate_up_grouped_body<A_BF16, FP4, false>(p, wl_off);
 }
 
 // The wide loads need 8 KiB of LDS per wavefront, so two workgroups share a CU;
 // the register budget is set to match (two wavefronts per SIMD).
 template <bool A_BF16, bool FP4>
 __global__ void __launch_bounds__(kGroupWaves * kWave, 2)
-moe_gate_up_grouped_wide_kernel(GateUpArgs p, int row_slots, int row_u, int wl_off)
+moe_gate_up_grouped_wide_kernel(GateUpArgs p, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, true>(p, row_slots, row_u, wl_off);
+    gate_up_grouped_body<A_BF16, FP4, true>(p, wl_off);
 }
 
 size_t gate_up_grouped_lds(int B, int k, int E, bool wide)
@@ -677,8 +588,7 @@ size_t gate_up_grouped_lds(int B, int k, int E, bool wide)
 }
 
 template <bool A_BF16, bool FP4, bool WIDE>
-hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int row_slots,
-                          int row_u, int wl_off)
+hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off)
 {
     if constexpr (WIDE) {
         // allow dynamic LDS beyond the default 64 KiB, once per device: up to
@@ -688,10 +598,9 @@ hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, cons
                                 65536 + kGroupWaves * kWideUnitsPerWave * (int)sizeof(u32x4));
         if (attr != hipSuccess)
             return attr;
-        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u,
-                           wl_off);
+        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, wl_off);
     } else {
-        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, row_slots, row_u, wl_off);
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, wl_off);
     }
     return hipGetLastError();
 }
@@ -702,7 +611,8 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
         return hipSuccess;
     const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
     const long items = (long)p.E * nblk;
-    const bool wide = t.gu_wide != 0;
+    // wide loads: rows of whole 256-byte steps and whole scale blocks
+    const bool wide = t.gu_wide != 0 && p.H % 512 == 0;
     const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide);
     const size_t wl = worklist_lds(p.E);
     // with the work list: at most gu_grid workgroups (and at least one per
@@ -715,31 +625,18 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const dim3 grid((unsigned)nwg);
     const dim3 block(kGroupWaves * kWave);
     const bool fp4 = p.wfmt == kMXFP4;
-    // row path: experts with at most row_slots slots whose x rows fit in the
-    // x-tile space (2 * kTiles * kXUnitsPerTile units of 16 bytes)
-    const int nch = fp4 ? p.H / 32 : p.H / 16;
-    const int nx = fp4 ? 4 : 2;
-    int row_slots = t.gu_rowslots < kRowSlots ? t.gu_rowslots : kRowSlots;
-    while (row_slots > 0 && (long)row_slots * nx * nch > 2L * kTiles * kXUnitsPerTile)
-        --row_slots;
-    // chunks per lane per pass: 1, 2 or 4 (longer rows take several passes; the
-    // chunks still enter each lane's sums in increasing order, as in the
-    // per-slot kernel)
-    int row_u = 1;
-    while (row_u < (fp4 ? 2 : 4) && row_u * kWave < nch)
-        row_u *= 2;
     if (fp4) {
         if (a_bf16)
-            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
-                        : launch_grouped<true, true, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
-        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
-                    : launch_grouped<false, true, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
+            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, wl_off)
+                        : launch_grouped<true, true, false>(grid, block, lds, s, p, wl_off);
+        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, wl_off)
+                    : launch_grouped<false, true, false>(grid, block, lds, s, p, wl_off);
     }
     if (a_bf16)
-        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
-                    : launch_grouped<true, false, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
-    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, row_slots, row_u, wl_off)
-                : launch_grouped<false, false, false>(grid, block, lds, s, p, row_slots, row_u, wl_off);
+        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, wl_off)
+                    : launch_grouped<true, false, false>(grid, block, lds, s, p, wl_off);
+    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, wl_off)
+                : launch_grouped<false, false, false>(grid, block, lds, s, p, wl_off);
 }
 
 }  // namespace moed

@@ -45,6 +45,28 @@ __device__ __forceinline__ bf16x8 decode8_scaled_fp4(uint32_t codes, float scale
     return r;
 }
 
+// Block scales for the wide weight loads. The scale bytes of a row's MX blocks
+// 16b .. 16b+15 (one "scale block": four 128-code groups of four blocks) are
+// fetched with one 8-byte load per lane, two lanes per row: lane L holds bytes
+// 8*(L % 2) .. +7 of row slot L / 2. Requested this way, a wavefront's scale
+// loads touch each row's scale line once per 16 blocks instead of once per
+// group and lane, which keeps their L2 requests well below the weight stream's
+// (per-lane byte loads cost the grouped kernels 4-9% of their bandwidth). The
+// lane that decodes block 4*gi + kb of row slot n (gi: group within the block)
+// takes the byte from lane 2n + gi/2, dword gi % 2, byte kb, by ds_bpermute.
+__device__ __forceinline__ u32x2 load_scale_block(const uint8_t* row_scales, int blk, int lane)
+{
+    return *reinterpret_cast<const u32x2*>(row_scales + 16 * (size_t)blk + 8 * (size_t)(lane % 2));
+}
+
+template <int GI>
+__device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
+{
+    const uint32_t v = (GI & 1) ? sb.y : sb.x;
+    const uint32_t d = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (2 * row_slot + GI / 2), (int)v);
+    return ue8m0_to_f32((d >> (8 * kb)) & 255u);
+}
+
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing
 // order) with pred(ids[t]). All threads of the workgroup must call it. The ids
 // of up to four 256-slot chunks are loaded together, so the list costs one

@@ -22,8 +22,6 @@ struct Tuning {
                         // (each routed row decoded once per 64 slots); 2 = expert-major once B*k >= 2E
     int dn_tiles = 0;   // expert-major down: 16-slot tiles per pass over a row (1..4; 0 = as many
                         // as fit in 64 KiB of LDS)
-    int gu_rowslots = 2; // expert-grouped gate/up: experts with at most this many slots (up to 4) take
-                         // the row path (whole rows per wavefront, x of the slots in LDS)
     int gu_wide = 1;    // expert-grouped gate/up, MFMA path: 1 = weight rows read in 256-byte runs per
                         // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read

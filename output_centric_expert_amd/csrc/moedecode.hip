@@ -507,7 +507,6 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
         else if (!strcmp(tok, "dn_wide") && v >= 0 && v <= 2) t.dn_wide = (int)v;
-        else if (!strcmp(tok, "gu_rowslots") && v >= 0 && v <= 4) t.gu_rowslots = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_order") && v >= 0 && v <= 2) t.gu_order = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;

@@ -147,9 +147,6 @@ def test_tuning_spec_parser(lib):
     assert _init(lib, b"dn_tiles=0") == md.MOED_OK
     assert _init(lib, b"dn_tiles=5") == md.MOED_ERR_SHAPE
     assert _init(lib, b"dn_rt=1") == md.MOED_OK
-    assert _init(lib, b"gu_rowslots=0") == md.MOED_OK
-    assert _init(lib, b"gu_rowslots=4") == md.MOED_OK
-    assert _init(lib, b"gu_rowslots=5") == md.MOED_ERR_SHAPE
     assert _init(lib, b"gu_wide=0") == md.MOED_OK
     assert _init(lib, b"gu_wide=1") == md.MOED_OK
     assert _init(lib, b"gu_wide=2") == md.MOED_ERR_SHAPE
@@ -157,7 +154,7 @@ def test_tuning_spec_parser(lib):
     assert _init(lib, b"dn_rt=3") == md.MOED_ERR_SHAPE
     assert _init(lib, b"dn_lanegroups=0") == md.MOED_OK
     assert _init(lib, b"dn_lanegroups=2") == md.MOED_ERR_SHAPE
-    for gone in (b"gu_dot=1", b"gu_npw=1", b"nt=2", b"dn_order=1", b"dn_rows=0"):   # removed knobs
+    for gone in (b"gu_dot=1", b"gu_npw=1", b"nt=2", b"dn_order=1", b"dn_rows=0", b"gu_rowslots=2"):   # removed knobs
         assert _init(lib, gone) == md.MOED_ERR_SHAPE
     assert _init(lib, b"dn_onepass=0") == md.MOED_OK
     assert _init(lib, b"dn_onepass=2") == md.MOED_ERR_SHAPE

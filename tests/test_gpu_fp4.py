@@ -134,7 +134,7 @@ def test_fp4_workload_large_full_parity(name):
     # batch = concatenation of single-token calls, bit for bit, on each kernel pair
     # (the per-slot/per-output and the expert-grouped kernels accumulate in different orders)
     x, ids, w = md.layer_device_inputs(L)
-    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1,gu_rowslots=0"):
+    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1"):
         with md.tuned(spec):
             full = run(L)
             for b in (0, B - 1):

@@ -184,7 +184,7 @@ def test_workload_large_full_parity(name):
         check_f32(a0.reshape(B, -1), a_ref.reshape(B, -1), name + " output-centric a")
     # batch = concatenation of single-token calls, bit for bit, on each kernel pair
     # (the per-slot/per-output and the grouped kernels accumulate in different orders)
-    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1,gu_rowslots=0"):
+    for spec in ("gu_group=0,dn_group=0", "gu_group=1,dn_group=1"):
         with md.tuned(spec):
             full = run(L, torch.float32)
             for b in (0, B // 3, B - 1):
@@ -650,47 +650,13 @@ def test_input_check_scale_range(monkeypatch):
             L.wg_s[e, 0, 0] = saved
     assert torch.equal(run(L), base)
 
-ROW_PATH = [
-    (24, 16, 2, 2080, 64),    # ~3 slots per expert (some above 4: MFMA path); a ragged second chunk per lane
-    (12, 8, 3, 4096, 128),    # four chunks per lane per pass
-    (40, 6, 1, 96, 160),      # short rows (6 chunks), more than 4 slots on most experts
-    (16, 64, 8, 7168, 64),    # 7168-value rows: x of at most 2 slots fits, several passes per row
-]
-
-
-@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
-@pytest.mark.parametrize("shape", ROW_PATH, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
-def test_grouped_row_path(shape, wformat):
-    """Experts with at most 4 slots in the expert-grouped gate/up take the row path: the same
-    float for every output as the per-slot kernel; the rest (MFMA path) within tolerance."""
-    B, E, k, H, I = shape
-    L = synth.make_layer(synth.LayerShape("rp", B, E, k, H, I), seed=sum(shape) + 9, device="cuda", wformat=wformat)
-    x, ids, _ = md.layer_device_inputs(L)
-    md.set_default_tuning("gu_group=0")
-    try:
-        a_slot = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
-        md.set_default_tuning("gu_group=1,gu_rowslots=4")
-        a_row = md.inter_to_bki(md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat))
-        torch.cuda.synchronize()
-    finally:
-        md.set_default_tuning(None)
-    counts = np.bincount(L.ids.ravel(), minlength=E)
-    slot_x = 2 * H if wformat == "mxfp8" else 2 * H    # bf16 x row bytes per slot
-    fits = max(0, min(4, 32768 // slot_x))
-    light = counts[L.ids] <= fits                       # [B, k]: slot's expert takes the row path
-    light_t = torch.from_numpy(light).cuda()
-    assert torch.equal(a_row[light_t], a_slot[light_t])
-    rms = float(a_slot.double().pow(2).mean().sqrt())
-    assert float((a_row - a_slot).abs().max()) <= 1e-5 * rms
-    assert light.any()
-
-
 WIDE = [
-    (40, 3, 2, 640, 160),     # ~27 slots per expert (2 tiles); 5 groups: whole steps + 1 group; waves past I
-    (72, 2, 2, 640, 96),      # 72 slots per expert: a 4-tile pass, then a 1-tile pass
-    (24, 6, 4, 2080, 64),     # 65 MX blocks: 16 groups and a leftover block
-    (20, 4, 3, 448, 128),     # 3 groups and 2 leftover blocks: no whole MXFP4 step
-    (16, 8, 8, 7168, 64),     # 56 groups of 7168-value rows
+    (40, 3, 2, 1024, 160),    # ~27 slots per expert (2 tiles); waves past I
+    (72, 2, 2, 512, 96),      # 72 slots per expert: a 4-tile pass, then a 1-tile pass; one scale block
+    (24, 6, 4, 2560, 64),     # 5 MXFP8 step pairs / 5 MXFP4 steps
+    (20, 4, 3, 1536, 128),    # 3 step pairs / 3 steps
+    (16, 8, 8, 7168, 64),     # 14 step pairs of 7168-value rows
+    (24, 6, 4, 2080, 64),     # H not a multiple of 512: the 128-byte slices either way
 ]
 
 
@@ -698,8 +664,9 @@ WIDE = [
 @pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
 def test_grouped_wide_loads(shape, wformat):
     """The MFMA path's wide weight loads (256-byte runs per row, moved to the operand layout
-    through LDS) feed every MFMA the codes the 128-byte tile slices do, in the same order:
-    the intermediate is the same floats (float32 and bf16), and the layer within tolerance of
+    through LDS, scales fetched in 16-byte blocks and handed out by ds_bpermute) feed every
+    MFMA the codes and scales the 128-byte tile slices do, in the same order: the
+    intermediate is the same floats (float32 and bf16), and the layer within tolerance of
     the oracle."""
     B, E, k, H, I = shape
     L = synth.make_layer(synth.LayerShape("wide", B, E, k, H, I), seed=sum(shape) + 21, device="cuda",
@@ -708,7 +675,7 @@ def test_grouped_wide_loads(shape, wformat):
     got = {}
     try:
         for wide in (0, 1):
-            md.set_default_tuning(f"gu_group=1,gu_rowslots=0,gu_wide={wide}")
+            md.set_default_tuning(f"gu_group=1,gu_wide={wide}")
             for dt in (torch.float32, torch.bfloat16):
                 got[wide, dt] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
                                                       inter_dtype=dt, wformat=wformat)
@@ -716,7 +683,7 @@ def test_grouped_wide_loads(shape, wformat):
         say(f"wide loads {shape} {wformat}: comparing")
         for dt in (torch.float32, torch.bfloat16):
             assert torch.equal(got[1, dt], got[0, dt]), f"{shape} {wformat} {dt}"
-        md.set_default_tuning("gu_group=1,gu_rowslots=0,gu_wide=1")
+        md.set_default_tuning("gu_group=1,gu_wide=1")
         ref, _ = oracle_tokens(L, [0, B - 1], wformat=wformat)
         xd, idd, wd = md.layer_device_inputs(L)
         out = md.moe_decode(xd, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
