@@ -303,26 +303,23 @@ template <bool FP4, int RT>
 struct DnStep {
     static constexpr int kGroups = FP4 ? 4 : 2;  // 128-code groups per 256-byte step
     u32x4 v[4 * RT];                             // pieces of rows L/16 + 4i
-    uint32_t sb[kGroups][RT];                    // scale bytes (as loaded) of the lane's rows, block kb
 };
 
 // 16-byte LDS units of one step, per wavefront
 template <int RT>
 constexpr int kDnWideUnits = 16 * RT * 16;
 
+// q0: the wavefront's first row (wave-uniform); lo: this lane's byte offset
+// (lane/16)*rstride + 16*(lane%16); rs4 = 4*rstride. A uniform base plus 32-bit
+// lane offsets keeps the addresses of the 4*RT loads in a few registers.
 template <bool FP4, int RT>
-__device__ __forceinline__ void load_dn_step(const uint8_t* q0, size_t rstride, const DnRow<RT>& r, int step,
-                                             int lane, DnStep<FP4, RT>& w)
+__device__ __forceinline__ void load_dn_step(const uint8_t* q0, uint32_t lo, uint32_t rs4, int step,
+                                             DnStep<FP4, RT>& w)
 {
-    const size_t off = (size_t)step * 256 + 16 * (size_t)(lane % 16);
+    const uint32_t base = lo + 256u * (uint32_t)step;
 #pragma unroll
     for (int i = 0; i < 4 * RT; ++i)
-        w.v[i] = *reinterpret_cast<const u32x4*>(q0 + (size_t)(lane / 16 + 4 * i) * rstride + off);
-#pragma unroll
-    for (int h = 0; h < DnStep<FP4, RT>::kGroups; ++h)
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-            w.sb[h][t] = r.s[t][4 * (step * DnStep<FP4, RT>::kGroups + h) + r.kb];
+        w.v[i] = *reinterpret_cast<const u32x4*>(q0 + (base + (uint32_t)i * rs4));
 }
 
 template <bool FP4, int RT>
@@ -354,17 +351,20 @@ __device__ __forceinline__ DnGroupW staged_dn_group(const u32x4* tb, const DnRow
     return w;
 }
 
-// expert_down_pass with the wide weight loads: one step of weights in flight
-// ahead (requested once the group before the step's last two has taken its a
-// loads), the slots' a two groups ahead as before; each wait for a group's a
-// therefore never waits for rows issued behind it. Groups after the last whole
-// step load their 128-byte slices directly; leftover blocks as in
-// expert_down_pass. q0 / rstride: the wavefront's first row and its row stride
-// (0 for a wavefront past H, which reads row H-1 throughout); tb: its LDS region.
+// expert_down_pass with the wide weight loads (I a multiple of 512: whole
+// 256-byte steps and, for MXFP8, whole two-step scale blocks): one step of
+// weights in flight ahead (requested once the group before the step's last two
+// has taken its a loads), with it the next scale block (16 bytes per row, two
+// lanes per row, handed out by ds_bpermute: see load_scale_block), the slots' a
+// two groups ahead as before; each wait for a group's a therefore never waits
+// for rows issued behind it. q0 / rstride: the wavefront's first row and its
+// row stride (0 for a wavefront past H, which reads row H-1 throughout); sq0:
+// the scale row of the lane's block-load row slot ((lane / 2) % (16*RT)); tb:
+// the wavefront's LDS region.
 template <int NTL, int RT, bool A_BF16, bool FP4>
 __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const DnRow<RT>& r, const uint8_t* q0,
-                                                      size_t rstride, const int* slots, int count, int t0,
-                                                      u32x4* xs, u32x4* tb, bool store, int h0, float* y)
+                                                      size_t rstride, const uint8_t* sq0, const int* slots, int count,
+                                                      int t0, u32x4* xs, u32x4* tb, bool store, int h0, float* y)
 {
     constexpr int GPS = DnStep<FP4, RT>::kGroups;
     const int I = p.I;
@@ -390,7 +390,9 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
         for (int tt = 0; tt < NTL; ++tt)
             d[t][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int ngroups = r.nsteps / 4;
-    const int nst = ngroups / GPS;                // whole 256-byte steps
+    const int nst = ngroups / GPS;                // 256-byte steps (even for MXFP8)
+    const uint32_t lo = (uint32_t)(lane / 16) * (uint32_t)rstride + 16u * (uint32_t)(lane % 16);
+    const uint32_t rs4 = 4u * (uint32_t)rstride;
     ARaw<A_BF16> raw[2][NTL];                     // a of groups g+1 and g+2, by group parity
     auto load_a = [&](ARaw<A_BF16> (&dst)[NTL], int g) {
 #pragma unroll
@@ -400,23 +402,20 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
     auto put_a = [&](const ARaw<A_BF16> (&src)[NTL], u32x4* buf) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt) {
-            u32x4 hi, lo;
-            split_a8<A_BF16>(src[tt], hi, lo);
+            u32x4 hi, lo16;
+            split_a8<A_BF16>(src[tt], hi, lo16);
             const int u = (tt * 16 + lcol) * 16 + (lc ^ lcol);
             buf[u] = hi;
             if constexpr (!A_BF16)
-                buf[kHalf + u] = lo;
+                buf[kHalf + u] = lo16;
         }
     };
-    DnStep<FP4, RT> sw{};
-    if (ngroups > 0) {
-        load_a(raw[0], 0);
-        if (ngroups > 1)
-            load_a(raw[1], 1);
-        if (nst > 0)
-            load_dn_step<FP4, RT>(q0, rstride, r, 0, lane, sw);
-        put_a(raw[0], xs);
-    }
+    DnStep<FP4, RT> sw;
+    load_a(raw[0], 0);
+    load_a(raw[1], 1);
+    load_dn_step<FP4, RT>(q0, lo, rs4, 0, sw);
+    u32x2 sb = load_scale_block(sq0, 0, lane);
+    put_a(raw[0], xs);
     __syncthreads();
     // a of group g+2 into set P = g & 1 (unconditional: the last groups re-read
     // the last group's a, so no load sits behind a branch)
@@ -428,9 +427,16 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
         load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // group g: the MFMAs on buffer g&1, then a of g+1 (set 1-P) split into the other buffer
-    auto group = [&](auto par, int g, const DnGroupW (&w)[RT]) {
+    // group g = step group h, scale-block group GI: the lane's codes and scale
+    // codes of its RT rows, the MFMAs on buffer g&1, then a of g+1 (set 1-P)
+    // split into the other buffer
+    auto group = [&](auto par, auto gi, int g, int h, const u32x2& blk) {
         constexpr int P = decltype(par)::value;
+        constexpr int GI = decltype(gi)::value;
+        DnGroupW w[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, block_scale_code<GI>(blk, 16 * t + r.col, r.kb));
         const u32x4* xb = xs + (g & 1) * kBuf;
         bf16x8 aw[RT][4];
 #pragma unroll
@@ -461,77 +467,52 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
     };
     constexpr auto P0 = std::integral_constant<int, 0>{};
     constexpr auto P1 = std::integral_constant<int, 1>{};
-    for (int s = 0; s < nst; ++s) {
-        stage_dn_step<FP4, RT>(sw, tb, lane);
-        const int g0 = s * GPS;                   // even: the parity of group g0 + h is that of h
-        const int snext = s + 1 < nst ? s + 1 : s;
-        DnGroupW w[RT];
-        uint32_t sbk[GPS][RT];                    // this step's scale bytes (sw is refilled below)
-#pragma unroll
-        for (int h = 0; h < GPS; ++h)
-#pragma unroll
-            for (int t = 0; t < RT; ++t)
-                sbk[h][t] = sw.sb[h][t];
-        auto staged_k = [&](int h) {
-#pragma unroll
-            for (int t = 0; t < RT; ++t)
-                w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, sbk[h][t]);
-        };
-        aload(P0, g0);
-        if constexpr (GPS == 2) {                 // MXFP8: next step during the first group
-            load_dn_step<FP4, RT>(q0, rstride, r, snext, lane, sw);
+    constexpr auto G0 = std::integral_constant<int, 0>{};
+    constexpr auto G1 = std::integral_constant<int, 1>{};
+    constexpr auto G2 = std::integral_constant<int, 2>{};
+    constexpr auto G3 = std::integral_constant<int, 3>{};
+    if constexpr (GPS == 2) {
+        // MXFP8: steps in pairs (one scale block); the next step (and, in the
+        // second step, the next block) requested during each step's first group
+        for (int s = 0; s < nst; s += 2) {
+            const int g0 = 2 * s;
+            const u32x2 blk = sb;                 // this pair's block (sb is refilled below)
+            stage_dn_step<FP4, RT>(sw, tb, lane);
+            aload(P0, g0);
+            load_dn_step<FP4, RT>(q0, lo, rs4, s + 1, sw);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        staged_k(0);
-        group(P0, g0, w);
-        aload(P1, g0 + 1);
-        staged_k(1);
-        group(P1, g0 + 1, w);
-        if constexpr (GPS == 4) {                 // MXFP4: next step during the third group
+            group(P0, G0, g0, 0, blk);
+            aload(P1, g0 + 1);
+            group(P1, G1, g0 + 1, 1, blk);
+            stage_dn_step<FP4, RT>(sw, tb, lane);
+            const int sn = s + 2 < nst ? s + 2 : s + 1;
             aload(P0, g0 + 2);
-            load_dn_step<FP4, RT>(q0, rstride, r, snext, lane, sw);
+            load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
+            sb = load_scale_block(sq0, sn / 2, lane);
             __builtin_amdgcn_sched_barrier(0);
-            staged_k(2);
-            group(P0, g0 + 2, w);
+            group(P0, G2, g0 + 2, 0, blk);
             aload(P1, g0 + 3);
-            staged_k(3);
-            group(P1, g0 + 3, w);
+            group(P1, G3, g0 + 3, 1, blk);
         }
-    }
-    for (int g = nst * GPS; g < ngroups; g += 2) {   // groups after the last whole step (g even)
-        DnGroupW w[RT];
-        aload(P0, g);
-        load_dn_w<FP4>(r, g, w);
-        group(P0, g, w);
-        if (g + 1 < ngroups) {
-            aload(P1, g + 1);
-            load_dn_w<FP4>(r, g + 1, w);
-            group(P1, g + 1, w);
-        }
-    }
-    for (int st = 4 * ngroups; st < r.nsteps; ++st) {   // leftover blocks: plain k order
-        const int k0 = st * 32 + 8 * r.kb;
-        bf16x8 aw[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            if constexpr (FP4)
-                aw[t] = decode8_scaled_fp4(*reinterpret_cast<const uint32_t*>(r.q[t] + k0 / 2),
-                                           ue8m0_to_f32(r.s[t][st]));
-            else
-                aw[t] = decode8_scaled(*reinterpret_cast<const u32x2*>(r.q[t] + k0), ue8m0_to_f32(r.s[t][st]));
-        }
-#pragma unroll
-        for (int tt = 0; tt < NTL; ++tt) {
-            u32x4 hi, lo;
-            split_a8<A_BF16>(load_a8<A_BF16>(p.a, bj[tt], k0, I), hi, lo);
-#pragma unroll
-            for (int t = 0; t < RT; ++t) {
-                d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, hi), d[t][tt],
-                                                                   0, 0, 0);
-                if constexpr (!A_BF16)
-                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], __builtin_bit_cast(bf16x8, lo),
-                                                                       d[t][tt], 0, 0, 0);
-            }
+    } else {
+        // MXFP4: one scale block per step; the next step and block requested
+        // during the step's third group
+        for (int s = 0; s < nst; ++s) {
+            const int g0 = 4 * s;
+            const u32x2 blk = sb;
+            stage_dn_step<FP4, RT>(sw, tb, lane);
+            const int sn = s + 1 < nst ? s + 1 : s;
+            aload(P0, g0);
+            group(P0, G0, g0, 0, blk);
+            aload(P1, g0 + 1);
+            group(P1, G1, g0 + 1, 1, blk);
+            aload(P0, g0 + 2);
+            load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
+            sb = load_scale_block(sq0, sn, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            group(P0, G2, g0 + 2, 2, blk);
+            aload(P1, g0 + 3);
+            group(P1, G3, g0 + 3, 3, blk);
         }
     }
     if (!store)
@@ -579,8 +560,12 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
     if constexpr (WIDE) {
         // the wavefront's first row (all rows clamped to H-1 past H), its row
         // stride, and its LDS region after the a tiles
-        const uint8_t* q0 = p.wd_q + ((size_t)e * (size_t)p.H + (size_t)(store ? h0 : p.H - 1)) * row_bytes;
+        const int wrow = __builtin_amdgcn_readfirstlane(store ? h0 : p.H - 1);   // wave-uniform
+        const uint8_t* q0 = p.wd_q + ((size_t)e * (size_t)p.H + (size_t)wrow) * row_bytes;
         const size_t rstride = store ? row_bytes : 0;
+        // the lane's scale row for the block loads: row slot (lane / 2) % (16*RT)
+        const int srow = store ? h0 + (lane / 2) % (16 * RT) : p.H - 1;
+        const uint8_t* sq0 = p.wd_s + ((size_t)e * (size_t)p.H + (size_t)srow) * (size_t)(p.I / 32);
         u32x4* tb = xs + 2 * (A_BF16 ? 1 : 2) * max_tiles * kDnUnits + w * kDnWideUnits<RT>;
         // at most 2 tiles of float32 a (3 of bf16) per pass here: the step
         // registers take the place of the last tile's (the launcher sizes the
@@ -590,11 +575,11 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
         for (int t0 = 0; t0 < ntiles; t0 += mt) {
             const int nt = ntiles - t0 < mt ? ntiles - t0 : mt;
             if (nt == 1) {
-                expert_down_pass_wide<1, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<1, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             } else if (nt == 2) {
-                expert_down_pass_wide<2, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<2, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             } else if constexpr (A_BF16) {
-                expert_down_pass_wide<3, RT, A_BF16, FP4>(p, r, q0, rstride, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<3, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             }
         }
         return;

@@ -60,11 +60,17 @@ __device__ __forceinline__ u32x2 load_scale_block(const uint8_t* row_scales, int
 }
 
 template <int GI>
-__device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
+__device__ __forceinline__ uint32_t block_scale_code(u32x2 sb, int row_slot, int kb)
 {
     const uint32_t v = (GI & 1) ? sb.y : sb.x;
     const uint32_t d = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (2 * row_slot + GI / 2), (int)v);
-    return ue8m0_to_f32((d >> (8 * kb)) & 255u);
+    return (d >> (8 * kb)) & 255u;
+}
+
+template <int GI>
+__device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
+{
+    return ue8m0_to_f32(block_scale_code<GI>(sb, row_slot, kb));
 }
 
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing

@@ -780,11 +780,12 @@ def test_grouped_work_list_matches_full_grid(shape, wformat):
 
 # (B, E, k, H, I) for the expert-major down's wide weight loads
 DOWN_WIDE = [
-    (40, 3, 2, 96, 640),      # ~27 slots per expert (2 tiles); 5 groups: whole steps + 1 group; waves past H
-    (72, 2, 2, 64, 768),      # 72 slots per expert: passes of 2 + 2 + 1 tiles (float32 a)
-    (24, 6, 4, 2080, 544),    # 17 MX blocks: 4 groups and a leftover block; waves past H in the last block
-    (20, 4, 3, 128, 448),     # 3 groups and 2 leftover blocks: no whole MXFP4 step
-    (16, 8, 8, 64, 7168),     # 56 groups per row
+    (40, 3, 2, 96, 1024),     # ~27 slots per expert (2 tiles); waves past H
+    (72, 2, 2, 64, 512),      # 72 slots per expert: passes of 2 + 2 + 1 tiles (float32 a); one scale block
+    (24, 6, 4, 2080, 1536),   # 3 MXFP8 step pairs / 3 MXFP4 steps; waves past H in the last block
+    (20, 4, 3, 128, 2560),    # 5 step pairs / 5 steps
+    (16, 8, 8, 64, 7168),     # 14 step pairs per row
+    (24, 6, 4, 2080, 544),    # I not a multiple of 512: the 128-byte slices either way
 ]
 
 
@@ -793,7 +794,8 @@ DOWN_WIDE = [
 @pytest.mark.parametrize("shape", DOWN_WIDE, ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
 def test_expert_major_down_wide_loads(shape, wformat, rt):
     """The expert-major down's wide weight loads (256-byte runs per row, moved to the operand
-    layout through LDS) feed every MFMA the codes the 128-byte slices do, in the same order:
+    layout through LDS, scales fetched in 16-byte blocks and handed out by ds_bpermute) feed
+    every MFMA the codes and scales the 128-byte slices do, in the same order:
     the layer output is the same floats for float32 and bf16 intermediates (an invalid id on
     the last token gives NaN there on both), and within tolerance of the oracle."""
     B, E, k, H, I = shape
