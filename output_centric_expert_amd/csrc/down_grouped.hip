@@ -427,16 +427,14 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
         load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // group g = step group h, scale-block group GI: the lane's codes and scale
-    // codes of its RT rows, the MFMAs on buffer g&1, then a of g+1 (set 1-P)
-    // split into the other buffer
-    auto group = [&](auto par, auto gi, int g, int h, const u32x2& blk) {
+    // group g = step group h with the scale codes of the lane's RT rows: the
+    // MFMAs on buffer g&1, then a of g+1 (set 1-P) split into the other buffer
+    auto group = [&](auto par, int g, int h, const uint32_t (&codes)[RT]) {
         constexpr int P = decltype(par)::value;
-        constexpr int GI = decltype(gi)::value;
         DnGroupW w[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t)
-            w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, block_scale_code<GI>(blk, 16 * t + r.col, r.kb));
+            w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, codes[t]);
         const u32x4* xb = xs + (g & 1) * kBuf;
         bf16x8 aw[RT][4];
 #pragma unroll
@@ -467,52 +465,69 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
     };
     constexpr auto P0 = std::integral_constant<int, 0>{};
     constexpr auto P1 = std::integral_constant<int, 1>{};
-    constexpr auto G0 = std::integral_constant<int, 0>{};
-    constexpr auto G1 = std::integral_constant<int, 1>{};
-    constexpr auto G2 = std::integral_constant<int, 2>{};
-    constexpr auto G3 = std::integral_constant<int, 3>{};
     if constexpr (GPS == 2) {
         // MXFP8: steps in pairs (one scale block); the next step (and, in the
         // second step, the next block) requested during each step's first group
         for (int s = 0; s < nst; s += 2) {
             const int g0 = 2 * s;
-            const u32x2 blk = sb;                 // this pair's block (sb is refilled below)
+            // each step's scale codes at the step start (sb is refilled in the
+            // second step, after its codes are taken)
+            uint32_t c0[RT], c1[RT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                c0[t] = block_scale_code<0>(sb, 16 * t + r.col, r.kb);
+                c1[t] = block_scale_code<1>(sb, 16 * t + r.col, r.kb);
+            }
             stage_dn_step<FP4, RT>(sw, tb, lane);
             aload(P0, g0);
             load_dn_step<FP4, RT>(q0, lo, rs4, s + 1, sw);
             __builtin_amdgcn_sched_barrier(0);
-            group(P0, G0, g0, 0, blk);
+            group(P0, g0, 0, c0);
             aload(P1, g0 + 1);
-            group(P1, G1, g0 + 1, 1, blk);
+            group(P1, g0 + 1, 1, c1);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                c0[t] = block_scale_code<2>(sb, 16 * t + r.col, r.kb);
+                c1[t] = block_scale_code<3>(sb, 16 * t + r.col, r.kb);
+            }
             stage_dn_step<FP4, RT>(sw, tb, lane);
             const int sn = s + 2 < nst ? s + 2 : s + 1;
             aload(P0, g0 + 2);
             load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
             sb = load_scale_block(sq0, sn / 2, lane);
             __builtin_amdgcn_sched_barrier(0);
-            group(P0, G2, g0 + 2, 0, blk);
+            group(P0, g0 + 2, 0, c0);
             aload(P1, g0 + 3);
-            group(P1, G3, g0 + 3, 1, blk);
+            group(P1, g0 + 3, 1, c1);
         }
     } else {
         // MXFP4: one scale block per step; the next step and block requested
         // during the step's third group
         for (int s = 0; s < nst; ++s) {
             const int g0 = 4 * s;
-            const u32x2 blk = sb;
+            // all four groups' scale codes at the step start (per group, a
+            // ds_bpermute round trip would sit before each decode)
+            uint32_t sc[4][RT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                sc[0][t] = block_scale_code<0>(sb, 16 * t + r.col, r.kb);
+                sc[1][t] = block_scale_code<1>(sb, 16 * t + r.col, r.kb);
+                sc[2][t] = block_scale_code<2>(sb, 16 * t + r.col, r.kb);
+                sc[3][t] = block_scale_code<3>(sb, 16 * t + r.col, r.kb);
+            }
             stage_dn_step<FP4, RT>(sw, tb, lane);
             const int sn = s + 1 < nst ? s + 1 : s;
             aload(P0, g0);
-            group(P0, G0, g0, 0, blk);
+            group(P0, g0, 0, sc[0]);
             aload(P1, g0 + 1);
-            group(P1, G1, g0 + 1, 1, blk);
+            group(P1, g0 + 1, 1, sc[1]);
             aload(P0, g0 + 2);
             load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
             sb = load_scale_block(sq0, sn, lane);
             __builtin_amdgcn_sched_barrier(0);
-            group(P0, G2, g0 + 2, 2, blk);
+            group(P0, g0 + 2, 2, sc[2]);
             aload(P1, g0 + 3);
-            group(P1, G3, g0 + 3, 3, blk);
+            group(P1, g0 + 3, 3, sc[3]);
         }
     }
     if (!store)

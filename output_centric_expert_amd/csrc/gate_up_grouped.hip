@@ -381,65 +381,73 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         constexpr int P = decltype(par)::value;
         load_x(xq[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
     };
-    // group g = step group h, scale-block group GI: the scales of the lane's
-    // gate and up rows (col and 16 + col of the block load) taken from the
-    // block just before the decode, the MFMAs on x buffer g&1, then x of g+1
-    // (set 1-P) into the other buffer
-    auto group = [&](auto par, auto gi, int g, int h, const u32x2& blk) {
+    // group g = step group h with the lane's gate and up scales: the MFMAs on
+    // x buffer g&1, then x of g+1 (set 1-P) into the other buffer
+    auto group = [&](auto par, int g, int h, float gsc, float usc) {
         constexpr int P = decltype(par)::value;
-        constexpr int GI = decltype(gi)::value;
-        const float gsc = block_scale<GI>(blk, r.col, r.kb);
-        const float usc = block_scale<GI>(blk, 16 + r.col, r.kb);
         group_mfma<NTL, FP4>(staged_group<FP4>(tb, r, h, gsc, usc), xs + (g & 1) * kBuf, r, dg, du);
         put_x(xq[1 - P], g + 1 < ngroups ? g + 1 : ngroups - 1);
         __syncthreads();
     };
     constexpr auto P0 = std::integral_constant<int, 0>{};
     constexpr auto P1 = std::integral_constant<int, 1>{};
-    constexpr auto G0 = std::integral_constant<int, 0>{};
-    constexpr auto G1 = std::integral_constant<int, 1>{};
-    constexpr auto G2 = std::integral_constant<int, 2>{};
-    constexpr auto G3 = std::integral_constant<int, 3>{};
     if constexpr (GPS == 2) {
         // MXFP8: a scale block spans two steps, so steps go in pairs; the next
         // step's rows (and, in the second step, the next block) are requested
         // during each step's first group
         for (int s = 0; s < nst; s += 2) {
             const int g0 = 2 * s;
-            const u32x2 blk = sb;                 // this pair's block (sb is refilled below)
+            // each step's two groups' scales at the step start (sb is refilled
+            // in the second step, after its scales are taken)
+            float gsc0 = block_scale<0>(sb, r.col, r.kb), usc0 = block_scale<0>(sb, 16 + r.col, r.kb);
+            float gsc1 = block_scale<1>(sb, r.col, r.kb), usc1 = block_scale<1>(sb, 16 + r.col, r.kb);
             stage_step<FP4>(sw, tb, lane);
             xload(P0, g0);
             sw = load_step<FP4>(gq0, uq0, lo, rs4, s + 1);
-            group(P0, G0, g0, 0, blk);
+            group(P0, g0, 0, gsc0, usc0);
             xload(P1, g0 + 1);
-            group(P1, G1, g0 + 1, 1, blk);
+            group(P1, g0 + 1, 1, gsc1, usc1);
+            gsc0 = block_scale<2>(sb, r.col, r.kb);
+            usc0 = block_scale<2>(sb, 16 + r.col, r.kb);
+            gsc1 = block_scale<3>(sb, r.col, r.kb);
+            usc1 = block_scale<3>(sb, 16 + r.col, r.kb);
             stage_step<FP4>(sw, tb, lane);
             const int sn = s + 2 < nst ? s + 2 : s + 1;
             xload(P0, g0 + 2);
             sw = load_step<FP4>(gq0, uq0, lo, rs4, sn);
             sb = load_scale_block(sq0, sn / 2, lane);
-            group(P0, G2, g0 + 2, 0, blk);
+            group(P0, g0 + 2, 0, gsc0, usc0);
             xload(P1, g0 + 3);
-            group(P1, G3, g0 + 3, 1, blk);
+            group(P1, g0 + 3, 1, gsc1, usc1);
         }
     } else {
         // MXFP4: one scale block per step; the next step and block are
         // requested during the step's third group
         for (int s = 0; s < nst; ++s) {
             const int g0 = 4 * s;
-            const u32x2 blk = sb;
+            // all four groups' scales at the step start (four groups per step: taking
+            // them per group would put a ds_bpermute round trip before each decode)
+            float gsc[4], usc[4];
+            gsc[0] = block_scale<0>(sb, r.col, r.kb);
+            usc[0] = block_scale<0>(sb, 16 + r.col, r.kb);
+            gsc[1] = block_scale<1>(sb, r.col, r.kb);
+            usc[1] = block_scale<1>(sb, 16 + r.col, r.kb);
+            gsc[2] = block_scale<2>(sb, r.col, r.kb);
+            usc[2] = block_scale<2>(sb, 16 + r.col, r.kb);
+            gsc[3] = block_scale<3>(sb, r.col, r.kb);
+            usc[3] = block_scale<3>(sb, 16 + r.col, r.kb);
             stage_step<FP4>(sw, tb, lane);
             const int sn = s + 1 < nst ? s + 1 : s;
             xload(P0, g0);
-            group(P0, G0, g0, 0, blk);
+            group(P0, g0, 0, gsc[0], usc[0]);
             xload(P1, g0 + 1);
-            group(P1, G1, g0 + 1, 1, blk);
+            group(P1, g0 + 1, 1, gsc[1], usc[1]);
             xload(P0, g0 + 2);
             sw = load_step<FP4>(gq0, uq0, lo, rs4, sn);
             sb = load_scale_block(sq0, sn, lane);
-            group(P0, G2, g0 + 2, 2, blk);
+            group(P0, g0 + 2, 2, gsc[2], usc[2]);
             xload(P1, g0 + 3);
-            group(P1, G3, g0 + 3, 3, blk);
+            group(P1, g0 + 3, 3, gsc[3], usc[3]);
         }
     }
     if (store)

@@ -26,9 +26,8 @@ struct Tuning {
                         // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
-    int dn_wide = 1;    // expert-major down: weight rows read in 256-byte runs per row and moved to the
-                        // operand layout through LDS (1 = for MXFP8 weights, 2 = for both formats),
-                        // or 0 = 128-byte slices per row and group
+    int dn_wide = 1;    // expert-major down: 1 = weight rows read in 256-byte runs per row and moved to the
+                        // operand layout through LDS (when I is a multiple of 512), 0 = 128-byte slices
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
                         // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once

@@ -87,12 +87,11 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
 // Expert-major down: used inside moe_decode (which owns a workspace for the
 // per-slot partials) once tokens share experts, about two or more slots per
 // expert on average (measured crossovers at 1.5-2 slots per expert).
-// The expert-major down's wide loads (rows of whole 256-byte steps and scale
-// blocks, I a multiple of 512): dn_wide 1 = for MXFP8 weights (measured faster
-// there, and slower for MXFP4), 2 = for both formats, 0 = never.
-bool down_wide(const moed::Tuning& t, int wfmt, int I)
+// The expert-major down's wide loads: rows of whole 256-byte steps and scale
+// blocks (I a multiple of 512), both weight formats, unless dn_wide = 0.
+bool down_wide(const moed::Tuning& t, int I)
 {
-    return I % 512 == 0 && (t.dn_wide == 2 || (t.dn_wide == 1 && wfmt == moed::kMXFP8));
+    return I % 512 == 0 && t.dn_wide != 0;
 }
 
 int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16, bool wide)
@@ -106,7 +105,7 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
                        hipStream_t s)
 {
     if (y) {
-        const bool wide = down_wide(t, p.wfmt, p.I);
+        const bool wide = down_wide(t, p.I);
         if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16, wide))
             return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, wide, t.dn_grid, s);
     }
@@ -195,7 +194,7 @@ int layer(const void* x, const int32_t* topk_ids, const float* topk_w, const uin
 {
     const bool a_bf16 = inter_dtype == MOED_BF16;
     if (check_enabled()) {
-        const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, weight_format, I)) != 0;
+        const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I)) != 0;
         if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
                                use_grouped(t, B, E, k, H, weight_format), expert_down, s))
             return st;
@@ -315,7 +314,7 @@ int moe_decode_down_tuned(const void* a, int inter_dtype, const int32_t* topk_id
     const bool a_bf16 = inter_dtype == MOED_BF16;
     if (check_enabled()) {
         const bool expert_down =
-            partials && pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, weight_format, I)) != 0;
+            partials && pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I)) != 0;
         if (int st = run_check(check_args(topk_ids, nullptr, nullptr, nullptr, nullptr, wd_q, wd_s, B, E, k, H, I,
                                           weight_format),
                                false, expert_down, s))
@@ -507,7 +506,7 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_group") && v >= 0 && v <= 2) t.dn_group = (int)v;
         else if (!strcmp(tok, "dn_tiles") && v >= 0 && v <= 4) t.dn_tiles = (int)v;
         else if (!strcmp(tok, "dn_rt") && v >= 1 && v <= 2) t.dn_rt = (int)v;
-        else if (!strcmp(tok, "dn_wide") && v >= 0 && v <= 2) t.dn_wide = (int)v;
+        else if (!strcmp(tok, "dn_wide") && (v == 0 || v == 1)) t.dn_wide = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_order") && v >= 0 && v <= 2) t.gu_order = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
