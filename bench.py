@@ -587,11 +587,13 @@ WEIGHT_DESC = {"mxfp8": "mxfp8 (e4m3 + ue8m0 per 32)", "mxfp4": "mxfp4 (e2m1 two
 
 def gate_up_kernel_name(L):
     """The gate/up kernel the library's built-in launch table picks for this layer: the
-    expert-grouped one once B*k*H >= 2458*E, else the per-slot exact-fit kernel when a row is
-    exactly 64*U 16-byte chunks (U <= 8), else the generic per-slot kernel."""
+    expert-grouped one once 4*B*k >= 3*E or (H >= 6144 and min(B*k, E)*ceil(I/64) >= 512) --
+    the wide form when H is a multiple of 512 -- else the per-slot exact-fit kernel when a row
+    is exactly 64*U 16-byte chunks (U <= 8), else the generic per-slot kernel."""
     sh = L.shape
-    if sh.B * sh.k * sh.H >= 2458 * sh.E:
-        return "moe_gate_up_grouped_wide_kernel"
+    slots = sh.B * sh.k
+    if 4 * slots >= 3 * sh.E or (sh.H >= 6144 and min(slots, sh.E) * -(-sh.I // 64) >= 512):
+        return "moe_gate_up_grouped_wide_kernel" if sh.H % 512 == 0 else "moe_gate_up_grouped_kernel"
     nch = sh.H // 32 if L.wformat == "mxfp4" else sh.H // 16
     return "moe_gate_up_exact_kernel" if nch % 64 == 0 and nch // 64 <= 8 else "moe_gate_up_kernel"
 

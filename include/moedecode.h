@@ -139,7 +139,8 @@ size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype);
  * weighted partial goes to the workspace, and a second launch adds each
  * token's k partials in slot order and stores the output once. Smaller batches
  * use the one-wavefront-per-output down of moe_decode_down(). Likewise the
- * gate/up step runs expert-grouped (MFMA) once B*k*H >= 2458*E.
+ * gate/up step runs expert-grouped (MFMA) once 4*B*k >= 3*E, or for rows of
+ * H >= 6144 values once min(B*k, E)*ceil(I/64) >= 512.
  *
  * Exact range of the large-batch kernels: they decode a weight to BF16 with
  * its block scale folded into the conversion, which is exact while every

@@ -30,8 +30,8 @@ struct Tuning {
                         // operand layout through LDS (when I is a multiple of 512), 0 = 128-byte slices
     int gu_umax = 8;    // gate/up: max 16-byte chunks per lane per row held in flight
     int gu_group = 2;   // gate/up: 0 = one wavefront per (token, slot, neuron); 1 = expert-grouped
-                        // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once
-                        // B*k*H >= 2458*E (about 1.2 slots per expert at H = 2048)
+                        // MFMA tiles (rows decoded once per 16 slots); 2 = grouped once 4*B*k >= 3*E,
+                        // or H >= 6144 with min(B*k, E)*ceil(I/64) >= 512
     int dn_umax = 8;    // down: max 16-byte chunks per lane held in flight
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
     int dn_onepass = 1; // down (staged, one output per wavefront): 1 = straight-line kernel when the

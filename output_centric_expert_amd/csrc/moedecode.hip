@@ -61,25 +61,31 @@ bool pick(const moed_tuning* user, moed::Tuning* t)
     return true;
 }
 
-// Expert-grouped gate/up pays off once tokens share experts: measured
-// crossovers (uniform routing, E = 128 and 256, k = 8) at about 1.2 slots per
-// expert for H = 2048, 0.6 for H = 4096 and below 0.5 for H = 7168 -- longer
-// rows amortise the workgroup's fixed costs sooner -- hence the rule
-// B*k*H >= 2458*E. Its slot list must fit in 64 KiB of LDS with the x tiles
-// (the wide loads add 32 KiB, within the 160 KiB of a workgroup).
-bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int wfmt)
+// Expert-grouped gate/up (each routed row read once per 16-slot tile) against
+// the per-slot kernel (each row read once per slot), measured with uniform
+// routing, k = 8, E = 128 and 256: the grouped kernel wins from about 0.75
+// slots per expert at H = 2048 and 4096 (it loses at 0.5: 41 vs 30 us, 133 vs
+// 122 us), and at H = 7168 from two tokens on (0.25 slots per expert: 256 vs
+// 327 us), once its items (expert, 64 neurons) fill the 512 workgroup slots
+// of the chip (one token: 47 vs 41 us). Hence the rule: grouped when
+// 4*B*k >= 3*E, or when H >= 6144 and min(B*k, E)*ceil(I/64) >= 512 (H between
+// 4096 and 6144 unmeasured). Its slot list must fit in 64 KiB of LDS with the
+// x tiles (the wide loads add 32 KiB, within the 160 KiB of a workgroup).
+bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int I, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel
     if (moed::gate_up_grouped_lds(B, k, E, false) > 65536 || t.gu_group == 0)
         return false;
     if (t.gu_group == 1)
         return true;
-    return (long long)B * k * H >= 2458LL * E;
+    const long long slots = (long long)B * k;
+    const long long items = (slots < E ? slots : E) * ((I + 63) / 64);
+    return 4 * slots >= 3LL * E || (H >= 6144 && items >= 512);
 }
 
 hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tuning& t, hipStream_t s)
 {
-    if (use_grouped(t, p.B, p.E, p.k, p.H, p.wfmt))
+    if (use_grouped(t, p.B, p.E, p.k, p.H, p.I, p.wfmt))
         return moed::launch_gate_up_grouped(p, a_bf16, t, s);
     return moed::launch_gate_up(p, a_bf16, t, s);
 }
@@ -196,7 +202,7 @@ int layer(const void* x, const int32_t* topk_ids, const float* topk_w, const uin
     if (check_enabled()) {
         const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I)) != 0;
         if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
-                               use_grouped(t, B, E, k, H, weight_format), expert_down, s))
+                               use_grouped(t, B, E, k, H, I, weight_format), expert_down, s))
             return st;
     }
     int st = hip_status(gate_up_launch(
@@ -274,7 +280,7 @@ int moe_decode_gate_up_tuned(const void* x, const int32_t* topk_ids, const uint8
     if (check_enabled()) {
         if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, nullptr, nullptr, B, E, k, H, I,
                                           weight_format),
-                               use_grouped(t, B, E, k, H, weight_format), false, s))
+                               use_grouped(t, B, E, k, H, I, weight_format), false, s))
             return st;
     }
     return hip_status(gate_up_launch(gate_up_args(x, topk_ids, wg_q, wg_s, wu_q, wu_s, weight_format, a,

@@ -602,7 +602,7 @@ def test_input_check_scale_range(monkeypatch):
     """MOED_CHECK=1 also reports routed block scales outside the range the large-batch kernels
     decode exactly (MXFP8 codes 10..245), as MOED_ERR_SCALE, and only for calls that take those
     kernels: the expert-grouped gate/up for gate/up scales, the expert-major down for down scales."""
-    L = small(40, 4, 2, 256, 64, seed=43)            # B*k*H >= 2458*E and B*k >= 2E: both grouped
+    L = small(40, 4, 2, 256, 64, seed=43)            # 4*B*k >= 3*E and B*k >= 2E: both grouped
     monkeypatch.setenv("MOED_CHECK", "1")
     base = run(L)
     routed = sorted(set(L.ids.ravel().tolist()))
