@@ -377,9 +377,12 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
     // group g uses x set P = g&1: the caller first requests x of g+2 into it
     // (xload) -- before a step's rows, so that waiting for that x later never
     // waits for rows issued behind it
+    // (the scheduling barrier keeps the x loads ahead of the rows requested
+    // next: issued after them, waiting for that x would wait for those rows)
     auto xload = [&](auto par, int g) {
         constexpr int P = decltype(par)::value;
         load_x(xq[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
+        __builtin_amdgcn_sched_barrier(0);
     };
     // group g = step group h with the lane's gate and up scales: the MFMAs on
     // x buffer g&1, then x of g+1 (set 1-P) into the other buffer
