@@ -237,9 +237,10 @@ __device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedR
         store_tiles<NTL, A_BF16>(p, r, bj, count, t0, dg, du);
 }
 
-// Wide weight loads (the default MFMA path). The 128-byte row slices of a
-// 16-row tile, one per lane group, cap the weight stream near 4.8 TB/s on
-// MI355X; runs of 256 bytes per row reach about 6 TB/s. So the wavefront reads
+// Wide weight loads (the default MFMA path when H is a multiple of 512). The
+// 128-byte row slices of a 16-row tile, one per lane group, cap the weight
+// stream near 4.8 TB/s on MI355X; runs of 256 bytes per row, streamed, with
+// the scales in 16-byte blocks, reach about 7 TB/s. So the wavefront reads
 // its 16 gate and 16 up rows in steps of 256 bytes per row (two 128-code
 // groups of MXFP8, four of MXFP4): load i of lane L takes the 16-byte piece
 // L % 16 of row L / 16 + 4i, and each load instruction covers four whole
