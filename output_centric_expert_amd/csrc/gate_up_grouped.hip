@@ -623,8 +623,10 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
         return hipSuccess;
     const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
     const long items = (long)p.E * nblk;
-    // wide loads: rows of whole 256-byte steps and whole scale blocks
-    const bool wide = t.gu_wide != 0 && p.H % 512 == 0;
+    // wide loads: rows of whole 256-byte steps and whole scale blocks, read as
+    // 8-byte pieces (scale arrays at 8-byte aligned bases; else the slices,
+    // which give the same floats)
+    const bool wide = t.gu_wide != 0 && p.H % 512 == 0 && (((uintptr_t)p.wg_s | (uintptr_t)p.wu_s) & 7u) == 0;
     const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide);
     const size_t wl = worklist_lds(p.E);
     // with the work list: at most gu_grid workgroups (and at least one per

@@ -94,10 +94,12 @@ hipError_t gate_up_launch(const moed::GateUpArgs& p, bool a_bf16, const moed::Tu
 // per-slot partials) once tokens share experts, about two or more slots per
 // expert on average (measured crossovers at 1.5-2 slots per expert).
 // The expert-major down's wide loads: rows of whole 256-byte steps and scale
-// blocks (I a multiple of 512), both weight formats, unless dn_wide = 0.
-bool down_wide(const moed::Tuning& t, int I)
+// blocks (I a multiple of 512, the scale array at an 8-byte aligned base: its
+// blocks are read as 8-byte pieces), both weight formats, unless dn_wide = 0;
+// otherwise the 128-byte slices, which give the same floats.
+bool down_wide(const moed::Tuning& t, int I, const uint8_t* wd_s)
 {
-    return I % 512 == 0 && t.dn_wide != 0;
+    return I % 512 == 0 && t.dn_wide != 0 && ((uintptr_t)wd_s & 7u) == 0;
 }
 
 int pick_down_tiles(const moed::Tuning& t, int B, int E, int k, bool a_bf16, bool wide)
@@ -111,7 +113,7 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
                        hipStream_t s)
 {
     if (y) {
-        const bool wide = down_wide(t, p.I);
+        const bool wide = down_wide(t, p.I, p.wd_s);
         if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16, wide))
             return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, wide, t.dn_grid, s);
     }
@@ -200,7 +202,7 @@ int layer(const void* x, const int32_t* topk_ids, const float* topk_w, const uin
 {
     const bool a_bf16 = inter_dtype == MOED_BF16;
     if (check_enabled()) {
-        const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I)) != 0;
+        const bool expert_down = pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I, wd_s)) != 0;
         if (int st = run_check(check_args(topk_ids, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, B, E, k, H, I, weight_format),
                                use_grouped(t, B, E, k, H, I, weight_format), expert_down, s))
             return st;
@@ -320,7 +322,7 @@ int moe_decode_down_tuned(const void* a, int inter_dtype, const int32_t* topk_id
     const bool a_bf16 = inter_dtype == MOED_BF16;
     if (check_enabled()) {
         const bool expert_down =
-            partials && pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I)) != 0;
+            partials && pick_down_tiles(t, B, E, k, a_bf16, down_wide(t, I, wd_s)) != 0;
         if (int st = run_check(check_args(topk_ids, nullptr, nullptr, nullptr, nullptr, wd_q, wd_s, B, E, k, H, I,
                                           weight_format),
                                false, expert_down, s))

@@ -778,6 +778,34 @@ def test_grouped_work_list_matches_full_grid(shape, wformat):
     check_f32(got[1][[0, B // 2, B - 2]], ref, f"work list {shape} {wformat}")
 
 
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+def test_grouped_kernels_with_unaligned_scale_arrays(wformat):
+    """The wide loads read each row's scale bytes in 8-byte pieces, so they need 8-byte aligned
+    scale arrays; scale arrays at odd addresses take the 128-byte slices instead, which give the
+    same floats: the layer output is bit-identical with aligned and unaligned scale arrays."""
+    B, E, k, H, I = 40, 3, 2, 1024, 512
+    L = synth.make_layer(synth.LayerShape("unal", B, E, k, H, I), seed=77, device="cuda", wformat=wformat)
+    x, ids, w = md.layer_device_inputs(L)
+
+    def shifted(t):                                   # the same bytes at an address 1 past a 16-byte boundary
+        buf = torch.empty(t.numel() + 16, dtype=torch.uint8, device="cuda")
+        v = buf[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 8 == 1
+        return v
+
+    scales = {"wg_s": shifted(L.wg_s), "wu_s": shifted(L.wu_s), "wd_s": shifted(L.wd_s)}
+    outs = []
+    with md.tuned("gu_group=1,dn_group=1"):
+        for gs, us, ds in ((L.wg_s, L.wu_s, L.wd_s), (scales["wg_s"], scales["wu_s"], scales["wd_s"])):
+            outs.append(md.moe_decode(x, ids, w, L.wg_q, gs, L.wu_q, us, L.wd_q, ds, out_dtype=torch.float32,
+                                      wformat=wformat))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    ref, _ = oracle_tokens(L, [0, B - 1], wformat=wformat)
+    check_f32(outs[1][[0, B - 1]], ref, f"unaligned scales {wformat}")
+
+
 # (B, E, k, H, I) for the expert-major down's wide weight loads
 DOWN_WIDE = [
     (40, 3, 2, 96, 1024),     # ~27 slots per expert (2 tiles); waves past H
