@@ -116,6 +116,99 @@ moe_gate_up_exact_kernel(GateUpArgs p)
     }
 }
 
+// Exact-fit form with two neighbouring neurons i0, i0+1 of one slot per
+// wavefront (x loaded once for both; four row loads per lane chunk), for
+// MXFP4 rows at B > 1: an MXFP4 row is half as long, so one neuron per
+// wavefront keeps only two 16-byte loads per lane in flight (B = 8 gate/up
+// 18.6 vs 20.0 us; at B = 1 the same, and slower for MXFP8, whose rows
+// already give four loads per lane). Per neuron the products, the FMA order
+// and the reduction are those of moe_gate_up_exact_kernel: the same floats.
+template <int U, bool A_BF16, bool FP4>
+__global__ void __launch_bounds__(256)
+moe_gate_up_exact_pair_kernel(GateUpArgs p)
+{
+    constexpr int NX = FP4 ? 4 : 2;               // 16-byte pieces of x per chunk
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wpb = blockDim.x / kWave;
+    const int n_pairs = p.B * p.k * (p.I / 2);
+    const int n_raw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * wpb + (int)(threadIdx.x / kWave));
+    const int n0 = n_raw < n_pairs ? n_raw : n_pairs - 1;   // no early exit; the extra waves store nothing
+    const int i0 = 2 * (n0 % (p.I / 2));
+    const int bj = n0 / (p.I / 2);
+    const int b = bj / p.k;
+    const int H = p.H;
+    const size_t row_bytes = FP4 ? (size_t)(H / 2) : (size_t)H;
+    const int e_raw = p.ids[bj];
+    const u32x4* xq = reinterpret_cast<const u32x4*>(p.x + (size_t)b * (size_t)H);
+    u32x4 xv[U][NX];
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+#pragma unroll
+        for (int t = 0; t < NX; ++t)
+            xv[m][t] = xq[NX * (lane + kWave * m) + t];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool bad_id = (unsigned)e_raw >= (unsigned)p.E;   // expert 0's rows are read, result NaN
+    const int e = bad_id ? 0 : e_raw;
+    u32x4 wg[2][U], wu[2][U];
+    uint32_t sg[2][U], su[2][U];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const size_t row = (size_t)e * (size_t)p.I + (size_t)(i0 + n);
+        const u32x4* gq = reinterpret_cast<const u32x4*>(p.wg_q + row * row_bytes);
+        const u32x4* uq = reinterpret_cast<const u32x4*>(p.wu_q + row * row_bytes);
+        const uint8_t* gs = p.wg_s + row * (size_t)(H / 32);
+        const uint8_t* us = p.wu_s + row * (size_t)(H / 32);
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            const int c = lane + kWave * m;
+            wg[n][m] = __builtin_nontemporal_load(gq + c);
+            wu[n][m] = __builtin_nontemporal_load(uq + c);
+            sg[n][m] = gs[FP4 ? c : c >> 1];
+            su[n][m] = us[FP4 ? c : c >> 1];
+        }
+    }
+    float g[2], u[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        g[n] = 0.0f;
+        u[n] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < U; ++m) {
+            const float pg = gu_chunk_dot<FP4, NX>(wg[n][m], xv[m]);
+            const float pu = gu_chunk_dot<FP4, NX>(wu[n][m], xv[m]);
+            g[n] = __builtin_fmaf(pg, ue8m0_to_f32(sg[n][m]), g[n]);
+            u[n] = __builtin_fmaf(pu, ue8m0_to_f32(su[n][m]), u[n]);
+        }
+        g[n] = wave_sum(g[n]);
+        u[n] = wave_sum(u[n]);
+    }
+    if (lane == 0 && n_raw < n_pairs) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const float v = bad_id ? __builtin_nanf("") : swiglu(g[n], u[n]);
+            const size_t a_idx = inter_index<A_BF16>(bj, i0 + n, p.I);
+            if constexpr (A_BF16)
+                static_cast<uint16_t*>(p.a)[a_idx] = f32_to_bf16_rne(v);
+            else
+                static_cast<float*>(p.a)[a_idx] = v;
+        }
+    }
+}
+
+template <bool A_BF16>
+static hipError_t dispatch_pair(int U, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
+{
+    switch (U) {
+#define MOED_GUP_CASE(N) \
+    case N: hipLaunchKernelGGL((moe_gate_up_exact_pair_kernel<N, A_BF16, true>), grid, block, 0, s, p); break;
+        MOED_GUP_CASE(1) MOED_GUP_CASE(2) MOED_GUP_CASE(3) MOED_GUP_CASE(4)
+#undef MOED_GUP_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <bool A_BF16, bool FP4>
 static hipError_t dispatch_exact(int U, bool nb, const GateUpArgs& p, dim3 grid, dim3 block, hipStream_t s)
 {
@@ -169,6 +262,11 @@ hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hip
         // neuron-block order where slots may share experts (B > 1); by default for
         // MXFP8 only (measured 3-4% faster at B = 8-16 there, 2% slower for MXFP4)
         const bool nb = (t.gu_order == 2 || (t.gu_order == 1 && !fp4)) && p.B > 1 && p.I % 16 == 0;
+        // MXFP4 at B > 1 (unless neuron-block order is asked for): two neurons per wavefront
+        if (fp4 && !nb && t.gu_pair != 0 && p.B > 1 && p.I % 2 == 0 && U <= 4) {
+            const dim3 g2((unsigned)((n_out / 2 + wpb - 1) / wpb));
+            return a_bf16 ? dispatch_pair<true>(U, p, g2, block, s) : dispatch_pair<false>(U, p, g2, block, s);
+        }
         if (fp4)
             return a_bf16 ? dispatch_exact<true, true>(U, nb, p, grid, block, s)
                           : dispatch_exact<false, true>(U, nb, p, grid, block, s);

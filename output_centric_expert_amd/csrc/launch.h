@@ -10,6 +10,8 @@ namespace moed {
 // can override them for sweeps.
 struct Tuning {
     int gu_wpb = 4;     // gate/up: wavefronts per workgroup (1..4)
+    int gu_pair = 1;    // exact-fit gate/up, MXFP4 at B > 1: two neighbouring neurons per wavefront
+                        // (0 = one)
     int gu_order = 1;   // exact-fit gate/up at B > 1: neuron-block order with XCD-contiguous workgroups
                         // (slots sharing an expert meet in one L2) for MXFP8 (1) or both formats (2);
                         // 0 = slot-major

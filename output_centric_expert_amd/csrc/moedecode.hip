@@ -517,6 +517,7 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_wide") && (v == 0 || v == 1)) t.dn_wide = (int)v;
         else if (!strcmp(tok, "gu_wide") && v >= 0 && v <= 1) t.gu_wide = (int)v;
         else if (!strcmp(tok, "gu_order") && v >= 0 && v <= 2) t.gu_order = (int)v;
+        else if (!strcmp(tok, "gu_pair") && (v == 0 || v == 1)) t.gu_pair = (int)v;
         else if (!strcmp(tok, "gu_umax") && v >= 1 && v <= 8) t.gu_umax = (int)v;
         else if (!strcmp(tok, "gu_group") && v >= 0 && v <= 2) t.gu_group = (int)v;
         else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;

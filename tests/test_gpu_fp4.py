@@ -145,23 +145,25 @@ def test_fp4_workload_large_full_parity(name):
                 assert torch.equal(one[0], full[b]), spec
 
 
-@pytest.mark.parametrize("shape", [(3, 12, 4, 2048, 256), (2, 9, 1, 4096, 544), (4, 16, 8, 2048, 768)],
+@pytest.mark.parametrize("shape", [(3, 12, 4, 2048, 256), (2, 9, 1, 4096, 544), (4, 16, 8, 2048, 768),
+                                   (3, 7, 2, 8192, 96)],
                          ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
 def test_fp4_exact_fit_neuron_block_order(shape):
-    """B > 1 with MXFP4 rows of exactly 64*U chunks: the exact-fit gate/up in neuron-block order
-    (gu_order=2) computes the same floats as in slot-major order (gu_order=0), and matches the
-    oracle."""
+    """B > 1 with MXFP4 rows of exactly 64*U chunks: the exact-fit gate/up with two neurons per
+    wavefront (the default here), with one (gu_pair=0), and in neuron-block order (gu_order=2)
+    computes the same floats, and matches the oracle."""
     B = shape[0]
     L = small(*shape, seed=sum(shape) + 21)
     x, ids, _ = md.layer_device_inputs(L)
     got = {}
-    for order in (0, 2):
-        with md.tuned(f"gu_group=0,gu_order={order}"):
-            got[order] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF)
+    for spec in ("gu_order=0", "gu_order=0,gu_pair=0", "gu_order=2"):
+        with md.tuned(f"gu_group=0,{spec}"):
+            got[spec] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=WF)
             torch.cuda.synchronize()
-    assert torch.equal(got[0], got[2])
+    assert torch.equal(got["gu_order=0"], got["gu_order=0,gu_pair=0"])
+    assert torch.equal(got["gu_order=0"], got["gu_order=2"])
     _, a_ref = oracle_tokens(L, list(range(B)))
-    check_f32(md.inter_to_bki(got[2]).reshape(B, -1), a_ref.reshape(B, -1), f"mxfp4 gu_order=2 a {shape}")
+    check_f32(md.inter_to_bki(got["gu_order=0"]).reshape(B, -1), a_ref.reshape(B, -1), f"mxfp4 pairs a {shape}")
     with md.tuned("gu_group=0,gu_order=2"):
         out = run(L)
     ref, _ = oracle_tokens(L, list(range(B)))
@@ -193,7 +195,8 @@ def test_fp4_ragged_shapes(shape):
 
 @pytest.mark.parametrize("spec", ["gu_umax=1,dn_umax=1", "dn_stage=0", "dn_stage=0,dn_umax=8", "gu_wpb=1,dn_wpb=3",
                                   "gu_group=1", "dn_group=1", "dn_lanegroups=0", "dn_umax=2", "gu_exact=0,gu_umax=1",
-                                  "dn_onepass=0", "dn_onepass=0,dn_lanegroups=0", "gu_exact=0", "gu_order=2"])
+                                  "dn_onepass=0", "dn_onepass=0,dn_lanegroups=0", "gu_exact=0", "gu_order=2",
+                                  "gu_pair=0"])
 def test_fp4_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 16448, 64), (4, 40, 4, 2048, 256)]:
         L = small(*shape, seed=3)
