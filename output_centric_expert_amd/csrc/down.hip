@@ -393,7 +393,14 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     if (staged && t.dn_onepass != 0 && !a_bf16 && nt && wpb == 8 && p.k == groups * per_group &&
         (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups &&
         (groups > 1 || rows <= 2)) {
-        return launch_down_onepass(q, per_group, groups, out_bf16, grid, block, lds, s);
+        // MXFP4 at B > 1: two outputs per wavefront (an MXFP4 chunk is dotted with
+        // 128 bytes of a from LDS, an MXFP8 one with 64: sharing each read between
+        // two rows pays for MXFP4 only -- measured), with 4 wavefronts per
+        // workgroup unless that leaves at least 2048 workgroups of 8
+        int pair_wpb = 0;
+        if (fp4 && t.dn_pair != 0 && p.B > 1 && p.H % 2 == 0)
+            pair_wpb = (long)p.B * (p.H / 16) >= 2048 ? 8 : 4;
+        return launch_down_onepass(q, per_group, groups, out_bf16, pair_wpb, grid, block, lds, s);
     }
     if (groups > 1) {
         const int per = (p.k + groups - 1) / groups;   // slots per group

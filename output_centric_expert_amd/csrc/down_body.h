@@ -157,6 +157,35 @@ __device__ __forceinline__ float down_group_dot(const u32x4* a_lds, int k, int j
     return acc;
 }
 
+// The same for R rows h .. h+R-1 of the lane's slots (one chunk per lane and
+// row, lane groups as above): each piece of a read from LDS serves all R rows,
+// and per row the FMAs, their operands and their order are those of
+// down_group_dot with CPL = 1, so every output is the same float.
+template <int JB, bool FP4, int G, int R>
+__device__ __forceinline__ void down_group_dot_multi(const u32x4* a_lds, int k, int lane, int cpr, int cpr16,
+                                                     const u32x4 (&wq)[R][JB], const uint32_t (&ws)[R][JB],
+                                                     const float (&wt)[JB], const float (&mask)[JB], float (&acc)[R])
+{
+    using LG = LaneGroups<G>;
+    constexpr int NP = APieces<FP4, false>::N;
+    const int js = LG::group(lane);
+    const int lc = LG::chunk(lane);
+    const int oc = lc < cpr ? lc : cpr - 1;
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const int j = js + G * jj < k ? js + G * jj : k - 1;
+        u32x4 av[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            av[q] = a_lds[a_unit<FP4, false>(j, oc, q, cpr16)];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float part = chunk_dot<FP4, false>(wq[r][jj], av);
+            acc[r] = __builtin_fmaf(wt[jj] * mask[jj], part * ue8m0_to_f32(ws[r][jj]), acc[r]);
+        }
+    }
+}
+
 // Variants for a wavefront that owns R consecutive outputs h0 .. h0+R-1 of one
 // token (rows Wd[e][h0+r] of the same experts): each piece of a read from LDS
 // serves all R rows. Per row the loads, the order of the FMAs and their

@@ -668,12 +668,30 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
     if (bad)
         acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     const size_t o = (size_t)b * (size_t)H + (size_t)h;
+    // one vector store when out is aligned for it (the usual case), else four
+    // element stores: the caller's out needs no alignment beyond its type
     if constexpr (OUT_BF16) {
+        uint16_t* ob = static_cast<uint16_t*>(out) + o;
         const uint32_t lo = f32x2_to_bf16x2_rne(acc.x, acc.y);
         const uint32_t hi = f32x2_to_bf16x2_rne(acc.z, acc.w);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o) = u32x2{lo, hi};
+        if (((uintptr_t)out & 7u) == 0) {
+            *reinterpret_cast<u32x2*>(ob) = u32x2{lo, hi};
+        } else {
+            ob[0] = (uint16_t)(lo & 0xFFFFu);
+            ob[1] = (uint16_t)(lo >> 16);
+            ob[2] = (uint16_t)(hi & 0xFFFFu);
+            ob[3] = (uint16_t)(hi >> 16);
+        }
     } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = acc;
+        float* of = static_cast<float*>(out) + o;
+        if (((uintptr_t)out & 15u) == 0) {
+            *reinterpret_cast<f32x4*>(of) = acc;
+        } else {
+            of[0] = acc.x;
+            of[1] = acc.y;
+            of[2] = acc.z;
+            of[3] = acc.w;
+        }
     }
 }
 

@@ -20,13 +20,17 @@ namespace moed {
 // order are those of moe_down_staged_kernel with the same lane groups, so the
 // results are the same floats. The workgroup order is always hidden-major and
 // XCD-contiguous (the default order of the other kernels). ONE_TOKEN: B = 1,
-// so the token index needs no division.
-template <int JB, int G, bool OUT_BF16, bool FP4, int NCP, bool ONE_TOKEN>
-__global__ void __launch_bounds__(512)
+// so the token index needs no division. R = 2: the wavefront owns the two
+// neighbouring outputs h, h+1 (H even): each lane loads its chunk of both
+// rows of every slot (the rows of one expert are contiguous) and each piece
+// of a read from LDS serves both, which halves the LDS reads and the copies
+// of a[b] per output; per output the arithmetic is unchanged. WPB: 8 or 4
+// wavefronts per workgroup (NCP then covers a[b] with WPB*64 threads).
+template <int JB, int G, bool OUT_BF16, bool FP4, int NCP, bool ONE_TOKEN, int R = 1, int WPB = 8>
+__global__ void __launch_bounds__(WPB * kWave)
 moe_down_onepass_kernel(DownArgs p)
 {
     extern __shared__ u32x4 a_lds[];
-    constexpr int WPB = 8;
     constexpr int NTH = WPB * kWave;
     constexpr int KS = G * JB;                    // slots per token (= p.k)
     using LG = LaneGroups<G>;
@@ -35,7 +39,7 @@ moe_down_onepass_kernel(DownArgs p)
     // the order argument ahead of the loads)
     const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
     const int b = ONE_TOKEN ? 0 : blk % p.B;
-    const int h = (ONE_TOKEN ? blk : blk / p.B) * WPB + (int)(threadIdx.x / kWave);
+    const int h = ((ONE_TOKEN ? blk : blk / p.B) * WPB + (int)(threadIdx.x / kWave)) * R;
     const bool active = h < p.H;                  // idle waves still help copy a[b]
     const int cpr16 = p.I / 16;
     const int cpr = FP4 ? p.I / 32 : cpr16;
@@ -94,16 +98,19 @@ moe_down_onepass_kernel(DownArgs p)
     const int hc = active ? h : 0;
     const int oc = lc < cpr ? lc : cpr - 1;
     const bool lane_live = active && lc < cpr;
-    u32x4 wq[JB][1];
-    uint32_t ws[JB][1];
-    float mask[JB][1];
+    u32x4 wq[R][JB];
+    uint32_t ws[R][JB];
+    float mask[JB];
 #pragma unroll
     for (int jj = 0; jj < JB; ++jj) {
         const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
-        const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)hc;
-        wq[jj][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes) + oc);
-        ws[jj][0] = p.wd_s[row * (size_t)(p.I / 32) + (FP4 ? oc : oc >> 1)];
-        mask[jj][0] = lane_live ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+        mask[jj] = lane_live ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t row = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H + (size_t)(hc + r);
+            wq[r][jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes) + oc);
+            ws[r][jj] = p.wd_s[row * (size_t)(p.I / 32) + (FP4 ? oc : oc >> 1)];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -115,13 +122,23 @@ moe_down_onepass_kernel(DownArgs p)
     __syncthreads();
     if (!active)
         return;                                   // after the only barrier
-    float acc = down_group_dot<1, JB, false, FP4, G>(a_lds, KS, 0, 0, lane, cpr, cpr16, wq, ws, wt, mask, 0.0f);
-    acc = wave_sum(acc);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+    down_group_dot_multi<JB, FP4, G, R>(a_lds, KS, lane, cpr, cpr16, wq, ws, wt, mask, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = wave_sum(acc[r]);
     if (lane == 0) {
-        if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(p.out)[(size_t)b * p.H + h] = f32_to_bf16_rne(acc);
-        else
-            static_cast<float*>(p.out)[(size_t)b * p.H + h] = acc;
+        const size_t o = (size_t)b * p.H + h;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {             // element stores: out needs no alignment beyond its type
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t*>(p.out)[o + r] = f32_to_bf16_rne(acc[r]);
+            else
+                static_cast<float*>(p.out)[o + r] = acc[r];
+        }
     }
 }
 
@@ -130,10 +147,30 @@ moe_down_onepass_kernel(DownArgs p)
 constexpr int onepass_max_ncp(int jb, bool fp4) { return fp4 ? jb : (jb >= 2 ? jb / 2 : 1); }
 
 template <int JB, int G, bool FP4>
-static hipError_t launch_jg(const DownArgs& p, bool out_bf16, int ncp, dim3 grid, dim3 block, size_t lds,
-                            hipStream_t s)
+static hipError_t launch_jg(const DownArgs& p, bool out_bf16, int pair_wpb, int ncp, dim3 grid, dim3 block,
+                            size_t lds, hipStream_t s)
 {
     constexpr int MAXN = onepass_max_ncp(JB, FP4);
+    if constexpr (FP4) {
+        if (pair_wpb != 0) {                      // two outputs per wavefront, 4 or 8 wavefronts per workgroup
+            const int wpb = pair_wpb;
+            const dim3 g2((unsigned)((long)p.B * ((p.H / 2 + wpb - 1) / wpb))), b2((unsigned)(wpb * kWave));
+            if (wpb == 4) {
+                if (out_bf16)
+                    hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, true, FP4, 2 * MAXN, false, 2, 4>), g2, b2,
+                                       lds, s, p);
+                else
+                    hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, false, FP4, 2 * MAXN, false, 2, 4>), g2, b2,
+                                       lds, s, p);
+            } else {
+                if (out_bf16)
+                    hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, true, FP4, MAXN, false, 2>), g2, b2, lds, s, p);
+                else
+                    hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, false, FP4, MAXN, false, 2>), g2, b2, lds, s, p);
+            }
+            return hipGetLastError();
+        }
+    }
 #define MOED_OP(O, N, ONE) \
     hipLaunchKernelGGL((moe_down_onepass_kernel<JB, G, O, FP4, N, ONE>), grid, block, lds, s, p)
     // single-token calls of k = 8 slots: the exact copy count (one to four loads)
@@ -161,34 +198,37 @@ static hipError_t launch_jg(const DownArgs& p, bool out_bf16, int ncp, dim3 grid
 }
 
 template <int G>
-static hipError_t launch_g(const DownArgs& p, int jb, bool out_bf16, int ncp, dim3 grid, dim3 block, size_t lds,
-                           hipStream_t s)
+static hipError_t launch_g(const DownArgs& p, int jb, bool out_bf16, int pair_wpb, int ncp, dim3 grid, dim3 block,
+                           size_t lds, hipStream_t s)
 {
     const bool fp4 = p.wfmt == kMXFP4;
     switch (jb * 2 + (fp4 ? 1 : 0)) {
-    case 1 * 2 + 0: return launch_jg<1, G, false>(p, out_bf16, ncp, grid, block, lds, s);
-    case 1 * 2 + 1: return launch_jg<1, G, true>(p, out_bf16, ncp, grid, block, lds, s);
-    case 2 * 2 + 0: return launch_jg<2, G, false>(p, out_bf16, ncp, grid, block, lds, s);
-    case 2 * 2 + 1: return launch_jg<2, G, true>(p, out_bf16, ncp, grid, block, lds, s);
-    case 4 * 2 + 0: return launch_jg<4, G, false>(p, out_bf16, ncp, grid, block, lds, s);
-    case 4 * 2 + 1: return launch_jg<4, G, true>(p, out_bf16, ncp, grid, block, lds, s);
-    case 8 * 2 + 0: return launch_jg<8, G, false>(p, out_bf16, ncp, grid, block, lds, s);
-    case 8 * 2 + 1: return launch_jg<8, G, true>(p, out_bf16, ncp, grid, block, lds, s);
+    case 1 * 2 + 0: return launch_jg<1, G, false>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 1 * 2 + 1: return launch_jg<1, G, true>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 2 * 2 + 0: return launch_jg<2, G, false>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 2 * 2 + 1: return launch_jg<2, G, true>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 4 * 2 + 0: return launch_jg<4, G, false>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 4 * 2 + 1: return launch_jg<4, G, true>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 8 * 2 + 0: return launch_jg<8, G, false>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
+    case 8 * 2 + 1: return launch_jg<8, G, true>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, dim3 grid, dim3 block,
-                               size_t lds, hipStream_t s)
+// pair_wpb: 0 = one output per wavefront, 8 wavefronts per workgroup; 4 or 8 =
+// two outputs per wavefront (H even; the caller checks) with that many
+// wavefronts per workgroup
+hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, int pair_wpb, dim3 grid,
+                               dim3 block, size_t lds, hipStream_t s)
 {
     const int units = p.k * 4 * (p.I / 16);       // float32 a[b] in 16-byte units
     const int ncp = (units + 511) / 512;
     if (groups == 1)
-        return launch_g<1>(p, jb, out_bf16, ncp, grid, block, lds, s);
+        return launch_g<1>(p, jb, out_bf16, pair_wpb, ncp, grid, block, lds, s);
     if (groups == 2)
-        return launch_g<2>(p, jb, out_bf16, ncp, grid, block, lds, s);
+        return launch_g<2>(p, jb, out_bf16, pair_wpb, ncp, grid, block, lds, s);
     if (groups == 4)
-        return launch_g<4>(p, jb, out_bf16, ncp, grid, block, lds, s);
+        return launch_g<4>(p, jb, out_bf16, pair_wpb, ncp, grid, block, lds, s);
     return hipErrorInvalidValue;
 }
 

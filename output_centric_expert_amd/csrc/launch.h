@@ -38,6 +38,8 @@ struct Tuning {
     int dn_lanegroups = 1; // down (staged): 1 = short rows share a wavefront among 2 or 4 slots
     int dn_onepass = 1; // down (staged, one output per wavefront): 1 = straight-line kernel when the
                         // token's slots form one group and a row is one chunk per lane
+    int dn_pair = 1;    // one-pass down, MXFP4 at B > 1 (H even): 1 = two neighbouring outputs per
+                        // wavefront sharing each read of a; 0 = one
     int gu_grid = 1024; // grouped gate/up: at most this many workgroups walk the items of the routed
                         // experts (0 = one workgroup per item of all E experts, empty ones included)
     int dn_grid = 2048; // expert-major down: the same for its items
@@ -77,7 +79,7 @@ size_t gate_up_grouped_lds(int B, int k, int E, bool wide);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 // One-pass down (float32 a, streaming loads, 8 wavefronts per workgroup): k = groups * jb slots,
 // rows of at most 64/groups chunks; hipErrorInvalidValue for a (jb, groups) it has no kernel for.
-hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, dim3 grid, dim3 block,
+hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, int pair_wpb, dim3 grid, dim3 block,
                                size_t lds, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -523,6 +523,7 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_umax") && v >= 1 && v <= 8) t.dn_umax = (int)v;
         else if (!strcmp(tok, "dn_lanegroups") && (v == 0 || v == 1)) t.dn_lanegroups = (int)v;
         else if (!strcmp(tok, "dn_onepass") && (v == 0 || v == 1)) t.dn_onepass = (int)v;
+        else if (!strcmp(tok, "dn_pair") && (v == 0 || v == 1)) t.dn_pair = (int)v;
         else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;
         else if (!strcmp(tok, "gu_grid") && v >= 0 && v <= 65536) t.gu_grid = (int)v;
         else if (!strcmp(tok, "dn_grid") && v >= 0 && v <= 65536) t.dn_grid = (int)v;

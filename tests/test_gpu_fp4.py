@@ -170,6 +170,26 @@ def test_fp4_exact_fit_neuron_block_order(shape):
     check_f32(out, ref, f"mxfp4 gu_order=2 {shape}")
 
 
+@pytest.mark.parametrize("shape", [(8, 128, 8, 2048, 768), (4, 40, 4, 1024, 256), (2, 16, 2, 256, 64),
+                                   (3, 20, 4, 96, 160), (6, 64, 8, 512, 1024), (16, 64, 2, 2048, 256)],
+                         ids=lambda s: "B{}_E{}_k{}_H{}_I{}".format(*s))
+def test_fp4_down_two_outputs_per_wavefront(shape):
+    """MXFP4: the one-pass down with two neighbouring outputs per wavefront (default at B > 1;
+    workgroups of 4 wavefronts, or of 8 once B*H/16 >= 2048 as in the last shape) gives the same
+    floats as with one (dn_pair=0), in float32 and bf16 output, and matches the oracle."""
+    B = shape[0]
+    L = small(*shape, seed=sum(shape) + 7)
+    got = {}
+    for spec in ("dn_pair=1", "dn_pair=0"):
+        with md.tuned(spec):
+            got[spec] = (run(L), run(L, out_dtype=torch.bfloat16))
+    for t1, t0 in zip(got["dn_pair=1"], got["dn_pair=0"]):
+        assert torch.equal(t1.view(torch.int16 if t1.dtype == torch.bfloat16 else torch.int32),
+                           t0.view(torch.int16 if t0.dtype == torch.bfloat16 else torch.int32)), shape
+    ref, _ = oracle_tokens(L, list(range(B)))
+    check_f32(got["dn_pair=1"][0], ref, f"mxfp4 down pairs {shape}")
+
+
 SHAPES = [
     (1, 4, 2, 32, 32),        # one MX block per row: a single 16-byte chunk
     (3, 6, 3, 96, 160),       # rows much shorter than a wave
@@ -196,7 +216,7 @@ def test_fp4_ragged_shapes(shape):
 @pytest.mark.parametrize("spec", ["gu_umax=1,dn_umax=1", "dn_stage=0", "dn_stage=0,dn_umax=8", "gu_wpb=1,dn_wpb=3",
                                   "gu_group=1", "dn_group=1", "dn_lanegroups=0", "dn_umax=2", "gu_exact=0,gu_umax=1",
                                   "dn_onepass=0", "dn_onepass=0,dn_lanegroups=0", "gu_exact=0", "gu_order=2",
-                                  "gu_pair=0"])
+                                  "gu_pair=0", "dn_pair=0"])
 def test_fp4_tuning_variants_keep_parity(spec):
     for shape in [(1, 128, 8, 2048, 768), (3, 6, 3, 96, 160), (2, 3, 2, 16448, 64), (4, 40, 4, 2048, 256)]:
         L = small(*shape, seed=3)
