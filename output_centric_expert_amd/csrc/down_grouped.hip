@@ -361,12 +361,23 @@ __device__ __forceinline__ DnGroupW staged_dn_group(const u32x4* tb, const DnRow
 // row stride (0 for a wavefront past H, which reads row H-1 throughout); sq0:
 // the scale row of the lane's block-load row slot ((lane / 2) % (16*RT)); tb:
 // the wavefront's LDS region.
-template <int NTL, int RT, bool A_BF16, bool FP4>
+//
+// NH = 2 (float32 a): 2*NTL tiles in one pass over the rows, in two halves of
+// NTL tiles that take turns in the two LDS buffers of NTL tiles: each K group
+// is decoded once and multiplied with half 0's a (buffer 0), then, after a
+// barrier, with half 1's a (buffer 1). The a of a half is requested one K
+// group ahead (two half-groups ahead, as with NH = 1). So 2*NTL tiles of
+// slots read the rows once, with the LDS of an NTL-tile pass; per output the
+// MFMAs, their operands and their order are those of the NTL-tile passes, so
+// the results are the same floats.
+template <int NTL, int RT, bool A_BF16, bool FP4, int NH = 1>
 __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const DnRow<RT>& r, const uint8_t* q0,
                                                       size_t rstride, const uint8_t* sq0, const int* slots, int count,
                                                       int t0, u32x4* xs, u32x4* tb, bool store, int h0, float* y)
 {
+    static_assert(NH == 1 || (NH == 2 && !A_BF16), "two halves only for float32 a");
     constexpr int GPS = DnStep<FP4, RT>::kGroups;
+    constexpr int NT = NH * NTL;                  // tiles of the pass
     const int I = p.I;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -374,30 +385,32 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
     const int lc = tid % 16;
     constexpr int kHalf = NTL * kDnUnits;
     constexpr int kBuf = (A_BF16 ? 1 : 2) * kHalf;
-    int ls[NTL];
-    int bj[NTL];
+    int ls[NT];
+    int bj[NT];
 #pragma unroll
-    for (int tt = 0; tt < NTL; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
         const int sl = (t0 + tt) * 16 + lcol;
         ls[tt] = slots[sl < count ? sl : count - 1];
         const int si = (t0 + tt) * 16 + r.col;
         bj[tt] = slots[si < count ? si : count - 1];
     }
-    f32x4 d[RT][NTL];
+    f32x4 d[RT][NT];
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int tt = 0; tt < NTL; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
             d[t][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int ngroups = r.nsteps / 4;
     const int nst = ngroups / GPS;                // 256-byte steps (even for MXFP8)
     const uint32_t lo = (uint32_t)(lane / 16) * (uint32_t)rstride + 16u * (uint32_t)(lane % 16);
     const uint32_t rs4 = 4u * (uint32_t)rstride;
-    ARaw<A_BF16> raw[2][NTL];                     // a of groups g+1 and g+2, by group parity
-    auto load_a = [&](ARaw<A_BF16> (&dst)[NTL], int g) {
+    // NH = 1: a of groups g+1 and g+2, by group parity; NH = 2: a of half 0
+    // and of half 1 (of the next K group, or of this one until it is in LDS)
+    ARaw<A_BF16> raw[2][NTL];
+    auto load_a = [&](ARaw<A_BF16> (&dst)[NTL], int g, int half) {
 #pragma unroll
         for (int tt = 0; tt < NTL; ++tt)
-            dst[tt] = load_a8<A_BF16>(p.a, ls[tt], g * 128 + 8 * lc, I);
+            dst[tt] = load_a8<A_BF16>(p.a, ls[half * NTL + tt], g * 128 + 8 * lc, I);
     };
     auto put_a = [&](const ARaw<A_BF16> (&src)[NTL], u32x4* buf) {
 #pragma unroll
@@ -411,37 +424,34 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
         }
     };
     DnStep<FP4, RT> sw;
-    load_a(raw[0], 0);
-    load_a(raw[1], 1);
+    if constexpr (NH == 1) {
+        load_a(raw[0], 0, 0);
+        load_a(raw[1], 1, 0);
+    } else {
+        load_a(raw[0], 0, 0);
+        load_a(raw[1], 0, 1);
+    }
     load_dn_step<FP4, RT>(q0, lo, rs4, 0, sw);
     u32x2 sb = load_scale_block(sq0, 0, lane);
     put_a(raw[0], xs);
     __syncthreads();
-    // a of group g+2 into set P = g & 1 (unconditional: the last groups re-read
-    // the last group's a, so no load sits behind a branch)
+    // NH = 1: a of group g+2 into set P = g & 1; NH = 2: half 0's a of group
+    // g+1 into set 0 (unconditional: the last groups re-read the last group's
+    // a, so no load sits behind a branch)
     // (the scheduling barrier keeps the loads issued ahead of the group's other
     // work: the split of the next group's a would otherwise be hoisted above
     // them and wait for every older load first)
     auto aload = [&](auto par, int g) {
         constexpr int P = decltype(par)::value;
-        load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1);
+        if constexpr (NH == 1)
+            load_a(raw[P], g + 2 < ngroups ? g + 2 : ngroups - 1, 0);
+        else
+            load_a(raw[0], g + 1 < ngroups ? g + 1 : ngroups - 1, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    // group g = step group h with the scale codes of the lane's RT rows: the
-    // MFMAs on buffer g&1, then a of g+1 (set 1-P) split into the other buffer
-    auto group = [&](auto par, int g, int h, const uint32_t (&codes)[RT]) {
-        constexpr int P = decltype(par)::value;
-        DnGroupW w[RT];
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-            w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, codes[t]);
-        const u32x4* xb = xs + (g & 1) * kBuf;
-        bf16x8 aw[RT][4];
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                aw[t][q] = dn_decode<FP4>(w[t], q);
+    // the MFMAs of the decoded group on one LDS buffer, into tiles T0 .. T0+NTL-1
+    auto mfmas = [&](auto tfirst, const bf16x8 (&aw)[RT][4], const u32x4* xb) {
+        constexpr int T0 = decltype(tfirst)::value;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = 4 * r.kb + q;
@@ -451,17 +461,54 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
                 const bf16x8 bh = __builtin_bit_cast(bf16x8, xb[u]);
 #pragma unroll
                 for (int t = 0; t < RT; ++t)
-                    d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bh, d[t][tt], 0, 0, 0);
+                    d[t][T0 + tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bh, d[t][T0 + tt], 0, 0, 0);
                 if constexpr (!A_BF16) {
                     const bf16x8 bl = __builtin_bit_cast(bf16x8, xb[kHalf + u]);
 #pragma unroll
                     for (int t = 0; t < RT; ++t)
-                        d[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bl, d[t][tt], 0, 0, 0);
+                        d[t][T0 + tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t][q], bl, d[t][T0 + tt], 0, 0, 0);
                 }
             }
         }
-        put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
-        __syncthreads();                          // buffer g&1 read by all, buffer (g+1)&1 written
+    };
+    // group g = step group h with the scale codes of the lane's RT rows. NH = 1:
+    // the MFMAs on buffer g&1, then a of g+1 (set 1-P) split into the other
+    // buffer. NH = 2: half 0 on buffer 0, half 1's a (set 1) into buffer 1; then
+    // half 1's a of group g+1 requested and half 1 on buffer 1, half 0's a of
+    // group g+1 (set 0) into buffer 0.
+    auto decode = [&](int h, const uint32_t (&codes)[RT], bf16x8 (&aw)[RT][4]) {
+        DnGroupW w[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            w[t] = staged_dn_group<FP4, RT>(tb, r, h, t, codes[t]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                aw[t][q] = dn_decode<FP4>(w[t], q);
+    };
+    auto group = [&](auto par, int g, int h, const uint32_t (&codes)[RT]) {
+        constexpr int P = decltype(par)::value;
+        bf16x8 aw[RT][4];
+        decode(h, codes, aw);
+        if constexpr (NH == 1) {
+            mfmas(std::integral_constant<int, 0>{}, aw, xs + (g & 1) * kBuf);
+            put_a(raw[1 - P], xs + ((g + 1) & 1) * kBuf);
+            __syncthreads();                      // buffer g&1 read by all, buffer (g+1)&1 written
+        } else {
+            mfmas(std::integral_constant<int, 0>{}, aw, xs);
+            put_a(raw[1], xs + kBuf);
+            __syncthreads();                      // buffer 0 read by all, buffer 1 written
+            load_a(raw[1], g + 1 < ngroups ? g + 1 : ngroups - 1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // decoded again from the staged step rather than held across the
+            // barrier (the registers are the scarce part)
+            bf16x8 aw1[RT][4];
+            decode(h, codes, aw1);
+            mfmas(std::integral_constant<int, NTL>{}, aw1, xs + kBuf);
+            put_a(raw[0], xs);
+            __syncthreads();                      // buffer 1 read by all, buffer 0 written
+        }
     };
     constexpr auto P0 = std::integral_constant<int, 0>{};
     constexpr auto P1 = std::integral_constant<int, 1>{};
@@ -533,7 +580,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
     if (!store)
         return;
 #pragma unroll
-    for (int tt = 0; tt < NTL; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
         if ((t0 + tt) * 16 + r.col < count) {
             const int s = bj[tt];
             const float wgt = p.w[s];
@@ -587,7 +634,17 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
         // LDS for the same)
         constexpr int kCap = A_BF16 ? 3 : 2;
         const int mt = max_tiles < kCap ? max_tiles : kCap;
-        for (int t0 = 0; t0 < ntiles; t0 += mt) {
+        int t0 = 0;
+        if constexpr (!A_BF16) {
+            // float32 a, more than 2 tiles: 4 per pass over the rows in two
+            // halves of 2 (the last may be partly empty), then the rest
+            if (mt == 2 && p.split != 0) {
+                for (; ntiles - t0 > 2; t0 += 4)
+                    expert_down_pass_wide<2, RT, A_BF16, FP4, 2>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb,
+                                                                 store, h0, y);
+            }
+        }
+        for (; t0 < ntiles; t0 += mt) {
             const int nt = ntiles - t0 < mt ? ntiles - t0 : mt;
             if (nt == 1) {
                 expert_down_pass_wide<1, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);

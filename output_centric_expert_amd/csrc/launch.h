@@ -26,6 +26,8 @@ struct Tuning {
                         // as fit in 64 KiB of LDS)
     int gu_wide = 1;    // expert-grouped gate/up, MFMA path: 1 = weight rows read in 256-byte runs per
                         // row and moved to the operand layout through LDS; 0 = 128-byte tile slices
+    int dn_split = 1;   // expert-major down, float32 a, wide loads: 1 = experts with 33..64 slots in one
+                        // pass over their rows (two halves of 2 tiles), 0 = passes of 2 tiles
     int dn_rt = 2;      // expert-major down: 16-row tiles per wavefront (1 or 2; 2 lets each LDS read
                         // of the slots' a serve two MFMAs)
     int dn_wide = 1;    // expert-major down: 1 = weight rows read in 256-byte runs per row and moved to the
@@ -71,6 +73,7 @@ struct DownArgs {
     int B, E, k, H, I;
     float inv_cpr;          // 1 / (I/16), for the chunk -> (slot, offset) split
     int wfmt;               // kMXFP8 or kMXFP4 (codes [E][H][I/2])
+    int split;              // expert-major down, float32 a: 1 = up to 4 tiles per pass in two halves
 };
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);

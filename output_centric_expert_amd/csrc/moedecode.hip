@@ -114,8 +114,11 @@ hipError_t down_launch(const moed::DownArgs& p, bool a_bf16, bool out_bf16, cons
 {
     if (y) {
         const bool wide = down_wide(t, p.I, p.wd_s);
-        if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16, wide))
-            return moed::launch_down_grouped(p, a_bf16, out_bf16, y, mt, t.dn_rt, wide, t.dn_grid, s);
+        if (int mt = pick_down_tiles(t, p.B, p.E, p.k, a_bf16, wide)) {
+            moed::DownArgs q = p;
+            q.split = t.dn_split;
+            return moed::launch_down_grouped(q, a_bf16, out_bf16, y, mt, t.dn_rt, wide, t.dn_grid, s);
+        }
     }
     return moed::launch_down(p, a_bf16, out_bf16, t, s);
 }
@@ -190,6 +193,7 @@ moed::DownArgs down_args(const void* a, const int32_t* ids, const float* w, cons
     p.B = B; p.E = E; p.k = k; p.H = H; p.I = I;
     p.inv_cpr = 1.0f / (float)(I / 16);
     p.wfmt = wfmt;
+    p.split = 0;
     return p;
 }
 
@@ -524,6 +528,7 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_lanegroups") && (v == 0 || v == 1)) t.dn_lanegroups = (int)v;
         else if (!strcmp(tok, "dn_onepass") && (v == 0 || v == 1)) t.dn_onepass = (int)v;
         else if (!strcmp(tok, "dn_pair") && (v == 0 || v == 1)) t.dn_pair = (int)v;
+        else if (!strcmp(tok, "dn_split") && (v == 0 || v == 1)) t.dn_split = (int)v;
         else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;
         else if (!strcmp(tok, "gu_grid") && v >= 0 && v <= 65536) t.gu_grid = (int)v;
         else if (!strcmp(tok, "dn_grid") && v >= 0 && v <= 65536) t.dn_grid = (int)v;

@@ -165,6 +165,8 @@ def test_tuning_spec_parser(lib):
     assert _init(lib, b"gu_pair=2") == md.MOED_ERR_SHAPE
     assert _init(lib, b"dn_pair=0") == md.MOED_OK
     assert _init(lib, b"dn_pair=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"dn_split=0") == md.MOED_OK
+    assert _init(lib, b"dn_split=2") == md.MOED_ERR_SHAPE
     assert _init(lib, b"gu_order=0") == md.MOED_OK
     assert _init(lib, b"gu_order=2") == md.MOED_OK
     assert _init(lib, b"gu_order=3") == md.MOED_ERR_SHAPE

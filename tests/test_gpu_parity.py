@@ -831,6 +831,8 @@ DOWN_WIDE = [
     (20, 4, 3, 128, 2560),    # 5 step pairs / 5 steps
     (16, 8, 8, 64, 7168),     # 14 step pairs per row
     (24, 6, 4, 2080, 544),    # I not a multiple of 512: the 128-byte slices either way
+    (40, 1, 1, 64, 512),      # 40 slots: 3 tiles in one pass of two halves, the last half partly empty
+    (64, 1, 1, 128, 1024),    # 64 slots: 4 tiles in one pass of two halves
 ]
 
 
@@ -840,9 +842,10 @@ DOWN_WIDE = [
 def test_expert_major_down_wide_loads(shape, wformat, rt):
     """The expert-major down's wide weight loads (256-byte runs per row, moved to the operand
     layout through LDS, scales fetched in 16-byte blocks and handed out by ds_bpermute) feed
-    every MFMA the codes and scales the 128-byte slices do, in the same order:
-    the layer output is the same floats for float32 and bf16 intermediates (an invalid id on
-    the last token gives NaN there on both), and within tolerance of the oracle."""
+    every MFMA the codes and scales the 128-byte slices do, in the same order, with passes of 2
+    float32 tiles or (the default) of up to 4 in two halves: the layer output is the same floats
+    for float32 and bf16 intermediates (an invalid id on the last token gives NaN there on all),
+    and within tolerance of the oracle."""
     B, E, k, H, I = shape
     L = synth.make_layer(synth.LayerShape("dwide", B, E, k, H, I), seed=sum(shape) + 41, device="cuda",
                          wformat=wformat)
@@ -851,21 +854,24 @@ def test_expert_major_down_wide_loads(shape, wformat, rt):
     x, _, wd = md.layer_device_inputs(L)
     idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
     got = {}
+    variants = ("dn_wide=0", "dn_wide=1,dn_split=0", "dn_wide=1")
     try:
-        for wide in (0, 1):
-            md.set_default_tuning(f"dn_group=1,dn_rt={rt},dn_wide={wide}")
-            say(f"down wide loads {shape} {wformat} rt={rt} wide={wide}")
+        for v in variants:
+            md.set_default_tuning(f"dn_group=1,dn_rt={rt},{v}")
+            say(f"down wide loads {shape} {wformat} rt={rt} {v}")
             for dt in (torch.float32, torch.bfloat16):
-                got[wide, dt] = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
-                                              out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
+                got[v, dt] = md.moe_decode(x, idd, wd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                                           out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
             torch.cuda.synchronize()
     finally:
         md.set_default_tuning(None)
     for dt in (torch.float32, torch.bfloat16):
-        o0, o1 = got[0, dt], got[1, dt]
-        assert torch.equal(torch.isnan(o0), torch.isnan(o1))
-        assert torch.equal(o0[:B - 1].view(torch.int32), o1[:B - 1].view(torch.int32)), f"{shape} {wformat} {dt}"
-        assert torch.isnan(o1[B - 1]).all()
-    toks = [0, B // 2, B - 2]
+        o0 = got[variants[0], dt]
+        for v in variants[1:]:
+            o1 = got[v, dt]
+            assert torch.equal(torch.isnan(o0), torch.isnan(o1))
+            assert torch.equal(o0[:B - 1].view(torch.int32), o1[:B - 1].view(torch.int32)), f"{shape} {wformat} {dt} {v}"
+            assert torch.isnan(o1[B - 1]).all()
+    toks = sorted({0, B // 2, B - 2})
     ref, _ = oracle_tokens(L, toks, ids=ids, wformat=wformat)
-    check_f32(got[1, torch.float32][toks], ref, f"down wide {shape} {wformat}")
+    check_f32(got["dn_wide=1", torch.float32][toks], ref, f"down wide {shape} {wformat}")
