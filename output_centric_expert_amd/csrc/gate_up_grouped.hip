@@ -426,7 +426,21 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         }
     } else {
         // MXFP4: one scale block per step; the next step and block are
-        // requested during the step's third group
+        // requested at the step start, a whole step (four groups) ahead. Every
+        // x the step waits for is requested before them: x of the step's groups
+        // 2..4 ahead of its rows (set (g % 4) of xq4 holds x of group g), x of
+        // group 1 a step earlier, x of the next step's group 1 during group 2
+        // (first waited for after the next step's rows are in).
+        u32x4 xq4[4][NTL];
+#pragma unroll
+        for (int tt = 0; tt < NTL; ++tt)
+            xq4[1][tt] = xq[1][tt];
+        auto xput = [&](int g, const u32x4 (&src)[NTL], int h, float gsc, float usc) {
+            group_mfma<NTL, FP4>(staged_group<FP4>(tb, r, h, gsc, usc), xs + (g & 1) * kBuf, r, dg, du);
+            put_x(src, g + 1 < ngroups ? g + 1 : ngroups - 1);
+            __syncthreads();
+        };
+        auto clampg = [&](int g) { return g < ngroups ? g : ngroups - 1; };
         for (int s = 0; s < nst; ++s) {
             const int g0 = 4 * s;
             // all four groups' scales at the step start (four groups per step: taking
@@ -441,17 +455,20 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
             gsc[3] = block_scale<3>(sb, r.col, r.kb);
             usc[3] = block_scale<3>(sb, 16 + r.col, r.kb);
             stage_step<FP4>(sw, tb, lane);
+            load_x(xq4[2], clampg(g0 + 2));
+            load_x(xq4[3], clampg(g0 + 3));
+            load_x(xq4[0], clampg(g0 + 4));
+            __builtin_amdgcn_sched_barrier(0);
             const int sn = s + 1 < nst ? s + 1 : s;
-            xload(P0, g0);
-            group(P0, g0, 0, gsc[0], usc[0]);
-            xload(P1, g0 + 1);
-            group(P1, g0 + 1, 1, gsc[1], usc[1]);
-            xload(P0, g0 + 2);
             sw = load_step<FP4>(gq0, uq0, lo, rs4, sn);
             sb = load_scale_block(sq0, sn, lane);
-            group(P0, g0 + 2, 2, gsc[2], usc[2]);
-            xload(P1, g0 + 3);
-            group(P1, g0 + 3, 3, gsc[3], usc[3]);
+            __builtin_amdgcn_sched_barrier(0);
+            xput(g0, xq4[1], 0, gsc[0], usc[0]);
+            xput(g0 + 1, xq4[2], 1, gsc[1], usc[1]);
+            load_x(xq4[1], clampg(g0 + 5));
+            __builtin_amdgcn_sched_barrier(0);
+            xput(g0 + 2, xq4[3], 2, gsc[2], usc[2]);
+            xput(g0 + 3, xq4[0], 3, gsc[3], usc[3]);
         }
     }
     if (store)
