@@ -312,20 +312,14 @@ constexpr int kDnWideUnits = 16 * RT * 16;
 // q0: the wavefront's first row (wave-uniform); lo: this lane's byte offset
 // (lane/16)*rstride + 16*(lane%16); rs4 = 4*rstride. A uniform base plus 32-bit
 // lane offsets keeps the addresses of the 4*RT loads in a few registers.
-// STREAM: non-temporal loads (the rows are read once per item).
-template <bool FP4, int RT, bool STREAM = false>
+template <bool FP4, int RT>
 __device__ __forceinline__ void load_dn_step(const uint8_t* q0, uint32_t lo, uint32_t rs4, int step,
                                              DnStep<FP4, RT>& w)
 {
     const uint32_t base = lo + 256u * (uint32_t)step;
 #pragma unroll
-    for (int i = 0; i < 4 * RT; ++i) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(q0 + (base + (uint32_t)i * rs4));
-        if constexpr (STREAM)
-            w.v[i] = __builtin_nontemporal_load(src);
-        else
-            w.v[i] = *src;
-    }
+    for (int i = 0; i < 4 * RT; ++i)
+        w.v[i] = *reinterpret_cast<const u32x4*>(q0 + (base + (uint32_t)i * rs4));
 }
 
 template <bool FP4, int RT>
@@ -376,7 +370,7 @@ __device__ __forceinline__ DnGroupW staged_dn_group(const u32x4* tb, const DnRow
 // slots read the rows once, with the LDS of an NTL-tile pass; per output the
 // MFMAs, their operands and their order are those of the NTL-tile passes, so
 // the results are the same floats.
-template <int NTL, int RT, bool A_BF16, bool FP4, int NH = 1, bool STREAM = false>
+template <int NTL, int RT, bool A_BF16, bool FP4, int NH = 1>
 __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const DnRow<RT>& r, const uint8_t* q0,
                                                       size_t rstride, const uint8_t* sq0, const int* slots, int count,
                                                       int t0, u32x4* xs, u32x4* tb, bool store, int h0, float* y)
@@ -437,7 +431,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
         load_a(raw[0], 0, 0);
         load_a(raw[1], 0, 1);
     }
-    load_dn_step<FP4, RT, STREAM>(q0, lo, rs4, 0, sw);
+    load_dn_step<FP4, RT>(q0, lo, rs4, 0, sw);
     u32x2 sb = load_scale_block(sq0, 0, lane);
     put_a(raw[0], xs);
     __syncthreads();
@@ -533,7 +527,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
             }
             stage_dn_step<FP4, RT>(sw, tb, lane);
             aload(P0, g0);
-            load_dn_step<FP4, RT, STREAM>(q0, lo, rs4, s + 1, sw);
+            load_dn_step<FP4, RT>(q0, lo, rs4, s + 1, sw);
             __builtin_amdgcn_sched_barrier(0);
             group(P0, g0, 0, c0);
             aload(P1, g0 + 1);
@@ -546,7 +540,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
             stage_dn_step<FP4, RT>(sw, tb, lane);
             const int sn = s + 2 < nst ? s + 2 : s + 1;
             aload(P0, g0 + 2);
-            load_dn_step<FP4, RT, STREAM>(q0, lo, rs4, sn, sw);
+            load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
             sb = load_scale_block(sq0, sn / 2, lane);
             __builtin_amdgcn_sched_barrier(0);
             group(P0, g0 + 2, 0, c0);
@@ -575,7 +569,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
             aload(P1, g0 + 1);
             group(P1, g0 + 1, 1, sc[1]);
             aload(P0, g0 + 2);
-            load_dn_step<FP4, RT, STREAM>(q0, lo, rs4, sn, sw);
+            load_dn_step<FP4, RT>(q0, lo, rs4, sn, sw);
             sb = load_scale_block(sq0, sn, lane);
             __builtin_amdgcn_sched_barrier(0);
             group(P0, g0 + 2, 2, sc[2]);
@@ -603,7 +597,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
 // list sits wl_off ints into the dynamic LDS and the workgroups walk the
 // items of the routed experts with a stride of the grid size; wl_off < 0: one
 // item per workgroup over all E experts (the grid is E * blocks).
-template <int RT, bool A_BF16, bool FP4, bool WIDE, bool STREAM = false>
+template <int RT, bool A_BF16, bool FP4, bool WIDE>
 __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, int max_tiles, int e, int hb,
                                                  int count, const int* slots, u32x4* xs)
 {
@@ -646,18 +640,18 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
             // halves of 2 (the last may be partly empty), then the rest
             if (mt == 2 && p.split != 0) {
                 for (; ntiles - t0 > 2; t0 += 4)
-                    expert_down_pass_wide<2, RT, A_BF16, FP4, 2, STREAM>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb,
+                    expert_down_pass_wide<2, RT, A_BF16, FP4, 2>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb,
                                                                       store, h0, y);
             }
         }
         for (; t0 < ntiles; t0 += mt) {
             const int nt = ntiles - t0 < mt ? ntiles - t0 : mt;
             if (nt == 1) {
-                expert_down_pass_wide<1, RT, A_BF16, FP4, 1, STREAM>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<1, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             } else if (nt == 2) {
-                expert_down_pass_wide<2, RT, A_BF16, FP4, 1, STREAM>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<2, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             } else if constexpr (A_BF16) {
-                expert_down_pass_wide<3, RT, A_BF16, FP4, 1, STREAM>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
+                expert_down_pass_wide<3, RT, A_BF16, FP4>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb, store, h0, y);
             }
         }
         return;
@@ -700,9 +694,7 @@ moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
         const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
         if (count == 0)
             continue;                             // whole workgroup (only without the work list)
-        // wide MXFP8 rows stream past the L2 (each is read once per item; measured
-        // faster for the layer), MXFP4 ones through it (measured faster)
-        expert_down_item<RT, A_BF16, FP4, WIDE, !FP4>(p, y, max_tiles, e, hb, count, slots, xs);
+        expert_down_item<RT, A_BF16, FP4, WIDE>(p, y, max_tiles, e, hb, count, slots, xs);
         __syncthreads();                          // the next item rewrites the slot list and the a tiles
     }
 }
