@@ -1,7 +1,8 @@
 // Down for large decode batches (tokens sharing experts): expert-major, so
-// each routed down row is read and decoded once per workgroup pass (up to 48
-// slots with a float32 intermediate, 64 with bf16) instead of once per
-// (token, slot).
+// each routed down row is read and decoded once per workgroup pass instead of
+// once per (token, slot). A pass takes up to 4 tiles of 16 slots with the
+// wide loads and a float32 intermediate (two halves of 2 tiles), 3 with bf16;
+// with the 128-byte slices 3 tiles of float32, 4 of bf16.
 //
 // Step 1, moe_down_expert_kernel: a workgroup owns (expert e, RT*64 output
 // rows), four wavefronts of RT tiles of 16 rows each. It compacts the list of slots
@@ -641,7 +642,7 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
             if (mt == 2 && p.split != 0) {
                 for (; ntiles - t0 > 2; t0 += 4)
                     expert_down_pass_wide<2, RT, A_BF16, FP4, 2>(p, r, q0, rstride, sq0, slots, count, t0, xs, tb,
-                                                                      store, h0, y);
+                                                                 store, h0, y);
             }
         }
         for (; t0 < ntiles; t0 += mt) {
