@@ -204,9 +204,10 @@ def main():
 
 def down_kernel_name(L):
     """The down kernel(s) the built-in launch table picks inside moe_decode: the expert-major
-    kernel plus its combine once B*k >= 2E, else the per-output one-pass kernel for float32 a when
-    the token's k slots form one lane-group set and a row is at most one chunk per lane, else the
-    staged per-output kernel."""
+    kernel plus its combine once B*k >= 2E; else, for float32 a when the token's k slots form one
+    lane-group set and a row is at most one chunk per lane, the blocks form of the one-pass kernel
+    once B*k >= E (H a multiple of 64) and the one-pass kernel below; else the staged per-output
+    kernel."""
     sh = L.shape
     if sh.B * sh.k >= 2 * sh.E:
         return "moe_down_expert_kernel + moe_down_combine_kernel"
@@ -215,8 +216,11 @@ def down_kernel_name(L):
     while groups < 4 and cpr <= 64 // (2 * groups) and 2 * groups <= sh.k:
         groups *= 2
     jb = sh.k // groups
-    if sh.k == groups * jb and jb & (jb - 1) == 0 and jb <= 8 and cpr <= 64 // groups and \
-            (groups > 1 or sh.B <= 2 or sh.B * sh.k < sh.E):
+    one_pass_shape = sh.k == groups * jb and jb & (jb - 1) == 0 and jb <= 8 and cpr <= 64 // groups and \
+        sh.k * sh.I * 4 <= 65536
+    if one_pass_shape and sh.B * sh.k >= sh.E and sh.H % 64 == 0 and not (L.wformat == "mxfp4" and jb == 8):
+        return "moe_down_blocks_kernel"
+    if one_pass_shape and sh.B * sh.k < sh.E and (groups > 1 or sh.B <= 2):
         return "moe_down_onepass_kernel"
     return "moe_down_staged_kernel"
 

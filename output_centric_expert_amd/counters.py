@@ -56,10 +56,10 @@ def pick(per: dict, needle: str):
 # The kernels one call of each layer step launches: the per-slot gate/up (generic or exact-fit) or
 # the expert-grouped one (128-byte tile slices or wide loads); the per-output down (staged,
 # one-pass, several rows per wave, or direct), or the expert-major down plus its combine.
-STEP_KERNELS = {"gate_up": ("moe_gate_up_kernel", "moe_gate_up_exact_kernel", "moe_gate_up_grouped_kernel",
-                            "moe_gate_up_grouped_wide_kernel"),
-                "down": ("moe_down_kernel", "moe_down_staged_kernel", "moe_down_onepass_kernel", "moe_down_rows_kernel",
-                         "moe_down_expert_kernel", "moe_down_combine_kernel")}
+STEP_KERNELS = {"gate_up": ("moe_gate_up_kernel", "moe_gate_up_exact_kernel", "moe_gate_up_exact_pair_kernel",
+                            "moe_gate_up_grouped_kernel", "moe_gate_up_grouped_wide_kernel"),
+                "down": ("moe_down_kernel", "moe_down_staged_kernel", "moe_down_onepass_kernel", "moe_down_blocks_kernel",
+                         "moe_down_rows_kernel", "moe_down_expert_kernel", "moe_down_combine_kernel")}
 
 
 def step_counter(per: dict, step: str):

@@ -390,6 +390,18 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
     // 17.7 us at k=8, I=768; at B*k >= E four rows stay faster)
     const int rows = (long)p.B * p.k >= (long)p.E ? 4 : (p.B >= 2 ? 2 : 1);
     const int per_group = p.k / groups;
+    // blocks form of the one-pass kernel where tokens share experts, below the
+    // expert-major switch of moe_decode (E <= B*k < 2E; measured there), for the
+    // one-pass shapes with H a multiple of 64; it replaces the four-row and
+    // lane-group kernels with the same floats per output. Not for MXFP4 rows
+    // of more than 32 chunks (eight slots per lane group: 210 registers, two
+    // wavefronts per SIMD), where it measured slower (B = 16, H = 4096,
+    // I = 1536: down 86.5 vs 81.9 us)
+    const bool one_pass_shape = staged && t.dn_onepass != 0 && !a_bf16 && wpb == 8 && p.k == groups * per_group &&
+                                (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups;
+    if (one_pass_shape && !nt && (long)p.B * p.k < 2L * (long)p.E && p.H % (8 * kDownBlocks) == 0 &&
+        !(fp4 && per_group == 8))
+        return launch_down_blocks(q, per_group, groups, out_bf16, lds, s);
     if (staged && t.dn_onepass != 0 && !a_bf16 && nt && wpb == 8 && p.k == groups * per_group &&
         (per_group & (per_group - 1)) == 0 && per_group <= 8 && cpr <= kWave / groups &&
         (groups > 1 || rows <= 2)) {

@@ -146,6 +146,129 @@ moe_down_onepass_kernel(DownArgs p)
 // kernel takes: I/16 <= 64/G for MXFP8 and <= 128/G for MXFP4.
 constexpr int onepass_max_ncp(int jb, bool fp4) { return fp4 ? jb : (jb >= 2 ? jb / 2 : 1); }
 
+// Blocks form of the one-pass kernel, for batches whose tokens share experts
+// (B*k >= E): a workgroup of 8 wavefronts copies a[b] into LDS once and then
+// takes RS blocks of 8 neighbouring outputs of its token in turn, one output
+// per wavefront per block. The next block's rows are requested before the
+// current block's dots, and the loads are cached: the other tokens routed to
+// an expert read the same rows, and the workgroup order (token fastest, then
+// the output blocks, each XCD a contiguous range) has them read those rows on
+// one XCD at about the same time. Per output the loads, the FMAs, their
+// operands and order, and the reduction are those of the one-pass kernel, so
+// every output is the same float. Measured against the four-outputs-per-
+// wavefront and lane-group kernels it replaces (E = 128, H = 2048, I = 768,
+// down step alone): B = 16 34.5 -> 30.9 us (MXFP8), 30.6 -> 22.4 us (MXFP4);
+// B = 24 46.7 -> 42.3 us, 43.1 -> 30.2 us.
+template <int JB, int G, bool OUT_BF16, bool FP4, int NCP, int RS>
+__global__ void __launch_bounds__(8 * kWave)
+moe_down_blocks_kernel(DownArgs p)
+{
+    extern __shared__ u32x4 a_lds[];
+    constexpr int WPB = 8;
+    constexpr int NTH = WPB * kWave;
+    constexpr int KS = G * JB;                    // slots per token (= p.k)
+    using LG = LaneGroups<G>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = (int)(threadIdx.x / kWave);
+    const int blk = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    const int b = blk % p.B;
+    const int hb = (blk / p.B) * (RS * WPB);      // the workgroup's first output
+    const int cpr16 = p.I / 16;
+    const int cpr = FP4 ? p.I / 32 : cpr16;
+    const int nunits = KS * 4 * cpr16;
+    const int* ids = p.ids + (size_t)b * KS;
+    const float* wts = p.w + (size_t)b * KS;
+    const u32x4* asrc = static_cast<const u32x4*>(p.a) + (size_t)b * (size_t)nunits;
+
+    // 1) the copy of a[b] (clamped, unconditional loads, as in the one-pass kernel)
+    u32x4 cp[NCP];
+#pragma unroll
+    for (int q = 0; q < NCP; ++q) {
+        const int u = (int)threadIdx.x + q * NTH;
+        cp[q] = asrc[u < nunits ? u : nunits - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2) the token's ids and routing weights, picked per lane group
+    const int g = LG::group(lane);
+    const int lc = LG::chunk(lane);
+    int id_all[KS];
+    float w_all[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+        id_all[t] = ids[t];
+        w_all[t] = wts[t];
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+        asm volatile("" ::"s"(id_all[t]), "s"(w_all[t]));
+    int eid[JB];
+    float wt[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        eid[jj] = id_all[G * jj];
+        wt[jj] = w_all[G * jj];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) {
+            eid[jj] = g == gg ? id_all[gg + G * jj] : eid[jj];
+            wt[jj] = g == gg ? w_all[gg + G * jj] : wt[jj];
+        }
+    }
+    // 3) the rows of block r: weight chunk and scale byte of each of the lane's
+    // slots (an invalid id reads expert 0's row and makes the output NaN; lanes
+    // past the row end re-read its last chunk with factor 0)
+    const size_t row_bytes = FP4 ? (size_t)(p.I / 2) : (size_t)p.I;
+    const int oc = lc < cpr ? lc : cpr - 1;
+    const bool lane_live = lc < cpr;
+    float mask[JB];
+    size_t row0[JB];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+        const bool ok = (unsigned)eid[jj] < (unsigned)p.E;
+        mask[jj] = lane_live ? (ok ? 1.0f : __builtin_nanf("")) : 0.0f;
+        row0[jj] = (size_t)(ok ? eid[jj] : 0) * (size_t)p.H;
+    }
+    u32x4 wq[2][1][JB];
+    uint32_t ws[2][1][JB];
+    auto load_block = [&](int r, u32x4 (&q)[1][JB], uint32_t (&sc)[1][JB]) {
+        const int h = hb + r * WPB + w;
+        const size_t hc = (size_t)(h < p.H ? h : p.H - 1);
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+            const size_t row = row0[jj] + hc;
+            q[0][jj] = reinterpret_cast<const u32x4*>(p.wd_q + row * row_bytes)[oc];
+            sc[0][jj] = p.wd_s[row * (size_t)(p.I / 32) + (FP4 ? oc : oc >> 1)];
+        }
+    };
+    load_block(0, wq[0], ws[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < NCP; ++q) {
+        const int u = (int)threadIdx.x + q * NTH;
+        if (u < nunits)
+            a_lds[u] = cp[q];
+    }
+    __syncthreads();                              // the only barrier
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+        const int cur = r & 1;
+        if (r + 1 < RS)
+            load_block(r + 1, wq[cur ^ 1], ws[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        float acc[1] = {0.0f};
+        down_group_dot_multi<JB, FP4, G, 1>(a_lds, KS, lane, cpr, cpr16, wq[cur], ws[cur], wt, mask, acc);
+        const float v = wave_sum(acc[0]);
+        const int h = hb + r * WPB + w;
+        if (lane == 0 && h < p.H) {
+            const size_t o = (size_t)b * p.H + h;
+            if constexpr (OUT_BF16)
+                static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
+            else
+                static_cast<float*>(p.out)[o] = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);        // one block's loads ahead of its dots, no more
+    }
+}
+
 template <int JB, int G, bool FP4>
 static hipError_t launch_jg(const DownArgs& p, bool out_bf16, int pair_wpb, int ncp, dim3 grid, dim3 block,
                             size_t lds, hipStream_t s)
@@ -213,6 +336,48 @@ static hipError_t launch_g(const DownArgs& p, int jb, bool out_bf16, int pair_wp
     case 8 * 2 + 1: return launch_jg<8, G, true>(p, out_bf16, pair_wpb, ncp, grid, block, lds, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <int JB, int G, bool FP4>
+static hipError_t launch_blocks_jg(const DownArgs& p, bool out_bf16, size_t lds, hipStream_t s)
+{
+    constexpr int MAXN = onepass_max_ncp(JB, FP4);
+    const dim3 grid((unsigned)((long)p.B * (p.H / (8 * kDownBlocks)))), block(8 * kWave);
+    if (out_bf16)
+        hipLaunchKernelGGL((moe_down_blocks_kernel<JB, G, true, FP4, MAXN, kDownBlocks>), grid, block, lds, s, p);
+    else
+        hipLaunchKernelGGL((moe_down_blocks_kernel<JB, G, false, FP4, MAXN, kDownBlocks>), grid, block, lds, s, p);
+    return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_blocks_g(const DownArgs& p, int jb, bool out_bf16, size_t lds, hipStream_t s)
+{
+    const bool fp4 = p.wfmt == kMXFP4;
+    switch (jb * 2 + (fp4 ? 1 : 0)) {
+    case 1 * 2 + 0: return launch_blocks_jg<1, G, false>(p, out_bf16, lds, s);
+    case 1 * 2 + 1: return launch_blocks_jg<1, G, true>(p, out_bf16, lds, s);
+    case 2 * 2 + 0: return launch_blocks_jg<2, G, false>(p, out_bf16, lds, s);
+    case 2 * 2 + 1: return launch_blocks_jg<2, G, true>(p, out_bf16, lds, s);
+    case 4 * 2 + 0: return launch_blocks_jg<4, G, false>(p, out_bf16, lds, s);
+    case 4 * 2 + 1: return launch_blocks_jg<4, G, true>(p, out_bf16, lds, s);
+    case 8 * 2 + 0: return launch_blocks_jg<8, G, false>(p, out_bf16, lds, s);
+    case 8 * 2 + 1: return launch_blocks_jg<8, G, true>(p, out_bf16, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_down_blocks(const DownArgs& p, int jb, int groups, bool out_bf16, size_t lds, hipStream_t s)
+{
+    if (p.H % (8 * kDownBlocks) != 0)
+        return hipErrorInvalidValue;
+    if (groups == 1)
+        return launch_blocks_g<1>(p, jb, out_bf16, lds, s);
+    if (groups == 2)
+        return launch_blocks_g<2>(p, jb, out_bf16, lds, s);
+    if (groups == 4)
+        return launch_blocks_g<4>(p, jb, out_bf16, lds, s);
+    return hipErrorInvalidValue;
 }
 
 // pair_wpb: 0 = one output per wavefront, 8 wavefronts per workgroup; 4 or 8 =

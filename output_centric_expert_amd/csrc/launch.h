@@ -84,6 +84,11 @@ hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuni
 // rows of at most 64/groups chunks; hipErrorInvalidValue for a (jb, groups) it has no kernel for.
 hipError_t launch_down_onepass(const DownArgs& p, int jb, int groups, bool out_bf16, int pair_wpb, dim3 grid, dim3 block,
                                size_t lds, hipStream_t s);
+// Blocks form of the one-pass down (float32 a, cached loads, B*k >= E): each
+// workgroup of 8 wavefronts takes kDownBlocks blocks of 8 outputs of one token;
+// H must be a multiple of 8*kDownBlocks (hipErrorInvalidValue otherwise).
+constexpr int kDownBlocks = 8;
+hipError_t launch_down_blocks(const DownArgs& p, int jb, int groups, bool out_bf16, size_t lds, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_bench_read_cfg(const void* src, size_t bytes, void* sink, int unroll, int waves_per_group,

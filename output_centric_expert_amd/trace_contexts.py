@@ -32,8 +32,10 @@ import json
 import statistics
 
 KINDS = (("moe_gate_up_grouped_wide_kernel", "gate_up"), ("moe_gate_up_grouped_kernel", "gate_up"),
-         ("moe_gate_up_exact_kernel", "gate_up"), ("moe_gate_up_kernel", "gate_up"),
+         ("moe_gate_up_exact_pair_kernel", "gate_up"), ("moe_gate_up_exact_kernel", "gate_up"),
+         ("moe_gate_up_kernel", "gate_up"),
          ("moe_down_rows_kernel", "down"), ("moe_down_staged_kernel", "down"), ("moe_down_onepass_kernel", "down"),
+         ("moe_down_blocks_kernel", "down"),
          ("moe_down_kernel", "down"),
          ("moe_down_expert_kernel", "down"), ("moe_down_combine_kernel", "combine"),
          ("moe_route_kernel", "route"))

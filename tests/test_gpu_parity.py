@@ -722,12 +722,17 @@ def test_grouped_wide_loads(shape, wformat):
                                    (5, 64, 8, 2048, 256),      # four lane groups at B=5
                                    (1, 6, 6, 1024, 640),       # k=6: not a power-of-two group (generic kernels)
                                    (1, 64, 8, 2048, 256),      # single token, four lane groups of two slots
-                                   (1, 32, 8, 1024, 1024)])    # single token, four copy loads per thread
+                                   (1, 32, 8, 1024, 1024),     # single token, four copy loads per thread
+                                   (16, 128, 8, 2048, 768),    # B*k = E: blocks form (G=1 JB=8 / G=2 JB=4)
+                                   (10, 64, 8, 1024, 1536),    # mxfp4 G=1 JB=8 (not the blocks form), mxfp8 generic
+                                   (6, 16, 4, 512, 256),       # blocks form with four lane groups of one slot
+                                   (8, 32, 4, 1056, 256)])     # B*k = E but H not a multiple of 64: generic
 def test_straight_line_kernels_match_generic(shape, wformat):
-    """The one-pass down and exact-fit gate/up kernels compute the same floats as the generic
-    staged / per-slot kernels they replace (same products, FMA order and reduction), so the
-    intermediate and both output dtypes agree bit for bit; both also meet the oracle gate.
-    The ids include an invalid one when B > 1 (its token's outputs NaN on both sides)."""
+    """The one-pass down (and its blocks form where tokens share experts) and the exact-fit gate/up
+    kernels compute the same floats as the generic staged / per-slot kernels they replace (same
+    products, FMA order and reduction), so the intermediate and both output dtypes agree bit for
+    bit; both also meet the oracle gate. The ids include an invalid one when B > 1 (its token's
+    outputs NaN on both sides)."""
     B, E, k, H, I = shape
     L = synth.make_layer(synth.LayerShape("sl", B, E, k, H, I), seed=sum(shape) + 5, device="cuda", wformat=wformat)
     ids = L.ids.copy()
