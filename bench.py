@@ -220,7 +220,7 @@ def down_kernel_name(L):
         sh.k * sh.I * 4 <= 65536
     if one_pass_shape and sh.B * sh.k >= sh.E and sh.H % 64 == 0 and not (L.wformat == "mxfp4" and jb == 8):
         return "moe_down_blocks_kernel"
-    if one_pass_shape and sh.B * sh.k < sh.E and (groups > 1 or sh.B <= 2):
+    if one_pass_shape and sh.B * sh.k < sh.E:
         return "moe_down_onepass_kernel"
     return "moe_down_staged_kernel"
 
