@@ -321,23 +321,34 @@ __device__ __forceinline__ GroupW staged_group(const u32x4* tb, const GroupedRow
 // loads issued after it. tb = this wavefront's LDS region (512 units);
 // gs0 / us0 / sstride: the scale row of the lane's block-load row slot (gate
 // for lanes 0-31, up for 32-63; row (L % 32) / 2) and the scale row stride.
-template <int NTL, bool A_BF16, bool FP4>
+// NW = 8: the workgroup's two halves of 4 wavefronts load alternate x tiles
+// (with an odd tile count both load the last one and store the same values).
+template <int NTL, bool A_BF16, bool FP4, int NW = kGroupWaves>
 __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const GroupedRow& r, const uint8_t* gq0,
                                                   const uint8_t* uq0, size_t rstride, const uint8_t* sq0,
                                                   const int* slots, int count, int t0, u32x4* xs, u32x4* tb, bool store)
 {
     constexpr int GPS = StepW<FP4>::kGroups;
+    constexpr int NH = NW / 4;                    // workgroup halves sharing the x loads
+    constexpr int NX = (NTL + NH - 1) / NH;       // x tiles per thread
     const int H = p.H;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int lcol = tid / 16;
+    const int half = NH == 1 ? 0 : tid / 256;
+    const int lcol = NH == 1 ? tid / 16 : (tid % 256) / 16;
     const int lc = tid % 16;
-    uint32_t xo[NTL];                             // element offset of this thread's x row, per tile
+    uint32_t xo[NX];                              // element offset of this thread's x row, per x tile
+    uint32_t xd[NX];                              // its LDS unit in a group's buffer
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const int tt = NH * i + half < NTL ? NH * i + half : NTL - 1;
+        const int sl = (t0 + tt) * 16 + lcol;
+        xo[i] = (uint32_t)(slots[sl < count ? sl : count - 1] / p.k) * (uint32_t)H + 8u * (uint32_t)lc;
+        xd[i] = (uint32_t)((tt * 16 + lcol) * 16 + (lc ^ lcol));
+    }
     int bj[NTL];
 #pragma unroll
     for (int tt = 0; tt < NTL; ++tt) {
-        const int sl = (t0 + tt) * 16 + lcol;
-        xo[tt] = (uint32_t)(slots[sl < count ? sl : count - 1] / p.k) * (uint32_t)H + 8u * (uint32_t)lc;
         const int si = (t0 + tt) * 16 + r.col;
         bj[tt] = slots[si < count ? si : count - 1];
     }
@@ -352,17 +363,17 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
     const uint32_t lo = (uint32_t)(lane / 16) * (uint32_t)rstride + 16u * (uint32_t)(lane % 16);
     const uint32_t rs4 = 4u * (uint32_t)rstride;
     constexpr int kBuf = NTL * kXUnitsPerTile;
-    u32x4 xq[2][NTL];                             // x of groups g+1 and g+2, by group parity
-    auto load_x = [&](u32x4 (&dst)[NTL], int g) {
+    u32x4 xq[2][NX];                              // x of groups g+1 and g+2, by group parity
+    auto load_x = [&](u32x4 (&dst)[NX], int g) {
 #pragma unroll
-        for (int tt = 0; tt < NTL; ++tt)
-            dst[tt] = *reinterpret_cast<const u32x4*>(p.x + (xo[tt] + 128u * (uint32_t)g));
+        for (int i = 0; i < NX; ++i)
+            dst[i] = *reinterpret_cast<const u32x4*>(p.x + (xo[i] + 128u * (uint32_t)g));
     };
-    auto put_x = [&](const u32x4 (&src)[NTL], int g) {
+    auto put_x = [&](const u32x4 (&src)[NX], int g) {
         u32x4* xn = xs + (g & 1) * kBuf;
 #pragma unroll
-        for (int tt = 0; tt < NTL; ++tt)
-            xn[(tt * 16 + lcol) * 16 + (lc ^ lcol)] = src[tt];
+        for (int i = 0; i < NX; ++i)
+            xn[xd[i]] = src[i];
     };
     load_x(xq[0], 0);
     load_x(xq[1], 1);
@@ -431,11 +442,11 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         // 2..4 ahead of its rows (set (g % 4) of xq4 holds x of group g), x of
         // group 1 a step earlier, x of the next step's group 1 during group 2
         // (first waited for after the next step's rows are in).
-        u32x4 xq4[4][NTL];
+        u32x4 xq4[4][NX];
 #pragma unroll
-        for (int tt = 0; tt < NTL; ++tt)
-            xq4[1][tt] = xq[1][tt];
-        auto xput = [&](int g, const u32x4 (&src)[NTL], int h, float gsc, float usc) {
+        for (int i = 0; i < NX; ++i)
+            xq4[1][i] = xq[1][i];
+        auto xput = [&](int g, const u32x4 (&src)[NX], int h, float gsc, float usc) {
             group_mfma<NTL, FP4>(staged_group<FP4>(tb, r, h, gsc, usc), xs + (g & 1) * kBuf, r, dg, du);
             put_x(src, g + 1 < ngroups ? g + 1 : ngroups - 1);
             __syncthreads();
@@ -477,7 +488,7 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
 
 // One item: expert e, neurons n_block .. n_block+63, the count >= 1 slots
 // routed to e in slots[] (slot order). Every thread of the workgroup calls it.
-template <bool A_BF16, bool FP4, bool WIDE>
+template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
 __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const int* slots,
                                              u32x4* xs)
 {
@@ -521,10 +532,10 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
         for (int t0 = 0; t0 < ntiles; t0 += kTiles) {
             const int nt = ntiles - t0 < kTiles ? ntiles - t0 : kTiles;
             switch (nt) {
-            case 1: grouped_pass_wide<1, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
-            case 2: grouped_pass_wide<2, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
-            case 3: grouped_pass_wide<3, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
-            default: grouped_pass_wide<4, A_BF16, FP4>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            case 1: grouped_pass_wide<1, A_BF16, FP4, NW>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            case 2: grouped_pass_wide<2, A_BF16, FP4, NW>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            case 3: grouped_pass_wide<3, A_BF16, FP4, NW>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
+            default: grouped_pass_wide<4, A_BF16, FP4, NW>(p, r, gq0, uq0, rstride, sq0, slots, count, t0, xs, tb, store); break;
             }
         }
     } else {
@@ -545,23 +556,24 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
 // items (expert, block of 64 neurons): with the work list (wl_off >= 0, its
 // place in the dynamic LDS) the routed experts' items with a stride of the
 // grid size, else one item per workgroup over all E experts.
-template <bool A_BF16, bool FP4, bool WIDE>
+template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
 __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl_off)
 {
     extern __shared__ int slots[];               // B*k entries, the x tiles, then the work list
-    __shared__ int wave_cnt[kGroupWaves];
-    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
+    __shared__ int wave_cnt[NW];
+    constexpr int kNeurons = 16 * NW;            // neurons per item
+    const int nblk = (p.I + kNeurons - 1) / kNeurons;
     const int nslots = p.B * p.k;
     const int E = p.E;
     const int I = p.I;
 
     if ((int)blockIdx.x < nblk) {
-        const int n_block = (int)blockIdx.x * kGroupNeurons;
-        const int nbad = compact_slots(nslots, p.ids, slots, wave_cnt,
+        const int n_block = (int)blockIdx.x * kNeurons;
+        const int nbad = compact_slots<NW>(nslots, p.ids, slots, wave_cnt,
                                        [&](int v) { return (unsigned)v >= (unsigned)E; });
-        for (int q = threadIdx.x; q < nbad * kGroupNeurons; q += blockDim.x) {
-            const int bj = slots[q / kGroupNeurons];
-            const int i = n_block + q % kGroupNeurons;
+        for (int q = threadIdx.x; q < nbad * kNeurons; q += blockDim.x) {
+            const int bj = slots[q / kNeurons];
+            const int i = n_block + q % kNeurons;
             if (i < I) {
                 const size_t idx = inter_index<A_BF16>(bj, i, I);
                 if constexpr (A_BF16)
@@ -578,15 +590,15 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl
     if (wl_off >= 0) {
         int* mark = slots + wl_off;
         int* list = mark + E;
-        n_items = routed_experts(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
+        n_items = routed_experts<NW>(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
         act = list;
     }
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int e = act ? act[item / nblk] : item / nblk;
-        const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
+        const int count = compact_slots<NW>(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
         if (count == 0)
             continue;                             // whole workgroup (only without the work list)
-        gate_up_item<A_BF16, FP4, WIDE>(p, e, (item % nblk) * kGroupNeurons, count, slots, xs);
+        gate_up_item<A_BF16, FP4, WIDE, NW>(p, e, (item % nblk) * kNeurons, count, slots, xs);
         __syncthreads();                          // the next item rewrites the slot list and the x tiles
     }
 }
@@ -598,36 +610,48 @@ moe_gate_up_grouped_kernel(GateUpArgs p, int wl_off)
     gate_up_grouped_body<A_BF16, FP4, false>(p, wl_off);
 }
 
-// The wide loads need 8 KiB of LDS per wavefront, so two workgroups share a CU;
-// the register budget is set to match (two wavefronts per SIMD).
-template <bool A_BF16, bool FP4>
-__global__ void __launch_bounds__(kGroupWaves * kWave, 2)
+// The wide loads need 8 KiB of LDS per wavefront: two workgroups of 4
+// wavefronts share a CU, or one of 8 (items of 128 neurons, each x tile
+// loaded once for twice the rows); the register budget is set to match (two
+// wavefronts per SIMD).
+template <bool A_BF16, bool FP4, int NW = kGroupWaves>
+__global__ void __launch_bounds__(NW * kWave, 8 / NW)
 moe_gate_up_grouped_wide_kernel(GateUpArgs p, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, true>(p, wl_off);
+    gate_up_grouped_body<A_BF16, FP4, true, NW>(p, wl_off);
 }
 
-size_t gate_up_grouped_lds(int B, int k, int E, bool wide)
+size_t gate_up_grouped_lds(int B, int k, int E, bool wide, int nw)
 {
     // slot list (rounded up to 16 bytes), two buffers of x tiles, with the
     // wide loads one 8 KiB region per wavefront, then the work list
     const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
     return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) +
-           (wide ? (size_t)kGroupWaves * kWideUnitsPerWave * sizeof(u32x4) : 0) + worklist_lds(E);
+           (wide ? (size_t)nw * kWideUnitsPerWave * sizeof(u32x4) : 0) + worklist_lds(E);
+}
+
+template <bool A_BF16, bool FP4, int NW>
+static hipError_t launch_wide(dim3 grid, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off)
+{
+    // allow dynamic LDS beyond the default 64 KiB, once per device: up to
+    // 64 KiB for the slot list and x tiles plus the wide-load regions
+    const hipError_t attr =
+        set_max_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW>),
+                            65536 + NW * kWideUnitsPerWave * (int)sizeof(u32x4));
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW>), grid, dim3(NW * kWave), lds, s, p,
+                       wl_off);
+    return hipGetLastError();
 }
 
 template <bool A_BF16, bool FP4, bool WIDE>
-hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off)
+hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off,
+                          int nw)
 {
     if constexpr (WIDE) {
-        // allow dynamic LDS beyond the default 64 KiB, once per device: up to
-        // 64 KiB for the slot list and x tiles plus the 32 KiB of wide-load regions
-        const hipError_t attr =
-            set_max_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4>),
-                                65536 + kGroupWaves * kWideUnitsPerWave * (int)sizeof(u32x4));
-        if (attr != hipSuccess)
-            return attr;
-        hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4>), grid, block, lds, s, p, wl_off);
+        return nw == 8 ? launch_wide<A_BF16, FP4, 8>(grid, lds, s, p, wl_off)
+                       : launch_wide<A_BF16, FP4, kGroupWaves>(grid, lds, s, p, wl_off);
     } else {
         hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, wl_off);
     }
@@ -638,13 +662,19 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
 {
     if ((long)p.B * p.k == 0)
         return hipSuccess;
-    const int nblk = (p.I + kGroupNeurons - 1) / kGroupNeurons;
-    const long items = (long)p.E * nblk;
     // wide loads: rows of whole 256-byte steps and whole scale blocks, read as
     // 8-byte pieces (scale arrays at 8-byte aligned bases; else the slices,
     // which give the same floats)
     const bool wide = t.gu_wide != 0 && p.H % 512 == 0 && (((uintptr_t)p.wg_s | (uintptr_t)p.wu_s) & 7u) == 0;
-    const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide);
+    // 8 wavefronts (items of 128 neurons) pay off once experts average 32 slots
+    // or more, where each 64-neuron item would fetch as many bytes of x from
+    // L2 as of weights from HBM; below that one 8-wave workgroup per CU hides
+    // its barriers worse than two of 4
+    const int nw = !wide ? kGroupWaves
+                         : t.gu_waves == 8 || (t.gu_waves == 0 && (long)p.B * p.k >= 32L * p.E) ? 8 : kGroupWaves;
+    const int nblk = (p.I + 16 * nw - 1) / (16 * nw);
+    const long items = (long)p.E * nblk;
+    const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide, nw);
     const size_t wl = worklist_lds(p.E);
     // with the work list: at most gu_grid workgroups (and at least one per
     // neuron block, for the invalid-slot pass) walk the routed experts' items
@@ -658,16 +688,16 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const bool fp4 = p.wfmt == kMXFP4;
     if (fp4) {
         if (a_bf16)
-            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, wl_off)
-                        : launch_grouped<true, true, false>(grid, block, lds, s, p, wl_off);
-        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, wl_off)
-                    : launch_grouped<false, true, false>(grid, block, lds, s, p, wl_off);
+            return wide ? launch_grouped<true, true, true>(grid, block, lds, s, p, wl_off, nw)
+                        : launch_grouped<true, true, false>(grid, block, lds, s, p, wl_off, nw);
+        return wide ? launch_grouped<false, true, true>(grid, block, lds, s, p, wl_off, nw)
+                    : launch_grouped<false, true, false>(grid, block, lds, s, p, wl_off, nw);
     }
     if (a_bf16)
-        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, wl_off)
-                    : launch_grouped<true, false, false>(grid, block, lds, s, p, wl_off);
-    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, wl_off)
-                : launch_grouped<false, false, false>(grid, block, lds, s, p, wl_off);
+        return wide ? launch_grouped<true, false, true>(grid, block, lds, s, p, wl_off, nw)
+                    : launch_grouped<true, false, false>(grid, block, lds, s, p, wl_off, nw);
+    return wide ? launch_grouped<false, false, true>(grid, block, lds, s, p, wl_off, nw)
+                : launch_grouped<false, false, false>(grid, block, lds, s, p, wl_off, nw);
 }
 
 }  // namespace moed

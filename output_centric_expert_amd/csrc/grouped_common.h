@@ -74,13 +74,14 @@ __device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
 }
 
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing
-// order) with pred(ids[t]). All threads of the workgroup must call it. The ids
+// order) with pred(ids[t]). All threads of the workgroup (NW wavefronts) must
+// call it. The ids
 // of up to four 256-slot chunks are loaded together, so the list costs one
 // round trip to L2 per 1024 slots.
-template <typename Pred>
+template <int NW = kGroupWaves, typename Pred>
 __device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, int* wave_cnt, Pred pred)
 {
-    constexpr int kChunk = kGroupWaves * kWave;
+    constexpr int kChunk = NW * kWave;
     constexpr int kBatch = 4;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -111,7 +112,7 @@ __device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, 
             if (f)
                 slots[off + before] = t;
             int sum = 0;
-            for (int q = 0; q < kGroupWaves; ++q)
+            for (int q = 0; q < NW; ++q)
                 sum += wave_cnt[q];
             __syncthreads();
             total += sum;
@@ -138,9 +139,10 @@ inline size_t worklist_lds(int E)
 // act[0..n) = the experts with at least one slot routed to them (ids in
 // [0, E)), in increasing order; mark is E ints of scratch. Returns n. All
 // threads of the workgroup must call it.
+template <int NW = kGroupWaves>
 __device__ __forceinline__ int routed_experts(int n_slots, const int* ids, int E, int* mark, int* act, int* wave_cnt)
 {
-    constexpr int kChunk = kGroupWaves * kWave;
+    constexpr int kChunk = NW * kWave;
     const int tid = threadIdx.x;
     for (int t = tid; t < E; t += kChunk)
         mark[t] = 0;
@@ -158,7 +160,7 @@ __device__ __forceinline__ int routed_experts(int n_slots, const int* ids, int E
                 mark[v[c]] = 1;                   // equal values: any order of the stores
     }
     __syncthreads();
-    return compact_slots(E, mark, act, wave_cnt, [](int v) { return v != 0; });
+    return compact_slots<NW>(E, mark, act, wave_cnt, [](int v) { return v != 0; });
 }
 
 }  // namespace moed

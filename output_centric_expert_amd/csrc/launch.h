@@ -42,7 +42,10 @@ struct Tuning {
                         // token's slots form one group and a row is one chunk per lane
     int dn_pair = 1;    // one-pass down, MXFP4 at B > 1 (H even): 1 = two neighbouring outputs per
                         // wavefront sharing each read of a; 0 = one
-    int gu_grid = 1024; // grouped gate/up: at most this many workgroups walk the items of the routed
+    int gu_waves = 0;   // grouped gate/up with wide loads: wavefronts per workgroup (4 or 8; 8 = items of
+                        // 128 neurons, the slots' x loaded once per 128 instead of 64 neurons);
+                        // 0 = 8 once B*k >= 32*E
+    int gu_grid = 512;  // grouped gate/up: at most this many workgroups walk the items of the routed
                         // experts (0 = one workgroup per item of all E experts, empty ones included)
     int dn_grid = 2048; // expert-major down: the same for its items
 };
@@ -78,7 +81,7 @@ struct DownArgs {
 
 hipError_t launch_gate_up(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s);
-size_t gate_up_grouped_lds(int B, int k, int E, bool wide);
+size_t gate_up_grouped_lds(int B, int k, int E, bool wide, int nw = 4);
 hipError_t launch_down(const DownArgs& p, bool a_bf16, bool out_bf16, const Tuning& t, hipStream_t s);
 // One-pass down (float32 a, streaming loads, 8 wavefronts per workgroup): k = groups * jb slots,
 // rows of at most 64/groups chunks; hipErrorInvalidValue for a (jb, groups) it has no kernel for.

@@ -530,6 +530,7 @@ int moed_tuning_init(moed_tuning* out, const char* spec)
         else if (!strcmp(tok, "dn_pair") && (v == 0 || v == 1)) t.dn_pair = (int)v;
         else if (!strcmp(tok, "dn_split") && (v == 0 || v == 1)) t.dn_split = (int)v;
         else if (!strcmp(tok, "gu_exact") && (v == 0 || v == 1)) t.gu_exact = (int)v;
+        else if (!strcmp(tok, "gu_waves") && (v == 0 || v == 4 || v == 8)) t.gu_waves = (int)v;
         else if (!strcmp(tok, "gu_grid") && v >= 0 && v <= 65536) t.gu_grid = (int)v;
         else if (!strcmp(tok, "dn_grid") && v >= 0 && v <= 65536) t.dn_grid = (int)v;
         else return MOED_ERR_SHAPE;

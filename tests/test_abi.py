@@ -172,6 +172,10 @@ def test_tuning_spec_parser(lib):
     assert _init(lib, b"gu_order=3") == md.MOED_ERR_SHAPE
     assert _init(lib, b"gu_exact=0") == md.MOED_OK
     assert _init(lib, b"gu_exact=2") == md.MOED_ERR_SHAPE
+    assert _init(lib, b"gu_waves=0") == md.MOED_OK
+    assert _init(lib, b"gu_waves=4") == md.MOED_OK
+    assert _init(lib, b"gu_waves=8") == md.MOED_OK
+    assert _init(lib, b"gu_waves=2") == md.MOED_ERR_SHAPE
     assert _init(lib, b"gu_grid=0,dn_grid=65536") == md.MOED_OK
     assert _init(lib, b"dn_grid=-1") == md.MOED_ERR_SHAPE
     assert _init(lib, b"grp_grid=1") == md.MOED_ERR_SHAPE

@@ -670,6 +670,7 @@ def test_input_check_scale_range(monkeypatch):
 WIDE = [
     (40, 3, 2, 1024, 160),    # ~27 slots per expert (2 tiles); waves past I
     (72, 2, 2, 512, 96),      # 72 slots per expert: a 4-tile pass, then a 1-tile pass; one scale block
+    (48, 2, 2, 1024, 192),    # 48 slots per expert: a 3-tile pass (an odd tile count for 8 wavefronts)
     (24, 6, 4, 2560, 64),     # 5 MXFP8 step pairs / 5 MXFP4 steps
     (20, 4, 3, 1536, 128),    # 3 step pairs / 3 steps
     (16, 8, 8, 7168, 64),     # 14 step pairs of 7168-value rows
@@ -682,24 +683,27 @@ WIDE = [
 def test_grouped_wide_loads(shape, wformat):
     """The MFMA path's wide weight loads (256-byte runs per row, moved to the operand layout
     through LDS, scales fetched in 16-byte blocks and handed out by ds_bpermute) feed every
-    MFMA the codes and scales the 128-byte tile slices do, in the same order: the
-    intermediate is the same floats (float32 and bf16), and the layer within tolerance of
-    the oracle."""
+    MFMA the codes and scales the 128-byte tile slices do, in the same order, with workgroups
+    of 4 wavefronts (items of 64 neurons) or 8 (items of 128, the two halves loading
+    alternate x tiles), and with the built-in choice between them: the intermediate is the
+    same floats (float32 and bf16), and the layer within tolerance of the oracle."""
     B, E, k, H, I = shape
     L = synth.make_layer(synth.LayerShape("wide", B, E, k, H, I), seed=sum(shape) + 21, device="cuda",
                          wformat=wformat)
     x, ids, _ = md.layer_device_inputs(L)
     got = {}
+    forms = ["gu_wide=0", "gu_wide=1,gu_waves=4", "gu_wide=1,gu_waves=8", "gu_wide=1"]
     try:
-        for wide in (0, 1):
-            md.set_default_tuning(f"gu_group=1,gu_wide={wide}")
+        for form in forms:
+            md.set_default_tuning(f"gu_group=1,{form}")
             for dt in (torch.float32, torch.bfloat16):
-                got[wide, dt] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
+                got[form, dt] = md.moe_decode_gate_up(x, ids, L.wg_q, L.wg_s, L.wu_q, L.wu_s,
                                                       inter_dtype=dt, wformat=wformat)
             torch.cuda.synchronize()
         say(f"wide loads {shape} {wformat}: comparing")
-        for dt in (torch.float32, torch.bfloat16):
-            assert torch.equal(got[1, dt], got[0, dt]), f"{shape} {wformat} {dt}"
+        for form in forms[1:]:
+            for dt in (torch.float32, torch.bfloat16):
+                assert torch.equal(got[form, dt], got[forms[0], dt]), f"{shape} {wformat} {form} {dt}"
         md.set_default_tuning("gu_group=1,gu_wide=1")
         ref, _ = oracle_tokens(L, [0, B - 1], wformat=wformat)
         xd, idd, wd = md.layer_device_inputs(L)
