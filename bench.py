@@ -163,7 +163,7 @@ def main():
             log(f"step: per-config {name}")
             per_config.append(config_entry(md, synth, name, args.wformat,
                                            reuse=(L, t) if name == args.workload else None,
-                                           cpu=not args.no_cpu))
+                                           cpu=not args.no_cpu, peak=peak))
             torch.cuda.empty_cache()
 
     cpu = None
@@ -326,13 +326,44 @@ CONFIG_PLAN = {"tiny_B1_E8_k2_H256_I128": (32, 1000), "wide_B1_E128_k8_H2048_I76
                "skewed_B64_E256_k8_H7168_I2048": (4, 32)}
 
 
-def config_entry(md, synth, name, wformat, reuse=None, cpu=True):
+def profile_entry(L, name):
+    """What the committed rocprofv3 summaries of this workload say (MXFP8 weights), while they
+    were taken from the current kernel sources: the layer's span under the kernel tracer (median,
+    p10, p90; start of gate/up to end of the down step), and per step the HBM bytes per launch
+    against the algorithmic bytes, the L2 hit rate and the VALU / MFMA busy percentages."""
+    if L.wformat != "mxfp8":
+        return None
+    files = LAYER_SOURCES if gate_up_kernel_name(L) != "moe_gate_up_grouped_wide_kernel" else GROUPED_SOURCES
+    out = {}
+    tr = load_profile("kernel_trace", name, files)
+    if tr is not None:
+        sp = tr["layer_spans"]["after the down step"]
+        out["rocprof_layer_us"] = {"median": round(sp["median_ns"] / 1e3, 3), "p10": round(sp["p10_ns"] / 1e3, 3),
+                                   "p90": round(sp["p90_ns"] / 1e3, 3), "layers": sp["layers"],
+                                   "source": tr["_file"]}
+    cn = load_profile("counters_layer", name, files)
+    if cn is not None:
+        for step in ("gate_up", "down"):
+            c = cn[step]
+            x = c.get("extra", {})
+            out[f"hbm_{step}"] = {"bytes_per_launch": round(c["hbm_bytes_per_launch"]),
+                                  "algorithmic_bytes": c["algorithmic_bytes_per_launch"],
+                                  "over_algorithmic": round(c["traffic_over_algorithmic"], 4),
+                                  "l2_hit_rate": round(x["L2_hit_rate"], 3) if "L2_hit_rate" in x else None,
+                                  "valu_busy_pct": round(x["VALUBusy"], 1) if "VALUBusy" in x else None,
+                                  "mfma_busy_pct": round(x["MfmaUtil"], 1) if "MfmaUtil" in x else None}
+        out["hbm_source"] = cn["_file"]
+    return out or None
+
+
+def config_entry(md, synth, name, wformat, reuse=None, cpu=True, peak=None):
     """One workload: µs per layer (graph of K layers over rotating weight copies; each step alone),
-    GB/s on unique routed-weight bytes and its fraction of 8 TB/s; accuracy against the float64
-    oracle on every token (float32 output: max|err|/rms, min cosine; bf16 output: max abs; the
-    FP32-accumulate path with BF16 intermediates: max|err|/rms), computed outside the timed
-    region; the oracle's own time for the layer on the host threads (and on one thread for the
-    three smaller workloads)."""
+    GB/s on unique routed-weight bytes and its fraction of 8 TB/s (and of the measured read peak,
+    when given); accuracy against the float64 oracle on every token (float32 output: max|err|/rms,
+    min cosine; bf16 output: max abs; the FP32-accumulate path with BF16 intermediates:
+    max|err|/rms), computed outside the timed region; the oracle's own time for the layer on the
+    host threads (and on one thread for the three smaller workloads); the committed profiles'
+    figures for the workload (profile_entry)."""
     import torch
 
     R, K = CONFIG_PLAN[name]
@@ -351,6 +382,9 @@ def config_entry(md, synth, name, wformat, reuse=None, cpu=True):
          "us_gate_up": round(t["ms_gate_up"] * 1e3, 3), "us_down": round(t["ms_down"] * 1e3, 3),
          "kernels": {"gate_up": gate_up_kernel_name(L), "down": down_kernel_name(L)},
          "steps": t.get("steps", K), "weight_copies": R if reuse is None else None}
+    if peak:
+        e["frac_of_measured_read_peak"] = round(gbs / peak, 4)
+    e["profile"] = profile_entry(L, name)
     e["accuracy"] = accuracy_entry(md, L, cpu_threads=oracle_threads(), one_thread=cpu and sh.B <= 8)
     return e
 
