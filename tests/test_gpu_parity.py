@@ -715,6 +715,44 @@ def test_grouped_wide_loads(shape, wformat):
         md.set_default_tuning(None)
 
 
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+def test_grouped_eight_waves_with_invalid_ids(wformat):
+    """The 8-wavefront gate/up (items of 128 neurons, its own choice here since B*k >= 32*E) with a
+    duplicated and two out-of-range ids: the intermediate is bit-identical to the 4-wavefront form,
+    NaN over all I neurons of exactly the invalid slots (its invalid-slot pass covers blocks of 128
+    neurons, the last one ragged at I = 160); the layer is NaN on those tokens and within tolerance
+    of the oracle on the others."""
+    B, E, k, H, I = 48, 3, 2, 1024, 160
+    L = synth.make_layer(synth.LayerShape("w8", B, E, k, H, I), seed=91, device="cuda", wformat=wformat)
+    ids = L.ids.copy()
+    ids[5, 1] = ids[5, 0]
+    ids[9, 0] = 3
+    ids[30, 1] = -2
+    x, _, w = md.layer_device_inputs(L)
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    got = {}
+    for form in ("gu_group=1,gu_waves=4", "gu_group=1,gu_waves=8", "gu_group=1"):
+        say(f"eight waves {wformat} {form}")
+        got[form] = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat, tuning=form)
+    torch.cuda.synchronize()
+    ref = got["gu_group=1,gu_waves=4"]
+    for form, a in got.items():
+        assert torch.equal(a.view(torch.int32), ref.view(torch.int32)), f"{wformat} {form}"
+    bad = torch.zeros(B, k, dtype=torch.bool)
+    bad[9, 0] = True
+    bad[30, 1] = True
+    nan_rows = torch.isnan(ref.cpu()).all(dim=2)
+    assert torch.equal(nan_rows, bad)
+    assert not torch.isnan(ref.cpu()[~bad]).any()
+    out = md.moe_decode(x, idd, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s, out_dtype=torch.float32,
+                        wformat=wformat, tuning="gu_group=1,dn_group=1")
+    torch.cuda.synchronize()
+    assert torch.isnan(out[9]).all() and torch.isnan(out[30]).all()
+    good = [0, 5, 17, B - 1]
+    ref_out, _ = oracle_tokens(L, good, ids=ids, wformat=wformat)
+    check_f32(out[good], ref_out, f"eight waves {wformat}")
+
+
 # (B, E, k, H, I): which straight-line kernels each shape takes --
 #   one-pass down: k = G*JB slots in one group, a row of at most 64/G chunks
 #   exact-fit gate/up: a row of exactly 64*U chunks
