@@ -5,8 +5,9 @@
 // When many tokens share an expert (batch 32-64 with top-8 of 128-256
 // experts), the per-slot kernel re-reads and re-decodes every routed row once
 // per (token, slot): 2-10x the unique weight bytes. Here a workgroup owns
-// (expert e, 64 neurons); it compacts the list of slots routed to e (in slot
-// order, from topk_ids), and each wavefront computes tiles of 16 neurons x 16
+// (expert e, 64 neurons; 128 with 8 wavefronts); it compacts the list of
+// slots routed to e (in slot order, from topk_ids), and each wavefront
+// computes tiles of 16 neurons x 16
 // of those slots (up to four tiles per pass over the rows) with MFMA:
 //   A = the gate (or up) rows, decoded exactly from MXFP8 (or MXFP4) to BF16
 //       with the block scale folded into the conversion
@@ -486,7 +487,7 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
         store_tiles<NTL, A_BF16>(p, r, bj, count, t0, dg, du);
 }
 
-// One item: expert e, neurons n_block .. n_block+63, the count >= 1 slots
+// One item: expert e, neurons n_block .. n_block+16*NW-1, the count >= 1 slots
 // routed to e in slots[] (slot order). Every thread of the workgroup calls it.
 template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
 __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const int* slots,
@@ -553,7 +554,7 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
 
 // The grouped gate/up: invalid slots first (workgroup q < blocks writes NaN
 // for neuron block q of every slot whose id is outside [0, E)), then the
-// items (expert, block of 64 neurons): with the work list (wl_off >= 0, its
+// items (expert, block of 16*NW neurons): with the work list (wl_off >= 0, its
 // place in the dynamic LDS) the routed experts' items with a stride of the
 // grid size, else one item per workgroup over all E experts.
 template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
