@@ -7,8 +7,8 @@
 // per (token, slot): 2-10x the unique weight bytes. Here a workgroup owns
 // (expert e, 64 neurons; 128 with 8 wavefronts); it compacts the list of
 // slots routed to e (in slot order, from topk_ids), and each wavefront
-// computes tiles of 16 neurons x 16
-// of those slots (up to four tiles per pass over the rows) with MFMA:
+// computes tiles of 16 neurons x 16 of those slots (up to four tiles per
+// pass over the rows) with MFMA:
 //   A = the gate (or up) rows, decoded exactly from MXFP8 (or MXFP4) to BF16
 //       with the block scale folded into the conversion
 //       (v_cvt_scalef32_pk_bf16_fp8 / _fp4; exact for scale codes 10..245
