@@ -718,7 +718,9 @@ def test_grouped_wide_loads(shape, wformat):
 @pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
 def test_grouped_eight_waves_with_invalid_ids(wformat):
     """The 8-wavefront gate/up (items of 128 neurons, its own choice here since B*k >= 32*E) with a
-    duplicated and two out-of-range ids: the intermediate is bit-identical to the 4-wavefront form,
+    duplicated and two out-of-range ids, with the work list at the built-in cap and at a cap of 3
+    workgroups, and with one workgroup per item of all E experts (gu_grid=0): the intermediate is
+    bit-identical to the 4-wavefront form,
     NaN over all I neurons of exactly the invalid slots (its invalid-slot pass covers blocks of 128
     neurons, the last one ragged at I = 160); the layer is NaN on those tokens and within tolerance
     of the oracle on the others."""
@@ -731,7 +733,8 @@ def test_grouped_eight_waves_with_invalid_ids(wformat):
     x, _, w = md.layer_device_inputs(L)
     idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
     got = {}
-    for form in ("gu_group=1,gu_waves=4", "gu_group=1,gu_waves=8", "gu_group=1"):
+    for form in ("gu_group=1,gu_waves=4", "gu_group=1,gu_waves=8", "gu_group=1",
+                 "gu_group=1,gu_waves=8,gu_grid=0", "gu_group=1,gu_waves=8,gu_grid=3"):
         say(f"eight waves {wformat} {form}")
         got[form] = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, wformat=wformat, tuning=form)
     torch.cuda.synchronize()
