@@ -145,7 +145,7 @@ __device__ __forceinline__ bf16x8 dn_decode(const DnGroupW& w, int q)
 // the loop carries no register copies that would wait for them); a group's a
 // is split into its LDS buffer after the previous group's MFMAs.
 template <int NTL, int RT, bool A_BF16, bool FP4>
-__device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<RT>& r, const int* slots,
+__device__ __forceinline__ void expert_down_pass(const DownArgs& p, const DnRow<RT>& r, const uint16_t* slots,
                                                  int count, int t0, u32x4* xs, bool store, int h0, float* y)
 {
     const int I = p.I;
@@ -373,7 +373,7 @@ __device__ __forceinline__ DnGroupW staged_dn_group(const u32x4* tb, const DnRow
 // the results are the same floats.
 template <int NTL, int RT, bool A_BF16, bool FP4, int NH = 1>
 __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const DnRow<RT>& r, const uint8_t* q0,
-                                                      size_t rstride, const uint8_t* sq0, const int* slots, int count,
+                                                      size_t rstride, const uint8_t* sq0, const uint16_t* slots, int count,
                                                       int t0, u32x4* xs, u32x4* tb, bool store, int h0, float* y)
 {
     static_assert(NH == 1 || (NH == 2 && !A_BF16), "two halves only for float32 a");
@@ -600,7 +600,7 @@ __device__ __forceinline__ void expert_down_pass_wide(const DownArgs& p, const D
 // item per workgroup over all E experts (the grid is E * blocks).
 template <int RT, bool A_BF16, bool FP4, bool WIDE>
 __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, int max_tiles, int e, int hb,
-                                                 int count, const int* slots, u32x4* xs)
+                                                 int count, const uint16_t* slots, u32x4* xs)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
@@ -675,16 +675,20 @@ template <int RT, bool A_BF16, bool FP4, bool WIDE>
 __global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
 moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
 {
-    extern __shared__ int slots[];                // B*k entries, the a tiles, then the work list
+    // B*k slot entries of 16 bits (B*k < 65536 wherever this kernel fits in LDS;
+    // half the space of ints, which keeps two tiles of a per pass up to about
+    // B*k = 7700), the a tiles, then the work list
+    extern __shared__ int smem[];
+    uint16_t* slots = reinterpret_cast<uint16_t*>(smem);
     __shared__ int wave_cnt[kGroupWaves];
     constexpr int kRows = 16 * RT * kGroupWaves;
     const int nblk = (p.H + kRows - 1) / kRows;
     const int nslots = p.B * p.k;
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 7) & ~7));
     const int* act = nullptr;
     int n_items = p.E * nblk;
     if (wl_off >= 0) {
-        int* mark = slots + wl_off;
+        int* mark = smem + wl_off;
         int* list = mark + p.E;
         n_items = routed_experts(nslots, p.ids, p.E, mark, list, wave_cnt) * nblk;
         act = list;
@@ -755,9 +759,10 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
 
 size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles, int row_tiles, bool wide)
 {
-    // slot list (rounded up to 16 bytes), two buffers of hi (and lo) tiles,
-    // with the wide loads one step region per wavefront, then the work list
-    const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
+    // slot list (16-bit entries, rounded up to 16 bytes), two buffers of hi
+    // (and lo) tiles, with the wide loads one step region per wavefront, then
+    // the work list
+    const size_t list = ((size_t)B * (size_t)k + 7) / 8 * 16;
     const size_t stage = wide ? (size_t)kGroupWaves * 16 * (size_t)row_tiles * 16 * sizeof(u32x4) : 0;
     return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4) + stage + worklist_lds(E);
 }
@@ -771,6 +776,8 @@ constexpr size_t kDnLdsAutoWide = 81920;
 
 int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested, int row_tiles, bool wide)
 {
+    if ((long)B * (long)k > 65535)
+        return 0;                                 // the slot list holds 16-bit slot indices
     const int cap = wide ? (a_bf16 ? 3 : 2) : kTiles;   // wide loads: 2 tiles of float32 a, 3 of bf16
     if (requested > 0) {
         const int mt = requested < cap ? requested : cap;

@@ -74,12 +74,12 @@ __device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
 }
 
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing
-// order) with pred(ids[t]). All threads of the workgroup (NW wavefronts) must
-// call it. The ids
-// of up to four 256-slot chunks are loaded together, so the list costs one
-// round trip to L2 per 1024 slots.
-template <int NW = kGroupWaves, typename Pred>
-__device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, int* wave_cnt, Pred pred)
+// order) with pred(ids[t]), stored as S (int, or uint16_t for n < 65536). All
+// threads of the workgroup (NW wavefronts) must call it. The ids of up to four
+// 256-slot chunks are loaded together, so the list costs one round trip to L2
+// per 1024 slots.
+template <int NW = kGroupWaves, typename Pred, typename S = int>
+__device__ __forceinline__ int compact_slots(int n, const int* ids, S* slots, int* wave_cnt, Pred pred)
 {
     constexpr int kChunk = NW * kWave;
     constexpr int kBatch = 4;
@@ -110,7 +110,7 @@ __device__ __forceinline__ int compact_slots(int n, const int* ids, int* slots, 
             for (int q = 0; q < w; ++q)
                 off += wave_cnt[q];
             if (f)
-                slots[off + before] = t;
+                slots[off + before] = (S)t;
             int sum = 0;
             for (int q = 0; q < NW; ++q)
                 sum += wave_cnt[q];

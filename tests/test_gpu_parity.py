@@ -521,10 +521,10 @@ def test_expert_major_down_without_partials_is_per_output():
 
 
 def test_long_slot_list_takes_fewer_tiles():
-    """B*k = 4800 slots: the slot list takes 19 KB of LDS, so the expert-major down takes two
-    tiles of float32 a per pass instead of three."""
-    L = small(600, 8, 8, 64, 64, seed=31)
-    toks = [0, 1, 299, 599]
+    """B*k = 8192 slots: the expert-major down's slot list (16-bit entries) takes 16 KB of LDS, so
+    it takes two tiles of float32 a per pass instead of three; the same bits as asking for two."""
+    L = small(1024, 8, 8, 64, 64, seed=31)
+    toks = [0, 1, 511, 1023]
     out = run(L)
     ref, _ = oracle_tokens(L, toks)
     check_f32(out[toks], ref, "B=600")
@@ -536,10 +536,10 @@ def test_long_slot_list_takes_fewer_tiles():
 
 
 def test_slot_list_beyond_lds_falls_back():
-    """B*k = 12800 slots: the slot list alone takes 50 KB of LDS, so neither grouped kernel fits
-    and the layer keeps the per-slot gate/up and the per-output down."""
-    L = small(1600, 8, 8, 64, 64, seed=33)
-    toks = [0, 1, 800, 1599]
+    """B*k = 25600 slots: the slot list alone takes 50 KB of LDS even with 16-bit entries, so
+    neither grouped kernel fits and the layer keeps the per-slot gate/up and the per-output down."""
+    L = small(3200, 8, 8, 64, 64, seed=33)
+    toks = [0, 1, 1600, 3199]
     out = run(L)
     md.set_default_tuning("gu_group=0,dn_group=0")
     try:
