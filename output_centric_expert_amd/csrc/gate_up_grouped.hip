@@ -175,7 +175,7 @@ __device__ __forceinline__ void store_tiles(const GateUpArgs& p, const GroupedRo
 // another order. Leftover blocks (H/32 not a multiple of 4) take x from
 // global memory in plain k order.
 template <int NTL, bool A_BF16, bool FP4>
-__device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedRow& r, const int* slots,
+__device__ __forceinline__ void grouped_pass(const GateUpArgs& p, const GroupedRow& r, const uint16_t* slots,
                                              int count, int t0, u32x4* xs, bool store)
 {
     const int H = p.H;
@@ -327,7 +327,7 @@ __device__ __forceinline__ GroupW staged_group(const u32x4* tb, const GroupedRow
 template <int NTL, bool A_BF16, bool FP4, int NW = kGroupWaves>
 __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const GroupedRow& r, const uint8_t* gq0,
                                                   const uint8_t* uq0, size_t rstride, const uint8_t* sq0,
-                                                  const int* slots, int count, int t0, u32x4* xs, u32x4* tb, bool store)
+                                                  const uint16_t* slots, int count, int t0, u32x4* xs, u32x4* tb, bool store)
 {
     constexpr int GPS = StepW<FP4>::kGroups;
     constexpr int NH = NW / 4;                    // workgroup halves sharing the x loads
@@ -490,7 +490,7 @@ __device__ __forceinline__ void grouped_pass_wide(const GateUpArgs& p, const Gro
 // One item: expert e, neurons n_block .. n_block+16*NW-1, the count >= 1 slots
 // routed to e in slots[] (slot order). Every thread of the workgroup calls it.
 template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
-__device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const int* slots,
+__device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_block, int count, const uint16_t* slots,
                                              u32x4* xs)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -560,7 +560,10 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
 template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
 __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl_off)
 {
-    extern __shared__ int slots[];               // B*k entries, the x tiles, then the work list
+    // B*k slot entries of 16 bits (B*k < 65536 wherever this kernel fits in LDS),
+    // the x tiles, then the work list
+    extern __shared__ int smem[];
+    uint16_t* slots = reinterpret_cast<uint16_t*>(smem);
     __shared__ int wave_cnt[NW];
     constexpr int kNeurons = 16 * NW;            // neurons per item
     const int nblk = (p.I + kNeurons - 1) / kNeurons;
@@ -585,11 +588,11 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl
         }
         __syncthreads();                          // the list is reused below
     }
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 3) & ~3));   // x tiles, after the slot list
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 7) & ~7));   // x tiles, after the slot list
     const int* act = nullptr;
     int n_items = E * nblk;
     if (wl_off >= 0) {
-        int* mark = slots + wl_off;
+        int* mark = smem + wl_off;
         int* list = mark + E;
         n_items = routed_experts<NW>(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
         act = list;
@@ -624,9 +627,9 @@ moe_gate_up_grouped_wide_kernel(GateUpArgs p, int wl_off)
 
 size_t gate_up_grouped_lds(int B, int k, int E, bool wide, int nw)
 {
-    // slot list (rounded up to 16 bytes), two buffers of x tiles, with the
-    // wide loads one 8 KiB region per wavefront, then the work list
-    const size_t list = ((size_t)B * (size_t)k + 3) / 4 * 16;
+    // slot list (16-bit entries, rounded up to 16 bytes), two buffers of x
+    // tiles, with the wide loads one 8 KiB region per wavefront, then the work list
+    const size_t list = ((size_t)B * (size_t)k + 7) / 8 * 16;
     return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) +
            (wide ? (size_t)nw * kWideUnitsPerWave * sizeof(u32x4) : 0) + worklist_lds(E);
 }
