@@ -671,36 +671,67 @@ __device__ __forceinline__ void expert_down_item(const DownArgs& p, float* y, in
     }
 }
 
-template <int RT, bool A_BF16, bool FP4, bool WIDE>
+// WIN: B*k > kSlotCap, the slots of an expert taken in windows of kSlotCap
+template <int RT, bool A_BF16, bool FP4, bool WIDE, bool WIN>
 __global__ void __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(4 - RT)))
 moe_down_expert_kernel(DownArgs p, float* y, int max_tiles, int wl_off)
 {
-    // B*k slot entries of 16 bits (B*k < 65536 wherever this kernel fits in LDS;
-    // half the space of ints, which keeps two tiles of a per pass up to about
-    // B*k = 7700), the a tiles, then the work list
+    // up to kSlotCap slot entries of 16 bits (B*k < 65536; a list of fixed
+    // size keeps two tiles of a per pass at any batch), the a tiles, then the
+    // work list
     extern __shared__ int smem[];
     uint16_t* slots = reinterpret_cast<uint16_t*>(smem);
     __shared__ int wave_cnt[kGroupWaves];
     constexpr int kRows = 16 * RT * kGroupWaves;
     const int nblk = (p.H + kRows - 1) / kRows;
     const int nslots = p.B * p.k;
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 7) & ~7));
+    const int cap = nslots < kSlotCap ? nslots : kSlotCap;
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((cap + 7) & ~7));
     const int* act = nullptr;
-    int n_items = p.E * nblk;
-    if (wl_off >= 0) {
-        int* mark = smem + wl_off;
-        int* list = mark + p.E;
-        n_items = routed_experts(nslots, p.ids, p.E, mark, list, wave_cnt) * nblk;
-        act = list;
-    }
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int e = act ? act[item / nblk] : item / nblk;
-        const int hb = (item % nblk) * kRows;
-        const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
-        if (count == 0)
-            continue;                             // whole workgroup (only without the work list)
-        expert_down_item<RT, A_BF16, FP4, WIDE>(p, y, max_tiles, e, hb, count, slots, xs);
-        __syncthreads();                          // the next item rewrites the slot list and the a tiles
+    if constexpr (WIN) {
+        // items (expert, row block, window of kSlotCap slots)
+        int nwin = (nslots + kSlotCap - 1) / kSlotCap;   // without the work list: as many as B*k could need
+        int n_items;
+        if (wl_off >= 0) {
+            int* mark = smem + wl_off;
+            int* list = mark + p.E;
+            n_items = routed_experts_windows(nslots, p.ids, p.E, mark, list, wave_cnt, nwin) * nblk * nwin;
+            act = list;
+        } else {
+            n_items = p.E * nblk * nwin;
+        }
+        const int ipe = nblk * nwin;
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            const int e = act ? act[item / ipe] : item / ipe;
+            const int hb = ((item % ipe) / nwin) * kRows;
+            const int lo = (item % nwin) * kSlotCap;
+            auto mine = [&](int v) { return v == e; };
+            const int count = compact_slots<kGroupWaves, decltype(mine), uint16_t, true>(nslots, p.ids, slots,
+                                                                                         wave_cnt, mine, lo, kSlotCap);
+            if (count <= lo)
+                continue;                         // whole workgroup (no slots in this window)
+            expert_down_item<RT, A_BF16, FP4, WIDE>(p, y, max_tiles, e, hb,
+                                                    count - lo < kSlotCap ? count - lo : kSlotCap, slots, xs);
+            __syncthreads();                      // the next item rewrites the slot list and the a tiles
+        }
+    } else {
+        // B*k <= kSlotCap: items (expert, row block), every slot in one list
+        int n_items = p.E * nblk;
+        if (wl_off >= 0) {
+            int* mark = smem + wl_off;
+            int* list = mark + p.E;
+            n_items = routed_experts(nslots, p.ids, p.E, mark, list, wave_cnt) * nblk;
+            act = list;
+        }
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            const int e = act ? act[item / nblk] : item / nblk;
+            const int hb = (item % nblk) * kRows;
+            const int count = compact_slots(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
+            if (count == 0)
+                continue;                         // whole workgroup (only without the work list)
+            expert_down_item<RT, A_BF16, FP4, WIDE>(p, y, max_tiles, e, hb, count, slots, xs);
+            __syncthreads();                      // the next item rewrites the slot list and the a tiles
+        }
     }
 }
 
@@ -759,10 +790,11 @@ moe_down_combine_kernel(const float* y, const int32_t* ids, int B, int E, int k,
 
 size_t down_grouped_lds(int B, int k, int E, bool a_bf16, int max_tiles, int row_tiles, bool wide)
 {
-    // slot list (16-bit entries, rounded up to 16 bytes), two buffers of hi
-    // (and lo) tiles, with the wide loads one step region per wavefront, then
-    // the work list
-    const size_t list = ((size_t)B * (size_t)k + 7) / 8 * 16;
+    // slot list (at most kSlotCap 16-bit entries, rounded up to 16 bytes), two
+    // buffers of hi (and lo) tiles, with the wide loads one step region per
+    // wavefront, then the work list
+    const long nslots = (long)B * (long)k;
+    const size_t list = (size_t)((nslots < kSlotCap ? nslots : kSlotCap) + 7) / 8 * 16;
     const size_t stage = wide ? (size_t)kGroupWaves * 16 * (size_t)row_tiles * 16 * sizeof(u32x4) : 0;
     return list + 2 * (a_bf16 ? 1 : 2) * (size_t)max_tiles * kDnUnits * sizeof(u32x4) + stage + worklist_lds(E);
 }
@@ -789,19 +821,27 @@ int down_grouped_tiles(int B, int k, int E, bool a_bf16, int requested, int row_
     return 0;
 }
 
-template <int RT, bool A, bool F, bool W>
-hipError_t launch_expert(dim3 grid, dim3 block, size_t lds, hipStream_t s, const DownArgs& p, float* y,
-                         int max_tiles, int wl_off)
+template <int RT, bool A, bool F, bool W, bool WIN>
+hipError_t launch_expert_win(dim3 grid, dim3 block, size_t lds, hipStream_t s, const DownArgs& p, float* y,
+                             int max_tiles, int wl_off)
 {
     if constexpr (W) {
         // allow dynamic LDS beyond the default 64 KiB, once per device
         const hipError_t attr = set_max_dynamic_lds(
-            reinterpret_cast<const void*>(&moe_down_expert_kernel<RT, A, F, W>), (int)kDnLdsMaxWide);
+            reinterpret_cast<const void*>(&moe_down_expert_kernel<RT, A, F, W, WIN>), (int)kDnLdsMaxWide);
         if (attr != hipSuccess)
             return attr;
     }
-    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F, W>), grid, block, lds, s, p, y, max_tiles, wl_off);
+    hipLaunchKernelGGL((moe_down_expert_kernel<RT, A, F, W, WIN>), grid, block, lds, s, p, y, max_tiles, wl_off);
     return hipGetLastError();
+}
+
+template <int RT, bool A, bool F, bool W>
+hipError_t launch_expert(dim3 grid, dim3 block, size_t lds, hipStream_t s, const DownArgs& p, float* y,
+                         int max_tiles, int wl_off)
+{
+    return (long)p.B * p.k > kSlotCap ? launch_expert_win<RT, A, F, W, true>(grid, block, lds, s, p, y, max_tiles, wl_off)
+                                      : launch_expert_win<RT, A, F, W, false>(grid, block, lds, s, p, y, max_tiles, wl_off);
 }
 
 hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, float* y, int max_tiles,
@@ -813,7 +853,7 @@ hipError_t launch_down_grouped(const DownArgs& p, bool a_bf16, bool out_bf16, fl
         (p.H % (16 * row_tiles)) != 0)
         return hipErrorInvalidValue;
     const int nblk = (p.H + 16 * row_tiles * kGroupWaves - 1) / (16 * row_tiles * kGroupWaves);
-    const long items = (long)p.E * nblk;
+    const long items = (long)p.E * nblk * (((long)p.B * p.k + kSlotCap - 1) / kSlotCap);   // x windows of slots
     const size_t lds = down_grouped_lds(p.B, p.k, p.E, a_bf16, max_tiles, row_tiles, wide);
     if (lds > (wide ? kDnLdsMaxWide : kDnLdsMax))
         return hipErrorInvalidValue;

@@ -557,11 +557,11 @@ __device__ __forceinline__ void gate_up_item(const GateUpArgs& p, int e, int n_b
 // items (expert, block of 16*NW neurons): with the work list (wl_off >= 0, its
 // place in the dynamic LDS) the routed experts' items with a stride of the
 // grid size, else one item per workgroup over all E experts.
-template <bool A_BF16, bool FP4, bool WIDE, int NW = kGroupWaves>
+template <bool A_BF16, bool FP4, bool WIDE, int NW, bool WIN>
 __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl_off)
 {
-    // B*k slot entries of 16 bits (B*k < 65536 wherever this kernel fits in LDS),
-    // the x tiles, then the work list
+    // up to kSlotCap slot entries of 16 bits (B*k < 65536), the x tiles, then
+    // the work list
     extern __shared__ int smem[];
     uint16_t* slots = reinterpret_cast<uint16_t*>(smem);
     __shared__ int wave_cnt[NW];
@@ -573,79 +573,146 @@ __device__ __forceinline__ void gate_up_grouped_body(const GateUpArgs& p, int wl
 
     if ((int)blockIdx.x < nblk) {
         const int n_block = (int)blockIdx.x * kNeurons;
-        const int nbad = compact_slots<NW>(nslots, p.ids, slots, wave_cnt,
-                                       [&](int v) { return (unsigned)v >= (unsigned)E; });
-        for (int q = threadIdx.x; q < nbad * kNeurons; q += blockDim.x) {
-            const int bj = slots[q / kNeurons];
-            const int i = n_block + q % kNeurons;
-            if (i < I) {
-                const size_t idx = inter_index<A_BF16>(bj, i, I);
-                if constexpr (A_BF16)
-                    static_cast<uint16_t*>(p.a)[idx] = 0x7FC0u;
-                else
-                    static_cast<float*>(p.a)[idx] = __builtin_nanf("");
+        auto bad = [&](int v) { return (unsigned)v >= (unsigned)E; };
+        for (int lo = 0;; lo += kSlotCap) {       // in windows of kSlotCap invalid slots
+            int nw;
+            if constexpr (WIN) {
+                const int nbad = compact_slots<NW, decltype(bad), uint16_t, true>(nslots, p.ids, slots, wave_cnt,
+                                                                                  bad, lo, kSlotCap);
+                nw = nbad - lo < kSlotCap ? nbad - lo : kSlotCap;
+            } else {
+                nw = compact_slots<NW>(nslots, p.ids, slots, wave_cnt, bad);   // the whole list at once
             }
+            for (int q = threadIdx.x; q < nw * kNeurons; q += blockDim.x) {
+                const int bj = slots[q / kNeurons];
+                const int i = n_block + q % kNeurons;
+                if (i < I) {
+                    const size_t idx = inter_index<A_BF16>(bj, i, I);
+                    if constexpr (A_BF16)
+                        static_cast<uint16_t*>(p.a)[idx] = 0x7FC0u;
+                    else
+                        static_cast<float*>(p.a)[idx] = __builtin_nanf("");
+                }
+            }
+            __syncthreads();                      // the list is rewritten next
+            if (!WIN || nw < kSlotCap)
+                break;
         }
-        __syncthreads();                          // the list is reused below
     }
-    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((nslots + 7) & ~7));   // x tiles, after the slot list
+    const int cap = WIN ? kSlotCap : nslots;
+    u32x4* xs = reinterpret_cast<u32x4*>(slots + ((cap + 7) & ~7));   // x tiles, after the slot list
     const int* act = nullptr;
-    int n_items = E * nblk;
-    if (wl_off >= 0) {
-        int* mark = smem + wl_off;
-        int* list = mark + E;
-        n_items = routed_experts<NW>(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
-        act = list;
-    }
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int e = act ? act[item / nblk] : item / nblk;
-        const int count = compact_slots<NW>(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
-        if (count == 0)
-            continue;                             // whole workgroup (only without the work list)
-        gate_up_item<A_BF16, FP4, WIDE, NW>(p, e, (item % nblk) * kNeurons, count, slots, xs);
-        __syncthreads();                          // the next item rewrites the slot list and the x tiles
+    if constexpr (WIN) {
+        // items (expert, neuron block, window of kSlotCap slots)
+        int nwin = (nslots + kSlotCap - 1) / kSlotCap;   // without the work list: as many as B*k could need
+        int n_items;
+        if (wl_off >= 0) {
+            int* mark = smem + wl_off;
+            int* list = mark + E;
+            n_items = routed_experts_windows<NW>(nslots, p.ids, E, mark, list, wave_cnt, nwin) * nblk * nwin;
+            act = list;
+        } else {
+            n_items = E * nblk * nwin;
+        }
+        const int ipe = nblk * nwin;
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            const int e = act ? act[item / ipe] : item / ipe;
+            const int lo = (item % nwin) * kSlotCap;
+            auto mine = [&](int v) { return v == e; };
+            const int count = compact_slots<NW, decltype(mine), uint16_t, true>(nslots, p.ids, slots, wave_cnt, mine,
+                                                                                lo, kSlotCap);
+            if (count <= lo)
+                continue;                         // whole workgroup (no slots in this window)
+            gate_up_item<A_BF16, FP4, WIDE, NW>(p, e, ((item % ipe) / nwin) * kNeurons,
+                                                count - lo < kSlotCap ? count - lo : kSlotCap, slots, xs);
+            __syncthreads();                      // the next item rewrites the slot list and the x tiles
+        }
+    } else {
+        // items (expert, neuron block), every slot in one list
+        int n_items = E * nblk;
+        if (wl_off >= 0) {
+            int* mark = smem + wl_off;
+            int* list = mark + E;
+            n_items = routed_experts<NW>(nslots, p.ids, E, mark, list, wave_cnt) * nblk;
+            act = list;
+        }
+        for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+            const int e = act ? act[item / nblk] : item / nblk;
+            const int count = compact_slots<NW>(nslots, p.ids, slots, wave_cnt, [&](int v) { return v == e; });
+            if (count == 0)
+                continue;                         // whole workgroup (only without the work list)
+            gate_up_item<A_BF16, FP4, WIDE, NW>(p, e, (item % nblk) * kNeurons, count, slots, xs);
+            __syncthreads();                      // the next item rewrites the slot list and the x tiles
+        }
     }
 }
 
-template <bool A_BF16, bool FP4>
+// WIN: the slots of an expert taken in windows of kSlotCap (B*k > kSlotCap)
+template <bool A_BF16, bool FP4, bool WIN>
 __global__ void __launch_bounds__(kGroupWaves * kWave)
 moe_gate_up_grouped_kernel(GateUpArgs p, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, false>(p, wl_off);
+    gate_up_grouped_body<A_BF16, FP4, false, kGroupWaves, WIN>(p, wl_off);
 }
 
 // The wide loads need 8 KiB of LDS per wavefront: two workgroups of 4
 // wavefronts share a CU, or one of 8 (items of 128 neurons, each x tile
 // loaded once for twice the rows); the register budget is set to match (two
 // wavefronts per SIMD).
-template <bool A_BF16, bool FP4, int NW = kGroupWaves>
+template <bool A_BF16, bool FP4, int NW, bool WIN>
 __global__ void __launch_bounds__(NW * kWave, 8 / NW)
 moe_gate_up_grouped_wide_kernel(GateUpArgs p, int wl_off)
 {
-    gate_up_grouped_body<A_BF16, FP4, true, NW>(p, wl_off);
+    gate_up_grouped_body<A_BF16, FP4, true, NW, WIN>(p, wl_off);
+}
+
+// The slot list holds all B*k entries while they fit in 64 KiB of LDS with the
+// x tiles and the work list (B*k up to about 16000); beyond that, windows of
+// kSlotCap. (Windows at smaller batches were measured slower here: each
+// workgroup first counts the slots of every expert.)
+static bool gate_up_windowed(int B, int k, int E)
+{
+    const long nslots = (long)B * (long)k;
+    return nslots > kSlotCap &&
+           (size_t)(nslots + 7) / 8 * 16 + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) + worklist_lds(E) > 65536;
 }
 
 size_t gate_up_grouped_lds(int B, int k, int E, bool wide, int nw)
 {
-    // slot list (16-bit entries, rounded up to 16 bytes), two buffers of x
-    // tiles, with the wide loads one 8 KiB region per wavefront, then the work list
-    const size_t list = ((size_t)B * (size_t)k + 7) / 8 * 16;
+    // slot list (16-bit entries, rounded up to 16 bytes; kSlotCap of them with
+    // windows), two buffers of x tiles, with the wide loads one 8 KiB region
+    // per wavefront, then the work list
+    const long nslots = gate_up_windowed(B, k, E) ? kSlotCap : (long)B * (long)k;
+    const size_t list = (size_t)(nslots + 7) / 8 * 16;
     return list + 2 * (size_t)kTiles * kXUnitsPerTile * sizeof(u32x4) +
            (wide ? (size_t)nw * kWideUnitsPerWave * sizeof(u32x4) : 0) + worklist_lds(E);
 }
 
-template <bool A_BF16, bool FP4, int NW>
+template <bool A_BF16, bool FP4, int NW, bool WIN>
 static hipError_t launch_wide(dim3 grid, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off)
 {
     // allow dynamic LDS beyond the default 64 KiB, once per device: up to
     // 64 KiB for the slot list and x tiles plus the wide-load regions
     const hipError_t attr =
-        set_max_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW>),
+        set_max_dynamic_lds(reinterpret_cast<const void*>(&moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW, WIN>),
                             65536 + NW * kWideUnitsPerWave * (int)sizeof(u32x4));
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW>), grid, dim3(NW * kWave), lds, s, p,
+    hipLaunchKernelGGL((moe_gate_up_grouped_wide_kernel<A_BF16, FP4, NW, WIN>), grid, dim3(NW * kWave), lds, s, p,
                        wl_off);
+    return hipGetLastError();
+}
+
+template <bool A_BF16, bool FP4, bool WIDE, bool WIN>
+hipError_t launch_grouped_win(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off,
+                              int nw)
+{
+    if constexpr (WIDE) {
+        return nw == 8 ? launch_wide<A_BF16, FP4, 8, WIN>(grid, lds, s, p, wl_off)
+                       : launch_wide<A_BF16, FP4, kGroupWaves, WIN>(grid, lds, s, p, wl_off);
+    } else {
+        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4, WIN>), grid, block, lds, s, p, wl_off);
+    }
     return hipGetLastError();
 }
 
@@ -653,13 +720,8 @@ template <bool A_BF16, bool FP4, bool WIDE>
 hipError_t launch_grouped(dim3 grid, dim3 block, size_t lds, hipStream_t s, const GateUpArgs& p, int wl_off,
                           int nw)
 {
-    if constexpr (WIDE) {
-        return nw == 8 ? launch_wide<A_BF16, FP4, 8>(grid, lds, s, p, wl_off)
-                       : launch_wide<A_BF16, FP4, kGroupWaves>(grid, lds, s, p, wl_off);
-    } else {
-        hipLaunchKernelGGL((moe_gate_up_grouped_kernel<A_BF16, FP4>), grid, block, lds, s, p, wl_off);
-    }
-    return hipGetLastError();
+    return gate_up_windowed(p.B, p.k, p.E) ? launch_grouped_win<A_BF16, FP4, WIDE, true>(grid, block, lds, s, p, wl_off, nw)
+                                           : launch_grouped_win<A_BF16, FP4, WIDE, false>(grid, block, lds, s, p, wl_off, nw);
 }
 
 hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning& t, hipStream_t s)
@@ -677,7 +739,9 @@ hipError_t launch_gate_up_grouped(const GateUpArgs& p, bool a_bf16, const Tuning
     const int nw = !wide ? kGroupWaves
                          : t.gu_waves == 8 || (t.gu_waves == 0 && (long)p.B * p.k >= 32L * p.E) ? 8 : kGroupWaves;
     const int nblk = (p.I + 16 * nw - 1) / (16 * nw);
-    const long items = (long)p.E * nblk;
+    // items: (expert, neuron block[, window of slots]); without the work list
+    // as many windows as B*k slots could need
+    const long items = (long)p.E * nblk * (gate_up_windowed(p.B, p.k, p.E) ? ((long)p.B * p.k + kSlotCap - 1) / kSlotCap : 1);
     const size_t lds = gate_up_grouped_lds(p.B, p.k, p.E, wide, nw);
     const size_t wl = worklist_lds(p.E);
     // with the work list: at most gu_grid workgroups (and at least one per

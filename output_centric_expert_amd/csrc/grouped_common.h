@@ -74,12 +74,23 @@ __device__ __forceinline__ float block_scale(u32x2 sb, int row_slot, int kb)
 }
 
 // Deterministic compaction: slots[0..count) = the indices t < n (in increasing
-// order) with pred(ids[t]), stored as S (int, or uint16_t for n < 65536). All
-// threads of the workgroup (NW wavefronts) must call it. The ids of up to four
-// 256-slot chunks are loaded together, so the list costs one round trip to L2
-// per 1024 slots.
-template <int NW = kGroupWaves, typename Pred, typename S = int>
-__device__ __forceinline__ int compact_slots(int n, const int* ids, S* slots, int* wave_cnt, Pred pred)
+// order) with pred(ids[t]), stored as S (int, or uint16_t for n < 65536); with
+// WIN, only those of rank lo .. lo+cap-1 are stored (at slots[rank - lo]).
+// Returns the count of all of them. All threads of the workgroup (NW
+// wavefronts) must call it. The ids of up to four 256-slot chunks are loaded
+// together, so the list costs one round trip to L2 per 1024 slots.
+//
+// Windows of slots (the expert-major down once B*k > kSlotCap, the grouped
+// gate/up once all B*k entries no longer fit in its LDS): at most kSlotCap
+// slots of an expert are in LDS at a time, and an expert with more is taken in
+// windows of kSlotCap (a multiple of the 16 slots of a tile, so each tile holds
+// the same slots as with one list): an item is (expert, block, window), with as
+// many windows per expert as the busiest routed expert needs (one unless an
+// expert has more than kSlotCap).
+constexpr int kSlotCap = 4096;
+template <int NW = kGroupWaves, typename Pred, typename S = int, bool WIN = false>
+__device__ __forceinline__ int compact_slots(int n, const int* ids, S* slots, int* wave_cnt, Pred pred, int lo = 0,
+                                             int cap = 0)
 {
     constexpr int kChunk = NW * kWave;
     constexpr int kBatch = 4;
@@ -109,8 +120,14 @@ __device__ __forceinline__ int compact_slots(int n, const int* ids, S* slots, in
             int off = total;
             for (int q = 0; q < w; ++q)
                 off += wave_cnt[q];
-            if (f)
-                slots[off + before] = (S)t;
+            if constexpr (WIN) {
+                const int rank = off + before;
+                if (f && rank >= lo && rank - lo < cap)
+                    slots[rank - lo] = (S)t;
+            } else {
+                if (f)
+                    slots[off + before] = (S)t;
+            }
             int sum = 0;
             for (int q = 0; q < NW; ++q)
                 sum += wave_cnt[q];
@@ -160,6 +177,58 @@ __device__ __forceinline__ int routed_experts(int n_slots, const int* ids, int E
                 mark[v[c]] = 1;                   // equal values: any order of the stores
     }
     __syncthreads();
+    return compact_slots<NW>(E, mark, act, wave_cnt, [](int v) { return v != 0; });
+}
+
+// routed_experts, and the window count of the items: 1 when n_slots <= kSlotCap;
+// otherwise the slots of each expert are counted with LDS atomic adds into mark
+// (exact in any order) and the count is ceil(largest count / kSlotCap). All
+// threads of the workgroup must call it.
+template <int NW = kGroupWaves>
+__device__ __forceinline__ int routed_experts_windows(int n_slots, const int* ids, int E, int* mark, int* act,
+                                                      int* wave_cnt, int& nwin)
+{
+    constexpr int kChunk = NW * kWave;
+    const int tid = threadIdx.x;
+    const bool counted = n_slots > kSlotCap;      // else no expert can have more than one window
+    for (int t = tid; t < E; t += kChunk)
+        mark[t] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_slots; base += 4 * kChunk) {
+        int v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int t = base + c * kChunk + tid;
+            v[c] = t < n_slots ? ids[t] : -1;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if ((unsigned)v[c] < (unsigned)E) {
+                if (counted)
+                    atomicAdd(&mark[v[c]], 1);
+                else
+                    mark[v[c]] = 1;
+            }
+    }
+    __syncthreads();
+    nwin = 1;
+    if (!counted)
+        return compact_slots<NW>(E, mark, act, wave_cnt, [](int v) { return v != 0; });
+    int m = 0;
+    for (int t = tid; t < E; t += kChunk)
+        m = mark[t] > m ? mark[t] : m;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const int o = __shfl_xor(m, off);
+        m = o > m ? o : m;
+    }
+    if ((tid & (kWave - 1)) == 0)
+        wave_cnt[tid / kWave] = m;
+    __syncthreads();
+    int mx = 0;
+    for (int q = 0; q < NW; ++q)
+        mx = wave_cnt[q] > mx ? wave_cnt[q] : mx;
+    __syncthreads();                              // wave_cnt is reused by the compaction
+    nwin = mx > kSlotCap ? (mx + kSlotCap - 1) / kSlotCap : 1;
     return compact_slots<NW>(E, mark, act, wave_cnt, [](int v) { return v != 0; });
 }
 

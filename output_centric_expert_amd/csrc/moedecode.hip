@@ -69,9 +69,9 @@ bool pick(const moed_tuning* user, moed::Tuning* t)
 // 327 us), once its items (expert, 64 neurons) fill the 512 workgroup slots
 // of the chip (one token: 47 vs 41 us). Hence the rule: grouped when
 // 4*B*k >= 3*E, or when H >= 6144 and min(B*k, E)*ceil(I/64) >= 512 (H between
-// 4096 and 6144 unmeasured). Its slot list (16-bit entries) must fit in 64 KiB
-// of LDS with the x tiles (the wide loads add 32-64 KiB, within the 160 KiB of
-// a workgroup).
+// 4096 and 6144 unmeasured). Its slot list (16-bit entries; past about 16000
+// of them, windows of 4096) fits in 64 KiB of LDS with the x tiles (the wide
+// loads add 32-64 KiB, within the 160 KiB of a workgroup) for B*k up to 65535.
 bool use_grouped(const moed::Tuning& t, int B, int E, int k, int H, int I, int wfmt)
 {
     (void)wfmt;                                   // both weight formats have a grouped kernel

@@ -520,26 +520,80 @@ def test_expert_major_down_without_partials_is_per_output():
         md.set_default_tuning(None)
 
 
-def test_long_slot_list_takes_fewer_tiles():
-    """B*k = 8192 slots: the expert-major down's slot list (16-bit entries) takes 16 KB of LDS, so
-    it takes two tiles of float32 a per pass instead of three; the same bits as asking for two."""
+def test_long_slot_list_keeps_three_tiles():
+    """B*k = 8192 slots: the expert-major down holds at most 4096 16-bit slot entries in LDS at a
+    time (8 KB), so three tiles of float32 a per pass still fit; the same bits as asking for two
+    or three."""
     L = small(1024, 8, 8, 64, 64, seed=31)
     toks = [0, 1, 511, 1023]
     out = run(L)
     ref, _ = oracle_tokens(L, toks)
-    check_f32(out[toks], ref, "B=600")
-    md.set_default_tuning("dn_tiles=2")
-    try:
-        assert torch.equal(run(L), out)
-    finally:
-        md.set_default_tuning(None)
+    check_f32(out[toks], ref, "B=1024")
+    for form in ("dn_tiles=2", "dn_tiles=3"):
+        md.set_default_tuning(form)
+        try:
+            assert torch.equal(run(L), out), form
+        finally:
+            md.set_default_tuning(None)
+
+
+def test_slot_windows():
+    """E = 2, k = 2, B = 9000: 18000 slots, past what the grouped gate/up holds in one list, and
+    each expert has about 9000 of them, more than the 4096 one item holds, so both grouped kernels
+    take each expert's slots in three windows (five without the work list, the last two empty).
+    One out-of-range id at token 4500. The intermediate is the same bits with and without the
+    work list and for 4 and 8 wavefronts; the layer output is the same bits with and without the
+    down's work list, NaN on token 4500 and within tolerance of the oracle on tokens of all three
+    windows. A second case puts 4200 out-of-range ids in the batch: the gate/up's invalid-slot
+    pass also goes in windows and marks every one of them."""
+    B, E, k, H, I = 9000, 2, 2, 512, 512
+    L = small(B, E, k, H, I, seed=51)
+    ids = L.ids.copy()
+    ids[4500, 0] = E
+    x, _, w = md.layer_device_inputs(L)
+    idd = torch.as_tensor(ids, dtype=torch.int32).cuda().contiguous()
+    got = {}
+    for form in ("gu_group=1,gu_waves=4", "gu_group=1,gu_waves=8", "gu_group=1,gu_grid=0",
+                 "gu_group=1,gu_waves=8,gu_grid=3"):
+        say(f"slot windows {form}")
+        got[form] = md.moe_decode_gate_up(x, idd, L.wg_q, L.wg_s, L.wu_q, L.wu_s, tuning=form)
+    torch.cuda.synchronize()
+    ref_a = got["gu_group=1,gu_waves=4"]
+    for form, a in got.items():
+        assert torch.equal(a.view(torch.int32), ref_a.view(torch.int32)), form
+    assert torch.isnan(ref_a[4500, 0]).all()
+    outs = {}
+    for form in ("gu_group=1,dn_group=1", "gu_group=1,dn_group=1,dn_grid=0"):
+        say(f"slot windows {form}")
+        outs[form] = md.moe_decode(x, idd, w, L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s,
+                                   out_dtype=torch.float32, tuning=form)
+    torch.cuda.synchronize()
+    out = outs["gu_group=1,dn_group=1"]
+    for form, o in outs.items():
+        assert torch.equal(o.view(torch.int32), out.view(torch.int32)), form
+    assert torch.isnan(out[4500]).all()
+    good = [0, 1, 2047, 4095, 4096, 4499, 4501, 8191, 8192, B - 1]
+    assert not torch.isnan(out[good]).any()
+    ref, _ = oracle_tokens(L, good, ids=ids)
+    check_f32(out[good], ref, "slot windows")
+
+    ids2 = L.ids.copy()
+    ids2[:4200, 1] = -1
+    idd2 = torch.as_tensor(ids2, dtype=torch.int32).cuda().contiguous()
+    a2 = md.moe_decode_gate_up(x, idd2, L.wg_q, L.wg_s, L.wu_q, L.wu_s, tuning="gu_group=1")
+    torch.cuda.synchronize()
+    bad = torch.zeros(B, k, dtype=torch.bool)
+    bad[:4200, 1] = True
+    nan_rows = torch.isnan(a2.cpu()).all(dim=2)
+    assert torch.equal(nan_rows, bad)
+    assert not torch.isnan(a2.cpu()[~bad]).any()
 
 
 def test_slot_list_beyond_lds_falls_back():
-    """B*k = 25600 slots: the slot list alone takes 50 KB of LDS even with 16-bit entries, so
-    neither grouped kernel fits and the layer keeps the per-slot gate/up and the per-output down."""
-    L = small(3200, 8, 8, 64, 64, seed=33)
-    toks = [0, 1, 1600, 3199]
+    """B*k = 65600 slots: past what 16-bit slot entries can name, so neither grouped kernel is
+    used and the layer keeps the per-slot gate/up and the per-output down."""
+    L = small(8200, 8, 8, 64, 64, seed=33)
+    toks = [0, 1, 4100, 8199]
     out = run(L)
     md.set_default_tuning("gu_group=0,dn_group=0")
     try:
@@ -547,7 +601,7 @@ def test_slot_list_beyond_lds_falls_back():
     finally:
         md.set_default_tuning(None)
     ref, _ = oracle_tokens(L, toks)
-    check_f32(out[toks], ref, "B=1600 fallback")
+    check_f32(out[toks], ref, "B=8200 fallback")
 
 
 def test_partials_untouched_below_threshold():
