@@ -140,7 +140,9 @@ size_t moed_workspace_bytes(int B, int k, int H, int I, int inter_dtype);
  * token's k partials in slot order and stores the output once. Smaller batches
  * use the one-wavefront-per-output down of moe_decode_down(). Likewise the
  * gate/up step runs expert-grouped (MFMA) once 4*B*k >= 3*E, or for rows of
- * H >= 6144 values once min(B*k, E)*ceil(I/64) >= 512.
+ * H >= 6144 values once min(B*k, E)*ceil(I/64) >= 512. Both large-batch forms
+ * hold slot indices in 16 bits: at B*k >= 65536 the layer keeps the per-slot
+ * gate/up and the per-output down (same results within the tolerance, slower).
  *
  * Exact range of the large-batch kernels: they decode a weight to BF16 with
  * its block scale folded into the conversion, which is exact while every
