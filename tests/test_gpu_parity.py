@@ -589,6 +589,30 @@ def test_slot_windows():
     assert not torch.isnan(a2.cpu()[~bad]).any()
 
 
+@pytest.mark.parametrize("wformat", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("inter", ["f32", "bf16"])
+def test_slot_windows_batch_invariance(wformat, inter):
+    """Windowed and whole-list forms give the same bits: B = 9000, E = 2, k = 2 takes both grouped
+    kernels in windows of 4096 slots; the first and the last 1024 tokens alone (2048 slots, one
+    list) must give the same output bits for those tokens, in both weight formats and with a
+    float32 or BF16 intermediate."""
+    B, E, k, H, I = 9000, 2, 2, 512, 512
+    L = synth.make_layer(synth.LayerShape("win", B, E, k, H, I), seed=52, device="cuda", wformat=wformat)
+    x, ids, w = md.layer_device_inputs(L)
+    dt = torch.float32 if inter == "f32" else torch.bfloat16
+    args = (L.wg_q, L.wg_s, L.wu_q, L.wu_s, L.wd_q, L.wd_s)
+    say(f"windows batch invariance {wformat} {inter}")
+    full = md.moe_decode(x, ids, w, *args, out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
+    for lo, hi in ((0, 1024), (B - 1024, B)):
+        part = md.moe_decode(x[lo:hi].contiguous(), ids[lo:hi].contiguous(), w[lo:hi].contiguous(), *args,
+                             out_dtype=torch.float32, inter_dtype=dt, wformat=wformat)
+        torch.cuda.synchronize()
+        assert torch.equal(part.view(torch.int32), full[lo:hi].view(torch.int32)), (wformat, inter, lo)
+    toks = [0, 4500, B - 1]
+    ref, _ = oracle_tokens(L, toks, wformat=wformat)
+    check_f32(full[toks], ref, f"windows {wformat} {inter}", tol=TOL if inter == "f32" else 5e-2)   # BF16 a: the reported variant's bound
+
+
 def test_slot_list_beyond_lds_falls_back():
     """B*k = 65600 slots: past what 16-bit slot entries can name, so neither grouped kernel is
     used and the layer keeps the per-slot gate/up and the per-output down."""
